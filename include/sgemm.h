@@ -1,0 +1,142 @@
+/*
+ * sgemm.h - single-precision general matrix multiply for AMD Instinct MI355X (gfx950).
+ *
+ * Computes C <- alpha * A * B + beta * C on row-major fp32 matrices:
+ *
+ *     A(i,k) = A[i*lda + k]    0 <= i < M, 0 <= k < K
+ *     B(k,j) = B[k*ldb + j]    0 <= k < K, 0 <= j < N
+ *     C(i,j) = C[i*ldc + j]    0 <= i < M, 0 <= j < N
+ *
+ * The operation is the BLAS-style form of the tiled kernels on the pages: the
+ * product accumulated in a register tile, then alpha times it plus beta times the
+ * old C, with C not read when beta is zero ("Micro_gemm_4x4 - cuBLAS micro GEMM
+ * skeleton", section 2 for the signature and section 9 for the final C write).
+ * Leading dimensions generalise the pages' packed A[row*K + k] indexing the way
+ * the GPT-2 post's kernel takes strided views ("GPU Target - GPT-2 on the GPU",
+ * section "Tiled matrix multiplication").
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are device pointers (hipMalloc or torch CUDA tensors). The library
+ *    never allocates, copies, frees or keeps them; the caller keeps every buffer
+ *    alive until the work queued on `stream` has finished.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    Calls are asynchronous: they queue one kernel (or none) and return.
+ *  - Only the M x N window of C is written. Entries of C with column >= N in the
+ *    ldc gap, and A and B, are never written.
+ *  - When beta == 0, C is write-only: NaN or Inf already in C does not propagate.
+ *    When alpha == 0 or K == 0, A and B are not read and C <- beta * C.
+ *  - C must not overlap A or B.
+ *  - Any alignment of at least 4 bytes is accepted. When A, B and C are 16-byte
+ *    aligned, lda, ldb, ldc are multiples of 4 and so are N and K, the kernels use
+ *    128-bit loads and stores; otherwise they use 32-bit ones. This is never an error.
+ *  - Results match the exact product within 4*max(K,1)*2^-24*(|alpha|*sum_k|a_ik*b_kj|
+ *    + |beta*c_ij|) per entry. For one configuration, sizes and alignment, results
+ *    are bitwise reproducible from run to run.
+ *
+ * Return values: 0 on success; -i when argument i (1-based, in declaration order)
+ * is invalid; SGEMM_ERROR_TOO_LARGE or SGEMM_ERROR_BAD_CONFIG for the cases named
+ * below; a positive hipError_t when the kernel launch fails. Errors raised while
+ * the kernel runs surface at the caller's next synchronisation. Nothing throws.
+ */
+#ifndef TILED_FP32_GEMM_SGEMM_H
+#define TILED_FP32_GEMM_SGEMM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGEMM_SUCCESS 0
+/* The tile grid of the problem does not fit one launch (more than 2^31-1 tiles). */
+#define SGEMM_ERROR_TOO_LARGE (-100)
+/* sgemm_ex: the configuration id is not in [-1, sgemm_config_count()). */
+#define SGEMM_ERROR_BAD_CONFIG (-101)
+
+/*
+ * C <- alpha * A * B + beta * C (row-major fp32), on `stream`.
+ *
+ * Arguments, by 1-based position (the number returned as -i when invalid):
+ *   1 M, 2 N, 3 K  >= 0. M == 0 or N == 0 returns 0 without touching any pointer.
+ *   4 alpha        any float.
+ *   5 A            device pointer; may be NULL only if A is not read (M == 0, N == 0,
+ *                  K == 0 or alpha == 0).
+ *   6 lda          >= max(1, K).
+ *   7 B            device pointer; NULL allowed under the same condition as A.
+ *   8 ldb          >= max(1, N).
+ *   9 beta         any float.
+ *  10 C            device pointer; NULL allowed only if M == 0 or N == 0.
+ *  11 ldc          >= max(1, N).
+ *  12 stream       hipStream_t or NULL.
+ */
+int sgemm(int M, int N, int K, float alpha,
+          const float *A, int lda,
+          const float *B, int ldb,
+          float beta, float *C, int ldc,
+          void *stream);
+
+/*
+ * Same as sgemm, with the kernel configuration chosen by the caller: `config` in
+ * [0, sgemm_config_count()) forces that configuration, -1 picks it as sgemm does.
+ * Argument positions in error codes are those of sgemm (config is not counted).
+ * Used by tests and tuning sweeps.
+ */
+int sgemm_ex(int config, int M, int N, int K, float alpha,
+             const float *A, int lda,
+             const float *B, int ldb,
+             float beta, float *C, int ldc,
+             void *stream);
+
+/*
+ * Strided-batched form: for b in [0, batch), C_b <- alpha * A_b * B_b + beta * C_b with
+ * A_b = A + b*strideA, B_b = B + b*strideB, C_b = C + b*strideC (strides in floats).
+ * All batches share M, N, K, the leading dimensions and the scalars. The batched
+ * product of the GPT-2 post's attention heads, which adds a third grid dimension
+ * indexed by batch ("GPU Target - GPT-2 on the GPU", section "Tiled matrix
+ * multiplication").
+ *
+ * Arguments by position: 1 M, 2 N, 3 K, 4 alpha, 5 A, 6 lda, 7 strideA, 8 B, 9 ldb,
+ * 10 strideB, 11 beta, 12 C, 13 ldc, 14 strideC, 15 batch, 16 stream.
+ * batch >= 0 and at most 65535; batch == 0 returns 0. strideA, strideB >= 0 (0 reuses
+ * one matrix for all batches). strideC must be >= (M-1)*ldc + N so the C windows do
+ * not overlap, unless batch == 1. Other rules as for sgemm.
+ */
+int sgemm_strided_batched(int M, int N, int K, float alpha,
+                          const float *A, int lda, long long strideA,
+                          const float *B, int ldb, long long strideB,
+                          float beta, float *C, int ldc, long long strideC,
+                          int batch, void *stream);
+
+/* Number of kernel configurations compiled into the library. */
+int sgemm_config_count(void);
+
+/* Short name of configuration `config` (e.g. "mfma_256x256x16_w2x4"), or NULL if out of range. */
+const char *sgemm_config_name(int config);
+
+/*
+ * The configuration sgemm would use for these arguments (host logic only; no GPU
+ * call). Returns an id in [0, sgemm_config_count()), or -1 when no kernel would
+ * run (M == 0 or N == 0) or the quick-return scaling kernel would (K == 0 or alpha == 0
+ * counts as -1 too).
+ */
+int sgemm_select_config(int M, int N, int K, float alpha,
+                        const float *A, int lda,
+                        const float *B, int ldb,
+                        const float *C, int ldc);
+
+/*
+ * Launch shape of configuration `config` for an M x N x K product (host logic only).
+ * Writes grid[3] and block[3] (dim3 order x, y, z). Returns 0, SGEMM_ERROR_BAD_CONFIG,
+ * SGEMM_ERROR_TOO_LARGE, or -1/-2/-3 for a negative M/N/K.
+ */
+int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3]);
+
+/* Static message for a status code returned by any entry point. */
+const char *sgemm_status_string(int status);
+
+/* Library version string. */
+const char *sgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILED_FP32_GEMM_SGEMM_H */

@@ -1,0 +1,170 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/sgemm.h
+declares, and its host logic (argument validation, quick returns, configuration
+choice, launch shapes) behaves as documented. No call here reaches a kernel
+launch: every case is rejected or returns before touching the GPU.
+"""
+
+import os
+import re
+
+import pytest
+
+import tiled_fp32_gemm_02_amd as sg
+from tiled_fp32_gemm_02_amd import build as sgbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm.h")
+BAD = 0xDEAD0  # a pointer value that must never be dereferenced in these tests
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    sgbuild.ensure_built()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_exports_every_declared_function():
+    import ctypes
+    lib = ctypes.CDLL(sg.lib_path())
+    names = declared_functions()
+    assert set(names) == set(sg.EXPORTED), names
+    for name in names:
+        assert hasattr(lib, name), f"libsgemm.so does not export {name}"
+
+
+def test_version_and_configs():
+    assert "gfx950" in sg.sgemm_version()
+    names = sg.configs()
+    assert len(names) == sg.sgemm_config_count() >= 2
+    assert names[0] == "tile16"
+    assert all(n.startswith("mfma_") for n in names[1:])
+    assert sg.sgemm_config_name(-1) is None and sg.sgemm_config_name(len(names)) is None
+
+
+@pytest.mark.parametrize("args,code", [
+    # (M, N, K, alpha, A, lda, B, ldb, beta, C, ldc)
+    ((-1, 4, 4, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4), -1),
+    ((4, -1, 4, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4), -2),
+    ((4, 4, -1, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4), -3),
+    ((4, 4, 4, 1.0, None, 4, BAD, 4, 0.0, BAD, 4), -5),
+    ((4, 4, 8, 1.0, BAD, 7, BAD, 4, 0.0, BAD, 4), -6),
+    ((4, 4, 0, 1.0, BAD, 0, BAD, 4, 0.0, BAD, 4), -6),   # lda >= max(1, K)
+    ((4, 4, 4, 1.0, BAD, 4, None, 4, 0.0, BAD, 4), -7),
+    ((4, 5, 4, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 5), -8),
+    ((4, 4, 4, 1.0, BAD, 4, BAD, 4, 0.0, None, 4), -10),
+    ((4, 5, 4, 1.0, BAD, 4, BAD, 5, 0.0, BAD, 4), -11),
+    ((4, 0, 4, 1.0, BAD, 4, BAD, 0, 0.0, BAD, 1), -8),   # ldb >= 1 even when N == 0
+])
+def test_invalid_arguments(args, code):
+    assert sg.sgemm(*args) == code
+    assert sg.sgemm_ex(-1, *args) == code
+    assert sg.sgemm_status_string(code) == f"invalid argument {-code}"
+
+
+def test_first_invalid_argument_wins():
+    assert sg.sgemm(-1, -1, -1, 1.0, None, 0, None, 0, 0.0, None, 0) == -1
+    assert sg.sgemm(3, 3, -1, 1.0, None, 0, None, 0, 0.0, None, 0) == -3
+
+
+def test_null_pointers_allowed_when_unread():
+    # empty result: nothing is touched
+    assert sg.sgemm(0, 7, 5, 1.0, None, 5, None, 7, 0.5, None, 7) == 0
+    assert sg.sgemm(7, 0, 5, 1.0, None, 5, None, 1, 0.5, None, 1) == 0
+    # A and B unread when alpha == 0 or K == 0, but C is still required
+    assert sg.sgemm(4, 4, 0, 1.0, None, 1, None, 4, 0.0, None, 4) == -10
+    assert sg.sgemm(4, 4, 3, 0.0, None, 3, None, 4, 0.0, None, 4) == -10
+
+
+def test_bad_config_id():
+    args = (4, 4, 4, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4)
+    assert sg.sgemm_ex(-2, *args) == sg.SGEMM_ERROR_BAD_CONFIG
+    assert sg.sgemm_ex(sg.sgemm_config_count(), *args) == sg.SGEMM_ERROR_BAD_CONFIG
+    assert "configuration" in sg.sgemm_status_string(sg.SGEMM_ERROR_BAD_CONFIG)
+
+
+@pytest.mark.parametrize("args,code", [
+    # (M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch)
+    ((-1, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, 2), -1),
+    ((4, 4, 4, 1.0, None, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, 2), -5),
+    ((4, 4, 8, 1.0, BAD, 7, 32, BAD, 4, 16, 0.0, BAD, 4, 16, 2), -6),
+    ((4, 4, 4, 1.0, BAD, 4, -1, BAD, 4, 16, 0.0, BAD, 4, 16, 2), -7),
+    ((4, 4, 4, 1.0, BAD, 4, 16, None, 4, 16, 0.0, BAD, 4, 16, 2), -8),
+    ((4, 5, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 5, 20, 2), -9),
+    ((4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, -4, 0.0, BAD, 4, 16, 2), -10),
+    ((4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, None, 4, 16, 2), -12),
+    ((4, 5, 4, 1.0, BAD, 4, 16, BAD, 5, 20, 0.0, BAD, 4, 20, 2), -13),
+    ((4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 15, 2), -14),  # C windows overlap
+    ((4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, -1), -15),
+    ((4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, 65536), -15),
+])
+def test_batched_invalid_arguments(args, code):
+    assert sg.sgemm_strided_batched(*args) == code
+
+
+def test_batched_quick_returns():
+    assert sg.sgemm_strided_batched(4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, 0) == 0
+    assert sg.sgemm_strided_batched(0, 4, 4, 1.0, None, 4, 0, None, 4, 0, 0.0, None, 4, 0, 9) == 0
+
+
+def test_launch_shape_tile16_matches_gpt2_post():
+    # The GPT-2 post covers a 64 x 256 matrix with a 4 x 16 grid of 16 x 16-thread
+    # blocks ("GPU Target", section "From loops to kernels"); its matmul kernel puts n
+    # on grid x and m on grid y ("Tiled matrix multiplication"), both ceil-divided.
+    assert sg.sgemm_launch_shape(0, 64, 256, 16) == (0, (16, 4, 1), (16, 16, 1))
+    assert sg.sgemm_launch_shape(0, 65, 257, 3) == (0, (17, 5, 1), (16, 16, 1))
+    assert sg.sgemm_launch_shape(0, 1, 1, 1) == (0, (1, 1, 1), (16, 16, 1))
+
+
+def test_launch_shape_mfma():
+    for cid, name in enumerate(sg.configs()):
+        if not name.startswith("mfma_"):
+            continue
+        bm, bn, _ = (int(x) for x in name.split("_")[1].split("x"))
+        wm, wn = (int(x) for x in name.split("_w")[1].split("x"))
+        for M, N in [(4096, 4096), (1000, 1537), (1, 1), (bm + 1, bn - 1)]:
+            st, grid, block = sg.sgemm_launch_shape(cid, M, N, 64)
+            assert st == 0
+            assert grid == (-(-M // bm) * -(-N // bn), 1, 1)
+            assert block == (wm * wn * 64, 1, 1)
+        assert sg.sgemm_launch_shape(cid, -1, 4, 4)[0] == -1
+    st, _, _ = sg.sgemm_launch_shape(1, 2**31 - 1, 2**31 - 1, 1)
+    assert st == sg.SGEMM_ERROR_TOO_LARGE
+    assert sg.sgemm_launch_shape(99, 4, 4, 4)[0] == sg.SGEMM_ERROR_BAD_CONFIG
+
+
+def test_select_config():
+    names = sg.configs()
+    sel = lambda M, N, K=64, alpha=1.0: sg.sgemm_select_config(M, N, K, alpha, BAD, K, BAD, N, BAD, N)
+    assert sel(0, 5) == -1 and sel(5, 0) == -1 and sel(5, 5, K=0) == -1 and sel(5, 5, alpha=0.0) == -1
+    assert names[sel(4096, 4096, 4096)] == "mfma_256x256x16_w2x4"   # 256 tiles: one per CU
+    # each choice still gives at least 256 workgroups when the problem allows it
+    for M, N in [(1024, 1024), (1024, 2304), (1024, 3072), (1024, 768), (1000, 1537), (256, 256)]:
+        name = names[sel(M, N)]
+        bm, bn, _ = (int(x) for x in name.split("_")[1].split("x"))
+        tiles = -(-M // bm) * -(-N // bn)
+        assert tiles >= 256 or bm == 64, (M, N, name, tiles)
+
+
+def test_status_strings():
+    assert sg.sgemm_status_string(0) == "success"
+    assert "too large" in sg.sgemm_status_string(sg.SGEMM_ERROR_TOO_LARGE)
+    assert sg.sgemm_status_string(-99) == "unknown status"
+    assert isinstance(sg.sgemm_status_string(1), str)  # a hipError_t message
+
+
+def test_tensor_form_validates_before_any_launch():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(4, 3)
+    with pytest.raises(ValueError, match="Dimension error"):
+        sg.gemm(torch.zeros(4), torch.zeros(4, 3))
+    with pytest.raises(ValueError, match="float32"):
+        sg.gemm(a.double(), torch.zeros(3, 2))
+    with pytest.raises(ValueError, match="GPU"):
+        sg.gemm(a, torch.zeros(3, 2))
+    with pytest.raises(ValueError, match="Dimension error"):
+        sg.gemm_batched(a, torch.zeros(3, 2))

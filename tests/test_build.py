@@ -1,0 +1,75 @@
+"""Every kernel compiles for gfx950 with the resources its launch assumes (CPU only).
+
+Checks, from the compiler's own kernel metadata for our device code:
+  - no private (scratch) memory and no register spills in any kernel;
+  - LDS per workgroup within gfx950's 160 KiB;
+  - the VGPR+AGPR count fits the waves a workgroup puts on each SIMD
+    (512 registers per lane per SIMD, waves spread over 4 SIMDs);
+  - the matrix kernels really issue the fp32 matrix instruction.
+The GPT-2 post assembles device code on GPU-less CI machines so malformed code
+fails before it reaches hardware ("GPU Target", section "NVVM to PTX"); this is
+the same idea for our gfx950 build.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+import yaml
+
+from tiled_fp32_gemm_02_amd import build as sgbuild
+
+LDS_LIMIT = 160 * 1024
+
+
+@pytest.fixture(scope="module")
+def kernels(tmp_path_factory):
+    path = str(tmp_path_factory.mktemp("asm") / "sgemm.s")
+    sgbuild.device_asm(path)
+    text = open(path).read()
+    meta = re.search(r"\.amdgpu_metadata\n(.*?)\.end_amdgpu_metadata", text, re.S).group(1)
+    meta = yaml.safe_load(meta.replace("\t", "  "))
+    out = {}
+    for k in meta["amdhsa.kernels"]:
+        name = k[".name"]
+        body = re.search(r"^" + re.escape(name) + r":[^\n]*\n(.*?)s_endpgm", text, re.S | re.M).group(1)
+        demangled = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip()
+        out[demangled] = (k, body)
+    return out
+
+
+def test_all_kernels_present(kernels):
+    names = " ".join(kernels)
+    assert "sgemm_tile16" in names and "sgemm_scale" in names
+    assert sum("sgemm_mfma<" in n for n in kernels) >= 3
+
+
+def test_no_scratch_no_spills(kernels):
+    for name, (k, _) in kernels.items():
+        assert k[".private_segment_fixed_size"] == 0, name
+        assert k[".vgpr_spill_count"] == 0 and k[".sgpr_spill_count"] == 0, name
+
+
+def test_lds_within_limit(kernels):
+    for name, (k, _) in kernels.items():
+        assert k[".group_segment_fixed_size"] <= LDS_LIMIT, name
+
+
+def test_registers_fit_the_launch(kernels):
+    for name, (k, _) in kernels.items():
+        threads = k[".max_flat_workgroup_size"]
+        waves_per_simd = -(-(threads // 64) // 4)
+        assert k[".vgpr_count"] <= 512 // waves_per_simd, (name, k[".vgpr_count"], threads)
+
+
+def test_matrix_kernels_use_fp32_mfma(kernels):
+    for name, (k, body) in kernels.items():
+        if "sgemm_mfma<" in name:
+            assert "v_mfma_f32_32x32x2_f32" in body, name
+
+
+def test_oracle_builds():
+    import oracle
+    path = oracle.build(force=True)
+    assert os.path.exists(path)

@@ -1,0 +1,238 @@
+"""Python binding of the MI355X fp32 GEMM library (``libsgemm.so``).
+
+Argument marshalling only: every entry point here forwards to the C function of
+the same name in ``include/sgemm.h``; all arithmetic runs in the library's HIP
+kernels. PyTorch supplies device memory and streams. There is no CPU fallback:
+if the library is missing or fails to load, every call raises.
+
+Raw entry points take device addresses as Python ints (or CUDA tensors, whose
+``data_ptr()`` is used) and return the library's status code:
+
+    sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    sgemm_ex(config, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    sgemm_strided_batched(M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch, stream)
+
+``gemm(A, B, C=None, alpha=1, beta=0)`` is the tensor-level form: it checks
+shapes, dtypes and devices, fills in the leading dimensions from the tensors'
+strides, raises ``ValueError``/``RuntimeError`` on bad input or a nonzero status,
+and returns C.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "load", "lib_path", "sgemm", "sgemm_ex", "sgemm_strided_batched", "sgemm_config_count",
+    "sgemm_config_name", "sgemm_select_config", "sgemm_launch_shape", "sgemm_status_string",
+    "sgemm_version", "configs", "gemm", "gemm_batched", "check", "SgemmError",
+    "SGEMM_ERROR_TOO_LARGE", "SGEMM_ERROR_BAD_CONFIG",
+]
+
+SGEMM_ERROR_TOO_LARGE = -100
+SGEMM_ERROR_BAD_CONFIG = -101
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsgemm.so")
+_lock = threading.Lock()
+_lib = None
+
+_fp = ctypes.c_void_p
+_SIGS = {
+    "sgemm": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int,
+                             _fp, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, _fp]),
+    "sgemm_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp,
+                                ctypes.c_int, _fp, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, _fp]),
+    "sgemm_strided_batched": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, ctypes.c_longlong,
+        _fp, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, _fp, ctypes.c_int, ctypes.c_longlong,
+        ctypes.c_int, _fp]),
+    "sgemm_config_count": (ctypes.c_int, []),
+    "sgemm_config_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "sgemm_select_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp,
+                                           ctypes.c_int, _fp, ctypes.c_int, _fp, ctypes.c_int]),
+    "sgemm_launch_shape": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]),
+    "sgemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sgemm_version": (ctypes.c_char_p, []),
+}
+EXPORTED = tuple(_SIGS)
+
+
+class SgemmError(RuntimeError):
+    """A nonzero status from the library."""
+
+    def __init__(self, status: int, what: str = "sgemm"):
+        self.status = status
+        super().__init__(f"{what}: status {status}: {sgemm_status_string(status)}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libsgemm.so (once). Raises RuntimeError if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(
+                    f"{_LIB_PATH} is missing: build the HIP library first "
+                    "(python -m tiled_fp32_gemm_02_amd.build, or __graft_entry__.build())")
+            lib = ctypes.CDLL(_LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _addr(x):
+    """Device address of a tensor or int (None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+# --------------------------------------------------------------------------- raw C-ABI forms
+
+def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    return load().sgemm(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc, _stream(stream))
+
+
+def sgemm_ex(config, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    return load().sgemm_ex(config, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                           _stream(stream))
+
+
+def sgemm_strided_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
+                          batch, stream=None) -> int:
+    return load().sgemm_strided_batched(M, N, K, alpha, _addr(A), lda, strideA, _addr(B), ldb, strideB,
+                                        beta, _addr(C), ldc, strideC, batch, _stream(stream))
+
+
+def sgemm_config_count() -> int:
+    return load().sgemm_config_count()
+
+
+def sgemm_config_name(config: int):
+    name = load().sgemm_config_name(config)
+    return name.decode() if name is not None else None
+
+
+def sgemm_select_config(M, N, K, alpha, A, lda, B, ldb, C, ldc) -> int:
+    return load().sgemm_select_config(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, _addr(C), ldc)
+
+
+def sgemm_launch_shape(config, M, N, K):
+    """Returns (status, grid, block)."""
+    grid = (ctypes.c_int * 3)()
+    block = (ctypes.c_int * 3)()
+    st = load().sgemm_launch_shape(config, M, N, K, grid, block)
+    return st, tuple(grid), tuple(block)
+
+
+def sgemm_status_string(status: int) -> str:
+    return load().sgemm_status_string(status).decode()
+
+
+def sgemm_version() -> str:
+    return load().sgemm_version().decode()
+
+
+def configs():
+    """List of configuration names, indexed by id."""
+    return [sgemm_config_name(i) for i in range(sgemm_config_count())]
+
+
+def check(status: int, what: str = "sgemm") -> None:
+    if status != 0:
+        raise SgemmError(status, what)
+
+
+# --------------------------------------------------------------------------- tensor form
+
+def _row_major_ld(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"Dimension error: {name} must be a 2-D matrix, got {t.dim()} dimensions")
+    if t.dtype.__str__() != "torch.float32":
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major with unit column stride (got strides {tuple(t.stride())})")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    return max(ld, cols, 1)
+
+
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None, config: int = -1):
+    """C <- alpha*A@B + beta*C on GPU float32 tensors (row-major, unit column stride).
+
+    A is M x K, B is K x N and C is M x N; C may be a view with a larger row stride.
+    When C is None a new M x N tensor is allocated (then beta must be 0). Returns C.
+    """
+    import torch
+
+    lda = _row_major_ld(A, "A")
+    ldb = _row_major_ld(B, "B")
+    M, K = A.shape
+    if B.shape[0] != K:
+        raise ValueError(f"Size error: A is {tuple(A.shape)} and B is {tuple(B.shape)}; inner sizes differ")
+    N = B.shape[1]
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    ldc = _row_major_ld(C, "C")
+    if tuple(C.shape) != (M, N):
+        raise ValueError(f"Size error: C is {tuple(C.shape)}, expected {(M, N)}")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    check(sgemm_ex(config, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream), "sgemm")
+    return C
+
+
+def gemm_batched(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    """Batched C[b] <- alpha*A[b]@B[b] + beta*C[b] on 3-D GPU float32 tensors.
+
+    Each operand is batch x rows x cols with unit column stride; the batch stride
+    and row stride come from the tensor. Returns C.
+    """
+    import torch
+
+    for name, t in (("A", A), ("B", B)):
+        if t.dim() != 3:
+            raise ValueError(f"Dimension error: {name} must be 3-D (batch, rows, cols)")
+    bsz, M, K = A.shape
+    if B.shape[0] != bsz or B.shape[1] != K:
+        raise ValueError(f"Size error: A is {tuple(A.shape)} and B is {tuple(B.shape)}")
+    N = B.shape[2]
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((bsz, M, N), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (bsz, M, N):
+        raise ValueError(f"Size error: C is {tuple(C.shape)}, expected {(bsz, M, N)}")
+    lda = _row_major_ld(A[0], "A[b]") if bsz else max(K, 1)
+    ldb = _row_major_ld(B[0], "B[b]") if bsz else max(N, 1)
+    ldc = _row_major_ld(C[0], "C[b]") if bsz else max(N, 1)
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    check(sgemm_strided_batched(M, N, K, alpha, A, lda, A.stride(0), B, ldb, B.stride(0), beta, C, ldc,
+                                C.stride(0), bsz, stream), "sgemm_strided_batched")
+    return C

@@ -1,0 +1,344 @@
+// Device kernels for row-major fp32 C = alpha*A*B + beta*C on gfx950 (MI355X).
+//
+// Three kernels:
+//  - sgemm_mfma: the hot path. A workgroup owns a BM x BN tile of C; each wave owns
+//    a (BM/WGM) x (BN/WGN) sub-tile made of 32x32 blocks computed with the CDNA fp32
+//    matrix instruction (32x32 outputs, 2 k-steps per issue). A and B tiles move
+//    HBM -> registers -> LDS in 128-bit chunks, into a two-stage LDS ring with one
+//    barrier per K-tile; the next K-tile's global loads are in flight while the
+//    current one is multiplied.
+//  - sgemm_tile16: the classic shared-memory kernel, one output per thread and
+//    16x16 tiles (the GPT-2 post's hand-written matmul). Kept as the simplest
+//    correct rung and as a baseline for the report.
+//  - sgemm_scale: C = beta*C for the quick-return cases (alpha == 0 or K == 0).
+//
+// Techniques from the pages and where they come from:
+//  - Tiling through local memory so each global element is fetched once per
+//    workgroup instead of once per thread (AutoMine++ #4, "Current algorithm";
+//    GPT-2 post, "Tiled matrix multiplication").
+//  - Thread coarsening with an outer-product update of a register tile
+//    (AutoMine++ #4, "Use registers" and "Matrix product by outer products"); here
+//    the register tile is the matrix-core accumulator and the outer products of
+//    2-deep k slices are what each matrix instruction adds.
+//  - Rectangular tiles and wide chunk loads (AutoMine++ #7, "Rectangular tiling"
+//    and "Fine tuning"); double buffering with register staging and one barrier
+//    per step (AutoMine++ #7, "Rectangular tiling"; Micro_gemm_4x4, section 3).
+//  - Zero-filled out-of-range loads, a ceil-divided grid and predicated stores
+//    (Micro_gemm_4x4, sections 6 and 9; GPT-2 post, "Tiled matrix multiplication").
+//  - alpha/beta epilogue that skips reading C when beta is zero (Micro_gemm_4x4,
+//    section 9).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm_impl {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+struct GemmArgs {
+    int M, N, K;
+    float alpha, beta;
+    const float *A;
+    const float *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+    int64_t strideA, strideB, strideC;  // per blockIdx.z (batched form); 0 otherwise
+};
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Map the linear workgroup id to a (tile_m, tile_n) pair.
+//
+// Workgroups are handed to the 8 XCDs in round-robin order of their id, and each
+// XCD has its own L2. The first step renumbers ids so that each XCD receives one
+// contiguous range of the logical order. The second walks that order in groups of
+// `group_m` tile rows, column by column, so workgroups that run together share A
+// row panels and B column panels in L2.
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int group_m,
+                                            int &tm, int &tn)
+{
+    const int total = tiles_m * tiles_n;
+    constexpr int XCDS = 8;
+    const int per = total / XCDS, rem = total % XCDS;
+    const int xcd = wg % XCDS, slot = wg / XCDS;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    const int band = group_m * tiles_n;
+    const int first_m = (logical / band) * group_m;
+    const int rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int in_band = logical % band;
+    tm = first_m + in_band % rows;
+    tn = in_band / rows;
+}
+
+// ---------------------------------------------------------------------------------
+// MFMA kernel.
+//
+// Template parameters: BM x BN workgroup tile, BK k-depth per LDS stage, WGM x WGN
+// waves. VEC selects 128-bit global loads/stores (all operands 16-byte aligned,
+// leading dimensions, N and K multiples of 4); EDGE enables the bounds checks needed
+// when M, N or K is not a multiple of the tile. Without VEC every element is checked.
+//
+// LDS layout per stage (floats): A tile as stored in memory, [BM][BK + 4] (row i,
+// k contiguous, 4 floats of padding so eight consecutive rows fall in distinct bank
+// groups for 128-bit reads), then B tile [BK][BN + 4] (k row, n contiguous).
+//
+// Lane layout of v_mfma_f32_32x32x2_f32 (one 32x32 block, k = 2): lane l supplies
+// A(l%32, l/32) and B(l/32, l%32); accumulator element e of lane l is
+// D(8*(e/4) + 4*(l/32) + e%4, l%32). Two remappings make every LDS read 128 or
+// 64 bits wide:
+//  - k: within each group of 8 k values, the half-wave h = l/32 takes k = 4h + s on
+//    matrix step s (s = 0..3). A and B use the same map, so each issue still adds
+//    A(:,k)B(k,:) for two distinct k and the 4 steps cover all 8. Lane l then reads
+//    A(row, 4h .. 4h+3) as one 128-bit word.
+//  - n: a wave's TN blocks along n are interleaved, block b column c <-> tile column
+//    c*TN + b, so lane l reads and writes TN consecutive columns.
+// ---------------------------------------------------------------------------------
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, bool EDGE>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+sgemm_mfma(GemmArgs p, int group_m)
+{
+    constexpr int NT = WGM * WGN * 64;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
+    constexpr int TM = WTM / 32, TN = WTN / 32;         // 32x32 blocks per wave
+    constexpr int SA = BK + 4, SB = BN + 4;             // LDS row strides (floats)
+    constexpr int A_STAGE = BM * SA, B_STAGE = BK * SB;
+    constexpr int STAGE = A_STAGE + B_STAGE;
+    constexpr int A_CPR = BK / 4, B_CPR = BN / 4;       // 4-float chunks per tile row
+    constexpr int A_CH = BM * BK / 4 / NT, B_CH = BK * BN / 4 / NT;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(TN == 1 || TN == 2 || TN == 4, "interleaved n blocks read 1, 2 or 4 floats");
+    static_assert(BK % 8 == 0, "k is consumed in groups of 8");
+    static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "loader needs whole chunks per thread");
+    static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS ring exceeds 160 KiB");
+
+    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+
+    const int M = p.M, N = p.N, K = p.K;
+    const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const float *__restrict__ A = p.A + (int64_t)blockIdx.z * p.strideA;
+    const float *__restrict__ B = p.B + (int64_t)blockIdx.z * p.strideB;
+    float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
+    const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int l32 = lane & 31, half = lane >> 5;
+
+    floatx4 ra[A_CH], rb[B_CH];
+
+    // Global -> registers for the K-tile starting at k0 (zero outside the matrix).
+    auto load_tile = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < A_CH; ++c) {
+            const int idx = tid + c * NT;
+            const int r = idx / A_CPR, kc = (idx % A_CPR) * 4;
+            const int gr = m0 + r, gk = k0 + kc;
+            const float *src = A + (int64_t)gr * lda + gk;
+            if (VEC) {
+                if (!EDGE || (gr < M && gk < K))
+                    ra[c] = *reinterpret_cast<const floatx4 *>(src);
+                else
+                    ra[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                const bool rok = gr < M;
+                ra[c].x = (rok && gk + 0 < K) ? src[0] : 0.f;
+                ra[c].y = (rok && gk + 1 < K) ? src[1] : 0.f;
+                ra[c].z = (rok && gk + 2 < K) ? src[2] : 0.f;
+                ra[c].w = (rok && gk + 3 < K) ? src[3] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < B_CH; ++c) {
+            const int idx = tid + c * NT;
+            const int r = idx / B_CPR, nc = (idx % B_CPR) * 4;
+            const int gk = k0 + r, gn = n0 + nc;
+            const float *src = B + (int64_t)gk * ldb + gn;
+            if (VEC) {
+                if (!EDGE || (gk < K && gn < N))
+                    rb[c] = *reinterpret_cast<const floatx4 *>(src);
+                else
+                    rb[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                const bool kok = gk < K;
+                rb[c].x = (kok && gn + 0 < N) ? src[0] : 0.f;
+                rb[c].y = (kok && gn + 1 < N) ? src[1] : 0.f;
+                rb[c].z = (kok && gn + 2 < N) ? src[2] : 0.f;
+                rb[c].w = (kok && gn + 3 < N) ? src[3] : 0.f;
+            }
+        }
+    };
+
+    // Registers -> LDS stage `st`.
+    auto store_tile = [&](int st) __attribute__((always_inline)) {
+        float *As = smem + st * STAGE;
+        float *Bs = As + A_STAGE;
+#pragma unroll
+        for (int c = 0; c < A_CH; ++c) {
+            const int idx = tid + c * NT;
+            *reinterpret_cast<floatx4 *>(&As[(idx / A_CPR) * SA + (idx % A_CPR) * 4]) = ra[c];
+        }
+#pragma unroll
+        for (int c = 0; c < B_CH; ++c) {
+            const int idx = tid + c * NT;
+            *reinterpret_cast<floatx4 *>(&Bs[(idx / B_CPR) * SB + (idx % B_CPR) * 4]) = rb[c];
+        }
+    };
+
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[a][b][e] = 0.f;
+
+    const int a_row = wm * WTM + l32;            // + a*32: this lane's A row in the tile
+    const int b_col = wn * WTN + l32 * TN;       // this lane's first B column in the tile
+
+    // One stage: BK/8 groups of 8 k values, 4 matrix steps each.
+    auto compute = [&](int st) __attribute__((always_inline)) {
+        const float *As = smem + st * STAGE;
+        const float *Bs = As + A_STAGE;
+#pragma unroll
+        for (int kg = 0; kg < BK; kg += 8) {
+            floatx4 af[TM];
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+                af[a] = *reinterpret_cast<const floatx4 *>(&As[(a_row + a * 32) * SA + kg + 4 * half]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float *brow = &Bs[(kg + 4 * half + s) * SB + b_col];
+                float bf[TN];
+                if constexpr (TN == 4) {
+                    const floatx4 v = *reinterpret_cast<const floatx4 *>(brow);
+                    bf[0] = v[0]; bf[1] = v[1]; bf[2] = v[2]; bf[3] = v[3];
+                } else if constexpr (TN == 2) {
+                    const floatx2 v = *reinterpret_cast<const floatx2 *>(brow);
+                    bf[0] = v[0]; bf[1] = v[1];
+                } else {
+                    bf[0] = brow[0];
+                }
+#pragma unroll
+                for (int a = 0; a < TM; ++a) {
+                    const float av = af[a][s];
+#pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bf[b], acc[a][b], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Pipeline. The last K-tile is peeled off so the loop body has no conditionals
+    // around the staging registers (which keeps them in VGPRs).
+    const int nk = ceil_div(K, BK);
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int t = 0; t + 1 < nk; ++t) {
+        load_tile((t + 1) * BK);         // in flight while this stage is multiplied
+        compute(t & 1);
+        store_tile((t + 1) & 1);         // other stage: its last reader finished before the previous barrier
+        __syncthreads();
+    }
+    compute((nk - 1) & 1);
+
+    // Epilogue: C = alpha*acc + beta*C, C unread when beta == 0.
+    const float alpha = p.alpha, beta = p.beta;
+    const int gc0 = n0 + b_col;
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int gr = m0 + wm * WTM + a * 32 + 8 * (e / 4) + 4 * half + (e % 4);
+            if (EDGE && gr >= M)
+                continue;
+            float *crow = C + (int64_t)gr * ldc + gc0;
+            float v[TN];
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+                v[b] = alpha * acc[a][b][e];
+            if (VEC && TN == 4 && (!EDGE || gc0 < N)) {
+                // VEC: N % 4 == 0 and gc0 % 4 == 0, so the whole chunk is in range.
+                floatx4 *c4 = reinterpret_cast<floatx4 *>(crow);
+                floatx4 out = {v[0], v[1], v[2], v[3]};
+                if (beta != 0.f)
+                    out += beta * *c4;
+                *c4 = out;
+            } else if (VEC && TN == 2 && (!EDGE || gc0 < N)) {
+                floatx2 *c2 = reinterpret_cast<floatx2 *>(crow);
+                floatx2 out = {v[0], v[1]};
+                if (beta != 0.f)
+                    out += beta * *c2;
+                *c2 = out;
+            } else {
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    if (EDGE && gc0 + b >= N)
+                        continue;
+                    float out = v[b];
+                    if (beta != 0.f)
+                        out += beta * crow[b];
+                    crow[b] = out;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Classic 16x16 shared-memory kernel: one output per thread. Each step stages one
+// element of A and one of B per thread (zero outside the matrix), a barrier makes the
+// tiles visible, 16 products are accumulated, and a second barrier keeps the next
+// step's stores off tiles still being read. Grid: ceil(N/16) x ceil(M/16) x batch.
+// ---------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) sgemm_tile16(GemmArgs p)
+{
+    __shared__ float sa[16][17];
+    __shared__ float sb[16][17];
+    const int tx = threadIdx.x, ty = threadIdx.y;
+    const int row = blockIdx.y * 16 + ty, col = blockIdx.x * 16 + tx;
+    const float *__restrict__ A = p.A + (int64_t)blockIdx.z * p.strideA;
+    const float *__restrict__ B = p.B + (int64_t)blockIdx.z * p.strideB;
+    float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
+    float sum = 0.f;
+    for (int k0 = 0; k0 < p.K; k0 += 16) {
+        sa[ty][tx] = (row < p.M && k0 + tx < p.K) ? A[(int64_t)row * p.lda + k0 + tx] : 0.f;
+        sb[ty][tx] = (k0 + ty < p.K && col < p.N) ? B[(int64_t)(k0 + ty) * p.ldb + col] : 0.f;
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+            sum += sa[ty][kk] * sb[kk][tx];
+        __syncthreads();
+    }
+    if (row < p.M && col < p.N) {
+        float *c = C + (int64_t)row * p.ldc + col;
+        float out = p.alpha * sum;
+        if (p.beta != 0.f)
+            out += p.beta * *c;
+        *c = out;
+    }
+}
+
+// C = beta*C over the M x N window (C not read when beta == 0). Grid-stride in both
+// dimensions; blockIdx.z selects the batch.
+__global__ void __launch_bounds__(256) sgemm_scale(GemmArgs p)
+{
+    float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
+    for (int i = blockIdx.y * blockDim.y + threadIdx.y; i < p.M; i += gridDim.y * blockDim.y)
+        for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < p.N; j += gridDim.x * blockDim.x) {
+            float *c = C + (int64_t)i * p.ldc + j;
+            *c = (p.beta == 0.f) ? 0.f : p.beta * *c;
+        }
+}
+
+}  // namespace sgemm_impl
