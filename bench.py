@@ -34,7 +34,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3          # MI355X dense fp32 (matrix and vector), AMD's published figure
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_sq4096_hbm_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_fp32_gemm_02_amd", "csrc", f)
                   for f in ("sgemm_kernels.hpp", "sgemm_api.hip")]
 
@@ -44,20 +43,27 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """sha256 of the kernel sources with comments and whitespace removed, so the
+    recorded counters stay valid across comment-only edits."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
 def recorded_traffic(workload: str, config_name: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on
     the current kernel source and the same workload and configuration; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = os.path.join(ROOT, "profiles", f"{config_name}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.lstrip().startswith("#"):
                 k, v = line.split(":", 1)
@@ -172,6 +178,7 @@ def main():
         raise SystemExit(f"bench: result outside the oracle bound (max |err|/bound = {worst})")
     log(f"bench: checked {rows.size} sampled entries, max |err|/bound = {worst:.3f}")
     dC.copy_(C0)
+    torch.cuda.synchronize()
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):

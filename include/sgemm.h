@@ -10,7 +10,7 @@
  * The operation is the BLAS-style form of the tiled kernels on the pages: the
  * product accumulated in a register tile, then alpha times it plus beta times the
  * old C, with C not read when beta is zero ("Micro_gemm_4x4 - cuBLAS micro GEMM
- * skeleton", section 2 for the signature and section 9 for the final C write).
+ * skeleton", sections "Kernel signature" and "Final C write (alpha, beta)").
  * Leading dimensions generalise the pages' packed A[row*K + k] indexing the way
  * the GPT-2 post's kernel takes strided views ("GPU Target - GPT-2 on the GPU",
  * section "Tiled matrix multiplication").

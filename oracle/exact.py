@@ -7,7 +7,7 @@ problems of a few thousand multiply-adds.
 It follows the same definition as the C oracle (each entry is the dot product
 of a row of A with a column of B; AutoMine++ #4, "Current algorithm"; the result
 is alpha*acc + beta*C with C unread when beta is zero; "Micro_gemm_4x4", section
-9), but in exact arithmetic, so it can pin the fp64 oracle: on small-integer
+"Final C write (alpha, beta)"), but in exact arithmetic, so it can pin the fp64 oracle: on small-integer
 inputs the two must agree exactly, and otherwise the oracle must sit within its
 own fp64 summation error of this result.
 """

@@ -19,10 +19,10 @@
  *    and B's rows gives the same matrix; same page, "Matrix product by outer
  *    products of vectors".
  *  - The result form alpha*acc + beta*C, with C not read when beta is zero;
- *    "Micro_gemm_4x4 - cuBLAS micro GEMM skeleton", section 9 (final C write,
- *    with alpha and beta). Its signature section writes the formula as
- *    "alpha*A + beta*C"; the code in section 9 multiplies the accumulated
- *    product, which is the reading taken here.
+ *    "Micro_gemm_4x4 - cuBLAS micro GEMM skeleton", section "Final C write
+ *    (alpha, beta)". Its "Kernel signature" section writes the formula as
+ *    alpha times A plus beta times C; the final-write code multiplies the
+ *    accumulated product, which is the reading taken here.
  *  - Tiled and library results differ only through the order of accumulation;
  *    "GPU Target - GPT-2 on the GPU", section "Running it". That is why the
  *    comparison is against a bound and not bitwise.

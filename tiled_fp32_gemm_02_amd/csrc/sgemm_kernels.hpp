@@ -22,11 +22,13 @@
 //    2-deep k slices are what each matrix instruction adds.
 //  - Rectangular tiles and wide chunk loads (AutoMine++ #7, "Rectangular tiling"
 //    and "Fine tuning"); double buffering with register staging and one barrier
-//    per step (AutoMine++ #7, "Rectangular tiling"; Micro_gemm_4x4, section 3).
+//    per step (AutoMine++ #7, "Rectangular tiling"; Micro_gemm_4x4, "Pipeline (double
+//    buffering)").
 //  - Zero-filled out-of-range loads, a ceil-divided grid and predicated stores
-//    (Micro_gemm_4x4, sections 6 and 9; GPT-2 post, "Tiled matrix multiplication").
+//    (Micro_gemm_4x4, "A/B tile load" and "Final C write"; GPT-2 post, "Tiled matrix
+//    multiplication").
 //  - alpha/beta epilogue that skips reading C when beta is zero (Micro_gemm_4x4,
-//    section 9).
+//    "Final C write (alpha, beta)").
 #pragma once
 
 #include <hip/hip_runtime.h>
