@@ -202,7 +202,8 @@ def main():
 
     props = torch.cuda.get_device_properties(dev)
     line = {
-        "metric": "FP32 SGEMM TFLOP/s at M=N=K=4096 and fraction of MI355X FP32 peak",
+        "metric": ("FP32 SGEMM TFLOP/s at M=N=K=4096 and fraction of MI355X FP32 peak" if w.name == "sq4096"
+                   else f"FP32 SGEMM TFLOP/s ({w.name}) and fraction of MI355X FP32 peak"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -124,13 +124,15 @@ def test_launch_shape_mfma():
     for cid, name in enumerate(sg.configs()):
         if not name.startswith("mfma_"):
             continue
-        bm, bn, _ = (int(x) for x in name.split("_")[1].split("x"))
-        wm, wn = (int(x) for x in name.split("_w")[1].split("x"))
+        m = re.fullmatch(r"mfma_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?", name)
+        assert m, name
+        bm, bn, _, wm, wn = (int(x) for x in m.groups()[:5])
+        wk = int(m.group(6) or 1)
         for M, N in [(4096, 4096), (1000, 1537), (1, 1), (bm + 1, bn - 1)]:
             st, grid, block = sg.sgemm_launch_shape(cid, M, N, 64)
             assert st == 0
             assert grid == (-(-M // bm) * -(-N // bn), 1, 1)
-            assert block == (wm * wn * 64, 1, 1)
+            assert block == (wm * wn * wk * 64, 1, 1)
         assert sg.sgemm_launch_shape(cid, -1, 4, 4)[0] == -1
     st, _, _ = sg.sgemm_launch_shape(1, 2**31 - 1, 2**31 - 1, 1)
     assert st == sg.SGEMM_ERROR_TOO_LARGE

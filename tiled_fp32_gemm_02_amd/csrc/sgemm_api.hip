@@ -30,17 +30,20 @@ struct Config {
     LaunchFn launch;
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, int GROUP_M>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int GROUP_M>
 hipError_t launch_mfma(const GemmArgs &p, int batch, bool vec, bool edge, hipStream_t s)
 {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    const dim3 grid(tiles, 1, batch), block(WGM * WGN * 64);
+    const dim3 grid(tiles, 1, batch), block(WGM * WGN * WGK * 64);
     if (vec && !edge)
-        hipLaunchKernelGGL((sgemm_impl::sgemm_mfma<BM, BN, BK, WGM, WGN, true, false>), grid, block, 0, s, p, GROUP_M);
+        hipLaunchKernelGGL((sgemm_impl::sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, true, false>), grid, block, 0, s, p,
+                           GROUP_M);
     else if (vec)
-        hipLaunchKernelGGL((sgemm_impl::sgemm_mfma<BM, BN, BK, WGM, WGN, true, true>), grid, block, 0, s, p, GROUP_M);
+        hipLaunchKernelGGL((sgemm_impl::sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, true, true>), grid, block, 0, s, p,
+                           GROUP_M);
     else
-        hipLaunchKernelGGL((sgemm_impl::sgemm_mfma<BM, BN, BK, WGM, WGN, false, true>), grid, block, 0, s, p, GROUP_M);
+        hipLaunchKernelGGL((sgemm_impl::sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, false, true>), grid, block, 0, s, p,
+                           GROUP_M);
     return hipGetLastError();
 }
 
@@ -52,14 +55,28 @@ hipError_t launch_tile16(const GemmArgs &p, int batch, bool, bool, hipStream_t s
 }
 
 // Configuration table. Ids are stable within one build; names encode the tile
-// (BM x BN x BK) and the wave grid (WGM x WGN).
+// (BM x BN x BK), the wave grid (WGM x WGN) and, after "k", the wave groups along k.
 const Config kConfigs[] = {
     {"tile16", KIND_TILE16, 16, 16, 16, 256, 1, launch_tile16},
-    {"mfma_64x64x16_w2x2", KIND_MFMA, 64, 64, 16, 256, 8, launch_mfma<64, 64, 16, 2, 2, 8>},
-    {"mfma_128x128x16_w2x2", KIND_MFMA, 128, 128, 16, 256, 8, launch_mfma<128, 128, 16, 2, 2, 8>},
-    {"mfma_128x128x32_w2x2", KIND_MFMA, 128, 128, 32, 256, 8, launch_mfma<128, 128, 32, 2, 2, 8>},
-    {"mfma_256x128x16_w2x2", KIND_MFMA, 256, 128, 16, 256, 4, launch_mfma<256, 128, 16, 2, 2, 4>},
-    {"mfma_256x256x16_w2x4", KIND_MFMA, 256, 256, 16, 512, 4, launch_mfma<256, 256, 16, 2, 4, 4>},
+    {"mfma_64x64x16_w2x2", KIND_MFMA, 64, 64, 16, 256, 8, launch_mfma<64, 64, 16, 2, 2, 1, 8>},
+    {"mfma_128x128x16_w2x2", KIND_MFMA, 128, 128, 16, 256, 8, launch_mfma<128, 128, 16, 2, 2, 1, 8>},
+    {"mfma_128x128x32_w2x2", KIND_MFMA, 128, 128, 32, 256, 8, launch_mfma<128, 128, 32, 2, 2, 1, 8>},
+    {"mfma_256x128x16_w2x2", KIND_MFMA, 256, 128, 16, 256, 4, launch_mfma<256, 128, 16, 2, 2, 1, 4>},
+    {"mfma_256x256x16_w2x4", KIND_MFMA, 256, 256, 16, 512, 4, launch_mfma<256, 256, 16, 2, 4, 1, 4>},
+    {"mfma_64x64x32_w2x2", KIND_MFMA, 64, 64, 32, 256, 8, launch_mfma<64, 64, 32, 2, 2, 1, 8>},
+    {"mfma_128x64x16_w2x2", KIND_MFMA, 128, 64, 16, 256, 8, launch_mfma<128, 64, 16, 2, 2, 1, 8>},
+    {"mfma_64x128x16_w2x2", KIND_MFMA, 64, 128, 16, 256, 8, launch_mfma<64, 128, 16, 2, 2, 1, 8>},
+    {"mfma_256x256x32_w2x4", KIND_MFMA, 256, 256, 32, 512, 4, launch_mfma<256, 256, 32, 2, 4, 1, 4>},
+    {"mfma_256x128x16_w4x2", KIND_MFMA, 256, 128, 16, 512, 4, launch_mfma<256, 128, 16, 4, 2, 1, 4>},
+    {"mfma_128x256x16_w2x4", KIND_MFMA, 128, 256, 16, 512, 8, launch_mfma<128, 256, 16, 2, 4, 1, 8>},
+    {"mfma_128x128x32_w4x4", KIND_MFMA, 128, 128, 32, 1024, 8, launch_mfma<128, 128, 32, 4, 4, 1, 8>},
+    {"mfma_64x64x16_w2x2k2", KIND_MFMA, 64, 64, 16, 512, 8, launch_mfma<64, 64, 16, 2, 2, 2, 8>},
+    {"mfma_64x64x32_w2x2k2", KIND_MFMA, 64, 64, 32, 512, 8, launch_mfma<64, 64, 32, 2, 2, 2, 8>},
+    {"mfma_64x64x32_w2x2k4", KIND_MFMA, 64, 64, 32, 1024, 8, launch_mfma<64, 64, 32, 2, 2, 4, 8>},
+    {"mfma_64x64x64_w2x2k4", KIND_MFMA, 64, 64, 64, 1024, 8, launch_mfma<64, 64, 64, 2, 2, 4, 8>},
+    {"mfma_128x64x32_w2x2k2", KIND_MFMA, 128, 64, 32, 512, 8, launch_mfma<128, 64, 32, 2, 2, 2, 8>},
+    {"mfma_64x128x32_w2x2k2", KIND_MFMA, 64, 128, 32, 512, 8, launch_mfma<64, 128, 32, 2, 2, 2, 8>},
+    {"mfma_128x128x32_w2x2k2", KIND_MFMA, 128, 128, 32, 512, 8, launch_mfma<128, 128, 32, 2, 2, 2, 8>},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -78,16 +95,56 @@ uint64_t tile_count(const Config &c, int M, int N)
     return (uint64_t)((M + c.bm - 1) / c.bm) * (uint64_t)((N + c.bn - 1) / c.bn);
 }
 
-// Auto-selection: the largest tile that still gives every CU at least one
-// workgroup; smaller tiles when the problem is too small to fill the chip.
-int choose(int M, int N)
+// Auto-selection by a small cost model. A candidate's tiles spread over the 256 CUs
+// take L = ceil(tiles / 256) rounds on the busiest CU; its time is L tiles of work
+// (in units of one 64x64 tile) divided by the CU's throughput with that many tiles
+// resident. Throughputs (fp32 TFLOP/s per CU) were measured on MI355X with the
+// whole chip busy: rate_one when a CU holds a single workgroup, rate_many when it
+// holds several (more waves to hide latency). The model picks the large tile when it
+// fills the chip in one round and the wave-split 64x64 tile when few tiles exist;
+// K cancels out because every candidate walks the same K.
+struct Candidate {
+    int id;
+    int units;          // tile area / (64 * 64)
+    double rate_one;    // per-CU rate with one resident workgroup
+    double rate_many;   // per-CU rate with two or more
+};
+
+const Candidate kCandidatesVec[] = {
+    {5, 16, 0.500, 0.500},    // mfma_256x256x16_w2x4: one workgroup per CU fits
+    {19, 4, 0.458, 0.458},    // mfma_128x128x32_w2x2k2: one per CU
+    {18, 2, 0.400, 0.452},    // mfma_64x128x32_w2x2k2: up to three per CU
+    {16, 1, 0.395, 0.436},    // mfma_64x64x64_w2x2k4: up to two per CU
+};
+// 32-bit path (unaligned operands): the 64-deep stage loses to 32-deep ones there.
+const Candidate kCandidatesScalar[] = {
+    {5, 16, 0.500, 0.500},
+    {19, 4, 0.458, 0.458},
+    {18, 2, 0.400, 0.452},
+    {14, 1, 0.380, 0.420},    // mfma_64x64x32_w2x2k2: up to four per CU
+};
+
+int choose(int M, int N, bool vec)
 {
-    constexpr int kCUs = 256;
-    const int order[] = {5, 2, 1};    // 256x256, 128x128, 64x64
-    for (int id : order)
-        if (tile_count(kConfigs[id], M, N) >= (uint64_t)kCUs)
-            return id;
-    return 1;
+    constexpr uint64_t kCUs = 256;
+    const Candidate *cands = vec ? kCandidatesVec : kCandidatesScalar;
+    const int count = vec ? (int)(sizeof(kCandidatesVec) / sizeof(Candidate))
+                          : (int)(sizeof(kCandidatesScalar) / sizeof(Candidate));
+    int best = cands[0].id;
+    double best_cost = 0.0;
+    bool first = true;
+    for (int i = 0; i < count; ++i) {
+        const Candidate &cand = cands[i];
+        const uint64_t tiles = tile_count(kConfigs[cand.id], M, N);
+        const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
+        const double cost = (double)rounds * cand.units / (rounds >= 2 ? cand.rate_many : cand.rate_one);
+        if (first || cost < best_cost) {
+            best = cand.id;
+            best_cost = cost;
+            first = false;
+        }
+    }
+    return best;
 }
 
 // Argument checks shared by the entry points. Returns 0 or -position (sgemm numbering).
@@ -126,13 +183,13 @@ int run(int config, int M, int N, int K, float alpha, const float *A, int lda, i
         const hipError_t e = hipGetLastError();
         return e == hipSuccess ? 0 : (int)e;
     }
-    const int id = config >= 0 ? config : choose(M, N);
+    const bool vec = vector_ok(N, K, A, lda, B, ldb, C, ldc) &&
+                     (batch == 1 || (sA % 4 == 0 && sB % 4 == 0 && sC % 4 == 0));
+    const int id = config >= 0 ? config : choose(M, N, vec);
     const Config &c = kConfigs[id];
     const uint64_t tiles = tile_count(c, M, N);
     if (c.kind == KIND_MFMA && tiles * (uint64_t)c.threads > 0xFFFFFFFFull)
         return SGEMM_ERROR_TOO_LARGE;
-    const bool vec = vector_ok(N, K, A, lda, B, ldb, C, ldc) &&
-                     (batch == 1 || (sA % 4 == 0 && sB % 4 == 0 && sC % 4 == 0));
     const bool edge = (M % c.bm) != 0 || (N % c.bn) != 0 || (K % c.bk) != 0;
     const hipError_t e = c.launch(p, batch, vec, edge, stream);
     return e == hipSuccess ? 0 : (int)e;
@@ -192,10 +249,9 @@ const char *sgemm_config_name(int config)
 int sgemm_select_config(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
                         int ldb, const float *C, int ldc)
 {
-    (void)A; (void)lda; (void)B; (void)ldb; (void)C; (void)ldc;
     if (M <= 0 || N <= 0 || K <= 0 || alpha == 0.0f)
         return -1;
-    return choose(M, N);
+    return choose(M, N, vector_ok(N, K, A, lda, B, ldb, C, ldc));
 }
 
 int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3])

@@ -79,7 +79,11 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 // MFMA kernel.
 //
 // Template parameters: BM x BN workgroup tile, BK k-depth per LDS stage, WGM x WGN
-// waves. VEC selects 128-bit global loads/stores (all operands 16-byte aligned,
+// waves over the tile, WGK wave groups along k. With WGK > 1 every wave group
+// multiplies its own BK/WGK slice of each stage into its own accumulators, and at the
+// end the groups add their accumulators through LDS in a fixed order (group 0 + 1 +
+// 2 ...), so results stay reproducible; this puts more waves on each CU when the
+// problem has few tiles, without any memory outside the workgroup. VEC selects 128-bit global loads/stores (all operands 16-byte aligned,
 // leading dimensions, N and K multiples of 4); EDGE enables the bounds checks needed
 // when M, N or K is not a multiple of the tile. Without VEC every element is checked.
 //
@@ -98,25 +102,31 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 //  - n: a wave's TN blocks along n are interleaved, block b column c <-> tile column
 //    c*TN + b, so lane l reads and writes TN consecutive columns.
 // ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, bool EDGE>
-__global__ void __launch_bounds__(WGM * WGN * 64)
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, bool VEC, bool EDGE>
+__global__ void __launch_bounds__(WGM * WGN * WGK * 64)
 sgemm_mfma(GemmArgs p, int group_m)
 {
-    constexpr int NT = WGM * WGN * 64;
+    constexpr int NT = WGM * WGN * WGK * 64;
+    constexpr int KSLICE = BK / WGK;                    // k per stage handled by one wave group
     constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
     constexpr int TM = WTM / 32, TN = WTN / 32;         // 32x32 blocks per wave
     constexpr int SA = BK + 4, SB = BN + 4;             // LDS row strides (floats)
     constexpr int A_STAGE = BM * SA, B_STAGE = BK * SB;
     constexpr int STAGE = A_STAGE + B_STAGE;
     constexpr int A_CPR = BK / 4, B_CPR = BN / 4;       // 4-float chunks per tile row
-    constexpr int A_CH = BM * BK / 4 / NT, B_CH = BK * BN / 4 / NT;
+    constexpr int A_CHUNKS = BM * BK / 4, B_CHUNKS = BK * BN / 4;
+    constexpr int A_CH = (A_CHUNKS + NT - 1) / NT, B_CH = (B_CHUNKS + NT - 1) / NT;   // chunks per thread
+    constexpr bool A_IDLE = A_CHUNKS % NT != 0, B_IDLE = B_CHUNKS % NT != 0;        // surplus threads idle
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(TN == 1 || TN == 2 || TN == 4, "interleaved n blocks read 1, 2 or 4 floats");
-    static_assert(BK % 8 == 0, "k is consumed in groups of 8");
-    static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "loader needs whole chunks per thread");
-    static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS ring exceeds 160 KiB");
+    static_assert(BK % (8 * WGK) == 0, "each wave group consumes k in groups of 8");
+    static_assert(A_CHUNKS % NT == 0 || A_CH == 1, "a partial loader round only when it is the only one");
+    static_assert(B_CHUNKS % NT == 0 || B_CH == 1, "a partial loader round only when it is the only one");
+    constexpr int RED = (WGK - 1) * BM * BN;            // partial sums of groups 1..WGK-1
+    constexpr int SMEM = 2 * STAGE > RED ? 2 * STAGE : RED;
+    static_assert(SMEM * 4 <= 160 * 1024, "LDS exceeds 160 KiB");
 
-    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) float smem[SMEM];
 
     const int M = p.M, N = p.N, K = p.K;
     const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
@@ -131,7 +141,8 @@ sgemm_mfma(GemmArgs p, int group_m)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WGN, wn = wave % WGN;
+    const int wk = wave / (WGM * WGN);
+    const int wm = (wave % (WGM * WGN)) / WGN, wn = wave % WGN;
     const int l32 = lane & 31, half = lane >> 5;
 
     floatx4 ra[A_CH], rb[B_CH];
@@ -141,6 +152,8 @@ sgemm_mfma(GemmArgs p, int group_m)
 #pragma unroll
         for (int c = 0; c < A_CH; ++c) {
             const int idx = tid + c * NT;
+            if (A_IDLE && idx >= A_CHUNKS)
+                break;
             const int r = idx / A_CPR, kc = (idx % A_CPR) * 4;
             const int gr = m0 + r, gk = k0 + kc;
             const float *src = A + (int64_t)gr * lda + gk;
@@ -160,6 +173,8 @@ sgemm_mfma(GemmArgs p, int group_m)
 #pragma unroll
         for (int c = 0; c < B_CH; ++c) {
             const int idx = tid + c * NT;
+            if (B_IDLE && idx >= B_CHUNKS)
+                break;
             const int r = idx / B_CPR, nc = (idx % B_CPR) * 4;
             const int gk = k0 + r, gn = n0 + nc;
             const float *src = B + (int64_t)gk * ldb + gn;
@@ -185,11 +200,15 @@ sgemm_mfma(GemmArgs p, int group_m)
 #pragma unroll
         for (int c = 0; c < A_CH; ++c) {
             const int idx = tid + c * NT;
+            if (A_IDLE && idx >= A_CHUNKS)
+                break;
             *reinterpret_cast<floatx4 *>(&As[(idx / A_CPR) * SA + (idx % A_CPR) * 4]) = ra[c];
         }
 #pragma unroll
         for (int c = 0; c < B_CH; ++c) {
             const int idx = tid + c * NT;
+            if (B_IDLE && idx >= B_CHUNKS)
+                break;
             *reinterpret_cast<floatx4 *>(&Bs[(idx / B_CPR) * SB + (idx % B_CPR) * 4]) = rb[c];
         }
     };
@@ -211,7 +230,8 @@ sgemm_mfma(GemmArgs p, int group_m)
         const float *As = smem + st * STAGE;
         const float *Bs = As + A_STAGE;
 #pragma unroll
-        for (int kg = 0; kg < BK; kg += 8) {
+        for (int kk = 0; kk < KSLICE; kk += 8) {
+            const int kg = wk * KSLICE + kk;
             floatx4 af[TM];
 #pragma unroll
             for (int a = 0; a < TM; ++a)
@@ -253,6 +273,38 @@ sgemm_mfma(GemmArgs p, int group_m)
         __syncthreads();
     }
     compute((nk - 1) & 1);
+
+    if constexpr (WGK > 1) {
+        // Groups 1..WGK-1 hand their partial sums to group 0 through LDS (the ring is
+        // free once every wave has passed the barrier); group 0 adds them in group order.
+        constexpr int PER_WAVE = TM * TN * 16 * 64;
+        const int slot = wm * WGN + wn;
+        __syncthreads();
+        if (wk > 0) {
+            float *dst = smem + ((wk - 1) * (WGM * WGN) + slot) * PER_WAVE;
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        dst[((a * TN + b) * 16 + e) * 64 + lane] = acc[a][b][e];
+        }
+        __syncthreads();
+        if (wk > 0)
+            return;
+#pragma unroll
+        for (int g = 1; g < WGK; ++g) {
+            const float *src = smem + ((g - 1) * (WGM * WGN) + slot) * PER_WAVE;
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc[a][b][e] += src[((a * TN + b) * 16 + e) * 64 + lane];
+        }
+    }
 
     // Epilogue: C = alpha*acc + beta*C, C unread when beta == 0.
     const float alpha = p.alpha, beta = p.beta;

@@ -90,8 +90,11 @@ def make(w: Gemm):
 
     C is drawn only when beta != 0; otherwise it is None (the product ignores it).
     Entries in the padding columns (index >= K, N, N) are NaN so that any read
-    of them shows up in a result.
+    of them shows up in a result. The GPT-2 workloads come from ``gpt2_linear_set``.
     """
+    if w.name.startswith("gpt2_"):
+        X, W = {name: (x, wt) for name, x, wt in gpt2_linear_set(w.seed)}[w.name]
+        return X, W, None
     rng = np.random.default_rng(w.seed)
     A = _padded(draw(rng, (w.M, w.K), w.dist_a), w.lda_)
     B = _padded(draw(rng, (w.K, w.N), w.dist_b), w.ldb_)
@@ -135,4 +138,10 @@ WORKLOADS = {
                    note="4096^3, A,B,C U[-1,1), alpha=1.5, beta=0.5 (full epilogue)"),
     "ragged": Gemm("ragged", 1000, 1537, 777, dist_a="normal", dist_b="normal", seed=3,
                    note="1000x1537x777, N(0,1), lda=777, ldb=ldc=1537 (unaligned rows)"),
+    "gpt2_qkv": Gemm("gpt2_qkv", 1024, 2304, 768, dist_a="normal", dist_b="normal002", seed=4,
+                     note="GPT-2-small QKV projection, 1024 tokens: X[1024x768] W[768x2304]"),
+    "gpt2_mlp_up": Gemm("gpt2_mlp_up", 1024, 3072, 768, dist_a="normal", dist_b="normal002", seed=4,
+                        note="GPT-2-small MLP up, 1024 tokens: X[1024x768] W[768x3072]"),
+    "gpt2_mlp_down": Gemm("gpt2_mlp_down", 1024, 768, 3072, dist_a="normal", dist_b="normal002", seed=4,
+                          note="GPT-2-small MLP down, 1024 tokens: X[1024x3072] W[3072x768]"),
 }
