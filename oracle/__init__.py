@@ -26,7 +26,11 @@ import threading
 
 import numpy as np
 
-__all__ = ["sgemm", "sgemm_entries", "within_bound", "threads", "build", "LIB_PATH"]
+__all__ = ["sgemm", "sgemm_entries", "gemm", "gemm_entries", "gelu_tanh", "within_bound", "threads",
+           "build", "LIB_PATH", "ACT_NONE", "ACT_GELU_TANH"]
+
+ACT_NONE = 0
+ACT_GELU_TANH = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC_PATH = os.path.join(_HERE, "sgemm_oracle.c")
@@ -70,6 +74,20 @@ def _load():
                 _F32P, ctypes.c_int64, _F32P, ctypes.c_int64,
                 ctypes.c_float, _F32P, ctypes.c_int64,
                 ctypes.c_int64, _I64P, _I64P, _F64P, _F64P]
+            lib.oracle_gemm_f64.restype = ctypes.c_int
+            lib.oracle_gemm_f64.argtypes = [
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                _F32P, ctypes.c_int64, _F32P, ctypes.c_int64,
+                ctypes.c_float, _F32P, ctypes.c_int64, _F32P, ctypes.c_int,
+                _F64P, ctypes.c_int64, _F64P, ctypes.c_int64]
+            lib.oracle_gemm_entries_f64.restype = ctypes.c_int
+            lib.oracle_gemm_entries_f64.argtypes = [
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                _F32P, ctypes.c_int64, _F32P, ctypes.c_int64,
+                ctypes.c_float, _F32P, ctypes.c_int64, _F32P, ctypes.c_int,
+                ctypes.c_int64, _I64P, _I64P, _F64P, _F64P]
+            lib.oracle_gelu_tanh.restype = ctypes.c_double
+            lib.oracle_gelu_tanh.argtypes = [ctypes.c_double]
             _lib = lib
     return _lib
 
@@ -137,6 +155,77 @@ def sgemm_entries(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, rows, cols):
         raise IndexError("sampled entry outside the M x N result")
     del ka, kb, kc
     return ref, bound
+
+
+def _operand_rows(op, rows_as_read, cols_as_read):
+    """Stored (rows, cols) of an operand read as rows_as_read x cols_as_read under op."""
+    return (cols_as_read, rows_as_read) if op else (rows_as_read, cols_as_read)
+
+
+def gemm(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias=None, act=ACT_NONE, *,
+         with_bound=True):
+    """Oracle (ref, bound) for act(alpha * op(A) op(B) + beta * C + bias) on the M x N window.
+
+    op == 0 reads an operand as stored, op == 1 its transpose (A stored K x M, B stored
+    N x K, row-major with leading dimension lda / ldb). bias has N entries (by column) or
+    is None; act is ACT_NONE or ACT_GELU_TANH.
+    """
+    lib = _load()
+    nonempty = M > 0 and N > 0
+    use_ab = nonempty and alpha != 0.0 and K > 0
+    ar, ac = _operand_rows(opA, M, K)
+    br, bc = _operand_rows(opB, K, N)
+    pa, ka = _fptr(A, ar if use_ab else 0, lda, ac, "A")
+    pb, kb = _fptr(B, br if use_ab else 0, ldb, bc, "B")
+    pc, kc = _fptr(C, M if (nonempty and beta != 0.0) else 0, ldc, N, "C")
+    pbias, kbias = _fptr(bias, 1 if (nonempty and bias is not None) else 0, N, N, "bias")
+    ref = np.empty((M, N), dtype=np.float64)
+    bound = np.empty((M, N), dtype=np.float64) if with_bound else None
+    rc = lib.oracle_gemm_f64(
+        int(opA), int(opB), M, N, K, float(alpha), pa, lda, pb, ldb, float(beta), pc, ldc, pbias, int(act),
+        ref.ctypes.data_as(_F64P), N,
+        bound.ctypes.data_as(_F64P) if with_bound else ctypes.cast(None, _F64P), N)
+    if rc == -2:
+        raise ValueError("op must be 0 or 1 and act must be ACT_NONE or ACT_GELU_TANH")
+    if rc != 0:
+        raise MemoryError("oracle_gemm_f64 could not allocate its row buffers")
+    del ka, kb, kc, kbias
+    return ref, bound
+
+
+def gemm_entries(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, rows, cols, bias=None,
+                 act=ACT_NONE):
+    """Oracle (ref, bound) for the sampled entries (rows[e], cols[e]) of ``gemm``."""
+    lib = _load()
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols must have the same shape")
+    nonempty = M > 0 and N > 0 and rows.size > 0
+    use_ab = nonempty and alpha != 0.0 and K > 0
+    ar, ac = _operand_rows(opA, M, K)
+    br, bc = _operand_rows(opB, K, N)
+    pa, ka = _fptr(A, ar if use_ab else 0, lda, ac, "A")
+    pb, kb = _fptr(B, br if use_ab else 0, ldb, bc, "B")
+    pc, kc = _fptr(C, M if (nonempty and beta != 0.0) else 0, ldc, N, "C")
+    pbias, kbias = _fptr(bias, 1 if (nonempty and bias is not None) else 0, N, N, "bias")
+    ref = np.empty(rows.shape, dtype=np.float64)
+    bound = np.empty(rows.shape, dtype=np.float64)
+    rc = lib.oracle_gemm_entries_f64(
+        int(opA), int(opB), M, N, K, float(alpha), pa, lda, pb, ldb, float(beta), pc, ldc, pbias, int(act),
+        rows.size, rows.ctypes.data_as(_I64P), cols.ctypes.data_as(_I64P),
+        ref.ctypes.data_as(_F64P), bound.ctypes.data_as(_F64P))
+    if rc == -2:
+        raise ValueError("op must be 0 or 1 and act must be ACT_NONE or ACT_GELU_TANH")
+    if rc != 0:
+        raise IndexError("sampled entry outside the M x N result")
+    del ka, kb, kc, kbias
+    return ref, bound
+
+
+def gelu_tanh(x: float) -> float:
+    """The oracle's fp64 tanh-form GELU, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    return float(_load().oracle_gelu_tanh(float(x)))
 
 
 def within_bound(c, ref, bound):

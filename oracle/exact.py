@@ -21,10 +21,15 @@ import numpy as np
 __all__ = ["sgemm_exact"]
 
 
-def sgemm_exact(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
-    """Return the exact result as an M x N nested list of Fractions."""
+def sgemm_exact(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, opA=0, opB=0, bias=None):
+    """Return the exact result as an M x N nested list of Fractions.
+
+    opA/opB = 1 read the transposed operand (A stored K x M, B stored N x K); bias
+    (length N, by column) is added after the scaled product.
+    """
     a = np.asarray(A, dtype=np.float32).reshape(-1)
     b = np.asarray(B, dtype=np.float32).reshape(-1)
+    bb = None if bias is None else np.asarray(bias, dtype=np.float32).reshape(-1)
     fa = Fraction(float(np.float32(alpha)))
     fb = Fraction(float(np.float32(beta)))
     out = []
@@ -34,11 +39,14 @@ def sgemm_exact(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
             s = Fraction(0)
             if fa != 0:
                 for k in range(K):
-                    s += Fraction(float(a[i * lda + k])) * Fraction(float(b[k * ldb + j]))
+                    av = a[k * lda + i] if opA else a[i * lda + k]
+                    bv = b[j * ldb + k] if opB else b[k * ldb + j]
+                    s += Fraction(float(av)) * Fraction(float(bv))
             t = Fraction(0)
             if fb != 0:
                 c = np.asarray(C, dtype=np.float32).reshape(-1)
                 t = fb * Fraction(float(c[i * ldc + j]))
-            row.append(fa * s + t)
+            bias_j = Fraction(0) if bb is None else Fraction(float(bb[j]))
+            row.append(fa * s + t + bias_j)
         out.append(row)
     return out

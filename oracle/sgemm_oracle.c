@@ -27,6 +27,9 @@
  *    "GPU Target - GPT-2 on the GPU", section "Running it". That is why the
  *    comparison is against a bound and not bitwise.
  *
+ * The general entry point also takes operand transposes, a per-column bias and a
+ * GELU activation (documented at oracle_gemm_f64 below).
+ *
  * Readings where the pages are silent:
  *  - alpha == 0 or K == 0: A and B are not read and s = g = 0 (the usual BLAS
  *    quick return), so the result is beta*C.
@@ -58,27 +61,74 @@ int oracle_threads(void)
 #endif
 }
 
-static double bound_scale(int K)
+/* Operand forms: op == 0 reads the matrix as stored, op == 1 reads its transpose. */
+static double a_at(const float *A, int64_t lda, int opA, int64_t i, int64_t k)
 {
-    return 4.0 * (double)(K > 1 ? K : 1) * ldexp(1.0, -24);
+    return (double)(opA ? A[k * lda + i] : A[i * lda + k]);
+}
+
+static double b_at(const float *B, int64_t ldb, int opB, int64_t k, int64_t j)
+{
+    return (double)(opB ? B[j * ldb + k] : B[k * ldb + j]);
+}
+
+/* GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). */
+double oracle_gelu_tanh(double x)
+{
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
+}
+
+/* Largest slope of the tanh-form GELU over the reals (attained near x = 2.1); the
+ * bound below carries an input error through the activation with this factor. */
+#define GELU_SLOPE_MAX 1.13
+
+/* Result and bound of one entry from its fp64 sums. */
+static void finish(double s, double g, double c0, int K, float alpha, float beta, const float *bias,
+                   int64_t j, int act, double *ref, double *bound)
+{
+    const double t_c = (beta == 0.0f) ? 0.0 : (double)beta * c0;
+    const double b = bias ? (double)bias[j] : 0.0;
+    const double t = (double)alpha * s + t_c + b;
+    const double mag = fabs((double)alpha) * g + fabs(t_c) + fabs(b);
+    /* The plain product keeps the bound 4 max(K,1) u (|alpha| g + |beta c|); one more
+     * rounding (the bias add) widens the factor to 4 (max(K,1) + 1). */
+    double e = 4.0 * (double)((K > 1 ? K : 1) + (bias || act ? 1 : 0)) * ldexp(1.0, -24) * mag;
+    double r = t;
+    if (act == 1) {
+        r = oracle_gelu_tanh(t);
+        /* input error through the activation, plus fp32 evaluation of the formula */
+        e = GELU_SLOPE_MAX * e + 8.0 * ldexp(1.0, -24) * (fabs(t) + fabs(r));
+    }
+    *ref = r;
+    if (bound)
+        *bound = e;
 }
 
 /*
- * Full oracle. Writes ref (M x N, row stride ldr) and, when bound != NULL, the
- * per-entry bound (row stride ldbd). Returns 0, or -1 if a work array cannot be
- * allocated. C0 may be NULL when beta == 0.
+ * General oracle: C = act(alpha * op(A) op(B) + beta * C + bias) for the M x N window.
+ * op(A) is M x K and op(B) is K x N:
+ *   opA == 0: a_ik = A[i*lda + k]      opA == 1: a_ik = A[k*lda + i]
+ *   opB == 0: b_kj = B[k*ldb + j]      opB == 1: b_kj = B[j*ldb + k]
+ * bias (length N, by column) may be NULL; act is 0 (none) or 1 (tanh-form GELU).
+ * Operand transposes as strided views follow the GPT-2 post ("Tiled matrix
+ * multiplication"); the bias add after a product, and the GELU after the first MLP
+ * product, follow its traced model ("The whole model as one kernel") and its GELU
+ * kernel built from a power and a tanh ("From loops to kernels").
+ * Writes ref (row stride ldr) and, if bound != NULL, the bound (row stride ldbd).
+ * Returns 0, -1 if a work array cannot be allocated, -2 for a bad op or act.
  */
-int oracle_sgemm_f64(int M, int N, int K, float alpha,
-                     const float *A, int64_t lda,
-                     const float *B, int64_t ldb,
-                     float beta, const float *C0, int64_t ldc,
-                     double *ref, int64_t ldr,
-                     double *bound, int64_t ldbd)
+int oracle_gemm_f64(int opA, int opB, int M, int N, int K, float alpha,
+                    const float *A, int64_t lda, const float *B, int64_t ldb,
+                    float beta, const float *C0, int64_t ldc,
+                    const float *bias, int act,
+                    double *ref, int64_t ldr, double *bound, int64_t ldbd)
 {
+    if (opA < 0 || opA > 1 || opB < 0 || opB > 1 || act < 0 || act > 1)
+        return -2;
     if (M <= 0 || N <= 0)
         return 0;
     const int use_ab = (alpha != 0.0f) && (K > 0);
-    const double scale = bound_scale(K);
     int failed = 0;
 
 #pragma omp parallel
@@ -100,25 +150,23 @@ int oracle_sgemm_f64(int M, int N, int K, float alpha,
             if (use_ab) {
                 /* i-k-j order: for every j the terms still arrive in ascending k. */
                 for (int k = 0; k < K; ++k) {
-                    const double a = (double)A[(int64_t)i * lda + k];
-                    const float *brow = B + (int64_t)k * ldb;
+                    const double a = a_at(A, lda, opA, i, k);
                     if (bound != NULL) {
                         for (int j = 0; j < N; ++j) {
-                            const double p = a * (double)brow[j];
+                            const double p = a * b_at(B, ldb, opB, k, j);
                             s[j] += p;
                             g[j] += fabs(p);
                         }
                     } else {
                         for (int j = 0; j < N; ++j)
-                            s[j] += a * (double)brow[j];
+                            s[j] += a * b_at(B, ldb, opB, k, j);
                     }
                 }
             }
             for (int j = 0; j < N; ++j) {
-                const double t = (beta == 0.0f) ? 0.0 : (double)beta * (double)C0[(int64_t)i * ldc + j];
-                ref[(int64_t)i * ldr + j] = (double)alpha * s[j] + t;
-                if (bound != NULL)
-                    bound[(int64_t)i * ldbd + j] = scale * (fabs((double)alpha) * g[j] + fabs(t));
+                const double c0 = (beta == 0.0f) ? 0.0 : (double)C0[(int64_t)i * ldc + j];
+                finish(s[j], g[j], c0, K, alpha, beta, bias, j, act, &ref[(int64_t)i * ldr + j],
+                       bound ? &bound[(int64_t)i * ldbd + j] : NULL);
             }
         }
         free(s);
@@ -127,20 +175,33 @@ int oracle_sgemm_f64(int M, int N, int K, float alpha,
     return failed ? -1 : 0;
 }
 
+/* The plain product C = alpha*A*B + beta*C (both operands as stored, no bias). */
+int oracle_sgemm_f64(int M, int N, int K, float alpha,
+                     const float *A, int64_t lda,
+                     const float *B, int64_t ldb,
+                     float beta, const float *C0, int64_t ldc,
+                     double *ref, int64_t ldr,
+                     double *bound, int64_t ldbd)
+{
+    return oracle_gemm_f64(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, NULL, 0, ref, ldr,
+                           bound, ldbd);
+}
+
 /*
  * Sampled oracle: the same definition for `count` chosen entries (rows[e], cols[e]),
  * each a dot product over ascending k. Used where the full product is too large
- * to evaluate in seconds. Returns 0, or -1 if an index is out of range.
+ * to evaluate in seconds. Returns 0, -1 if an index is out of range, -2 for a bad op or act.
  */
-int oracle_sgemm_entries_f64(int M, int N, int K, float alpha,
-                             const float *A, int64_t lda,
-                             const float *B, int64_t ldb,
-                             float beta, const float *C0, int64_t ldc,
-                             int64_t count, const int64_t *rows, const int64_t *cols,
-                             double *ref, double *bound)
+int oracle_gemm_entries_f64(int opA, int opB, int M, int N, int K, float alpha,
+                            const float *A, int64_t lda, const float *B, int64_t ldb,
+                            float beta, const float *C0, int64_t ldc,
+                            const float *bias, int act,
+                            int64_t count, const int64_t *rows, const int64_t *cols,
+                            double *ref, double *bound)
 {
+    if (opA < 0 || opA > 1 || opB < 0 || opB > 1 || act < 0 || act > 1)
+        return -2;
     const int use_ab = (alpha != 0.0f) && (K > 0);
-    const double scale = bound_scale(K);
     for (int64_t e = 0; e < count; ++e)
         if (rows[e] < 0 || rows[e] >= M || cols[e] < 0 || cols[e] >= N)
             return -1;
@@ -151,15 +212,24 @@ int oracle_sgemm_entries_f64(int M, int N, int K, float alpha,
         double s = 0.0, g = 0.0;
         if (use_ab) {
             for (int k = 0; k < K; ++k) {
-                const double p = (double)A[i * lda + k] * (double)B[(int64_t)k * ldb + j];
+                const double p = a_at(A, lda, opA, i, k) * b_at(B, ldb, opB, k, j);
                 s += p;
                 g += fabs(p);
             }
         }
-        const double t = (beta == 0.0f) ? 0.0 : (double)beta * (double)C0[i * ldc + j];
-        ref[e] = (double)alpha * s + t;
-        if (bound != NULL)
-            bound[e] = scale * (fabs((double)alpha) * g + fabs(t));
+        const double c0 = (beta == 0.0f) ? 0.0 : (double)C0[i * ldc + j];
+        finish(s, g, c0, K, alpha, beta, bias, j, act, &ref[e], bound ? &bound[e] : NULL);
     }
     return 0;
+}
+
+int oracle_sgemm_entries_f64(int M, int N, int K, float alpha,
+                             const float *A, int64_t lda,
+                             const float *B, int64_t ldb,
+                             float beta, const float *C0, int64_t ldc,
+                             int64_t count, const int64_t *rows, const int64_t *cols,
+                             double *ref, double *bound)
+{
+    return oracle_gemm_entries_f64(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, NULL, 0, count,
+                                   rows, cols, ref, bound);
 }
