@@ -34,8 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3          # MI355X dense fp32 (matrix and vector), AMD's published figure
-KERNEL_SOURCES = [os.path.join(ROOT, "tiled_fp32_gemm_02_amd", "csrc", f)
-                  for f in ("sgemm_kernels.hpp", "sgemm_api.hip")]
+CSRC = os.path.join(ROOT, "tiled_fp32_gemm_02_amd", "csrc")
 
 
 def log(msg):
@@ -47,8 +46,10 @@ def kernel_source_hash() -> str:
     recorded counters stay valid across comment-only edits."""
     import re
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p) as f:
+    for name in sorted(os.listdir(CSRC)):
+        if not name.endswith((".hip", ".hpp", ".inc")):
+            continue
+        with open(os.path.join(CSRC, name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)

@@ -33,8 +33,8 @@
  *    + |beta*c_ij|) per entry. For one configuration, sizes and alignment, results
  *    are bitwise reproducible from run to run.
  *
- * Return values: 0 on success; -i when argument i (1-based, in declaration order)
- * is invalid; SGEMM_ERROR_TOO_LARGE or SGEMM_ERROR_BAD_CONFIG for the cases named
+ * Return values: 0 on success; -i when argument i (1-based, in declaration order;
+ * the first invalid one) is invalid; SGEMM_ERROR_TOO_LARGE or SGEMM_ERROR_BAD_CONFIG for the cases named
  * below; a positive hipError_t when the kernel launch fails. Errors raised while
  * the kernel runs surface at the caller's next synchronisation. Nothing throws.
  */
@@ -48,8 +48,17 @@ extern "C" {
 #define SGEMM_SUCCESS 0
 /* The tile grid of the problem does not fit one launch (more than 2^31-1 tiles). */
 #define SGEMM_ERROR_TOO_LARGE (-100)
-/* sgemm_ex: the configuration id is not in [-1, sgemm_config_count()). */
+/* sgemm_ex / sgemm_general: the configuration id is not in [-1, sgemm_config_count()). */
 #define SGEMM_ERROR_BAD_CONFIG (-101)
+
+/* Operand forms: read the matrix as stored, or its transpose. */
+#define SGEMM_OP_N 0
+#define SGEMM_OP_T 1
+
+/* Activations applied after the bias (sgemm_bias_act, sgemm_general). */
+#define SGEMM_ACT_NONE 0
+/* tanh-form GELU: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). */
+#define SGEMM_ACT_GELU_TANH 1
 
 /*
  * C <- alpha * A * B + beta * C (row-major fp32), on `stream`.
@@ -84,6 +93,57 @@ int sgemm_ex(int config, int M, int N, int K, float alpha,
              const float *B, int ldb,
              float beta, float *C, int ldc,
              void *stream);
+
+/*
+ * C <- alpha * op(A) * op(B) + beta * C, with op(A) M x K and op(B) K x N, where
+ *   opA == SGEMM_OP_N: op(A)(i,k) = A[i*lda + k]  (A stored M x K, lda >= max(1, K))
+ *   opA == SGEMM_OP_T: op(A)(i,k) = A[k*lda + i]  (A stored K x M, lda >= max(1, M))
+ *   opB == SGEMM_OP_N: op(B)(k,j) = B[k*ldb + j]  (B stored K x N, ldb >= max(1, N))
+ *   opB == SGEMM_OP_T: op(B)(k,j) = B[j*ldb + k]  (B stored N x K, ldb >= max(1, K))
+ * Transposed operands are read in place: the GPT-2 post's kernel takes transposed
+ * views without copies ("GPU Target - GPT-2 on the GPU", section "Tiled matrix
+ * multiplication"). The 128-bit path needs the stored rows' contiguous extent (K or M
+ * for A, N or K for B) to be a multiple of 4; otherwise as for sgemm.
+ *
+ * Arguments by position: 1 opA, 2 opB, 3 M, 4 N, 5 K, 6 alpha, 7 A, 8 lda, 9 B, 10 ldb,
+ * 11 beta, 12 C, 13 ldc, 14 stream. opA and opB must be SGEMM_OP_N or SGEMM_OP_T.
+ */
+int sgemm_op(int opA, int opB, int M, int N, int K, float alpha,
+             const float *A, int lda,
+             const float *B, int ldb,
+             float beta, float *C, int ldc,
+             void *stream);
+
+/*
+ * C <- act(alpha * op(A) * op(B) + beta * C + bias), with bias[j] added to column j
+ * (bias has N entries, or is NULL for none) and act SGEMM_ACT_NONE or
+ * SGEMM_ACT_GELU_TANH applied last. This is a GPT-2 linear layer, x @ W + b, optionally
+ * followed by its GELU ("GPU Target - GPT-2 on the GPU", sections "The whole model as
+ * one kernel" and "From loops to kernels"), fused into the product's final write.
+ * With alpha == 0 or K == 0 the result is act(beta * C + bias).
+ * Results match the oracle within 4*(max(K,1)+1)*2^-24*(|alpha|*sum|a*b| + |beta*c| +
+ * |bias_j|), carried through GELU with a factor 1.13 plus 8*2^-24*(|t| + |gelu(t)|).
+ *
+ * Arguments by position: 1 opA, 2 opB, 3 M, 4 N, 5 K, 6 alpha, 7 A, 8 lda, 9 B, 10 ldb,
+ * 11 beta, 12 C, 13 ldc, 14 bias, 15 act, 16 stream.
+ */
+int sgemm_bias_act(int opA, int opB, int M, int N, int K, float alpha,
+                   const float *A, int lda,
+                   const float *B, int ldb,
+                   float beta, float *C, int ldc,
+                   const float *bias, int act,
+                   void *stream);
+
+/*
+ * sgemm_bias_act with the kernel configuration chosen by the caller (config as for
+ * sgemm_ex; it is not counted in argument positions). Used by tests and sweeps.
+ */
+int sgemm_general(int config, int opA, int opB, int M, int N, int K, float alpha,
+                  const float *A, int lda,
+                  const float *B, int ldb,
+                  float beta, float *C, int ldc,
+                  const float *bias, int act,
+                  void *stream);
 
 /*
  * Strided-batched form: for b in [0, batch), C_b <- alpha * A_b * B_b + beta * C_b with

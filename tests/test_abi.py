@@ -170,3 +170,43 @@ def test_tensor_form_validates_before_any_launch():
         sg.gemm(a, torch.zeros(3, 2))
     with pytest.raises(ValueError, match="Dimension error"):
         sg.gemm_batched(a, torch.zeros(3, 2))
+
+
+@pytest.mark.parametrize("args,code", [
+    # sgemm_op(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc)
+    ((2, 0, 4, 4, 4, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4), -1),
+    ((0, -1, 4, 4, 4, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4), -2),
+    ((0, 0, -1, 4, 4, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4), -3),
+    ((0, 0, 4, 4, -1, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4), -5),
+    ((0, 0, 4, 4, 4, 1.0, None, 4, BAD, 4, 0.0, BAD, 4), -7),
+    ((1, 0, 6, 4, 8, 1.0, BAD, 5, BAD, 4, 0.0, BAD, 4), -8),     # transposed A: lda >= M
+    ((0, 1, 4, 6, 8, 1.0, BAD, 8, BAD, 7, 0.0, BAD, 6), -10),    # transposed B: ldb >= K
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, BAD, 4, 0.0, None, 4), -12),
+    ((0, 0, 4, 5, 4, 1.0, BAD, 4, BAD, 5, 0.0, BAD, 4), -13),
+])
+def test_op_invalid_arguments(args, code):
+    assert sg.sgemm_op(*args) == code
+    # the fused form numbers the same arguments the same way
+    assert sg.sgemm_bias_act(*args, None, sg.SGEMM_ACT_NONE) == code
+
+
+def test_bias_act_invalid_act():
+    args = (0, 0, 4, 4, 4, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4, None)
+    assert sg.sgemm_bias_act(*args, 2) == -15
+    assert sg.sgemm_bias_act(*args, -1) == -15
+    assert sg.sgemm_general(0, *args, 7) == -15
+    assert sg.sgemm_general(-2, *args, 0) == sg.SGEMM_ERROR_BAD_CONFIG
+
+
+def test_op_quick_returns_touch_nothing():
+    assert sg.sgemm_op(1, 1, 0, 5, 3, 1.0, None, 1, None, 3, 0.0, None, 5) == 0
+    assert sg.sgemm_bias_act(1, 0, 5, 0, 3, 1.0, None, 5, None, 1, 0.0, None, 1, None, 1) == 0
+
+
+def test_tensor_form_rejects_host_views():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(6, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        sg.gemm(x.t(), torch.zeros(6, 3))
+    with pytest.raises(ValueError, match="Dimension error"):
+        sg.gemm(torch.zeros(2, 3, 4), torch.zeros(4, 3))

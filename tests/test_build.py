@@ -28,21 +28,23 @@ def kernels(tmp_path_factory):
     path = str(tmp_path_factory.mktemp("asm") / "sgemm.s")
     sgbuild.device_asm(path)
     text = open(path).read()
-    meta = re.search(r"\.amdgpu_metadata\n(.*?)\.end_amdgpu_metadata", text, re.S).group(1)
-    meta = yaml.safe_load(meta.replace("\t", "  "))
     out = {}
-    for k in meta["amdhsa.kernels"]:
-        name = k[".name"]
-        body = re.search(r"^" + re.escape(name) + r":[^\n]*\n(.*?)s_endpgm", text, re.S | re.M).group(1)
-        demangled = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip()
-        out[demangled] = (k, body)
+    for block in re.findall(r"\.amdgpu_metadata\n(.*?)\.end_amdgpu_metadata", text, re.S):
+        meta = yaml.safe_load(block.replace("\t", "  "))
+        for k in meta["amdhsa.kernels"]:
+            name = k[".name"]
+            body = re.search(r"^" + re.escape(name) + r":[^\n]*\n(.*?)s_endpgm", text, re.S | re.M).group(1)
+            demangled = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip()
+            out[demangled] = (k, body)
     return out
 
 
 def test_all_kernels_present(kernels):
     names = " ".join(kernels)
     assert "sgemm_tile16" in names and "sgemm_scale" in names
-    assert sum("sgemm_mfma<" in n for n in kernels) >= 3
+    mfma = [n for n in kernels if "sgemm_mfma<" in n]
+    # every configuration x 4 operand forms x 3 alignment/edge variants
+    assert len(mfma) == 12 * (len(__import__("tiled_fp32_gemm_02_amd").configs()) - 1), len(mfma)
 
 
 def test_no_scratch_no_spills(kernels):

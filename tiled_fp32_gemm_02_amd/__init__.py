@@ -10,12 +10,16 @@ Raw entry points take device addresses as Python ints (or CUDA tensors, whose
 
     sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
     sgemm_ex(config, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    sgemm_op(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    sgemm_bias_act(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream)
+    sgemm_general(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream)
     sgemm_strided_batched(M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch, stream)
 
-``gemm(A, B, C=None, alpha=1, beta=0)`` is the tensor-level form: it checks
-shapes, dtypes and devices, fills in the leading dimensions from the tensors'
-strides, raises ``ValueError``/``RuntimeError`` on bad input or a nonzero status,
-and returns C.
+``gemm(A, B, C=None, alpha=1, beta=0, bias=None, act=None)`` is the tensor-level
+form: it checks shapes, dtypes and devices, reads a transposed view (unit row
+stride) as a transposed operand in place, fills in the leading dimensions from the
+tensors' strides, raises ``ValueError``/``RuntimeError`` on bad input or a nonzero
+status, and returns C.
 """
 
 from __future__ import annotations
@@ -27,12 +31,17 @@ import threading
 __all__ = [
     "load", "lib_path", "sgemm", "sgemm_ex", "sgemm_strided_batched", "sgemm_config_count",
     "sgemm_config_name", "sgemm_select_config", "sgemm_launch_shape", "sgemm_status_string",
-    "sgemm_version", "configs", "gemm", "gemm_batched", "check", "SgemmError",
-    "SGEMM_ERROR_TOO_LARGE", "SGEMM_ERROR_BAD_CONFIG",
+    "sgemm_version", "sgemm_op", "sgemm_bias_act", "sgemm_general", "configs", "gemm", "gemm_batched",
+    "check", "SgemmError", "SGEMM_ERROR_TOO_LARGE", "SGEMM_ERROR_BAD_CONFIG", "SGEMM_OP_N", "SGEMM_OP_T",
+    "SGEMM_ACT_NONE", "SGEMM_ACT_GELU_TANH",
 ]
 
 SGEMM_ERROR_TOO_LARGE = -100
 SGEMM_ERROR_BAD_CONFIG = -101
+SGEMM_OP_N = 0
+SGEMM_OP_T = 1
+SGEMM_ACT_NONE = 0
+SGEMM_ACT_GELU_TANH = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsgemm.so")
@@ -45,6 +54,15 @@ _SIGS = {
                              _fp, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, _fp]),
     "sgemm_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp,
                                 ctypes.c_int, _fp, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, _fp]),
+    "sgemm_op": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int, ctypes.c_float, _fp,
+                                ctypes.c_int, _fp]),
+    "sgemm_bias_act": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int, ctypes.c_float,
+                                      _fp, ctypes.c_int, _fp, ctypes.c_int, _fp]),
+    "sgemm_general": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int,
+                                     ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int, _fp]),
     "sgemm_strided_batched": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, ctypes.c_longlong,
         _fp, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, _fp, ctypes.c_int, ctypes.c_longlong,
@@ -119,6 +137,21 @@ def sgemm_ex(config, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) 
                            _stream(stream))
 
 
+def sgemm_op(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    return load().sgemm_op(opA, opB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                           _stream(stream))
+
+
+def sgemm_bias_act(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream=None) -> int:
+    return load().sgemm_bias_act(opA, opB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                                 _addr(bias), act, _stream(stream))
+
+
+def sgemm_general(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream=None) -> int:
+    return load().sgemm_general(config, opA, opB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C),
+                                ldc, _addr(bias), act, _stream(stream))
+
+
 def sgemm_strided_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
                           batch, stream=None) -> int:
     return load().sgemm_strided_batched(M, N, K, alpha, _addr(A), lda, strideA, _addr(B), ldb, strideB,
@@ -166,13 +199,18 @@ def check(status: int, what: str = "sgemm") -> None:
 
 # --------------------------------------------------------------------------- tensor form
 
-def _row_major_ld(t, name):
+def _check_matrix(t, name):
     if t.dim() != 2:
         raise ValueError(f"Dimension error: {name} must be a 2-D matrix, got {t.dim()} dimensions")
-    if t.dtype.__str__() != "torch.float32":
+    if str(t.dtype) != "torch.float32":
         raise ValueError(f"{name} must be float32, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _row_major_ld(t, name):
+    """Leading dimension of a row-major matrix view (unit column stride)."""
+    _check_matrix(t, name)
     rows, cols = t.shape
     if cols > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must be row-major with unit column stride (got strides {tuple(t.stride())})")
@@ -180,20 +218,48 @@ def _row_major_ld(t, name):
     return max(ld, cols, 1)
 
 
-def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None, config: int = -1):
-    """C <- alpha*A@B + beta*C on GPU float32 tensors (row-major, unit column stride).
+def _operand(t, name):
+    """(op, ld) for an operand view: a row-major view is read as stored (SGEMM_OP_N);
+    a transposed view of a row-major matrix (unit row stride) is read in place as a
+    transpose (SGEMM_OP_T), with the stored matrix's row stride as ld."""
+    _check_matrix(t, name)
+    rows, cols = t.shape
+    if cols <= 1 or t.stride(1) == 1:
+        return SGEMM_OP_N, _row_major_ld(t, name)
+    if rows <= 1 or t.stride(0) == 1:
+        ld = t.stride(1) if cols > 1 else max(rows, 1)
+        return SGEMM_OP_T, max(ld, rows, 1)
+    raise ValueError(f"{name} needs a unit stride in one dimension (got strides {tuple(t.stride())})")
 
-    A is M x K, B is K x N and C is M x N; C may be a view with a larger row stride.
-    When C is None a new M x N tensor is allocated (then beta must be 0). Returns C.
+
+_ACTS = {None: SGEMM_ACT_NONE, "none": SGEMM_ACT_NONE, "gelu_tanh": SGEMM_ACT_GELU_TANH}
+
+
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None, config: int = -1, bias=None,
+         act=None):
+    """C <- act(alpha*A@B + beta*C + bias) on GPU float32 tensors.
+
+    A is M x K, B is K x N and C is M x N. A and B may be row-major views or
+    transposed views (``x.t()``) of row-major matrices, read in place. C must be
+    row-major and may have a larger row stride. bias is a length-N float32 GPU
+    vector or None; act is None, "none" or "gelu_tanh". When C is None a new
+    M x N tensor is allocated (then beta must be 0). Returns C.
     """
     import torch
 
-    lda = _row_major_ld(A, "A")
-    ldb = _row_major_ld(B, "B")
+    opA, lda = _operand(A, "A")
+    opB, ldb = _operand(B, "B")
     M, K = A.shape
     if B.shape[0] != K:
         raise ValueError(f"Size error: A is {tuple(A.shape)} and B is {tuple(B.shape)}; inner sizes differ")
     N = B.shape[1]
+    if act not in _ACTS:
+        raise ValueError(f"act must be one of {sorted(k for k in _ACTS if k)} or None, got {act!r}")
+    if bias is not None:
+        if bias.dim() != 1 or bias.shape[0] != N or str(bias.dtype) != "torch.float32" or not bias.is_cuda:
+            raise ValueError(f"bias must be a float32 GPU vector of length {N}")
+        if bias.stride(0) != 1 and N > 1:
+            raise ValueError("bias must be contiguous")
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an input C")
@@ -203,7 +269,8 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None, confi
         raise ValueError(f"Size error: C is {tuple(C.shape)}, expected {(M, N)}")
     if stream is None:
         stream = torch.cuda.current_stream(A.device)
-    check(sgemm_ex(config, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream), "sgemm")
+    check(sgemm_general(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, _ACTS[act],
+                        stream), "sgemm_general")
     return C
 
 

@@ -1,10 +1,16 @@
 """Build the HIP library ``libsgemm.so`` in-tree for gfx950.
 
-One translation unit (``csrc/sgemm_api.hip``, which includes the kernels) is
-compiled by hipcc into a shared library next to this file. Flags:
+Translation units, compiled in parallel by hipcc and linked into one shared
+library next to this file:
+
+* ``csrc/sgemm_api.hip``: the C ABI, the 16x16 baseline kernel and the scale kernel;
+* ``csrc/sgemm_inst.hip`` four times, once per operand form (SGEMM_TA, SGEMM_TB),
+  each instantiating every MFMA configuration of ``csrc/sgemm_configs.inc``.
+
+Flags:
 
 * ``--offload-arch=gfx950``: MI355X only; no other targets, no CUDA.
-* ``-O3 -std=c++17 -fPIC -shared``.
+* ``-O3 -std=c++17 -fPIC``.
 * ``-Xclang -target-feature -Xclang -packed-fp32-ops``: keep the compiler from
   emitting packed fp32 VALU instructions. The GEMM's arithmetic runs on the
   matrix cores; the packed forms are not trusted on the target machines.
@@ -15,13 +21,13 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = [os.path.join(CSRC, "sgemm_api.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, "sgemm_kernels.hpp"), os.path.join(INCLUDE, "sgemm.h")]
 LIB_PATH = os.path.join(HERE, "libsgemm.so")
 ARCH = "gfx950"
 
@@ -31,6 +37,14 @@ COMMON_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
+# (source, extra defines, object stem)
+UNITS = [("sgemm_api.hip", [], "api")] + [
+    ("sgemm_inst.hip", [f"-DSGEMM_TA={ta}", f"-DSGEMM_TB={tb}"], f"inst_{'t' if ta else 'n'}{'t' if tb else 'n'}")
+    for ta in (0, 1) for tb in (0, 1)
+]
+SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                 if f.endswith((".hip", ".hpp", ".inc")))
+
 
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -38,24 +52,52 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libsgemm.so (always recompiles). Returns its path."""
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *COMMON_FLAGS, "-fPIC", "-shared", *SOURCES, "-o", tmp]
+def _jobs() -> int:
+    return max(1, min(len(UNITS), os.cpu_count() or 1, int(os.environ.get("MAX_JOBS", "16"))))
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}: {' '.join(cmd)}")
+    return res
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libsgemm.so (always recompiles). Returns its path."""
+    with tempfile.TemporaryDirectory(prefix="sgemm_build_") as tmpdir:
+        objs = []
+        cmds = []
+        for src, defs, stem in UNITS:
+            obj = os.path.join(tmpdir, stem + ".o")
+            objs.append(obj)
+            cmds.append([hipcc(), *COMMON_FLAGS, "-fPIC", *defs, "-c", os.path.join(CSRC, src), "-o", obj])
+        with ThreadPoolExecutor(max_workers=_jobs()) as pool:
+            list(pool.map(lambda c: _run(c, verbose), cmds))
+        tmp = LIB_PATH + f".tmp{os.getpid()}"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
 
 def device_asm(out_path: str) -> str:
-    """Write the gfx950 assembly of the library's device code (for resource checks)."""
-    cmd = [hipcc(), *COMMON_FLAGS, "--cuda-device-only", "-S", *SOURCES, "-o", out_path]
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    """Write the gfx950 assembly of all device code (the units' .s files, concatenated)."""
+    with tempfile.TemporaryDirectory(prefix="sgemm_asm_") as tmpdir:
+        cmds, outs = [], []
+        for src, defs, stem in UNITS:
+            out = os.path.join(tmpdir, stem + ".s")
+            outs.append(out)
+            cmds.append([hipcc(), *COMMON_FLAGS, *defs, "--cuda-device-only", "-S", os.path.join(CSRC, src),
+                         "-o", out])
+        with ThreadPoolExecutor(max_workers=_jobs()) as pool:
+            list(pool.map(lambda c: _run(c, False), cmds))
+        with open(out_path, "w") as f:
+            for out in outs:
+                f.write(open(out).read())
+                f.write("\n")
     return out_path
 
 

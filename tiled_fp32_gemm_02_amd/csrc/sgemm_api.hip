@@ -2,16 +2,17 @@
 //
 // Host work per call: validate the arguments (BLAS-style argument positions in the
 // error code), take the quick returns (empty result; alpha == 0 or K == 0 leaves
-// beta*C), choose a kernel configuration from the shape and alignment, and queue
-// one kernel on the caller's stream. No allocation, copy or synchronisation.
+// act(beta*C + bias)), choose a kernel configuration from the shape and alignment,
+// and queue one kernel on the caller's stream. No allocation, copy or
+// synchronisation.
 #include <hip/hip_runtime.h>
 
-#include <climits>
 #include <cstdint>
-#include <cstring>
 
 #include "sgemm.h"
-#include "sgemm_kernels.hpp"
+#include "sgemm_configs.inc"
+#include "sgemm_aux_kernels.hpp"
+#include "sgemm_launch.hpp"
 
 using sgemm_impl::GemmArgs;
 
@@ -19,75 +20,65 @@ namespace {
 
 enum Kind { KIND_TILE16 = 0, KIND_MFMA = 1 };
 
-typedef hipError_t (*LaunchFn)(const GemmArgs &, int batch, bool vec, bool edge, hipStream_t);
+typedef hipError_t (*LaunchFn)(const GemmArgs &, int batch, bool ta, bool tb, bool vec, bool edge, hipStream_t);
 
 struct Config {
     const char *name;
     Kind kind;
     int bm, bn, bk;      // workgroup tile (tile16: 16 x 16 x 16)
     int threads;         // threads per workgroup
-    int group_m;         // tile rows per L2 band in the workgroup order
     LaunchFn launch;
 };
 
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int GROUP_M>
-hipError_t launch_mfma(const GemmArgs &p, int batch, bool vec, bool edge, hipStream_t s)
+hipError_t launch_mfma(const GemmArgs &p, int batch, bool ta, bool tb, bool vec, bool edge, hipStream_t s)
 {
-    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    const dim3 grid(tiles, 1, batch), block(WGM * WGN * WGK * 64);
-    if (vec && !edge)
-        hipLaunchKernelGGL((sgemm_impl::sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, true, false>), grid, block, 0, s, p,
-                           GROUP_M);
-    else if (vec)
-        hipLaunchKernelGGL((sgemm_impl::sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, true, true>), grid, block, 0, s, p,
-                           GROUP_M);
-    else
-        hipLaunchKernelGGL((sgemm_impl::sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, false, true>), grid, block, 0, s, p,
-                           GROUP_M);
-    return hipGetLastError();
+    if (!ta && !tb)
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, GROUP_M, false, false>(p, batch, vec, edge, s);
+    if (!ta && tb)
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, GROUP_M, false, true>(p, batch, vec, edge, s);
+    if (ta && !tb)
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, GROUP_M, true, false>(p, batch, vec, edge, s);
+    return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, GROUP_M, true, true>(p, batch, vec, edge, s);
 }
 
-hipError_t launch_tile16(const GemmArgs &p, int batch, bool, bool, hipStream_t s)
+hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, bool, hipStream_t s)
 {
     const dim3 grid((p.N + 15) / 16, (p.M + 15) / 16, batch), block(16, 16);
-    hipLaunchKernelGGL(sgemm_impl::sgemm_tile16, grid, block, 0, s, p);
+    if (!ta && !tb)
+        hipLaunchKernelGGL((sgemm_impl::sgemm_tile16<false, false>), grid, block, 0, s, p);
+    else if (!ta && tb)
+        hipLaunchKernelGGL((sgemm_impl::sgemm_tile16<false, true>), grid, block, 0, s, p);
+    else if (ta && !tb)
+        hipLaunchKernelGGL((sgemm_impl::sgemm_tile16<true, false>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((sgemm_impl::sgemm_tile16<true, true>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
-// Configuration table. Ids are stable within one build; names encode the tile
-// (BM x BN x BK), the wave grid (WGM x WGN) and, after "k", the wave groups along k.
+// Configuration table: id 0 is the 16x16 baseline kernel, ids 1.. the MFMA
+// configurations of sgemm_configs.inc in order. Names encode the tile (BM x BN x BK),
+// the wave grid (WGM x WGN) and, after "k", the wave groups along k.
+#define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, GROUP_M) \
+    {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, launch_mfma<BM, BN, BK, WGM, WGN, WGK, GROUP_M>},
 const Config kConfigs[] = {
-    {"tile16", KIND_TILE16, 16, 16, 16, 256, 1, launch_tile16},
-    {"mfma_64x64x16_w2x2", KIND_MFMA, 64, 64, 16, 256, 8, launch_mfma<64, 64, 16, 2, 2, 1, 8>},
-    {"mfma_128x128x16_w2x2", KIND_MFMA, 128, 128, 16, 256, 8, launch_mfma<128, 128, 16, 2, 2, 1, 8>},
-    {"mfma_128x128x32_w2x2", KIND_MFMA, 128, 128, 32, 256, 8, launch_mfma<128, 128, 32, 2, 2, 1, 8>},
-    {"mfma_256x128x16_w2x2", KIND_MFMA, 256, 128, 16, 256, 4, launch_mfma<256, 128, 16, 2, 2, 1, 4>},
-    {"mfma_256x256x16_w2x4", KIND_MFMA, 256, 256, 16, 512, 4, launch_mfma<256, 256, 16, 2, 4, 1, 4>},
-    {"mfma_64x64x32_w2x2", KIND_MFMA, 64, 64, 32, 256, 8, launch_mfma<64, 64, 32, 2, 2, 1, 8>},
-    {"mfma_128x64x16_w2x2", KIND_MFMA, 128, 64, 16, 256, 8, launch_mfma<128, 64, 16, 2, 2, 1, 8>},
-    {"mfma_64x128x16_w2x2", KIND_MFMA, 64, 128, 16, 256, 8, launch_mfma<64, 128, 16, 2, 2, 1, 8>},
-    {"mfma_256x256x32_w2x4", KIND_MFMA, 256, 256, 32, 512, 4, launch_mfma<256, 256, 32, 2, 4, 1, 4>},
-    {"mfma_256x128x16_w4x2", KIND_MFMA, 256, 128, 16, 512, 4, launch_mfma<256, 128, 16, 4, 2, 1, 4>},
-    {"mfma_128x256x16_w2x4", KIND_MFMA, 128, 256, 16, 512, 8, launch_mfma<128, 256, 16, 2, 4, 1, 8>},
-    {"mfma_128x128x32_w4x4", KIND_MFMA, 128, 128, 32, 1024, 8, launch_mfma<128, 128, 32, 4, 4, 1, 8>},
-    {"mfma_64x64x16_w2x2k2", KIND_MFMA, 64, 64, 16, 512, 8, launch_mfma<64, 64, 16, 2, 2, 2, 8>},
-    {"mfma_64x64x32_w2x2k2", KIND_MFMA, 64, 64, 32, 512, 8, launch_mfma<64, 64, 32, 2, 2, 2, 8>},
-    {"mfma_64x64x32_w2x2k4", KIND_MFMA, 64, 64, 32, 1024, 8, launch_mfma<64, 64, 32, 2, 2, 4, 8>},
-    {"mfma_64x64x64_w2x2k4", KIND_MFMA, 64, 64, 64, 1024, 8, launch_mfma<64, 64, 64, 2, 2, 4, 8>},
-    {"mfma_128x64x32_w2x2k2", KIND_MFMA, 128, 64, 32, 512, 8, launch_mfma<128, 64, 32, 2, 2, 2, 8>},
-    {"mfma_64x128x32_w2x2k2", KIND_MFMA, 64, 128, 32, 512, 8, launch_mfma<64, 128, 32, 2, 2, 2, 8>},
-    {"mfma_128x128x32_w2x2k2", KIND_MFMA, 128, 128, 32, 512, 8, launch_mfma<128, 128, 32, 2, 2, 2, 8>},
+    {"tile16", KIND_TILE16, 16, 16, 16, 256, launch_tile16},
+    SGEMM_MFMA_CONFIGS(SGEMM_TABLE_ROW)
 };
+#undef SGEMM_TABLE_ROW
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// 128-bit path: every operand 16-byte aligned and every row start 16-byte aligned,
-// and the K and N extents whole 4-float chunks (so a chunk is all in or all out).
-bool vector_ok(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc)
+// 128-bit path: every operand 16-byte aligned, every row start 16-byte aligned, and
+// each operand's contiguous extent a whole number of 4-float chunks (so a chunk is
+// all in or all out): K for plain A, M for transposed A, N for plain B, K for
+// transposed B, N for C.
+bool vector_ok(int opA, int opB, int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+               const float *C, int ldc)
 {
-    return aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 &&
-           ldc % 4 == 0 && N % 4 == 0 && K % 4 == 0;
+    return aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0 &&
+           (opA ? M : K) % 4 == 0 && (opB ? K : N) % 4 == 0 && N % 4 == 0;
 }
 
 uint64_t tile_count(const Config &c, int M, int N)
@@ -111,17 +102,17 @@ struct Candidate {
 };
 
 const Candidate kCandidatesVec[] = {
-    {5, 16, 0.500, 0.500},    // mfma_256x256x16_w2x4: one workgroup per CU fits
-    {19, 4, 0.458, 0.458},    // mfma_128x128x32_w2x2k2: one per CU
-    {18, 2, 0.400, 0.452},    // mfma_64x128x32_w2x2k2: up to three per CU
-    {16, 1, 0.395, 0.436},    // mfma_64x64x64_w2x2k4: up to two per CU
+    {3, 16, 0.500, 0.500},    // mfma_256x256x16_w2x4: one workgroup per CU fits
+    {9, 4, 0.458, 0.458},     // mfma_128x128x32_w2x2k2: one per CU
+    {8, 2, 0.400, 0.452},     // mfma_64x128x32_w2x2k2: up to three per CU
+    {7, 1, 0.395, 0.436},     // mfma_64x64x64_w2x2k4: up to two per CU
 };
 // 32-bit path (unaligned operands): the 64-deep stage loses to 32-deep ones there.
 const Candidate kCandidatesScalar[] = {
-    {5, 16, 0.500, 0.500},
-    {19, 4, 0.458, 0.458},
-    {18, 2, 0.400, 0.452},
-    {14, 1, 0.380, 0.420},    // mfma_64x64x32_w2x2k2: up to four per CU
+    {3, 16, 0.500, 0.500},
+    {9, 4, 0.458, 0.458},
+    {8, 2, 0.400, 0.452},
+    {6, 1, 0.380, 0.420},     // mfma_64x64x32_w2x2k2: up to four per CU
 };
 
 int choose(int M, int N, bool vec)
@@ -132,58 +123,73 @@ int choose(int M, int N, bool vec)
                           : (int)(sizeof(kCandidatesScalar) / sizeof(Candidate));
     int best = cands[0].id;
     double best_cost = 0.0;
-    bool first = true;
     for (int i = 0; i < count; ++i) {
         const Candidate &cand = cands[i];
         const uint64_t tiles = tile_count(kConfigs[cand.id], M, N);
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
         const double cost = (double)rounds * cand.units / (rounds >= 2 ? cand.rate_many : cand.rate_one);
-        if (first || cost < best_cost) {
+        if (i == 0 || cost < best_cost) {
             best = cand.id;
             best_cost = cost;
-            first = false;
         }
     }
     return best;
 }
 
-// Argument checks shared by the entry points. Returns 0 or -position (sgemm numbering).
-int check_args(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
-               const float *C, int ldc)
+// Arguments that can be invalid, independent of any entry point's numbering.
+enum Arg { ARG_OK = 0, ARG_OPA, ARG_OPB, ARG_M, ARG_N, ARG_K, ARG_A, ARG_LDA, ARG_B, ARG_LDB, ARG_C, ARG_LDC,
+           ARG_ACT };
+
+// The first invalid argument, in declaration order, or ARG_OK.
+Arg check_args(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+               int ldb, const float *C, int ldc, int act)
 {
-    if (M < 0) return -1;
-    if (N < 0) return -2;
-    if (K < 0) return -3;
+    if (opA != SGEMM_OP_N && opA != SGEMM_OP_T) return ARG_OPA;
+    if (opB != SGEMM_OP_N && opB != SGEMM_OP_T) return ARG_OPB;
+    if (M < 0) return ARG_M;
+    if (N < 0) return ARG_N;
+    if (K < 0) return ARG_K;
     const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
-    if (reads_ab && A == nullptr) return -5;
-    if (lda < (K > 1 ? K : 1)) return -6;
-    if (reads_ab && B == nullptr) return -7;
-    if (ldb < (N > 1 ? N : 1)) return -8;
-    if (M > 0 && N > 0 && C == nullptr) return -10;
-    if (ldc < (N > 1 ? N : 1)) return -11;
-    return 0;
+    if (reads_ab && A == nullptr) return ARG_A;
+    const int a_cols = opA ? M : K;     // the contiguous extent of A as stored
+    if (lda < (a_cols > 1 ? a_cols : 1)) return ARG_LDA;
+    if (reads_ab && B == nullptr) return ARG_B;
+    const int b_cols = opB ? K : N;
+    if (ldb < (b_cols > 1 ? b_cols : 1)) return ARG_LDB;
+    if (M > 0 && N > 0 && C == nullptr) return ARG_C;
+    if (ldc < (N > 1 ? N : 1)) return ARG_LDC;
+    if (act != SGEMM_ACT_NONE && act != SGEMM_ACT_GELU_TANH) return ARG_ACT;
+    return ARG_OK;
 }
 
-int run(int config, int M, int N, int K, float alpha, const float *A, int lda, int64_t sA,
-        const float *B, int ldb, int64_t sB, float beta, float *C, int ldc, int64_t sC, int batch,
-        hipStream_t stream)
+// Positions (1-based) of each Arg in the entry points' signatures; 0 = not an argument.
+//                       OK opA opB M  N  K  A  lda B  ldb C   ldc act
+const int kPosPlain[] = {0, 0, 0, 1, 2, 3, 5, 6, 7, 8, 10, 11, 0};     // sgemm, sgemm_ex
+const int kPosOp[] = {0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 12, 13, 0};       // sgemm_op
+const int kPosFused[] = {0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 12, 13, 15};   // sgemm_bias_act, sgemm_general
+const int kPosBatched[] = {0, 0, 0, 1, 2, 3, 5, 6, 8, 9, 12, 13, 0};   // sgemm_strided_batched
+
+int run(int config, int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, int64_t sA,
+        const float *B, int ldb, int64_t sB, float beta, float *C, int ldc, int64_t sC, const float *bias,
+        int act, int batch, hipStream_t stream)
 {
     GemmArgs p;
     p.M = M; p.N = N; p.K = K;
     p.alpha = alpha; p.beta = beta;
     p.A = A; p.B = B; p.C = C;
+    p.bias = bias; p.act = act;
     p.lda = lda; p.ldb = ldb; p.ldc = ldc;
     p.strideA = sA; p.strideB = sB; p.strideC = sC;
 
     if (K == 0 || alpha == 0.0f) {
-        // C <- beta*C; A and B are not read.
+        // C <- act(beta*C + bias); A and B are not read.
         const int gx = (N + 255) / 256 < 64 ? (N + 255) / 256 : 64;
         const int gy = M < 1024 ? M : 1024;
         hipLaunchKernelGGL(sgemm_impl::sgemm_scale, dim3(gx, gy, batch), dim3(256, 1), 0, stream, p);
         const hipError_t e = hipGetLastError();
         return e == hipSuccess ? 0 : (int)e;
     }
-    const bool vec = vector_ok(N, K, A, lda, B, ldb, C, ldc) &&
+    const bool vec = vector_ok(opA, opB, M, N, K, A, lda, B, ldb, C, ldc) &&
                      (batch == 1 || (sA % 4 == 0 && sB % 4 == 0 && sC % 4 == 0));
     const int id = config >= 0 ? config : choose(M, N, vec);
     const Config &c = kConfigs[id];
@@ -191,52 +197,78 @@ int run(int config, int M, int N, int K, float alpha, const float *A, int lda, i
     if (c.kind == KIND_MFMA && tiles * (uint64_t)c.threads > 0xFFFFFFFFull)
         return SGEMM_ERROR_TOO_LARGE;
     const bool edge = (M % c.bm) != 0 || (N % c.bn) != 0 || (K % c.bk) != 0;
-    const hipError_t e = c.launch(p, batch, vec, edge, stream);
+    const hipError_t e = c.launch(p, batch, opA != 0, opB != 0, vec, edge, stream);
     return e == hipSuccess ? 0 : (int)e;
+}
+
+int general(const int *pos, int config, int opA, int opB, int M, int N, int K, float alpha, const float *A,
+            int lda, const float *B, int ldb, float beta, float *C, int ldc, const float *bias, int act,
+            void *stream)
+{
+    if (config < -1 || config >= kNumConfigs)
+        return SGEMM_ERROR_BAD_CONFIG;
+    const Arg bad = check_args(opA, opB, M, N, K, alpha, A, lda, B, ldb, C, ldc, act);
+    if (bad != ARG_OK)
+        return -pos[bad];
+    if (M == 0 || N == 0)
+        return SGEMM_SUCCESS;
+    return run(config, opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, bias, act, 1,
+               static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
 
 extern "C" {
 
-int sgemm_ex(int config, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb, float beta,
+          float *C, int ldc, void *stream)
+{
+    return general(kPosPlain, -1, SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, nullptr,
+                   SGEMM_ACT_NONE, stream);
+}
+
+int sgemm_ex(int config, int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream)
+{
+    return general(kPosPlain, config, SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                   nullptr, SGEMM_ACT_NONE, stream);
+}
+
+int sgemm_op(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
              int ldb, float beta, float *C, int ldc, void *stream)
 {
-    if (config < -1 || config >= kNumConfigs)
-        return SGEMM_ERROR_BAD_CONFIG;
-    const int bad = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
-    if (bad != 0)
-        return bad;
-    if (M == 0 || N == 0)
-        return SGEMM_SUCCESS;
-    return run(config, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
-               static_cast<hipStream_t>(stream));
+    return general(kPosOp, -1, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, SGEMM_ACT_NONE,
+                   stream);
 }
 
-int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
-          float beta, float *C, int ldc, void *stream)
+int sgemm_bias_act(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                   int ldb, float beta, float *C, int ldc, const float *bias, int act, void *stream)
 {
-    return sgemm_ex(-1, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return general(kPosFused, -1, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream);
 }
 
-int sgemm_strided_batched(int M, int N, int K, float alpha, const float *A, int lda,
-                          long long strideA, const float *B, int ldb, long long strideB, float beta,
-                          float *C, int ldc, long long strideC, int batch, void *stream)
+int sgemm_general(int config, int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+                  const float *B, int ldb, float beta, float *C, int ldc, const float *bias, int act,
+                  void *stream)
 {
-    // Positions: 1 M, 2 N, 3 K, 4 alpha, 5 A, 6 lda, 7 strideA, 8 B, 9 ldb, 10 strideB,
-    // 11 beta, 12 C, 13 ldc, 14 strideC, 15 batch.
-    static const int remap[12] = {0, -1, -2, -3, 0, -5, -6, -8, -9, 0, -12, -13};
-    const int bad = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
-    if (bad != 0)
-        return remap[-bad];
+    return general(kPosFused, config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream);
+}
+
+int sgemm_strided_batched(int M, int N, int K, float alpha, const float *A, int lda, long long strideA,
+                          const float *B, int ldb, long long strideB, float beta, float *C, int ldc,
+                          long long strideC, int batch, void *stream)
+{
+    const Arg bad = check_args(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, C, ldc, SGEMM_ACT_NONE);
+    if (bad != ARG_OK)
+        return -kPosBatched[bad];
     if (strideA < 0) return -7;
     if (strideB < 0) return -10;
     if (batch < 0 || batch > 65535) return -15;
     if (batch > 1 && M > 0 && N > 0 && strideC < (long long)(M - 1) * ldc + N) return -14;
     if (M == 0 || N == 0 || batch == 0)
         return SGEMM_SUCCESS;
-    return run(-1, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
-               static_cast<hipStream_t>(stream));
+    return run(-1, SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+               strideC, nullptr, SGEMM_ACT_NONE, batch, static_cast<hipStream_t>(stream));
 }
 
 int sgemm_config_count(void) { return kNumConfigs; }
@@ -246,12 +278,12 @@ const char *sgemm_config_name(int config)
     return (config >= 0 && config < kNumConfigs) ? kConfigs[config].name : nullptr;
 }
 
-int sgemm_select_config(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
-                        int ldb, const float *C, int ldc)
+int sgemm_select_config(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+                        const float *C, int ldc)
 {
     if (M <= 0 || N <= 0 || K <= 0 || alpha == 0.0f)
         return -1;
-    return choose(M, N, vector_ok(N, K, A, lda, B, ldb, C, ldc));
+    return choose(M, N, vector_ok(SGEMM_OP_N, SGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc));
 }
 
 int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3])
@@ -294,6 +326,6 @@ const char *sgemm_status_string(int status)
     return "unknown status";
 }
 
-const char *sgemm_version(void) { return "tiled_fp32_gemm_02_amd 0.1 (gfx950)"; }
+const char *sgemm_version(void) { return "tiled_fp32_gemm_02_amd 0.2 (gfx950)"; }
 
 }  // extern "C"

@@ -1,16 +1,15 @@
-// Device kernels for row-major fp32 C = alpha*A*B + beta*C on gfx950 (MI355X).
+// Device kernels for row-major fp32 C = act(alpha*op(A)*op(B) + beta*C + bias) on
+// gfx950 (MI355X). op is the identity or a transpose; bias (per column) and act (none
+// or tanh-form GELU) are optional and off for the plain product.
 //
-// Three kernels:
-//  - sgemm_mfma: the hot path. A workgroup owns a BM x BN tile of C; each wave owns
+// This header holds the MFMA kernel, sgemm_mfma, and the helpers shared with the
+// small kernels in sgemm_aux_kernels.hpp (16x16 baseline, quick-return scaling).
+// sgemm_mfma is the hot path. A workgroup owns a BM x BN tile of C; each wave owns
 //    a (BM/WGM) x (BN/WGN) sub-tile made of 32x32 blocks computed with the CDNA fp32
 //    matrix instruction (32x32 outputs, 2 k-steps per issue). A and B tiles move
 //    HBM -> registers -> LDS in 128-bit chunks, into a two-stage LDS ring with one
 //    barrier per K-tile; the next K-tile's global loads are in flight while the
 //    current one is multiplied.
-//  - sgemm_tile16: the classic shared-memory kernel, one output per thread and
-//    16x16 tiles (the GPT-2 post's hand-written matmul). Kept as the simplest
-//    correct rung and as a baseline for the report.
-//  - sgemm_scale: C = beta*C for the quick-return cases (alpha == 0 or K == 0).
 //
 // Techniques from the pages and where they come from:
 //  - Tiling through local memory so each global element is fetched once per
@@ -20,15 +19,19 @@
 //    (AutoMine++ #4, "Use registers" and "Matrix product by outer products"); here
 //    the register tile is the matrix-core accumulator and the outer products of
 //    2-deep k slices are what each matrix instruction adds.
-//  - Rectangular tiles and wide chunk loads (AutoMine++ #7, "Rectangular tiling"
-//    and "Fine tuning"); double buffering with register staging and one barrier
-//    per step (AutoMine++ #7, "Rectangular tiling"; Micro_gemm_4x4, "Pipeline (double
+//  - Rectangular tiles and wide chunk loads, with a flat thread-to-chunk map in
+//    which surplus threads idle (AutoMine++ #7, "Rectangular tiling" and "Fine
+//    tuning"); double buffering with register staging and one barrier per step
+//    (AutoMine++ #7, "Rectangular tiling"; Micro_gemm_4x4, "Pipeline (double
 //    buffering)").
 //  - Zero-filled out-of-range loads, a ceil-divided grid and predicated stores
 //    (Micro_gemm_4x4, "A/B tile load" and "Final C write"; GPT-2 post, "Tiled matrix
 //    multiplication").
 //  - alpha/beta epilogue that skips reading C when beta is zero (Micro_gemm_4x4,
 //    "Final C write (alpha, beta)").
+//  - Transposed operands read in place, as the GPT-2 post's kernel takes transposed
+//    views ("Tiled matrix multiplication"); bias and GELU applied to the product as in
+//    its linear layers ("The whole model as one kernel", "From loops to kernels").
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,17 +43,43 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
+enum Act { ACT_NONE = 0, ACT_GELU_TANH = 1 };
+
 struct GemmArgs {
     int M, N, K;
     float alpha, beta;
-    const float *A;
-    const float *B;
+    const float *A;             // op(A) is M x K: A[i*lda + k], or A[k*lda + i] when transposed
+    const float *B;             // op(B) is K x N: B[k*ldb + j], or B[j*ldb + k] when transposed
     float *C;
+    const float *bias;          // N entries (one per column) or null
+    int act;                    // Act
     int64_t lda, ldb, ldc;
     int64_t strideA, strideB, strideC;  // per blockIdx.z (batched form); 0 otherwise
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// tanh-form GELU in fp32: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
+__device__ __forceinline__ float gelu_tanh(float x)
+{
+    const float c = 0.7978845608028654f;    // sqrt(2/pi)
+    return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+}
+
+// The epilogue value of one entry: act(alpha*acc + beta*c + bias_j); c is read only
+// when beta != 0.
+__device__ __forceinline__ float finish(float acc, float alpha, float beta, const float *cptr,
+                                        const float *bias, int j, int act)
+{
+    float out = alpha * acc;
+    if (beta != 0.f)
+        out += beta * *cptr;
+    if (bias)
+        out += bias[j];
+    if (act == ACT_GELU_TANH)
+        out = gelu_tanh(out);
+    return out;
+}
 
 // Map the linear workgroup id to a (tile_m, tile_n) pair.
 //
@@ -75,34 +104,111 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
     tn = in_band / rows;
 }
 
+// One operand tile as it sits in memory: TR rows of TC contiguous floats (row stride
+// ld), copied HBM -> registers -> LDS in 4-float chunks. Thread t takes chunks
+// t, t + NT, ...; consecutive threads take consecutive chunks along a row, and when
+// the tile has fewer chunks than threads the surplus threads idle. The LDS copy keeps
+// the same layout with 4 floats of row padding (stride TC + 4).
+template <int TR, int TC, int NT>
+struct TileIO {
+    static constexpr int CPR = TC / 4;
+    static constexpr int CHUNKS = TR * TC / 4;
+    static constexpr int CH = (CHUNKS + NT - 1) / NT;
+    static constexpr bool IDLE = CHUNKS % NT != 0;
+    static constexpr int LD = TC + 4;
+    static constexpr int SIZE = TR * LD;
+    static_assert(TC % 4 == 0, "rows are whole 4-float chunks");
+    static_assert(CHUNKS % NT == 0 || CH == 1, "a partial loader round only when it is the only one");
+
+    // src points at the tile origin; rows/cols are how many rows and columns from the
+    // origin lie inside the matrix. VEC: 128-bit loads (row starts 16-byte aligned and
+    // the column extent a multiple of 4, so a chunk is wholly in or out); otherwise every
+    // float is checked. EDGE = false promises the whole tile is inside.
+    template <bool VEC, bool EDGE>
+    __device__ __forceinline__ static void load(floatx4 (&r)[CH], const float *__restrict__ src, int64_t ld,
+                                                int rows, int cols, int tid)
+    {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int idx = tid + c * NT;
+            if (IDLE && idx >= CHUNKS)
+                break;
+            const int rr = idx / CPR, cc = (idx % CPR) * 4;
+            const float *p = src + (int64_t)rr * ld + cc;
+            if (VEC) {
+                if (!EDGE || (rr < rows && cc < cols))
+                    r[c] = *reinterpret_cast<const floatx4 *>(p);
+                else
+                    r[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                const bool rok = rr < rows;
+                r[c].x = (rok && cc + 0 < cols) ? p[0] : 0.f;
+                r[c].y = (rok && cc + 1 < cols) ? p[1] : 0.f;
+                r[c].z = (rok && cc + 2 < cols) ? p[2] : 0.f;
+                r[c].w = (rok && cc + 3 < cols) ? p[3] : 0.f;
+            }
+        }
+    }
+
+    __device__ __forceinline__ static void store(const floatx4 (&r)[CH], float *lds, int tid)
+    {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int idx = tid + c * NT;
+            if (IDLE && idx >= CHUNKS)
+                break;
+            *reinterpret_cast<floatx4 *>(&lds[(idx / CPR) * LD + (idx % CPR) * 4]) = r[c];
+        }
+    }
+};
+
+// W consecutive floats from LDS (W = 1, 2 or 4) as one 32-, 64- or 128-bit read.
+template <int W>
+__device__ __forceinline__ void lds_read(const float *p, float (&out)[W])
+{
+    if constexpr (W == 4) {
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(p);
+        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    } else if constexpr (W == 2) {
+        const floatx2 v = *reinterpret_cast<const floatx2 *>(p);
+        out[0] = v[0]; out[1] = v[1];
+    } else {
+        out[0] = p[0];
+    }
+}
+
 // ---------------------------------------------------------------------------------
 // MFMA kernel.
 //
 // Template parameters: BM x BN workgroup tile, BK k-depth per LDS stage, WGM x WGN
-// waves over the tile, WGK wave groups along k. With WGK > 1 every wave group
-// multiplies its own BK/WGK slice of each stage into its own accumulators, and at the
-// end the groups add their accumulators through LDS in a fixed order (group 0 + 1 +
-// 2 ...), so results stay reproducible; this puts more waves on each CU when the
-// problem has few tiles, without any memory outside the workgroup. VEC selects 128-bit global loads/stores (all operands 16-byte aligned,
-// leading dimensions, N and K multiples of 4); EDGE enables the bounds checks needed
-// when M, N or K is not a multiple of the tile. Without VEC every element is checked.
+// waves over the tile, WGK wave groups along k, TA / TB whether op(A) / op(B) is a
+// transpose. With WGK > 1 every wave group multiplies its own BK/WGK slice of each
+// stage into its own accumulators, and at the end the groups add their accumulators
+// through LDS in a fixed order (group 0 + 1 + 2 ...), so results stay reproducible;
+// this puts more waves on each CU when the problem has few tiles, without any memory
+// outside the workgroup. VEC selects 128-bit global loads/stores (operands 16-byte
+// aligned, leading dimensions and contiguous extents multiples of 4); EDGE enables
+// the bounds checks needed when M, N or K is not a multiple of the tile. Without VEC
+// every element is checked.
 //
-// LDS layout per stage (floats): A tile as stored in memory, [BM][BK + 4] (row i,
-// k contiguous, 4 floats of padding so eight consecutive rows fall in distinct bank
-// groups for 128-bit reads), then B tile [BK][BN + 4] (k row, n contiguous).
+// Each operand tile is staged in LDS in its memory layout (TileIO): A as [BM][BK+4]
+// (k contiguous), or [BK][BM+4] when transposed (m contiguous); B as [BK][BN+4] (n
+// contiguous), or [BN][BK+4] when transposed (k contiguous).
 //
 // Lane layout of v_mfma_f32_32x32x2_f32 (one 32x32 block, k = 2): lane l supplies
 // A(l%32, l/32) and B(l/32, l%32); accumulator element e of lane l is
-// D(8*(e/4) + 4*(l/32) + e%4, l%32). Two remappings make every LDS read 128 or
-// 64 bits wide:
+// D(8*(e/4) + 4*(l/32) + e%4, l%32). Remappings make every LDS read wide:
 //  - k: within each group of 8 k values, the half-wave h = l/32 takes k = 4h + s on
 //    matrix step s (s = 0..3). A and B use the same map, so each issue still adds
-//    A(:,k)B(k,:) for two distinct k and the 4 steps cover all 8. Lane l then reads
-//    A(row, 4h .. 4h+3) as one 128-bit word.
-//  - n: a wave's TN blocks along n are interleaved, block b column c <-> tile column
-//    c*TN + b, so lane l reads and writes TN consecutive columns.
+//    A(:,k)B(k,:) for two distinct k and the 4 steps cover all 8. An operand stored
+//    k-contiguous (A plain, B transposed) then gives lane l its four values as one
+//    128-bit read.
+//  - m / n: an operand stored m- or n-contiguous (A transposed, B plain) has the
+//    wave's blocks along that dimension interleaved, block b index c <-> wave index
+//    c*T + b (T blocks), so lane l reads T consecutive values for one k in one read,
+//    and for B writes T consecutive columns of C.
 // ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, bool VEC, bool EDGE>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, bool TA, bool TB, bool VEC, bool EDGE>
 __global__ void __launch_bounds__(WGM * WGN * WGK * 64)
 sgemm_mfma(GemmArgs p, int group_m)
 {
@@ -110,18 +216,13 @@ sgemm_mfma(GemmArgs p, int group_m)
     constexpr int KSLICE = BK / WGK;                    // k per stage handled by one wave group
     constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
     constexpr int TM = WTM / 32, TN = WTN / 32;         // 32x32 blocks per wave
-    constexpr int SA = BK + 4, SB = BN + 4;             // LDS row strides (floats)
-    constexpr int A_STAGE = BM * SA, B_STAGE = BK * SB;
-    constexpr int STAGE = A_STAGE + B_STAGE;
-    constexpr int A_CPR = BK / 4, B_CPR = BN / 4;       // 4-float chunks per tile row
-    constexpr int A_CHUNKS = BM * BK / 4, B_CHUNKS = BK * BN / 4;
-    constexpr int A_CH = (A_CHUNKS + NT - 1) / NT, B_CH = (B_CHUNKS + NT - 1) / NT;   // chunks per thread
-    constexpr bool A_IDLE = A_CHUNKS % NT != 0, B_IDLE = B_CHUNKS % NT != 0;        // surplus threads idle
+    using AIO = TileIO<TA ? BK : BM, TA ? BM : BK, NT>;
+    using BIO = TileIO<TB ? BN : BK, TB ? BK : BN, NT>;
+    constexpr int STAGE = AIO::SIZE + BIO::SIZE;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(TN == 1 || TN == 2 || TN == 4, "interleaved n blocks read 1, 2 or 4 floats");
+    static_assert(!TA || TM == 1 || TM == 2 || TM == 4, "interleaved m blocks read 1, 2 or 4 floats");
+    static_assert(TB || TN == 1 || TN == 2 || TN == 4, "interleaved n blocks read 1, 2 or 4 floats");
     static_assert(BK % (8 * WGK) == 0, "each wave group consumes k in groups of 8");
-    static_assert(A_CHUNKS % NT == 0 || A_CH == 1, "a partial loader round only when it is the only one");
-    static_assert(B_CHUNKS % NT == 0 || B_CH == 1, "a partial loader round only when it is the only one");
     constexpr int RED = (WGK - 1) * BM * BN;            // partial sums of groups 1..WGK-1
     constexpr int SMEM = 2 * STAGE > RED ? 2 * STAGE : RED;
     static_assert(SMEM * 4 <= 160 * 1024, "LDS exceeds 160 KiB");
@@ -145,72 +246,25 @@ sgemm_mfma(GemmArgs p, int group_m)
     const int wm = (wave % (WGM * WGN)) / WGN, wn = wave % WGN;
     const int l32 = lane & 31, half = lane >> 5;
 
-    floatx4 ra[A_CH], rb[B_CH];
+    floatx4 ra[AIO::CH], rb[BIO::CH];
 
     // Global -> registers for the K-tile starting at k0 (zero outside the matrix).
     auto load_tile = [&](int k0) __attribute__((always_inline)) {
-#pragma unroll
-        for (int c = 0; c < A_CH; ++c) {
-            const int idx = tid + c * NT;
-            if (A_IDLE && idx >= A_CHUNKS)
-                break;
-            const int r = idx / A_CPR, kc = (idx % A_CPR) * 4;
-            const int gr = m0 + r, gk = k0 + kc;
-            const float *src = A + (int64_t)gr * lda + gk;
-            if (VEC) {
-                if (!EDGE || (gr < M && gk < K))
-                    ra[c] = *reinterpret_cast<const floatx4 *>(src);
-                else
-                    ra[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-            } else {
-                const bool rok = gr < M;
-                ra[c].x = (rok && gk + 0 < K) ? src[0] : 0.f;
-                ra[c].y = (rok && gk + 1 < K) ? src[1] : 0.f;
-                ra[c].z = (rok && gk + 2 < K) ? src[2] : 0.f;
-                ra[c].w = (rok && gk + 3 < K) ? src[3] : 0.f;
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < B_CH; ++c) {
-            const int idx = tid + c * NT;
-            if (B_IDLE && idx >= B_CHUNKS)
-                break;
-            const int r = idx / B_CPR, nc = (idx % B_CPR) * 4;
-            const int gk = k0 + r, gn = n0 + nc;
-            const float *src = B + (int64_t)gk * ldb + gn;
-            if (VEC) {
-                if (!EDGE || (gk < K && gn < N))
-                    rb[c] = *reinterpret_cast<const floatx4 *>(src);
-                else
-                    rb[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-            } else {
-                const bool kok = gk < K;
-                rb[c].x = (kok && gn + 0 < N) ? src[0] : 0.f;
-                rb[c].y = (kok && gn + 1 < N) ? src[1] : 0.f;
-                rb[c].z = (kok && gn + 2 < N) ? src[2] : 0.f;
-                rb[c].w = (kok && gn + 3 < N) ? src[3] : 0.f;
-            }
-        }
+        if constexpr (TA)
+            AIO::template load<VEC, EDGE>(ra, A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, tid);
+        else
+            AIO::template load<VEC, EDGE>(ra, A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, tid);
+        if constexpr (TB)
+            BIO::template load<VEC, EDGE>(rb, B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, tid);
+        else
+            BIO::template load<VEC, EDGE>(rb, B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, tid);
     };
 
     // Registers -> LDS stage `st`.
     auto store_tile = [&](int st) __attribute__((always_inline)) {
         float *As = smem + st * STAGE;
-        float *Bs = As + A_STAGE;
-#pragma unroll
-        for (int c = 0; c < A_CH; ++c) {
-            const int idx = tid + c * NT;
-            if (A_IDLE && idx >= A_CHUNKS)
-                break;
-            *reinterpret_cast<floatx4 *>(&As[(idx / A_CPR) * SA + (idx % A_CPR) * 4]) = ra[c];
-        }
-#pragma unroll
-        for (int c = 0; c < B_CH; ++c) {
-            const int idx = tid + c * NT;
-            if (B_IDLE && idx >= B_CHUNKS)
-                break;
-            *reinterpret_cast<floatx4 *>(&Bs[(idx / B_CPR) * SB + (idx % B_CPR) * 4]) = rb[c];
-        }
+        AIO::store(ra, As, tid);
+        BIO::store(rb, As + AIO::SIZE, tid);
     };
 
     floatx16 acc[TM][TN];
@@ -222,40 +276,53 @@ sgemm_mfma(GemmArgs p, int group_m)
             for (int e = 0; e < 16; ++e)
                 acc[a][b][e] = 0.f;
 
-    const int a_row = wm * WTM + l32;            // + a*32: this lane's A row in the tile
-    const int b_col = wn * WTN + l32 * TN;       // this lane's first B column in the tile
+    // This lane's first row of A / column of B inside the tile: plain A rows are
+    // a*32 + l32 (blocks side by side), transposed A rows l32*TM + a (interleaved);
+    // likewise for B columns with the roles swapped.
+    const int a_idx = wm * WTM + (TA ? l32 * TM : l32);
+    const int b_idx = wn * WTN + (TB ? l32 : l32 * TN);
 
-    // One stage: BK/8 groups of 8 k values, 4 matrix steps each.
+    // One stage: KSLICE/8 groups of 8 k values, 4 matrix steps each.
     auto compute = [&](int st) __attribute__((always_inline)) {
         const float *As = smem + st * STAGE;
-        const float *Bs = As + A_STAGE;
+        const float *Bs = As + AIO::SIZE;
 #pragma unroll
         for (int kk = 0; kk < KSLICE; kk += 8) {
             const int kg = wk * KSLICE + kk;
-            floatx4 af[TM];
+            floatx4 af[TA ? 1 : TM], bf[TB ? TN : 1];
+            if constexpr (!TA) {
 #pragma unroll
-            for (int a = 0; a < TM; ++a)
-                af[a] = *reinterpret_cast<const floatx4 *>(&As[(a_row + a * 32) * SA + kg + 4 * half]);
+                for (int a = 0; a < TM; ++a)
+                    af[a] = *reinterpret_cast<const floatx4 *>(&As[(a_idx + a * 32) * AIO::LD + kg + 4 * half]);
+            }
+            if constexpr (TB) {
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    bf[b] = *reinterpret_cast<const floatx4 *>(&Bs[(b_idx + b * 32) * BIO::LD + kg + 4 * half]);
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const float *brow = &Bs[(kg + 4 * half + s) * SB + b_col];
-                float bf[TN];
-                if constexpr (TN == 4) {
-                    const floatx4 v = *reinterpret_cast<const floatx4 *>(brow);
-                    bf[0] = v[0]; bf[1] = v[1]; bf[2] = v[2]; bf[3] = v[3];
-                } else if constexpr (TN == 2) {
-                    const floatx2 v = *reinterpret_cast<const floatx2 *>(brow);
-                    bf[0] = v[0]; bf[1] = v[1];
+                const int k = kg + 4 * half + s;
+                float av[TM], bv[TN];
+                if constexpr (TA) {
+                    lds_read<TM>(&As[k * AIO::LD + a_idx], av);
                 } else {
-                    bf[0] = brow[0];
-                }
 #pragma unroll
-                for (int a = 0; a < TM; ++a) {
-                    const float av = af[a][s];
+                    for (int a = 0; a < TM; ++a)
+                        av[a] = af[a][s];
+                }
+                if constexpr (TB) {
 #pragma unroll
                     for (int b = 0; b < TN; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bf[b], acc[a][b], 0, 0, 0);
+                        bv[b] = bf[b][s];
+                } else {
+                    lds_read<TN>(&Bs[k * BIO::LD + b_idx], bv);
                 }
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+#pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
             }
         }
     };
@@ -306,93 +373,58 @@ sgemm_mfma(GemmArgs p, int group_m)
         }
     }
 
-    // Epilogue: C = alpha*acc + beta*C, C unread when beta == 0.
+    // Epilogue: C = act(alpha*acc + beta*C + bias), C unread when beta == 0.
     const float alpha = p.alpha, beta = p.beta;
-    const int gc0 = n0 + b_col;
+    const float *bias = p.bias;
+    const int act = p.act;
+    const bool plain = bias == nullptr && act == ACT_NONE;
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int gr = m0 + wm * WTM + a * 32 + 8 * (e / 4) + 4 * half + (e % 4);
+            const int r = 8 * (e / 4) + 4 * half + (e % 4);          // row inside the 32x32 block
+            const int gr = m0 + wm * WTM + (TA ? r * TM + a : a * 32 + r);
             if (EDGE && gr >= M)
                 continue;
-            float *crow = C + (int64_t)gr * ldc + gc0;
-            float v[TN];
+            float *crow = C + (int64_t)gr * ldc;
+            if constexpr (!TB) {
+                // TN consecutive columns per lane
+                const int gc0 = n0 + b_idx;
+                float *cp = crow + gc0;
+                if (VEC && TN == 4 && plain && (!EDGE || gc0 < N)) {
+                    // VEC: N % 4 == 0 and gc0 % 4 == 0, so the whole chunk is in range.
+                    floatx4 *c4 = reinterpret_cast<floatx4 *>(cp);
+                    floatx4 out = {alpha * acc[a][0][e], alpha * acc[a][1 % TN][e], alpha * acc[a][2 % TN][e],
+                                   alpha * acc[a][3 % TN][e]};
+                    if (beta != 0.f)
+                        out += beta * *c4;
+                    *c4 = out;
+                } else if (VEC && TN == 2 && plain && (!EDGE || gc0 < N)) {
+                    floatx2 *c2 = reinterpret_cast<floatx2 *>(cp);
+                    floatx2 out = {alpha * acc[a][0][e], alpha * acc[a][1 % TN][e]};
+                    if (beta != 0.f)
+                        out += beta * *c2;
+                    *c2 = out;
+                } else {
 #pragma unroll
-            for (int b = 0; b < TN; ++b)
-                v[b] = alpha * acc[a][b][e];
-            if (VEC && TN == 4 && (!EDGE || gc0 < N)) {
-                // VEC: N % 4 == 0 and gc0 % 4 == 0, so the whole chunk is in range.
-                floatx4 *c4 = reinterpret_cast<floatx4 *>(crow);
-                floatx4 out = {v[0], v[1], v[2], v[3]};
-                if (beta != 0.f)
-                    out += beta * *c4;
-                *c4 = out;
-            } else if (VEC && TN == 2 && (!EDGE || gc0 < N)) {
-                floatx2 *c2 = reinterpret_cast<floatx2 *>(crow);
-                floatx2 out = {v[0], v[1]};
-                if (beta != 0.f)
-                    out += beta * *c2;
-                *c2 = out;
+                    for (int b = 0; b < TN; ++b) {
+                        if (EDGE && gc0 + b >= N)
+                            continue;
+                        cp[b] = finish(acc[a][b][e], alpha, beta, cp + b, bias, gc0 + b, act);
+                    }
+                }
             } else {
+                // one column per block: lanes 0..31 write 32 consecutive columns
 #pragma unroll
                 for (int b = 0; b < TN; ++b) {
-                    if (EDGE && gc0 + b >= N)
+                    const int gc = n0 + b_idx + b * 32;
+                    if (EDGE && gc >= N)
                         continue;
-                    float out = v[b];
-                    if (beta != 0.f)
-                        out += beta * crow[b];
-                    crow[b] = out;
+                    crow[gc] = finish(acc[a][b][e], alpha, beta, crow + gc, bias, gc, act);
                 }
             }
         }
     }
-}
-
-// ---------------------------------------------------------------------------------
-// Classic 16x16 shared-memory kernel: one output per thread. Each step stages one
-// element of A and one of B per thread (zero outside the matrix), a barrier makes the
-// tiles visible, 16 products are accumulated, and a second barrier keeps the next
-// step's stores off tiles still being read. Grid: ceil(N/16) x ceil(M/16) x batch.
-// ---------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) sgemm_tile16(GemmArgs p)
-{
-    __shared__ float sa[16][17];
-    __shared__ float sb[16][17];
-    const int tx = threadIdx.x, ty = threadIdx.y;
-    const int row = blockIdx.y * 16 + ty, col = blockIdx.x * 16 + tx;
-    const float *__restrict__ A = p.A + (int64_t)blockIdx.z * p.strideA;
-    const float *__restrict__ B = p.B + (int64_t)blockIdx.z * p.strideB;
-    float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
-    float sum = 0.f;
-    for (int k0 = 0; k0 < p.K; k0 += 16) {
-        sa[ty][tx] = (row < p.M && k0 + tx < p.K) ? A[(int64_t)row * p.lda + k0 + tx] : 0.f;
-        sb[ty][tx] = (k0 + ty < p.K && col < p.N) ? B[(int64_t)(k0 + ty) * p.ldb + col] : 0.f;
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
-            sum += sa[ty][kk] * sb[kk][tx];
-        __syncthreads();
-    }
-    if (row < p.M && col < p.N) {
-        float *c = C + (int64_t)row * p.ldc + col;
-        float out = p.alpha * sum;
-        if (p.beta != 0.f)
-            out += p.beta * *c;
-        *c = out;
-    }
-}
-
-// C = beta*C over the M x N window (C not read when beta == 0). Grid-stride in both
-// dimensions; blockIdx.z selects the batch.
-__global__ void __launch_bounds__(256) sgemm_scale(GemmArgs p)
-{
-    float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
-    for (int i = blockIdx.y * blockDim.y + threadIdx.y; i < p.M; i += gridDim.y * blockDim.y)
-        for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < p.N; j += gridDim.x * blockDim.x) {
-            float *c = C + (int64_t)i * p.ldc + j;
-            *c = (p.beta == 0.f) ? 0.f : p.beta * *c;
-        }
 }
 
 }  // namespace sgemm_impl

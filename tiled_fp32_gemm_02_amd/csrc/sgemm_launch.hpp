@@ -1,0 +1,15 @@
+// Host-side launcher of one MFMA kernel configuration for one operand form. Declared
+// here, defined in sgemm_launch_impl.hpp and instantiated in sgemm_inst.hip, which is
+// compiled once per operand form (TA, TB) so the four sets build in parallel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "sgemm_kernels.hpp"
+
+namespace sgemm_impl {
+
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int GROUP_M, bool TA, bool TB>
+hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, hipStream_t s);
+
+}  // namespace sgemm_impl
