@@ -30,16 +30,16 @@ struct Config {
     LaunchFn launch;
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int GROUP_M>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, int GROUP_M>
 hipError_t launch_mfma(const GemmArgs &p, int batch, bool ta, bool tb, bool vec, bool edge, hipStream_t s)
 {
     if (!ta && !tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, GROUP_M, false, false>(p, batch, vec, edge, s);
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M, false, false>(p, batch, vec, edge, s);
     if (!ta && tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, GROUP_M, false, true>(p, batch, vec, edge, s);
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M, false, true>(p, batch, vec, edge, s);
     if (ta && !tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, GROUP_M, true, false>(p, batch, vec, edge, s);
-    return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, GROUP_M, true, true>(p, batch, vec, edge, s);
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M, true, false>(p, batch, vec, edge, s);
+    return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M, true, true>(p, batch, vec, edge, s);
 }
 
 hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, bool, hipStream_t s)
@@ -58,9 +58,10 @@ hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, b
 
 // Configuration table: id 0 is the 16x16 baseline kernel, ids 1.. the MFMA
 // configurations of sgemm_configs.inc in order. Names encode the tile (BM x BN x BK),
-// the wave grid (WGM x WGN) and, after "k", the wave groups along k.
-#define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, GROUP_M) \
-    {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, launch_mfma<BM, BN, BK, WGM, WGN, WGK, GROUP_M>},
+// the wave grid (WGM x WGN), after "k" the wave groups along k and after "p" the
+// K-tiles prefetched ahead (1 when absent).
+#define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M) \
+    {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M>},
 const Config kConfigs[] = {
     {"tile16", KIND_TILE16, 16, 16, 16, 256, launch_tile16},
     SGEMM_MFMA_CONFIGS(SGEMM_TABLE_ROW)
@@ -101,30 +102,26 @@ struct Candidate {
     double rate_many;   // per-CU rate with two or more
 };
 
-const Candidate kCandidatesVec[] = {
-    {3, 16, 0.500, 0.500},    // mfma_256x256x16_w2x4: one workgroup per CU fits
-    {9, 4, 0.458, 0.458},     // mfma_128x128x32_w2x2k2: one per CU
-    {8, 2, 0.400, 0.452},     // mfma_64x128x32_w2x2k2: up to three per CU
-    {7, 1, 0.395, 0.436},     // mfma_64x64x64_w2x2k4: up to two per CU
-};
-// 32-bit path (unaligned operands): the 64-deep stage loses to 32-deep ones there.
-const Candidate kCandidatesScalar[] = {
-    {3, 16, 0.500, 0.500},
-    {9, 4, 0.458, 0.458},
-    {8, 2, 0.400, 0.452},
-    {6, 1, 0.380, 0.420},     // mfma_64x64x32_w2x2k2: up to four per CU
+// Rates measured with every candidate prefetching two K-tiles ahead; fitted to the
+// sweep over 256^3 ... 4096^3, the GPT-2 linear layers and the 1000 x 1537 x 777
+// unaligned case (which the same table serves).
+const Candidate kCandidates[] = {
+    {10, 16, 0.500, 0.500},   // mfma_256x256x16_w2x4p2: one workgroup per CU
+    {14, 4, 0.484, 0.466},    // mfma_128x128x32_w2x2k2p2: one per CU
+    {13, 2, 0.459, 0.461},    // mfma_64x128x32_w2x2k2p2: up to two per CU
+    {12, 1, 0.380, 0.390},    // mfma_64x64x64_w2x2k4p2: one per CU, 16 waves
+    {11, 1, 0.360, 0.410},    // mfma_64x64x32_w2x2k2p2: up to four per CU
 };
 
 int choose(int M, int N, bool vec)
 {
+    (void)vec;    // one table serves the 128-bit and the 32-bit paths
     constexpr uint64_t kCUs = 256;
-    const Candidate *cands = vec ? kCandidatesVec : kCandidatesScalar;
-    const int count = vec ? (int)(sizeof(kCandidatesVec) / sizeof(Candidate))
-                          : (int)(sizeof(kCandidatesScalar) / sizeof(Candidate));
-    int best = cands[0].id;
+    constexpr int count = (int)(sizeof(kCandidates) / sizeof(Candidate));
+    int best = kCandidates[0].id;
     double best_cost = 0.0;
     for (int i = 0; i < count; ++i) {
-        const Candidate &cand = cands[i];
+        const Candidate &cand = kCandidates[i];
         const uint64_t tiles = tile_count(kConfigs[cand.id], M, N);
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
         const double cost = (double)rounds * cand.units / (rounds >= 2 ? cand.rate_many : cand.rate_one);

@@ -208,10 +208,11 @@ __device__ __forceinline__ void lds_read(const float *p, float (&out)[W])
 //    c*T + b (T blocks), so lane l reads T consecutive values for one k in one read,
 //    and for B writes T consecutive columns of C.
 // ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, bool TA, bool TB, bool VEC, bool EDGE>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool TA, bool TB, bool VEC, bool EDGE>
 __global__ void __launch_bounds__(WGM * WGN * WGK * 64)
 sgemm_mfma(GemmArgs p, int group_m)
 {
+    static_assert(PF == 1 || PF == 2, "K-tiles in flight ahead of the one being multiplied");
     constexpr int NT = WGM * WGN * WGK * 64;
     constexpr int KSLICE = BK / WGK;                    // k per stage handled by one wave group
     constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
@@ -246,25 +247,28 @@ sgemm_mfma(GemmArgs p, int group_m)
     const int wm = (wave % (WGM * WGN)) / WGN, wn = wave % WGN;
     const int l32 = lane & 31, half = lane >> 5;
 
-    floatx4 ra[AIO::CH], rb[BIO::CH];
+    // PF sets of staging registers: with PF = 2 a K-tile's global loads are issued two
+    // stages before it is multiplied. `slot` is always a compile-time constant after
+    // inlining, so the sets stay in registers.
+    floatx4 ra[PF][AIO::CH], rb[PF][BIO::CH];
 
-    // Global -> registers for the K-tile starting at k0 (zero outside the matrix).
-    auto load_tile = [&](int k0) __attribute__((always_inline)) {
+    // Global -> registers set `slot` for the K-tile starting at k0 (zero outside the matrix).
+    auto load_tile = [&](int k0, int slot) __attribute__((always_inline)) {
         if constexpr (TA)
-            AIO::template load<VEC, EDGE>(ra, A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, tid);
+            AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, tid);
         else
-            AIO::template load<VEC, EDGE>(ra, A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, tid);
+            AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, tid);
         if constexpr (TB)
-            BIO::template load<VEC, EDGE>(rb, B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, tid);
+            BIO::template load<VEC, EDGE>(rb[slot], B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, tid);
         else
-            BIO::template load<VEC, EDGE>(rb, B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, tid);
+            BIO::template load<VEC, EDGE>(rb[slot], B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, tid);
     };
 
-    // Registers -> LDS stage `st`.
-    auto store_tile = [&](int st) __attribute__((always_inline)) {
+    // Registers set `slot` -> LDS stage `st`.
+    auto store_tile = [&](int st, int slot) __attribute__((always_inline)) {
         float *As = smem + st * STAGE;
-        AIO::store(ra, As, tid);
-        BIO::store(rb, As + AIO::SIZE, tid);
+        AIO::store(ra[slot], As, tid);
+        BIO::store(rb[slot], As + AIO::SIZE, tid);
     };
 
     floatx16 acc[TM][TN];
@@ -327,17 +331,45 @@ sgemm_mfma(GemmArgs p, int group_m)
         }
     };
 
-    // Pipeline. The last K-tile is peeled off so the loop body has no conditionals
-    // around the staging registers (which keeps them in VGPRs).
+    // Pipeline over nk K-tiles, two LDS stages, one barrier per K-tile. The last K-tile
+    // is peeled off so the loop bodies have no conditionals around the staging
+    // registers (which keeps them in VGPRs).
     const int nk = ceil_div(K, BK);
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int t = 0; t + 1 < nk; ++t) {
-        load_tile((t + 1) * BK);         // in flight while this stage is multiplied
-        compute(t & 1);
-        store_tile((t + 1) & 1);         // other stage: its last reader finished before the previous barrier
+    if constexpr (PF == 1) {
+        load_tile(0, 0);
+        store_tile(0, 0);
         __syncthreads();
+        for (int t = 0; t + 1 < nk; ++t) {
+            load_tile((t + 1) * BK, 0);  // in flight while this stage is multiplied
+            compute(t & 1);
+            store_tile((t + 1) & 1, 0);  // other stage: its last reader finished before the previous barrier
+            __syncthreads();
+        }
+    } else {
+        // Entering step t: stage t%2 holds K-tile t, register set (t+1)%2 holds tile t+1
+        // (loaded during step t-1) and set t%2 is free. Step t loads tile t+2 into set
+        // t%2 (the last tile again once past the end, so the load needs no condition),
+        // multiplies stage t%2, then stores set (t+1)%2 into stage (t+1)%2.
+        auto step = [&](int t, int s) __attribute__((always_inline)) {
+            const int ahead = t + 2 < nk ? t + 2 : nk - 1;
+            load_tile(ahead * BK, s);
+            compute(s);
+            store_tile(1 - s, 1 - s);
+            __syncthreads();
+        };
+        load_tile(0, 0);
+        load_tile((nk > 1 ? 1 : 0) * BK, 1);
+        store_tile(0, 0);
+        __syncthreads();
+        int t = 0;
+        for (; t + 2 < nk; t += 2) {     // steps t and t+1, both before the last tile
+            step(t, 0);
+            step(t + 1, 1);
+        }
+        if (t + 1 < nk) {
+            step(t, 0);
+            ++t;
+        }
     }
     compute((nk - 1) & 1);
 
