@@ -96,7 +96,7 @@ uint64_t tile_count(const Config &c, int M, int N)
 // fills the chip in one round and the wave-split 64x64 tile when few tiles exist;
 // K cancels out because every candidate walks the same K.
 struct Candidate {
-    int id;
+    const char *name;   // configuration name in the table
     int units;          // tile area / (64 * 64)
     double rate_one;    // per-CU rate with one resident workgroup
     double rate_many;   // per-CU rate with two or more
@@ -106,27 +106,47 @@ struct Candidate {
 // sweep over 256^3 ... 4096^3, the GPT-2 linear layers and the 1000 x 1537 x 777
 // unaligned case (which the same table serves).
 const Candidate kCandidates[] = {
-    {10, 16, 0.500, 0.500},   // mfma_256x256x16_w2x4p2: one workgroup per CU
-    {14, 4, 0.484, 0.466},    // mfma_128x128x32_w2x2k2p2: one per CU
-    {13, 2, 0.459, 0.461},    // mfma_64x128x32_w2x2k2p2: up to two per CU
-    {12, 1, 0.380, 0.390},    // mfma_64x64x64_w2x2k4p2: one per CU, 16 waves
-    {11, 1, 0.360, 0.410},    // mfma_64x64x32_w2x2k2p2: up to four per CU
+    {"mfma_256x256x16_w2x4p2", 16, 0.500, 0.500},     // one workgroup per CU
+    {"mfma_128x128x32_w2x2k2p2", 4, 0.484, 0.466},    // one per CU
+    {"mfma_64x128x32_w2x2k2p2", 2, 0.459, 0.461},     // up to two per CU
+    {"mfma_64x64x64_w2x2k4p2", 1, 0.380, 0.390},      // one per CU, 16 waves
+    {"mfma_64x64x32_w2x2k2p2", 1, 0.360, 0.410},      // up to four per CU
+};
+constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
+
+int find_config(const char *name)
+{
+    for (int i = 0; i < kNumConfigs; ++i) {
+        const char *a = kConfigs[i].name, *b = name;
+        while (*a && *a == *b) { ++a; ++b; }
+        if (*a == *b)
+            return i;
+    }
+    return -1;
+}
+
+// Table ids of the candidates, looked up once.
+struct CandidateIds {
+    int id[kNumCandidates];
+    CandidateIds() { for (int i = 0; i < kNumCandidates; ++i) id[i] = find_config(kCandidates[i].name); }
 };
 
 int choose(int M, int N, bool vec)
 {
     (void)vec;    // one table serves the 128-bit and the 32-bit paths
+    static const CandidateIds ids;
     constexpr uint64_t kCUs = 256;
-    constexpr int count = (int)(sizeof(kCandidates) / sizeof(Candidate));
-    int best = kCandidates[0].id;
+    int best = -1;
     double best_cost = 0.0;
-    for (int i = 0; i < count; ++i) {
+    for (int i = 0; i < kNumCandidates; ++i) {
         const Candidate &cand = kCandidates[i];
-        const uint64_t tiles = tile_count(kConfigs[cand.id], M, N);
+        if (ids.id[i] < 0)
+            continue;
+        const uint64_t tiles = tile_count(kConfigs[ids.id[i]], M, N);
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
         const double cost = (double)rounds * cand.units / (rounds >= 2 ? cand.rate_many : cand.rate_one);
-        if (i == 0 || cost < best_cost) {
-            best = cand.id;
+        if (best < 0 || cost < best_cost) {
+            best = ids.id[i];
             best_cost = cost;
         }
     }

@@ -108,17 +108,25 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 // ld), copied HBM -> registers -> LDS in 4-float chunks. Thread t takes chunks
 // t, t + NT, ...; consecutive threads take consecutive chunks along a row, and when
 // the tile has fewer chunks than threads the surplus threads idle. The LDS copy keeps
-// the same layout with 4 floats of row padding (stride TC + 4).
+// the same layout, with 4 floats of padding after every G rows, G = 64 / TC for rows
+// of 16 or 32 floats and G = 1 for longer rows. Then the G rows that one group of 16
+// lanes stores with 128-bit writes fill the 64 LDS banks exactly once, and 16
+// consecutive rows read at one column (a fragment read) start in 16 distinct 4-bank
+// groups. (The bank-conflict counter confirms this on gfx950: a plain 4-float row
+// padding leaves the stores of 16-float rows colliding two ways.)
 template <int TR, int TC, int NT>
 struct TileIO {
     static constexpr int CPR = TC / 4;
     static constexpr int CHUNKS = TR * TC / 4;
     static constexpr int CH = (CHUNKS + NT - 1) / NT;
     static constexpr bool IDLE = CHUNKS % NT != 0;
-    static constexpr int LD = TC + 4;
-    static constexpr int SIZE = TR * LD;
-    static_assert(TC % 4 == 0, "rows are whole 4-float chunks");
-    static_assert(CHUNKS % NT == 0 || CH == 1, "a partial loader round only when it is the only one");
+    static constexpr int G = TC >= 64 ? 1 : 64 / TC;       // rows per 4-float pad
+    static constexpr int SIZE = TR * TC + (TR / G) * 4;
+    static_assert(TC % 16 == 0, "rows are multiples of 16 floats");
+    static_assert(TR % G == 0, "whole groups of rows");
+
+    // Offset (floats) of row r of the tile in LDS.
+    __device__ __forceinline__ static int row(int r) { return r * TC + (r / G) * 4; }
 
     // src points at the tile origin; rows/cols are how many rows and columns from the
     // origin lie inside the matrix. VEC: 128-bit loads (row starts 16-byte aligned and
@@ -157,7 +165,7 @@ struct TileIO {
             const int idx = tid + c * NT;
             if (IDLE && idx >= CHUNKS)
                 break;
-            *reinterpret_cast<floatx4 *>(&lds[(idx / CPR) * LD + (idx % CPR) * 4]) = r[c];
+            *reinterpret_cast<floatx4 *>(&lds[row(idx / CPR) + (idx % CPR) * 4]) = r[c];
         }
     }
 };
@@ -191,9 +199,9 @@ __device__ __forceinline__ void lds_read(const float *p, float (&out)[W])
 // the bounds checks needed when M, N or K is not a multiple of the tile. Without VEC
 // every element is checked.
 //
-// Each operand tile is staged in LDS in its memory layout (TileIO): A as [BM][BK+4]
-// (k contiguous), or [BK][BM+4] when transposed (m contiguous); B as [BK][BN+4] (n
-// contiguous), or [BN][BK+4] when transposed (k contiguous).
+// Each operand tile is staged in LDS in its memory layout (TileIO, padded rows): A as
+// [BM][BK] (k contiguous), or [BK][BM] when transposed (m contiguous); B as [BK][BN] (n
+// contiguous), or [BN][BK] when transposed (k contiguous).
 //
 // Lane layout of v_mfma_f32_32x32x2_f32 (one 32x32 block, k = 2): lane l supplies
 // A(l%32, l/32) and B(l/32, l%32); accumulator element e of lane l is
@@ -297,19 +305,19 @@ sgemm_mfma(GemmArgs p, int group_m)
             if constexpr (!TA) {
 #pragma unroll
                 for (int a = 0; a < TM; ++a)
-                    af[a] = *reinterpret_cast<const floatx4 *>(&As[(a_idx + a * 32) * AIO::LD + kg + 4 * half]);
+                    af[a] = *reinterpret_cast<const floatx4 *>(&As[AIO::row(a_idx + a * 32) + kg + 4 * half]);
             }
             if constexpr (TB) {
 #pragma unroll
                 for (int b = 0; b < TN; ++b)
-                    bf[b] = *reinterpret_cast<const floatx4 *>(&Bs[(b_idx + b * 32) * BIO::LD + kg + 4 * half]);
+                    bf[b] = *reinterpret_cast<const floatx4 *>(&Bs[BIO::row(b_idx + b * 32) + kg + 4 * half]);
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int k = kg + 4 * half + s;
                 float av[TM], bv[TN];
                 if constexpr (TA) {
-                    lds_read<TM>(&As[k * AIO::LD + a_idx], av);
+                    lds_read<TM>(&As[AIO::row(k) + a_idx], av);
                 } else {
 #pragma unroll
                     for (int a = 0; a < TM; ++a)
@@ -320,7 +328,7 @@ sgemm_mfma(GemmArgs p, int group_m)
                     for (int b = 0; b < TN; ++b)
                         bv[b] = bf[b][s];
                 } else {
-                    lds_read<TN>(&Bs[k * BIO::LD + b_idx], bv);
+                    lds_read<TN>(&Bs[BIO::row(k) + b_idx], bv);
                 }
 #pragma unroll
                 for (int a = 0; a < TM; ++a)
