@@ -12,8 +12,19 @@ roofline of the kernel (flops per launch / mean launch time from HIP events on
 the launch stream, against the MI355X fp32 matrix peak of 157.3 TFLOP/s), and
 the CPU oracle timed on a bounded sample of the same product on this host.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--config ID]
-                    [--no-cpu-baseline] [--copy-probe]
+    python bench.py [--steps K] [--warmup W] [--settle-seconds S] [--workload NAME]
+                    [--config ID] [--no-cpu-baseline] [--copy-probe]
+
+Before the W warm-up steps the step runs back to back, untimed, for S seconds
+(default 1): the GPU's clock ramps up over the first tens of milliseconds of
+load, and a short warm-up alone times the kernel partly at the lower clock. The
+timed region is exactly K steps, bracketed by synchronisations; an event is
+recorded on the launch stream between steps, so the line also carries the
+median, minimum and 90th percentile of the per-step times. The shader clock is
+read from sysfs before and after the timed steps where the driver exposes it.
+
+``--workload gpt2_seq`` times the three GPT-2-small linears (QKV, MLP up, MLP
+down) in that order as one step: total flops over total time.
 
 ``--copy-probe`` instead runs a plain device-to-device copy of a known size, the
 calibration run for the HBM byte counters.
@@ -39,6 +50,21 @@ CSRC = os.path.join(ROOT, "tiled_fp32_gemm_02_amd", "csrc")
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def read_sclk():
+    """Current shader clock in MHz from the amdgpu driver's sysfs table (the entry
+    marked '*'), or None where it is not readable."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().lower().replace("mhz", "").strip(" *"))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
 
 
 def kernel_source_hash() -> str:
@@ -78,29 +104,32 @@ def recorded_traffic(workload: str, config_name: str):
         return None
 
 
-def cpu_baseline(w, A, B, C, target_s: float):
-    """Time the CPU oracle on the first R rows of the product (R chosen from a pilot
-    run so the sample takes about `target_s` seconds). Returns the JSON object."""
+def cpu_baseline(probs, target_s: float):
+    """Time the CPU oracle on the first rows of each product of the step (the same
+    fraction of every product's rows, chosen from a pilot run so that the sample
+    takes about `target_s` seconds). Returns the JSON object."""
     import oracle
-    N, K = w.N, w.K
 
-    def run(rows):
+    def run(p, rows):
+        w = p["w"]
         t0 = time.perf_counter()
-        oracle.sgemm(rows, N, K, w.alpha, A, w.lda_, B, w.ldb_, w.beta, C, w.ldc_, with_bound=False)
+        oracle.sgemm(rows, w.N, w.K, w.alpha, p["A"], w.lda_, p["B"], w.ldb_, w.beta, p["C"], w.ldc_,
+                     with_bound=False)
         return time.perf_counter() - t0
 
-    pilot_rows = min(w.M, 16)
-    t_pilot = run(pilot_rows)
-    rows = int(min(w.M, max(pilot_rows, round(target_s * pilot_rows / max(t_pilot, 1e-6)))))
-    t = run(rows)
-    flops = 2.0 * rows * N * K
+    pilot = [min(p["w"].M, 16) for p in probs]
+    t_pilot = sum(run(p, r) for p, r in zip(probs, pilot))
+    frac = min(1.0, target_s / max(t_pilot, 1e-6) * sum(pilot) / sum(p["w"].M for p in probs))
+    rows = [int(min(p["w"].M, max(r, round(frac * p["w"].M)))) for p, r in zip(probs, pilot)]
+    t = sum(run(p, r) for p, r in zip(probs, rows))
+    flops = sum(2.0 * r * p["w"].N * p["w"].K for p, r in zip(probs, rows))
+    what = "; ".join(f"rows 0..{r - 1} of the {p['w'].M}x{p['w'].N}x{p['w'].K} product" for p, r in zip(probs, rows))
     return {
         "value": round(flops / t / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": oracle.threads(),
         "kind": "oracle",
-        "sample": (f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} product ({rows}x{N}x{K}, "
-                   f"{flops / 1e9:.1f} GFLOP, fp64 accumulation, {t:.1f} s wall)"),
+        "sample": f"{what} ({flops / 1e9:.1f} GFLOP, fp64 accumulation, {t:.1f} s wall)",
     }
 
 
@@ -121,6 +150,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="untimed back-to-back steps before the warm-up, for the clock to ramp")
     ap.add_argument("--workload", default="sq4096")
     ap.add_argument("--config", type=int, default=-1, help="force a kernel configuration id")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,69 +173,102 @@ def main():
     from tiled_fp32_gemm_02_amd import build as sgbuild
     sgbuild.ensure_built()
     import tiled_fp32_gemm_02_amd as sg
+    import oracle
     from workloads import WORKLOADS, make, flops
 
-    w = WORKLOADS[args.workload]
-    A, B, C = make(w)
+    names = ["gpt2_qkv", "gpt2_mlp_up", "gpt2_mlp_down"] if args.workload == "gpt2_seq" else [args.workload]
     dev = torch.device("cuda:0")
-    dA = torch.from_numpy(A).to(dev)
-    dB = torch.from_numpy(B).to(dev)
-    dC = torch.from_numpy(C).to(dev) if C is not None else torch.empty((w.M, w.ldc_), device=dev)
-    C0 = dC.clone()
-    cfg = args.config if args.config >= 0 else sg.sgemm_select_config(
-        w.M, w.N, w.K, w.alpha, dA, w.lda_, dB, w.ldb_, dC, w.ldc_)
-    cfg_name = sg.sgemm_config_name(cfg)
+    probs = []
+    for name in names:
+        w = WORKLOADS[name]
+        A, B, C = make(w)
+        dA = torch.from_numpy(A).to(dev)
+        dB = torch.from_numpy(B).to(dev)
+        dC = torch.from_numpy(C).to(dev) if C is not None else torch.empty((w.M, w.ldc_), device=dev)
+        cfg = args.config if args.config >= 0 else sg.sgemm_select_config(
+            w.M, w.N, w.K, w.alpha, dA, w.lda_, dB, w.ldb_, dC, w.ldc_)
+        probs.append({"w": w, "A": A, "B": B, "C": C, "dA": dA, "dB": dB, "dC": dC, "C0": dC.clone(),
+                      "cfg": cfg, "cfg_name": sg.sgemm_config_name(cfg)})
     stream = torch.cuda.Stream(device=dev)
     s_handle = int(stream.cuda_stream)
 
     def step():
-        st = sg.sgemm_ex(args.config, w.M, w.N, w.K, w.alpha, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
-                         w.beta, dC.data_ptr(), w.ldc_, s_handle)
-        if st != 0:
-            raise RuntimeError(f"sgemm failed: {sg.sgemm_status_string(st)}")
+        for p in probs:
+            w = p["w"]
+            st = sg.sgemm_ex(args.config, w.M, w.N, w.K, w.alpha, p["dA"].data_ptr(), w.lda_, p["dB"].data_ptr(),
+                             w.ldb_, w.beta, p["dC"].data_ptr(), w.ldc_, s_handle)
+            if st != 0:
+                raise RuntimeError(f"sgemm failed: {sg.sgemm_status_string(st)}")
 
     # One checked call on a fresh C: sampled entries against the oracle.
-    log(f"bench: workload {w.name} {w.M}x{w.N}x{w.K} config {cfg} {cfg_name}")
+    for p in probs:
+        log(f"bench: workload {p['w'].name} {p['w'].M}x{p['w'].N}x{p['w'].K} config {p['cfg']} {p['cfg_name']}")
     step()
     torch.cuda.synchronize()
-    out = dC.cpu().numpy()
-    rng = np.random.default_rng(12345)
-    rows = np.concatenate([[0, w.M - 1], rng.integers(0, w.M, 254)])
-    cols = np.concatenate([[0, w.N - 1], rng.integers(0, w.N, 254)])
-    import oracle
-    ref, bound = oracle.sgemm_entries(w.M, w.N, w.K, w.alpha, A, w.lda_, B, w.ldb_, w.beta, C, w.ldc_,
-                                      rows, cols)
-    ok, worst, _ = oracle.within_bound(out[rows, cols], ref, bound)
-    if not ok:
-        raise SystemExit(f"bench: result outside the oracle bound (max |err|/bound = {worst})")
-    log(f"bench: checked {rows.size} sampled entries, max |err|/bound = {worst:.3f}")
-    dC.copy_(C0)
+    worst_all, checked = 0.0, 0
+    for p in probs:
+        w = p["w"]
+        out = p["dC"].cpu().numpy()
+        rng = np.random.default_rng(12345)
+        rows = np.concatenate([[0, w.M - 1], rng.integers(0, w.M, 254)])
+        cols = np.concatenate([[0, w.N - 1], rng.integers(0, w.N, 254)])
+        ref, bound = oracle.sgemm_entries(w.M, w.N, w.K, w.alpha, p["A"], w.lda_, p["B"], w.ldb_, w.beta, p["C"],
+                                          w.ldc_, rows, cols)
+        ok, worst, _ = oracle.within_bound(out[rows, cols], ref, bound)
+        if not ok:
+            raise SystemExit(f"bench: {w.name} outside the oracle bound (max |err|/bound = {worst})")
+        worst_all, checked = max(worst_all, worst), checked + rows.size
+        p["dC"].copy_(p["C0"])
+    log(f"bench: checked {checked} sampled entries, max |err|/bound = {worst_all:.3f}")
     torch.cuda.synchronize()
 
     with torch.cuda.stream(stream):
+        t_end = time.perf_counter() + args.settle_seconds
+        settle = 0
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                step()
+            settle += 8
+            torch.cuda.synchronize()
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
+        sclk_before = read_sclk()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         t0 = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(args.steps):
+        evs[0].record(stream)
+        for i in range(args.steps):
             step()
-        ev1.record(stream)
+            evs[i + 1].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        sclk_after = read_sclk()
     wall_s = t1 - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
-    fl = flops(w.M, w.N, w.K)
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])    # ms
+    kernel_ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    fl = sum(flops(p["w"].M, p["w"].N, p["w"].K) for p in probs)
     value = fl * args.steps / wall_s / 1e12
     achieved = fl / (kernel_ms * 1e-3) / 1e12
-    log(f"bench: {args.steps} steps in {wall_s * 1e3:.2f} ms wall; mean kernel {kernel_ms * 1e3:.1f} us")
+    log(f"bench: {settle} settle steps, {args.warmup} warm-up; {args.steps} steps in {wall_s * 1e3:.2f} ms wall; "
+        f"mean step {kernel_ms * 1e3:.1f} us (events)")
 
     props = torch.cuda.get_device_properties(dev)
+    w0 = probs[0]["w"]
+    if len(probs) == 1:
+        config = {"workload": w0.name, "M": w0.M, "N": w0.N, "K": w0.K, "alpha": w0.alpha, "beta": w0.beta,
+                  "inputs": w0.note, "kernel": probs[0]["cfg_name"], "parallelism": "none (one GPU)"}
+        metric = ("FP32 SGEMM TFLOP/s at M=N=K=4096 and fraction of MI355X FP32 peak" if w0.name == "sq4096"
+                  else f"FP32 SGEMM TFLOP/s ({w0.name}) and fraction of MI355X FP32 peak")
+        traffic = recorded_traffic(w0.name, probs[0]["cfg_name"])
+    else:
+        config = {"workload": args.workload,
+                  "sequence": [{"name": p["w"].name, "M": p["w"].M, "N": p["w"].N, "K": p["w"].K,
+                                "kernel": p["cfg_name"]} for p in probs],
+                  "inputs": probs[0]["w"].note, "parallelism": "none (one GPU)"}
+        metric = f"FP32 SGEMM TFLOP/s ({args.workload}: the products in sequence) and fraction of MI355X FP32 peak"
+        traffic = None
     line = {
-        "metric": ("FP32 SGEMM TFLOP/s at M=N=K=4096 and fraction of MI355X FP32 peak" if w.name == "sq4096"
-                   else f"FP32 SGEMM TFLOP/s ({w.name}) and fraction of MI355X FP32 peak"),
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -216,23 +280,26 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
-                   "inputs": w.note, "kernel": cfg_name, "parallelism": "none (one GPU)"},
+        "config": config,
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": PEAK_FP32_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-            "traffic": recorded_traffic(w.name, cfg_name),
+            "traffic": traffic,
         },
+        "timing": {"settle_steps": settle, "step_us_median": round(float(np.median(per_step)) * 1e3, 2),
+                   "step_us_min": round(float(per_step.min()) * 1e3, 2),
+                   "step_us_p90": round(float(np.percentile(per_step, 90)) * 1e3, 2),
+                   "sclk_mhz_before": sclk_before, "sclk_mhz_after": sclk_after},
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
-        "check": {"sampled_entries": int(rows.size), "max_err_over_bound": round(worst, 4)},
+        "check": {"sampled_entries": int(checked), "max_err_over_bound": round(worst_all, 4)},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(w, A, B, C, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(probs, args.cpu_seconds)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

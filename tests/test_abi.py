@@ -124,7 +124,7 @@ def test_launch_shape_mfma():
     for cid, name in enumerate(sg.configs()):
         if not name.startswith("mfma_"):
             continue
-        m = re.fullmatch(r"mfma_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?", name)
+        m = re.fullmatch(r"mfma_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
         assert m, name
         bm, bn, _, wm, wn = (int(x) for x in m.groups()[:5])
         wk = int(m.group(6) or 1)

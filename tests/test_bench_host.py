@@ -1,0 +1,43 @@
+"""Host-side pieces of bench.py (CPU only): the one-GPU guard, the sysfs clock
+reader and the oracle's bounded CPU sample."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from workloads import Gemm, make  # noqa: E402
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+def test_read_sclk_is_an_int_or_none():
+    v = bench.read_sclk()
+    assert v is None or (isinstance(v, int) and v > 0)
+
+def test_cpu_baseline_samples_every_product():
+    probs = []
+    for name, (M, N, K) in {"p1": (64, 48, 40), "p2": (32, 80, 24)}.items():
+        w = Gemm(name, M, N, K, alpha=1.5, beta=0.5, seed=7)
+        A, B, C = make(w)
+        probs.append({"w": w, "A": A, "B": B, "C": C})
+    out = bench.cpu_baseline(probs, 0.05)
+    assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s" and out["value"] > 0
+    assert out["cores"] >= 1
+    assert "64x48x40" in out["sample"] and "32x80x24" in out["sample"]
+
+def test_kernel_source_hash_ignores_comments(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("int f() { return 1; } // one\n/* block */\n")
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    h1 = bench.kernel_source_hash()
+    src.write_text("int f() {   return 1; }   // a different comment\n")
+    assert bench.kernel_source_hash() == h1
+    src.write_text("int f() { return 2; }\n")
+    assert bench.kernel_source_hash() != h1

@@ -39,12 +39,36 @@ def kernels(tmp_path_factory):
     return out
 
 
+def expected_mfma_kernels(config_names):
+    """Template arguments <BM,BN,BK,WGM,WGN,WGK,PF,DMA,TA,TB,VEC,EDGE> of every matrix
+    kernel the launcher can start: per configuration and operand form, the aligned
+    whole-tile and edge variants as configured, and the unaligned variant with one
+    K-tile in flight (K-tile 16 * WGK for direct-copy configurations)."""
+    out = set()
+    for name in config_names:
+        m = re.fullmatch(r"mfma_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
+        assert m, name
+        bm, bn, bk, wm, wn = (int(x) for x in m.groups()[:5])
+        wk, pf, dma = int(m.group(6) or 1), int(m.group(7) or 1), m.group(8) is not None
+        for ta in (0, 1):
+            for tb in (0, 1):
+                for edge in (0, 1):
+                    out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge))
+                out.add((bm, bn, 16 * wk if dma else bk, wm, wn, wk, 1, 0, ta, tb, 0, 1))
+    return out
+
+
 def test_all_kernels_present(kernels):
     names = " ".join(kernels)
     assert "sgemm_tile16" in names and "sgemm_scale" in names
-    mfma = [n for n in kernels if "sgemm_mfma<" in n]
-    # every configuration x 4 operand forms x 3 alignment/edge variants
-    assert len(mfma) == 12 * (len(__import__("tiled_fp32_gemm_02_amd").configs()) - 1), len(mfma)
+    found = set()
+    for n in kernels:
+        m = re.search(r"sgemm_mfma<([^>]*)>", n)
+        if m:
+            found.add(tuple(int(x) if x.strip().lstrip("-").isdigit() else int(x.strip() == "true")
+                            for x in m.group(1).split(",")))
+    import tiled_fp32_gemm_02_amd as sg
+    assert found == expected_mfma_kernels(sg.configs()[1:])
 
 
 def test_no_scratch_no_spills(kernels):

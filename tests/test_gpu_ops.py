@@ -78,6 +78,41 @@ def test_every_config_every_op(opA, opB, M, N, K):
             assert ok, (cid, "plain", worst, idx)
 
 
+@pytest.mark.parametrize("opA,opB", OPS)
+@pytest.mark.parametrize("M,N,K", [(512, 512, 16), (256, 512, 32), (512, 768, 384), (768, 512, 1024)])
+def test_every_config_whole_tiles(opA, opB, M, N, K):
+    """Shapes every configuration covers with whole, aligned tiles: the fast kernels
+    (including the direct HBM -> LDS copy pipeline) over 1, 2, many and odd counts of
+    K-tiles, every operand form, several workgroups."""
+    rng = np.random.default_rng(M + 5 * N + 9 * K + 17 * opA + 19 * opB)
+    a, b, c = draw(rng, (M, K), "normal"), draw(rng, (K, N), "normal"), draw(rng, (M, N), "uniform")
+    ref, bound = oracle.gemm(opA, opB, M, N, K, 1.25, stored(opA, a), stored(opA, a).shape[1],
+                             stored(opB, b), stored(opB, b).shape[1], 0.5, c, N)
+    for cid in configs():
+        say(f"whole tiles op {opA}{opB} config {cid} {M}x{N}x{K}")
+        st, out, checks = run_general(cid, opA, opB, M, N, K, 1.25, a, b, 0.5, c, None, oracle.ACT_NONE)
+        assert st == 0 and all(checks.values()), checks
+        ok, worst, idx = oracle.within_bound(out, ref, bound)
+        assert ok, (cid, worst, idx, out[idx], ref[idx])
+
+
+@pytest.mark.parametrize("opA,opB", OPS)
+@pytest.mark.parametrize("M,N,K", [(300, 260, 132), (516, 772, 36), (4, 8, 4), (260, 1028, 1000)])
+def test_every_config_aligned_edges(opA, opB, M, N, K):
+    """16-byte aligned operands whose tiles cross the M, N and K edges: the aligned edge
+    kernels, including direct copies that zero-fill what lies outside the matrix."""
+    rng = np.random.default_rng(M + 7 * N + 3 * K + 23 * opA + 29 * opB)
+    a, b, c = draw(rng, (M, K), "normal"), draw(rng, (K, N), "normal"), draw(rng, (M, N), "uniform")
+    ref, bound = oracle.gemm(opA, opB, M, N, K, -0.75, stored(opA, a), stored(opA, a).shape[1],
+                             stored(opB, b), stored(opB, b).shape[1], 1.5, c, N)
+    for cid in configs():
+        say(f"aligned edges op {opA}{opB} config {cid} {M}x{N}x{K}")
+        st, out, checks = run_general(cid, opA, opB, M, N, K, -0.75, a, b, 1.5, c, None, oracle.ACT_NONE)
+        assert st == 0 and all(checks.values()), checks
+        ok, worst, idx = oracle.within_bound(out, ref, bound)
+        assert ok, (cid, worst, idx, out[idx], ref[idx])
+
+
 @pytest.mark.parametrize("opA,opB", OPS[1:])
 def test_transposes_small_integers_bitwise(opA, opB):
     rng = np.random.default_rng(21 + opA + 2 * opB)

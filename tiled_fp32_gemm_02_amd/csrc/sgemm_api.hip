@@ -27,19 +27,24 @@ struct Config {
     Kind kind;
     int bm, bn, bk;      // workgroup tile (tile16: 16 x 16 x 16)
     int threads;         // threads per workgroup
+    bool dma;            // aligned operands are copied HBM -> LDS directly
     LaunchFn launch;
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, int GROUP_M>
+// Row strides (floats) from which the direct-copy kernels' 32-bit in-tile offsets
+// could overflow; such calls take the element-wise (unaligned) variant instead.
+constexpr int kDmaMaxLd = 1 << 24;
+
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M>
 hipError_t launch_mfma(const GemmArgs &p, int batch, bool ta, bool tb, bool vec, bool edge, hipStream_t s)
 {
     if (!ta && !tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M, false, false>(p, batch, vec, edge, s);
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, false>(p, batch, vec, edge, s);
     if (!ta && tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M, false, true>(p, batch, vec, edge, s);
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, true>(p, batch, vec, edge, s);
     if (ta && !tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M, true, false>(p, batch, vec, edge, s);
-    return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M, true, true>(p, batch, vec, edge, s);
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, false>(p, batch, vec, edge, s);
+    return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, true>(p, batch, vec, edge, s);
 }
 
 hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, bool, hipStream_t s)
@@ -58,12 +63,12 @@ hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, b
 
 // Configuration table: id 0 is the 16x16 baseline kernel, ids 1.. the MFMA
 // configurations of sgemm_configs.inc in order. Names encode the tile (BM x BN x BK),
-// the wave grid (WGM x WGN), after "k" the wave groups along k and after "p" the
-// K-tiles prefetched ahead (1 when absent).
-#define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M) \
-    {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, GROUP_M>},
+// the wave grid (WGM x WGN), after "k" the wave groups along k, after "p" the K-tiles
+// prefetched ahead (1 when absent), and a final "d" marks direct HBM -> LDS copies.
+#define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M) \
+    {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>},
 const Config kConfigs[] = {
-    {"tile16", KIND_TILE16, 16, 16, 16, 256, launch_tile16},
+    {"tile16", KIND_TILE16, 16, 16, 16, 256, false, launch_tile16},
     SGEMM_MFMA_CONFIGS(SGEMM_TABLE_ROW)
 };
 #undef SGEMM_TABLE_ROW
@@ -214,7 +219,8 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     if (c.kind == KIND_MFMA && tiles * (uint64_t)c.threads > 0xFFFFFFFFull)
         return SGEMM_ERROR_TOO_LARGE;
     const bool edge = (M % c.bm) != 0 || (N % c.bn) != 0 || (K % c.bk) != 0;
-    const hipError_t e = c.launch(p, batch, opA != 0, opB != 0, vec, edge, stream);
+    const bool vec_c = vec && !(c.dma && (lda >= kDmaMaxLd || ldb >= kDmaMaxLd));
+    const hipError_t e = c.launch(p, batch, opA != 0, opB != 0, vec_c, edge, stream);
     return e == hipSuccess ? 0 : (int)e;
 }
 

@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sgemm_impl {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -76,6 +78,21 @@ __device__ __forceinline__ float finish(float acc, float alpha, float beta, cons
         out += beta * *cptr;
     if (bias)
         out += bias[j];
+    if (act == ACT_GELU_TANH)
+        out = gelu_tanh(out);
+    return out;
+}
+
+// The same value with C's entry already loaded (c, used only when beta != 0) and the
+// bias entry bj (used only when has_bias), in the same order of operations.
+__device__ __forceinline__ float finish_value(float acc, float alpha, float beta, float c, bool has_bias,
+                                              float bj, int act)
+{
+    float out = alpha * acc;
+    if (beta != 0.f)
+        out += beta * c;
+    if (has_bias)
+        out += bj;
     if (act == ACT_GELU_TANH)
         out = gelu_tanh(out);
     return out;
@@ -125,8 +142,9 @@ struct TileIO {
     static_assert(TC % 16 == 0, "rows are multiples of 16 floats");
     static_assert(TR % G == 0, "whole groups of rows");
 
-    // Offset (floats) of row r of the tile in LDS.
+    // Offset (floats) of row r, and of element (r, col), of the tile in LDS.
     __device__ __forceinline__ static int row(int r) { return r * TC + (r / G) * 4; }
+    __device__ __forceinline__ static int elem(int r, int col) { return row(r) + col; }
 
     // src points at the tile origin; rows/cols are how many rows and columns from the
     // origin lie inside the matrix. VEC: 128-bit loads (row starts 16-byte aligned and
@@ -169,6 +187,94 @@ struct TileIO {
         }
     }
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// The same operand tile copied HBM -> LDS directly, with no staging registers, by
+// 16-byte buffer loads into LDS: one such instruction of one wave fills 64 consecutive
+// 16-byte LDS slots, lane l the l-th. The tile is TR rows of CPR slots with no padding;
+// inside row r, chunk c sits in slot c ^ swz(r). A lane fetches whichever global chunk
+// belongs in its slot, so the copy stays contiguous while the reads stay free of bank
+// conflicts on the 64-bank LDS:
+//  - KCONTIG (rows run along k: plain A, transposed B): 16 consecutive rows read at one
+//    chunk land in 16 distinct 4-bank groups;
+//  - otherwise (rows run along m or n): consecutive lanes read consecutive chunks of one
+//    row, and rows 4 apart (the two half-waves) use opposite halves of each 16-slot window.
+// Chunks outside the matrix are fetched at an offset past the buffer's range, which
+// the hardware answers with zeros, so partial tiles arrive zero-padded as in TileIO.
+// Needs 16-byte aligned rows and pointers (the VEC kernels) and row strides below 2^24
+// floats (the byte offsets inside one instruction's rows stay below 2^30).
+template <int TR, int TC, int NT, bool KCONTIG>
+struct TileDMA {
+    static constexpr int CPR = TC / 4;
+    static constexpr int CHUNKS = TR * CPR;
+    static constexpr int CH = CHUNKS / NT;              // copy instructions per thread
+    static constexpr int SIZE = TR * TC;
+    static_assert(NT % 64 == 0 && CHUNKS % NT == 0, "whole copy instructions per wave");
+    static_assert(CPR <= 64 ? 64 % CPR == 0 : CPR % 64 == 0, "a wave's copy covers whole rows or part of one");
+    static_assert(KCONTIG ? (CPR >= 4) : (CPR >= 16), "slot swizzle needs these row lengths");
+
+    __device__ __forceinline__ static int swz(int r)
+    {
+        if (KCONTIG)
+            return CPR >= 16 ? (r & 15) : ((r / (16 / CPR)) & (CPR - 1));
+        return ((r >> 2) & 1) << 3;
+    }
+    __device__ __forceinline__ static int elem(int r, int col)
+    {
+        return 4 * (r * CPR + ((col >> 2) ^ swz(r))) + (col & 3);
+    }
+
+    // Queue this thread's copies of the tile at src (row stride ld) into lds; rows/cols
+    // are how many rows and columns from the origin lie inside the matrix (EDGE only).
+    template <bool EDGE>
+    __device__ __forceinline__ static void load(const float *src, int64_t ld, int rows, int cols, float *lds,
+                                                int tid)
+    {
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: resource and LDS base in SGPRs
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int s0 = wave * 64 + c * NT;          // first slot of this wave's copy
+            const int r0 = s0 / CPR;                    // its first row (same for the whole wave)
+            const int q = s0 % CPR + lane;
+            const int dr = q / CPR, r = r0 + dr, chunk = (q % CPR) ^ swz(r);
+            unsigned off = static_cast<unsigned>((dr * ld + 4 * chunk) * 4);
+            if (EDGE && !(r < rows && 4 * chunk < cols))
+                off = 0x80000000u;                      // past num_records: reads as zeros
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float *>(src + (int64_t)r0 * ld), 0, 0x7fffffff, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + 4 * s0), 16, off, 0, 0, 0);
+        }
+    }
+};
+
+// Wait until at most n vector-memory operations of this wave are outstanding (the
+// LDS copies above count as such); the other counters are left alone.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier of the direct-copy pipeline: this wave's LDS reads have finished
+// and at most n of its LDS copies are still in flight, then all waves meet. The
+// __syncthreads() fence would also wait for every copy in flight (it counts them as
+// LDS stores), which would leave no tile in flight across the barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it instead, and the
+// scheduling barriers keep the matrix instructions on their side of it.
+template <int n>
+__device__ __forceinline__ void copy_barrier()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));  // vmcnt(n) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // W consecutive floats from LDS (W = 1, 2 or 4) as one 32-, 64- or 128-bit read.
 template <int W>
@@ -216,24 +322,29 @@ __device__ __forceinline__ void lds_read(const float *p, float (&out)[W])
 //    c*T + b (T blocks), so lane l reads T consecutive values for one k in one read,
 //    and for B writes T consecutive columns of C.
 // ---------------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool TA, bool TB, bool VEC, bool EDGE>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
+          bool EDGE>
 __global__ void __launch_bounds__(WGM * WGN * WGK * 64)
 sgemm_mfma(GemmArgs p, int group_m)
 {
     static_assert(PF == 1 || PF == 2, "K-tiles in flight ahead of the one being multiplied");
+    constexpr bool USE_DMA = DMA && VEC;                // aligned operands: direct HBM -> LDS copies
     constexpr int NT = WGM * WGN * WGK * 64;
     constexpr int KSLICE = BK / WGK;                    // k per stage handled by one wave group
     constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
     constexpr int TM = WTM / 32, TN = WTN / 32;         // 32x32 blocks per wave
-    using AIO = TileIO<TA ? BK : BM, TA ? BM : BK, NT>;
-    using BIO = TileIO<TB ? BN : BK, TB ? BK : BN, NT>;
+    using AIO = typename std::conditional<USE_DMA, TileDMA<TA ? BK : BM, TA ? BM : BK, NT, !TA>,
+                                          TileIO<TA ? BK : BM, TA ? BM : BK, NT>>::type;
+    using BIO = typename std::conditional<USE_DMA, TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB>,
+                                          TileIO<TB ? BN : BK, TB ? BK : BN, NT>>::type;
     constexpr int STAGE = AIO::SIZE + BIO::SIZE;
+    constexpr int NSTAGE = USE_DMA ? PF + 1 : 2;         // LDS stages in the ring
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(!TA || TM == 1 || TM == 2 || TM == 4, "interleaved m blocks read 1, 2 or 4 floats");
     static_assert(TB || TN == 1 || TN == 2 || TN == 4, "interleaved n blocks read 1, 2 or 4 floats");
     static_assert(BK % (8 * WGK) == 0, "each wave group consumes k in groups of 8");
     constexpr int RED = (WGK - 1) * BM * BN;            // partial sums of groups 1..WGK-1
-    constexpr int SMEM = 2 * STAGE > RED ? 2 * STAGE : RED;
+    constexpr int SMEM = NSTAGE * STAGE > RED ? NSTAGE * STAGE : RED;
     static_assert(SMEM * 4 <= 160 * 1024, "LDS exceeds 160 KiB");
 
     __shared__ __attribute__((aligned(16))) float smem[SMEM];
@@ -258,25 +369,44 @@ sgemm_mfma(GemmArgs p, int group_m)
     // PF sets of staging registers: with PF = 2 a K-tile's global loads are issued two
     // stages before it is multiplied. `slot` is always a compile-time constant after
     // inlining, so the sets stay in registers.
-    floatx4 ra[PF][AIO::CH], rb[PF][BIO::CH];
+    floatx4 ra[USE_DMA ? 1 : PF][AIO::CH], rb[USE_DMA ? 1 : PF][BIO::CH];
 
     // Global -> registers set `slot` for the K-tile starting at k0 (zero outside the matrix).
     auto load_tile = [&](int k0, int slot) __attribute__((always_inline)) {
-        if constexpr (TA)
-            AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, tid);
-        else
-            AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, tid);
-        if constexpr (TB)
-            BIO::template load<VEC, EDGE>(rb[slot], B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, tid);
-        else
-            BIO::template load<VEC, EDGE>(rb[slot], B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, tid);
+        if constexpr (!USE_DMA) {
+            if constexpr (TA)
+                AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, tid);
+            else
+                AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, tid);
+            if constexpr (TB)
+                BIO::template load<VEC, EDGE>(rb[slot], B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, tid);
+            else
+                BIO::template load<VEC, EDGE>(rb[slot], B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, tid);
+        }
     };
 
     // Registers set `slot` -> LDS stage `st`.
     auto store_tile = [&](int st, int slot) __attribute__((always_inline)) {
-        float *As = smem + st * STAGE;
-        AIO::store(ra[slot], As, tid);
-        BIO::store(rb[slot], As + AIO::SIZE, tid);
+        if constexpr (!USE_DMA) {
+            float *As = smem + st * STAGE;
+            AIO::store(ra[slot], As, tid);
+            BIO::store(rb[slot], As + AIO::SIZE, tid);
+        }
+    };
+
+    // Direct copies of the K-tile starting at k0 into LDS stage `st` (DMA path).
+    auto copy_tile = [&](int k0, int st) __attribute__((always_inline)) {
+        if constexpr (USE_DMA) {
+            float *As = smem + st * STAGE;
+            if constexpr (TA)
+                AIO::template load<EDGE>(A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, As, tid);
+            else
+                AIO::template load<EDGE>(A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, As, tid);
+            if constexpr (TB)
+                BIO::template load<EDGE>(B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, As + AIO::SIZE, tid);
+            else
+                BIO::template load<EDGE>(B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, As + AIO::SIZE, tid);
+        }
     };
 
     floatx16 acc[TM][TN];
@@ -305,19 +435,19 @@ sgemm_mfma(GemmArgs p, int group_m)
             if constexpr (!TA) {
 #pragma unroll
                 for (int a = 0; a < TM; ++a)
-                    af[a] = *reinterpret_cast<const floatx4 *>(&As[AIO::row(a_idx + a * 32) + kg + 4 * half]);
+                    af[a] = *reinterpret_cast<const floatx4 *>(&As[AIO::elem(a_idx + a * 32, kg + 4 * half)]);
             }
             if constexpr (TB) {
 #pragma unroll
                 for (int b = 0; b < TN; ++b)
-                    bf[b] = *reinterpret_cast<const floatx4 *>(&Bs[BIO::row(b_idx + b * 32) + kg + 4 * half]);
+                    bf[b] = *reinterpret_cast<const floatx4 *>(&Bs[BIO::elem(b_idx + b * 32, kg + 4 * half)]);
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int k = kg + 4 * half + s;
                 float av[TM], bv[TN];
                 if constexpr (TA) {
-                    lds_read<TM>(&As[AIO::row(k) + a_idx], av);
+                    lds_read<TM>(&As[AIO::elem(k, a_idx)], av);
                 } else {
 #pragma unroll
                     for (int a = 0; a < TM; ++a)
@@ -328,7 +458,7 @@ sgemm_mfma(GemmArgs p, int group_m)
                     for (int b = 0; b < TN; ++b)
                         bv[b] = bf[b][s];
                 } else {
-                    lds_read<TN>(&Bs[BIO::row(k) + b_idx], bv);
+                    lds_read<TN>(&Bs[BIO::elem(k, b_idx)], bv);
                 }
 #pragma unroll
                 for (int a = 0; a < TM; ++a)
@@ -339,11 +469,89 @@ sgemm_mfma(GemmArgs p, int group_m)
         }
     };
 
-    // Pipeline over nk K-tiles, two LDS stages, one barrier per K-tile. The last K-tile
-    // is peeled off so the loop bodies have no conditionals around the staging
-    // registers (which keeps them in VGPRs).
+    // Fragment form used by the direct-copy pipeline: the A and B values of one group
+    // of 8 k (4 per lane) for every block, read from LDS in one batch, so the reads of
+    // the next group can be in flight while this one is multiplied.
+    constexpr int NG = KSLICE / 8;                      // groups of 8 k per stage and wave group
+    float fa[USE_DMA ? 2 : 1][4][TM], fb[USE_DMA ? 2 : 1][4][TN];
+    auto read_frag = [&](int st, int g, int buf) __attribute__((always_inline)) {
+        const float *As = smem + st * STAGE;
+        const float *Bs = As + AIO::SIZE;
+        const int kg = wk * KSLICE + 8 * g + 4 * half;
+        if constexpr (TA) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                lds_read<TM>(&As[AIO::elem(kg + s, a_idx)], fa[buf][s]);
+        } else {
+#pragma unroll
+            for (int a = 0; a < TM; ++a) {
+                const floatx4 v = *reinterpret_cast<const floatx4 *>(&As[AIO::elem(a_idx + a * 32, kg)]);
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    fa[buf][s][a] = v[s];
+            }
+        }
+        if constexpr (TB) {
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                const floatx4 v = *reinterpret_cast<const floatx4 *>(&Bs[BIO::elem(b_idx + b * 32, kg)]);
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    fb[buf][s][b] = v[s];
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                lds_read<TN>(&Bs[BIO::elem(kg + s, b_idx)], fb[buf][s]);
+        }
+    };
+    auto mma_frag = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[buf][s][a], fb[buf][s][b], acc[a][b], 0, 0, 0);
+    };
+
+    // Pipeline over nk K-tiles, one barrier per K-tile.
     const int nk = ceil_div(K, BK);
-    if constexpr (PF == 1) {
+    if constexpr (USE_DMA) {
+        // PF + 1 LDS stages. Step t queues the copies of tile t+PF into stage (t+PF) %
+        // NSTAGE (read last during step t-1, so free after that step's barrier),
+        // multiplies stage t % NSTAGE, waits until its own copies of tile t+1 have landed
+        // (the PF-1 newer tiles may stay in flight) and meets the others at the barrier.
+        // Past the end the last tile is copied again, so the count of copies in flight
+        // is the same on every step.
+        // Inside a step, group g+1's fragments are read while group g is multiplied; the
+        // last group is multiplied after the barrier, while group 0 of the next stage
+        // is read (past the last step that read is of a stage nobody uses; harmless).
+        static_assert(NG % 2 == 0, "fragment buffers alternate within a stage");
+        constexpr int COPIES = AIO::CH + BIO::CH;       // copy instructions per thread per tile
+#pragma unroll
+        for (int q = 0; q < PF; ++q)
+            copy_tile((q < nk ? q : nk - 1) * BK, q);
+        wait_vmcnt<0>();
+        __syncthreads();
+        read_frag(0, 0, 0);
+        for (int t = 0; t < nk; ++t) {
+            const int ahead = t + PF < nk ? t + PF : nk - 1;
+            copy_tile(ahead * BK, (t + PF) % NSTAGE);
+            const int st = t % NSTAGE;
+#pragma unroll
+            for (int g = 0; g + 1 < NG; ++g) {
+                read_frag(st, g + 1, (g + 1) & 1);
+                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+                mma_frag(g & 1);
+            }
+            copy_barrier<(PF - 1) * COPIES>();
+            read_frag((t + 1) % NSTAGE, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_frag(1);
+        }
+        wait_vmcnt<0>();    // no copy may still write LDS once it is reused or released
+    } else if constexpr (PF == 1) {
         load_tile(0, 0);
         store_tile(0, 0);
         __syncthreads();
@@ -379,7 +587,8 @@ sgemm_mfma(GemmArgs p, int group_m)
             ++t;
         }
     }
-    compute((nk - 1) & 1);
+    if constexpr (!USE_DMA)
+        compute((nk - 1) & 1);
 
     if constexpr (WGK > 1) {
         // Groups 1..WGK-1 hand their partial sums to group 0 through LDS (the ring is
@@ -413,55 +622,80 @@ sgemm_mfma(GemmArgs p, int group_m)
         }
     }
 
-    // Epilogue: C = act(alpha*acc + beta*C + bias), C unread when beta == 0.
+    // Epilogue: C = act(alpha*acc + beta*C + bias), C unread when beta == 0. One 32-row
+    // block at a time: all of the block's reads of C are issued before the first is
+    // used, so the block waits out one memory round trip (two with EB = 8) rather than
+    // one per entry. Lane columns: TN consecutive ones (plain B), or one per 32-column block
+    // (transposed B). Rows: those of accumulator element e, see the mapping above.
     const float alpha = p.alpha, beta = p.beta;
     const float *bias = p.bias;
     const int act = p.act;
-    const bool plain = bias == nullptr && act == ACT_NONE;
+    const bool read_c = beta != 0.f, has_bias = bias != nullptr;
+    const bool full = !EDGE || (m0 + BM <= M && n0 + BN <= N);   // whole tile inside C
+    // 128- or 64-bit accesses of a lane's TN consecutive columns: aligned, and (N % 4 == 0,
+    // first column a multiple of TN) the group is either wholly inside C or wholly out.
+    constexpr bool VCOL = VEC && !TB && (TN == 2 || TN == 4);
+    int gc[TN];
 #pragma unroll
-    for (int a = 0; a < TM; ++a) {
+    for (int b = 0; b < TN; ++b)
+        gc[b] = n0 + b_idx + (TB ? 32 * b : b);
+    float bj[TN];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = 8 * (e / 4) + 4 * half + (e % 4);          // row inside the 32x32 block
-            const int gr = m0 + wm * WTM + (TA ? r * TM + a : a * 32 + r);
-            if (EDGE && gr >= M)
-                continue;
-            float *crow = C + (int64_t)gr * ldc;
-            if constexpr (!TB) {
-                // TN consecutive columns per lane
-                const int gc0 = n0 + b_idx;
-                float *cp = crow + gc0;
-                if (VEC && TN == 4 && plain && (!EDGE || gc0 < N)) {
-                    // VEC: N % 4 == 0 and gc0 % 4 == 0, so the whole chunk is in range.
-                    floatx4 *c4 = reinterpret_cast<floatx4 *>(cp);
-                    floatx4 out = {alpha * acc[a][0][e], alpha * acc[a][1 % TN][e], alpha * acc[a][2 % TN][e],
-                                   alpha * acc[a][3 % TN][e]};
-                    if (beta != 0.f)
-                        out += beta * *c4;
-                    *c4 = out;
-                } else if (VEC && TN == 2 && plain && (!EDGE || gc0 < N)) {
-                    floatx2 *c2 = reinterpret_cast<floatx2 *>(cp);
-                    floatx2 out = {alpha * acc[a][0][e], alpha * acc[a][1 % TN][e]};
-                    if (beta != 0.f)
-                        out += beta * *c2;
-                    *c2 = out;
+    for (int b = 0; b < TN; ++b)
+        bj[b] = (has_bias && (full || gc[b] < N)) ? bias[gc[b]] : 0.f;
+    auto row_of = [&](int a, int e) __attribute__((always_inline)) {
+        const int r = 8 * (e / 4) + 4 * half + (e % 4);          // row inside the 32x32 block
+        return m0 + wm * WTM + (TA ? r * TM + a : a * 32 + r);
+    };
+    // Entries per batch of reads: 16 (the whole block), or 8 where four waves share a
+    // SIMD and each has only 128 registers.
+    constexpr int EB = NT >= 1024 ? 8 : 16;
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int e0 = 0; e0 < 16; e0 += EB) {
+        float cv[16][TN];
+        if (read_c) {
+#pragma unroll
+            for (int e = e0; e < e0 + EB; ++e) {
+                const int gr = row_of(a, e);
+                const float *crow = C + (int64_t)gr * ldc;
+                if constexpr (VCOL) {
+                    using vec_t = typename std::conditional<TN == 4, floatx4, floatx2>::type;
+                    vec_t v{};
+                    if (full || (gr < M && gc[0] < N))
+                        v = *reinterpret_cast<const vec_t *>(crow + gc[0]);
+#pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        cv[e][b] = v[b];
                 } else {
 #pragma unroll
-                    for (int b = 0; b < TN; ++b) {
-                        if (EDGE && gc0 + b >= N)
-                            continue;
-                        cp[b] = finish(acc[a][b][e], alpha, beta, cp + b, bias, gc0 + b, act);
-                    }
+                    for (int b = 0; b < TN; ++b)
+                        cv[e][b] = (full || (gr < M && gc[b] < N)) ? crow[gc[b]] : 0.f;
                 }
-            } else {
-                // one column per block: lanes 0..31 write 32 consecutive columns
+            }
+        }
 #pragma unroll
-                for (int b = 0; b < TN; ++b) {
-                    const int gc = n0 + b_idx + b * 32;
-                    if (EDGE && gc >= N)
-                        continue;
-                    crow[gc] = finish(acc[a][b][e], alpha, beta, crow + gc, bias, gc, act);
-                }
+        for (int e = e0; e < e0 + EB; ++e) {
+            const int gr = row_of(a, e);
+            float *crow = C + (int64_t)gr * ldc;
+            float out[TN];
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+                out[b] = finish_value(acc[a][b][e], alpha, beta, read_c ? cv[e][b] : 0.f, has_bias, bj[b], act);
+            if constexpr (VCOL) {
+                using vec_t = typename std::conditional<TN == 4, floatx4, floatx2>::type;
+                vec_t v;
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    v[b] = out[b];
+                if (full || (gr < M && gc[0] < N))
+                    *reinterpret_cast<vec_t *>(crow + gc[0]) = v;
+            } else {
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    if (full || (gr < M && gc[b] < N))
+                        crow[gc[b]] = out[b];
             }
         }
     }

@@ -9,7 +9,7 @@
 
 namespace sgemm_impl {
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, int GROUP_M, bool TA, bool TB>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, bool TA, bool TB>
 hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, hipStream_t s);
 
 }  // namespace sgemm_impl
