@@ -42,6 +42,8 @@
 namespace sgemm_impl {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+// Four floats at an address that is only 4-byte aligned (same registers as floatx4).
+typedef float floatx4u __attribute__((ext_vector_type(4), aligned(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
@@ -167,11 +169,18 @@ struct TileIO {
                 else
                     r[c] = floatx4{0.f, 0.f, 0.f, 0.f};
             } else {
+                // Rows only 4-byte aligned: a chunk wholly inside is still one 16-byte
+                // load (global memory takes dword-aligned vector accesses); the chunk that
+                // straddles the end of a row, or lies outside, is read float by float.
                 const bool rok = rr < rows;
-                r[c].x = (rok && cc + 0 < cols) ? p[0] : 0.f;
-                r[c].y = (rok && cc + 1 < cols) ? p[1] : 0.f;
-                r[c].z = (rok && cc + 2 < cols) ? p[2] : 0.f;
-                r[c].w = (rok && cc + 3 < cols) ? p[3] : 0.f;
+                if (!EDGE || (rok && cc + 3 < cols)) {
+                    r[c] = *reinterpret_cast<const floatx4u *>(p);
+                } else {
+                    r[c].x = (rok && cc + 0 < cols) ? p[0] : 0.f;
+                    r[c].y = (rok && cc + 1 < cols) ? p[1] : 0.f;
+                    r[c].z = (rok && cc + 2 < cols) ? p[2] : 0.f;
+                    r[c].w = (rok && cc + 3 < cols) ? p[3] : 0.f;
+                }
             }
         }
     }
