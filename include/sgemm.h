@@ -34,12 +34,14 @@
  *    are bitwise reproducible from run to run.
  *
  * Return values: 0 on success; -i when argument i (1-based, in declaration order;
- * the first invalid one) is invalid; SGEMM_ERROR_TOO_LARGE or SGEMM_ERROR_BAD_CONFIG for the cases named
- * below; a positive hipError_t when the kernel launch fails. Errors raised while
+ * the first invalid one) is invalid; SGEMM_ERROR_TOO_LARGE, SGEMM_ERROR_BAD_CONFIG or
+ * SGEMM_ERROR_WORKSPACE for the cases named below; a positive hipError_t when the kernel launch fails. Errors raised while
  * the kernel runs surface at the caller's next synchronisation. Nothing throws.
  */
 #ifndef TILED_FP32_GEMM_SGEMM_H
 #define TILED_FP32_GEMM_SGEMM_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -50,6 +52,9 @@ extern "C" {
 #define SGEMM_ERROR_TOO_LARGE (-100)
 /* sgemm_ex / sgemm_general: the configuration id is not in [-1, sgemm_config_count()). */
 #define SGEMM_ERROR_BAD_CONFIG (-101)
+/* A stream-K configuration was requested without a workspace of sgemm_workspace_size()
+ * bytes (or for a strided-batched call, which stream-K does not serve). */
+#define SGEMM_ERROR_WORKSPACE (-102)
 
 /* Operand forms: read the matrix as stored, or its transpose. */
 #define SGEMM_OP_N 0
@@ -165,6 +170,59 @@ int sgemm_strided_batched(int M, int N, int K, float alpha,
                           float beta, float *C, int ldc, long long strideC,
                           int batch, void *stream);
 
+/*
+ * sgemm_general with a workspace, which lets the library use stream-K configurations
+ * (names starting "sk_"). Those split the product's tiles x K-tiles work into one equal
+ * contiguous share per compute unit, so the chip stays full when the tile count does
+ * not divide evenly over the compute units (the GPT-2 layer shapes, 1024^3, odd sizes).
+ * A tile shared by several workgroups is finished by the one that arrives last, which
+ * adds the partial sums in a fixed order: results stay bitwise reproducible from run
+ * to run, and within the same error bound as every other configuration. Stream-K runs
+ * on 16-byte aligned operands (as defined for sgemm); with unaligned ones a stream-K
+ * configuration runs the data-parallel kernel of its tile instead.
+ *
+ *  workspace        device memory of workspace_bytes, 16-byte aligned, owned by the
+ *                   caller. Zero-fill it once before its first use: its first 64 KiB
+ *                   hold per-tile counters, which every call leaves at zero again; the
+ *                   rest holds partial tiles while a call runs. Calls that may run at
+ *                   the same time (on different streams) need separate workspaces.
+ *                   NULL with workspace_bytes == 0 is allowed.
+ *  workspace_bytes  its size. With config == -1 the library considers the stream-K
+ *                   configurations whose sgemm_workspace_size() fits, and otherwise
+ *                   behaves as sgemm_general; a forced stream-K configuration whose
+ *                   workspace does not fit returns SGEMM_ERROR_WORKSPACE.
+ *
+ * Arguments by position: 1 opA, 2 opB, 3 M, 4 N, 5 K, 6 alpha, 7 A, 8 lda, 9 B, 10 ldb,
+ * 11 beta, 12 C, 13 ldc, 14 bias, 15 act, 16 workspace, 17 workspace_bytes, 18 stream
+ * (config is not counted). -16 when workspace is misaligned, or NULL with a nonzero size.
+ */
+int sgemm_general_ws(int config, int opA, int opB, int M, int N, int K, float alpha,
+                     const float *A, int lda,
+                     const float *B, int ldb,
+                     float beta, float *C, int ldc,
+                     const float *bias, int act,
+                     void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/*
+ * Workspace bytes that stream-K configuration `config` needs on the current device
+ * (64 KiB of counters plus two partial tiles per compute unit), or with config == -1
+ * the most any of them needs. 0 for other configurations, or when the device cannot be
+ * queried.
+ */
+size_t sgemm_workspace_size(int config);
+
+/*
+ * The configuration sgemm_general_ws would pick for a plain product with a workspace
+ * of workspace_bytes (as sgemm_select_config otherwise; queries the current device's
+ * compute-unit count when workspace_bytes > 0).
+ */
+int sgemm_select_config_ws(int M, int N, int K, float alpha,
+                           const float *A, int lda,
+                           const float *B, int ldb,
+                           const float *C, int ldc,
+                           size_t workspace_bytes);
+
 /* Number of kernel configurations compiled into the library. */
 int sgemm_config_count(void);
 
@@ -184,7 +242,9 @@ int sgemm_select_config(int M, int N, int K, float alpha,
 
 /*
  * Launch shape of configuration `config` for an M x N x K product (host logic only).
- * Writes grid[3] and block[3] (dim3 order x, y, z). Returns 0, SGEMM_ERROR_BAD_CONFIG,
+ * Writes grid[3] and block[3] (dim3 order x, y, z). Stream-K configurations launch one
+ * workgroup per compute unit, and at most one per K-tile step (tiles x ceil(K / BK));
+ * the shape reported for them assumes MI355X's 256 compute units. Returns 0, SGEMM_ERROR_BAD_CONFIG,
  * SGEMM_ERROR_TOO_LARGE, or -1/-2/-3 for a negative M/N/K.
  */
 int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3]);

@@ -42,7 +42,9 @@ def test_version_and_configs():
     names = sg.configs()
     assert len(names) == sg.sgemm_config_count() >= 2
     assert names[0] == "tile16"
-    assert all(n.startswith("mfma_") for n in names[1:])
+    # data-parallel configurations first, then the stream-K ones
+    kinds = [n.split("_")[0] for n in names[1:]]
+    assert set(kinds) == {"mfma", "sk"} and kinds == sorted(kinds)
     assert sg.sgemm_config_name(-1) is None and sg.sgemm_config_name(len(names)) is None
 
 
@@ -210,3 +212,83 @@ def test_tensor_form_rejects_host_views():
         sg.gemm(x.t(), torch.zeros(6, 3))
     with pytest.raises(ValueError, match="Dimension error"):
         sg.gemm(torch.zeros(2, 3, 4), torch.zeros(4, 3))
+
+
+# --------------------------------------------------------------------------- workspace entry point
+
+WS_ARGS = (0, 0, 4, 4, 4, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4, None, 0)   # opA .. act
+
+
+def sk_ids():
+    return [i for i, n in enumerate(sg.configs()) if n.startswith("sk_")]
+
+
+def test_workspace_argument_checks():
+    # misaligned, or NULL with a size: argument 16
+    assert sg.sgemm_general_ws(-1, *WS_ARGS, BAD + 4, 1 << 20) == -16
+    assert sg.sgemm_general_ws(-1, *WS_ARGS, None, 64) == -16
+    # other arguments keep the positions of sgemm_general
+    bad_lda = (0, 0, 4, 4, 8, 1.0, BAD, 7, BAD, 4, 0.0, BAD, 4, None, 0)
+    assert sg.sgemm_general_ws(-1, *bad_lda, None, 0) == -8
+    assert sg.sgemm_general_ws(-2, *WS_ARGS, None, 0) == sg.SGEMM_ERROR_BAD_CONFIG
+    # quick return: nothing is launched and the workspace is not needed
+    assert sg.sgemm_general_ws(-1, 0, 0, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, None, 0, None, 0) == 0
+
+
+def test_forced_stream_k_needs_a_workspace():
+    for cid in sk_ids():
+        assert sg.sgemm_general_ws(cid, *WS_ARGS, None, 0) == sg.SGEMM_ERROR_WORKSPACE
+        assert sg.sgemm_general(cid, *WS_ARGS) == sg.SGEMM_ERROR_WORKSPACE
+    assert "workspace" in sg.sgemm_status_string(sg.SGEMM_ERROR_WORKSPACE)
+
+
+def test_workspace_size_without_a_device_is_zero():
+    import ctypes
+    try:
+        n = ctypes.c_int(0)
+        have_gpu = ctypes.CDLL("libamdhip64.so").hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0
+    except OSError:
+        have_gpu = False
+    if not have_gpu:
+        assert sg.sgemm_workspace_size(-1) == 0
+    assert sg.sgemm_workspace_size(1) == 0      # data-parallel configurations need none
+
+
+def test_launch_shape_stream_k():
+    for cid in sk_ids():
+        st, grid, block = sg.sgemm_launch_shape(cid, 1024, 2304, 768)
+        assert st == 0 and grid == (256, 1, 1) and block[0] in (256, 512, 1024)
+        # fewer K-tile steps than compute units: one workgroup per step
+        st, grid, _ = sg.sgemm_launch_shape(cid, 100, 130, 64)
+        bm, bn, bk = (int(x) for x in sg.sgemm_config_name(cid).split("_")[1].split("x"))
+        assert st == 0 and grid[0] == -(-100 // bm) * -(-130 // bn) * -(-64 // bk)
+
+
+def test_select_without_workspace_never_picks_stream_k():
+    names = sg.configs()
+    for M, N, K in [(1024, 2304, 768), (1024, 768, 3072), (1025, 1025, 1025), (4096, 4096, 4096)]:
+        assert not names[sg.sgemm_select_config(M, N, K, 1.0, BAD, K, BAD, N, BAD, N)].startswith("sk_")
+        assert not names[sg.sgemm_select_config_ws(M, N, K, 1.0, BAD, K, BAD, N, BAD, N, 0)].startswith("sk_")
+
+
+def test_workspace_cache_does_not_deadlock(monkeypatch):
+    """workspace_for() queries the library (which takes the loader's lock) while
+    filling its cache: it must not hold a lock the loader also takes. The CUDA pieces
+    are stubbed so the host path runs here; a deadlock shows up as the thread never
+    finishing."""
+    import contextlib
+    import threading
+    torch = pytest.importorskip("torch")
+    real_zeros = torch.zeros
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda device=None: None)
+    monkeypatch.setattr(torch.cuda, "device", lambda dev: contextlib.nullcontext())
+    monkeypatch.setattr(torch, "zeros", lambda *a, **k: real_zeros(*a, dtype=k.get("dtype")))
+    monkeypatch.setattr(sg, "_workspaces", {})
+    out = []
+    th = threading.Thread(target=lambda: out.append(sg.workspace_for()), daemon=True)
+    th.start()
+    th.join(timeout=20)
+    assert not th.is_alive(), "workspace_for() deadlocked"
+    assert out and out[0].numel() >= 16 and int(out[0].sum()) == 0
+    assert sg.workspace_for() is out[0]      # cached

@@ -39,6 +39,13 @@ def kernels(tmp_path_factory):
     return out
 
 
+def parse_config(name):
+    m = re.fullmatch(r"(?:mfma|sk)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
+    assert m, name
+    bm, bn, bk, wm, wn = (int(x) for x in m.groups()[:5])
+    return bm, bn, bk, wm, wn, int(m.group(6) or 1), int(m.group(7) or 1), m.group(8) is not None
+
+
 def expected_mfma_kernels(config_names):
     """Template arguments <BM,BN,BK,WGM,WGN,WGK,PF,DMA,TA,TB,VEC,EDGE> of every matrix
     kernel the launcher can start: per configuration and operand form, the aligned
@@ -46,29 +53,43 @@ def expected_mfma_kernels(config_names):
     K-tile in flight (K-tile 16 * WGK for direct-copy configurations)."""
     out = set()
     for name in config_names:
-        m = re.fullmatch(r"mfma_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
-        assert m, name
-        bm, bn, bk, wm, wn = (int(x) for x in m.groups()[:5])
-        wk, pf, dma = int(m.group(6) or 1), int(m.group(7) or 1), m.group(8) is not None
+        bm, bn, bk, wm, wn, wk, pf, dma = parse_config(name)
+        for ta in (0, 1):
+            for tb in (0, 1):
+                if name.startswith("mfma_"):
+                    for edge in (0, 1):
+                        out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge))
+                out.add((bm, bn, 16 * wk if dma else bk, wm, wn, wk, 1, 0, ta, tb, 0, 1))
+    return out
+
+
+def expected_sk_kernels(config_names):
+    """Stream-K kernels: the aligned whole-tile and edge variants of each stream-K
+    configuration (unaligned operands run the data-parallel kernel of the tile)."""
+    out = set()
+    for name in config_names:
+        bm, bn, bk, wm, wn, wk, pf, dma = parse_config(name)
         for ta in (0, 1):
             for tb in (0, 1):
                 for edge in (0, 1):
                     out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge))
-                out.add((bm, bn, 16 * wk if dma else bk, wm, wn, wk, 1, 0, ta, tb, 0, 1))
     return out
 
 
 def test_all_kernels_present(kernels):
     names = " ".join(kernels)
     assert "sgemm_tile16" in names and "sgemm_scale" in names
-    found = set()
-    for n in kernels:
-        m = re.search(r"sgemm_mfma<([^>]*)>", n)
-        if m:
-            found.add(tuple(int(x) if x.strip().lstrip("-").isdigit() else int(x.strip() == "true")
-                            for x in m.group(1).split(",")))
     import tiled_fp32_gemm_02_amd as sg
-    assert found == expected_mfma_kernels(sg.configs()[1:])
+    names = sg.configs()[1:]
+    for kind, expected in (("sgemm_mfma", expected_mfma_kernels(names)),
+                           ("sgemm_mfma_sk", expected_sk_kernels([c for c in names if c.startswith("sk_")]))):
+        found = set()
+        for n in kernels:
+            m = re.search(kind + r"<([^>]*)>", n)
+            if m:
+                found.add(tuple(int(x) if x.strip().lstrip("-").isdigit() else int(x.strip() == "true")
+                                for x in m.group(1).split(",")))
+        assert found == expected, kind
 
 
 def test_no_scratch_no_spills(kernels):
@@ -91,7 +112,7 @@ def test_registers_fit_the_launch(kernels):
 
 def test_matrix_kernels_use_fp32_mfma(kernels):
     for name, (k, body) in kernels.items():
-        if "sgemm_mfma<" in name:
+        if "sgemm_mfma<" in name or "sgemm_mfma_sk<" in name:
             assert "v_mfma_f32_32x32x2_f32" in body, name
 
 

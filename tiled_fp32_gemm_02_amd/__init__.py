@@ -13,13 +13,17 @@ Raw entry points take device addresses as Python ints (or CUDA tensors, whose
     sgemm_op(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
     sgemm_bias_act(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream)
     sgemm_general(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream)
+    sgemm_general_ws(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
+                     workspace, workspace_bytes, stream)
     sgemm_strided_batched(M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch, stream)
 
 ``gemm(A, B, C=None, alpha=1, beta=0, bias=None, act=None)`` is the tensor-level
 form: it checks shapes, dtypes and devices, reads a transposed view (unit row
 stride) as a transposed operand in place, fills in the leading dimensions from the
 tensors' strides, raises ``ValueError``/``RuntimeError`` on bad input or a nonzero
-status, and returns C.
+status, and returns C. By default it passes a workspace (one zero-filled buffer per
+device and stream, made once with PyTorch) so that the library may pick its stream-K
+configurations; ``workspace=None`` keeps to the data-parallel ones.
 """
 
 from __future__ import annotations
@@ -33,11 +37,13 @@ __all__ = [
     "sgemm_config_name", "sgemm_select_config", "sgemm_launch_shape", "sgemm_status_string",
     "sgemm_version", "sgemm_op", "sgemm_bias_act", "sgemm_general", "configs", "gemm", "gemm_batched",
     "check", "SgemmError", "SGEMM_ERROR_TOO_LARGE", "SGEMM_ERROR_BAD_CONFIG", "SGEMM_OP_N", "SGEMM_OP_T",
-    "SGEMM_ACT_NONE", "SGEMM_ACT_GELU_TANH",
+    "SGEMM_ACT_NONE", "SGEMM_ACT_GELU_TANH", "SGEMM_ERROR_WORKSPACE", "sgemm_general_ws", "sgemm_workspace_size",
+    "sgemm_select_config_ws", "workspace_for",
 ]
 
 SGEMM_ERROR_TOO_LARGE = -100
 SGEMM_ERROR_BAD_CONFIG = -101
+SGEMM_ERROR_WORKSPACE = -102
 SGEMM_OP_N = 0
 SGEMM_OP_T = 1
 SGEMM_ACT_NONE = 0
@@ -63,6 +69,13 @@ _SIGS = {
     "sgemm_general": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int,
                                      ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int, _fp]),
+    "sgemm_general_ws": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int,
+                                        ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int, _fp,
+                                        ctypes.c_size_t, _fp]),
+    "sgemm_workspace_size": (ctypes.c_size_t, [ctypes.c_int]),
+    "sgemm_select_config_ws": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp,
+                                              ctypes.c_int, _fp, ctypes.c_int, _fp, ctypes.c_int, ctypes.c_size_t]),
     "sgemm_strided_batched": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, ctypes.c_longlong,
         _fp, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, _fp, ctypes.c_int, ctypes.c_longlong,
@@ -152,6 +165,22 @@ def sgemm_general(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc
                                 ldc, _addr(bias), act, _stream(stream))
 
 
+def sgemm_general_ws(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, workspace,
+                     workspace_bytes, stream=None) -> int:
+    return load().sgemm_general_ws(config, opA, opB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                                   _addr(C), ldc, _addr(bias), act, _addr(workspace), workspace_bytes,
+                                   _stream(stream))
+
+
+def sgemm_workspace_size(config: int = -1) -> int:
+    return load().sgemm_workspace_size(config)
+
+
+def sgemm_select_config_ws(M, N, K, alpha, A, lda, B, ldb, C, ldc, workspace_bytes) -> int:
+    return load().sgemm_select_config_ws(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
+                                         workspace_bytes)
+
+
 def sgemm_strided_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
                           batch, stream=None) -> int:
     return load().sgemm_strided_batched(M, N, K, alpha, _addr(A), lda, strideA, _addr(B), ldb, strideB,
@@ -233,17 +262,41 @@ def _operand(t, name):
 
 
 _ACTS = {None: SGEMM_ACT_NONE, "none": SGEMM_ACT_NONE, "gelu_tanh": SGEMM_ACT_GELU_TANH}
+_workspaces = {}
+_ws_lock = threading.Lock()      # guards _workspaces only; never held while calling the library
+
+
+def workspace_for(device=None, stream=None):
+    """The stream-K workspace for (device, stream): a zero-filled uint8 GPU tensor of
+    sgemm_workspace_size() bytes, made once and reused. Calls on one stream run in
+    order, so they can share it; each stream gets its own."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    key = (dev.index, _stream(stream))
+    with _ws_lock:
+        ws = _workspaces.get(key)
+    if ws is not None:
+        return ws
+    with torch.cuda.device(dev):
+        nbytes = sgemm_workspace_size(-1)   # loads the library: not under _ws_lock
+    fresh = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    with _ws_lock:
+        return _workspaces.setdefault(key, fresh)
 
 
 def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None, config: int = -1, bias=None,
-         act=None):
+         act=None, workspace="auto"):
     """C <- act(alpha*A@B + beta*C + bias) on GPU float32 tensors.
 
     A is M x K, B is K x N and C is M x N. A and B may be row-major views or
     transposed views (``x.t()``) of row-major matrices, read in place. C must be
     row-major and may have a larger row stride. bias is a length-N float32 GPU
     vector or None; act is None, "none" or "gelu_tanh". When C is None a new
-    M x N tensor is allocated (then beta must be 0). Returns C.
+    M x N tensor is allocated (then beta must be 0). workspace is "auto" (the cached
+    buffer of ``workspace_for()`` for this device and stream), None (no stream-K), or a
+    zero-initialised uint8 GPU tensor of the caller's. Returns C.
     """
     import torch
 
@@ -269,8 +322,10 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None, confi
         raise ValueError(f"Size error: C is {tuple(C.shape)}, expected {(M, N)}")
     if stream is None:
         stream = torch.cuda.current_stream(A.device)
-    check(sgemm_general(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, _ACTS[act],
-                        stream), "sgemm_general")
+    ws = workspace_for(A.device, stream) if isinstance(workspace, str) and workspace == "auto" else workspace
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(sgemm_general_ws(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, _ACTS[act],
+                           ws, nbytes, stream), "sgemm_general_ws")
     return C
 
 

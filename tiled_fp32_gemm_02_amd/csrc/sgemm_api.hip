@@ -4,9 +4,11 @@
 // error code), take the quick returns (empty result; alpha == 0 or K == 0 leaves
 // act(beta*C + bias)), choose a kernel configuration from the shape and alignment,
 // and queue one kernel on the caller's stream. No allocation, copy or
-// synchronisation.
+// synchronisation. Stream-K launches use a workspace that the caller passes in.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cstddef>
 #include <cstdint>
 
 #include "sgemm.h"
@@ -18,9 +20,13 @@ using sgemm_impl::GemmArgs;
 
 namespace {
 
-enum Kind { KIND_TILE16 = 0, KIND_MFMA = 1 };
+using sgemm_impl::StreamK;
+
+enum Kind { KIND_TILE16 = 0, KIND_MFMA = 1, KIND_SK = 2 };
 
 typedef hipError_t (*LaunchFn)(const GemmArgs &, int batch, bool ta, bool tb, bool vec, bool edge, hipStream_t);
+typedef hipError_t (*LaunchSkFn)(const GemmArgs &, const StreamK &, int grid, bool ta, bool tb, bool vec,
+                                 bool edge, hipStream_t);
 
 struct Config {
     const char *name;
@@ -28,8 +34,42 @@ struct Config {
     int bm, bn, bk;      // workgroup tile (tile16: 16 x 16 x 16)
     int threads;         // threads per workgroup
     bool dma;            // aligned operands are copied HBM -> LDS directly
-    LaunchFn launch;
+    int group_m;         // band height of the tile order
+    LaunchFn launch;     // data-parallel launch (KIND_TILE16, KIND_MFMA)
+    LaunchSkFn launch_sk;    // stream-K launch (KIND_SK)
 };
+
+// Stream-K workspace: per-tile counters at a fixed offset (so a call with more tiles
+// never meets a previous call's partial sums there), then two partial-tile slots per
+// workgroup.
+constexpr int kSkMaxTiles = 16384;
+constexpr size_t kSkCounterBytes = (size_t)kSkMaxTiles * sizeof(unsigned);
+
+size_t sk_workspace_bytes(const Config &c, int cus)
+{
+    return kSkCounterBytes + (size_t)cus * 2 * (size_t)c.bm * (size_t)c.bn * sizeof(float);
+}
+
+// Compute units of the current device (one stream-K workgroup each), cached per device;
+// 0 if the device cannot be queried.
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0)
+            return v;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 0;
+    if (dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
 
 // Row strides (floats) from which the direct-copy kernels' 32-bit in-tile offsets
 // could overflow; such calls take the element-wise (unaligned) variant instead.
@@ -47,6 +87,23 @@ hipError_t launch_mfma(const GemmArgs &p, int batch, bool ta, bool tb, bool vec,
     return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, true>(p, batch, vec, edge, s);
 }
 
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M>
+hipError_t launch_sk(const GemmArgs &p, const StreamK &sk, int grid, bool ta, bool tb, bool vec, bool edge,
+                     hipStream_t s)
+{
+    if (!ta && !tb)
+        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, false>(p, sk, grid,
+                                                                                                        vec, edge, s);
+    if (!ta && tb)
+        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, true>(p, sk, grid,
+                                                                                                       vec, edge, s);
+    if (ta && !tb)
+        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, false>(p, sk, grid,
+                                                                                                       vec, edge, s);
+    return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, true>(p, sk, grid, vec,
+                                                                                                  edge, s);
+}
+
 hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, bool, hipStream_t s)
 {
     const dim3 grid((p.N + 15) / 16, (p.M + 15) / 16, batch), block(16, 16);
@@ -61,17 +118,23 @@ hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, b
     return hipGetLastError();
 }
 
-// Configuration table: id 0 is the 16x16 baseline kernel, ids 1.. the MFMA
-// configurations of sgemm_configs.inc in order. Names encode the tile (BM x BN x BK),
+// Configuration table: id 0 is the 16x16 baseline kernel, then the MFMA configurations
+// of sgemm_configs.inc in order, then its stream-K configurations. Names encode the tile (BM x BN x BK),
 // the wave grid (WGM x WGN), after "k" the wave groups along k, after "p" the K-tiles
 // prefetched ahead (1 when absent), and a final "d" marks direct HBM -> LDS copies.
-#define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M) \
-    {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>},
+#define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M)                               \
+    {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, GROUP_M,                                   \
+     launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>, nullptr},
+#define SGEMM_SK_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M)                            \
+    {name, KIND_SK, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, GROUP_M, nullptr,                            \
+     launch_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>},
 const Config kConfigs[] = {
-    {"tile16", KIND_TILE16, 16, 16, 16, 256, false, launch_tile16},
+    {"tile16", KIND_TILE16, 16, 16, 16, 256, false, 1, launch_tile16, nullptr},
     SGEMM_MFMA_CONFIGS(SGEMM_TABLE_ROW)
+    SGEMM_SK_CONFIGS(SGEMM_SK_TABLE_ROW)
 };
 #undef SGEMM_TABLE_ROW
+#undef SGEMM_SK_TABLE_ROW
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -92,32 +155,53 @@ uint64_t tile_count(const Config &c, int M, int N)
     return (uint64_t)((M + c.bm - 1) / c.bm) * (uint64_t)((N + c.bn - 1) / c.bn);
 }
 
-// Auto-selection by a small cost model. A candidate's tiles spread over the 256 CUs
-// take L = ceil(tiles / 256) rounds on the busiest CU; its time is L tiles of work
-// (in units of one 64x64 tile) divided by the CU's throughput with that many tiles
-// resident. Throughputs (fp32 TFLOP/s per CU) were measured on MI355X with the
-// whole chip busy: rate_one when a CU holds a single workgroup, rate_many when it
-// holds several (more waves to hide latency). The model picks the large tile when it
-// fills the chip in one round and the wave-split 64x64 tile when few tiles exist;
-// K cancels out because every candidate walks the same K.
+// The stream-K kernel splits work with 32-bit arithmetic: (CUs + 1) * work < 2^31.
+bool sk_work_fits(const Config &c, int M, int N, int K, int cus)
+{
+    const uint64_t tiles = tile_count(c, M, N);
+    const uint64_t work = tiles * (uint64_t)((K + c.bk - 1) / c.bk);
+    return tiles <= (uint64_t)kSkMaxTiles && work * (uint64_t)(cus + 1) < (1ull << 31);
+}
+
+// Auto-selection by a small cost model of the kernel time.
+//
+// Data-parallel candidates: the tiles spread over the CUs take L = ceil(tiles / CUs)
+// rounds on the busiest CU, so the time is L tiles of work (one unit is a 64x64 tile,
+// 2 * 64 * 64 * K flop) at the CU's throughput with that many tiles resident.
+// Throughputs (fp32 TFLOP/s per CU) were measured on MI355X with the whole chip busy:
+// rate_one when a CU holds a single workgroup, rate_many when it holds several.
+//
+// Stream-K candidates (only with a large enough workspace): every CU gets the same
+// share, tiles * units / CUs, at the one-workgroup rate, plus a fixed cost for the
+// partial tiles (each partial is written once and read once by the tile's last
+// contributor, and that contributor's epilogue runs after the others').
 struct Candidate {
     const char *name;   // configuration name in the table
     int units;          // tile area / (64 * 64)
     double rate_one;    // per-CU rate with one resident workgroup
     double rate_many;   // per-CU rate with two or more
+    double fixed_us;    // stream-K only: cost of combining partial tiles
 };
 
 // Rates measured with every candidate prefetching two K-tiles ahead; fitted to the
 // sweep over 256^3 ... 4096^3, the GPT-2 linear layers and the 1000 x 1537 x 777
 // unaligned case (which the same table serves).
 const Candidate kCandidates[] = {
-    {"mfma_256x256x16_w2x4p2", 16, 0.500, 0.500},     // one workgroup per CU
-    {"mfma_128x128x32_w2x2k2p2", 4, 0.484, 0.466},    // one per CU
-    {"mfma_64x128x32_w2x2k2p2", 2, 0.459, 0.461},     // up to two per CU
-    {"mfma_64x64x64_w2x2k4p2", 1, 0.380, 0.390},      // one per CU, 16 waves
-    {"mfma_64x64x32_w2x2k2p2", 1, 0.360, 0.410},      // up to four per CU
+    {"mfma_256x256x16_w2x4p2", 16, 0.500, 0.500, 0.0},     // one workgroup per CU
+    {"mfma_128x128x32_w2x2k2p2", 4, 0.484, 0.466, 0.0},    // one per CU
+    {"mfma_64x128x32_w2x2k2p2", 2, 0.459, 0.461, 0.0},     // up to two per CU
+    {"mfma_64x64x64_w2x2k4p2", 1, 0.380, 0.390, 0.0},      // one per CU, 16 waves
+    {"mfma_64x64x32_w2x2k2p2", 1, 0.360, 0.410, 0.0},      // up to four per CU
+};
+// Stream-K rates and fixed costs fitted to 1024^3, 3072^3 and the GPT-2 layers (time =
+// work / (CUs * rate) + fixed): the fixed part covers the per-range pipeline fill, the
+// partial-tile traffic and the last contributor's serial epilogue.
+const Candidate kSkCandidates[] = {
+    {"sk_128x128x32_w2x2k2p2", 4, 0.50, 0.50, 16.0},
+    {"sk_64x128x32_w2x2k2p2", 2, 0.46, 0.46, 9.0},
 };
 constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
+constexpr int kNumSkCandidates = sizeof(kSkCandidates) / sizeof(kSkCandidates[0]);
 
 int find_config(const char *name)
 {
@@ -132,27 +216,48 @@ int find_config(const char *name)
 
 // Table ids of the candidates, looked up once.
 struct CandidateIds {
-    int id[kNumCandidates];
-    CandidateIds() { for (int i = 0; i < kNumCandidates; ++i) id[i] = find_config(kCandidates[i].name); }
+    int id[kNumCandidates], sk[kNumSkCandidates];
+    CandidateIds()
+    {
+        for (int i = 0; i < kNumCandidates; ++i) id[i] = find_config(kCandidates[i].name);
+        for (int i = 0; i < kNumSkCandidates; ++i) sk[i] = find_config(kSkCandidates[i].name);
+    }
 };
 
-int choose(int M, int N, bool vec)
+// The configuration with the least modelled time. Stream-K candidates are considered
+// only when `ws_bytes` holds their workspace for `cus` compute units (cus > 0).
+int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0)
 {
-    (void)vec;    // one table serves the 128-bit and the 32-bit paths
+    // One data-parallel table serves the 128-bit and the 32-bit paths.
     static const CandidateIds ids;
-    constexpr uint64_t kCUs = 256;
+    const uint64_t kCUs = cus > 0 ? (uint64_t)cus : 256;
+    const double unit_mflop = 2.0 * 64 * 64 * (double)K * 1e-6;    // one 64x64 tile, MFLOP
     int best = -1;
-    double best_cost = 0.0;
+    double best_us = 0.0;
     for (int i = 0; i < kNumCandidates; ++i) {
         const Candidate &cand = kCandidates[i];
         if (ids.id[i] < 0)
             continue;
         const uint64_t tiles = tile_count(kConfigs[ids.id[i]], M, N);
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
-        const double cost = (double)rounds * cand.units / (rounds >= 2 ? cand.rate_many : cand.rate_one);
-        if (best < 0 || cost < best_cost) {
+        const double us = (double)rounds * cand.units * unit_mflop / (rounds >= 2 ? cand.rate_many : cand.rate_one);
+        if (best < 0 || us < best_us) {
             best = ids.id[i];
-            best_cost = cost;
+            best_us = us;
+        }
+    }
+    for (int i = 0; vec && cus > 0 && i < kNumSkCandidates; ++i) {   // stream-K kernels: aligned operands
+        const Candidate &cand = kSkCandidates[i];
+        if (ids.sk[i] < 0)
+            continue;
+        const Config &c = kConfigs[ids.sk[i]];
+        const uint64_t tiles = tile_count(c, M, N);
+        if (!sk_work_fits(c, M, N, K, cus) || ws_bytes < sk_workspace_bytes(c, cus))
+            continue;
+        const double us = (double)tiles * cand.units / (double)kCUs * unit_mflop / cand.rate_one + cand.fixed_us;
+        if (us < best_us) {
+            best = ids.sk[i];
+            best_us = us;
         }
     }
     return best;
@@ -193,7 +298,7 @@ const int kPosBatched[] = {0, 0, 0, 1, 2, 3, 5, 6, 8, 9, 12, 13, 0};   // sgemm_
 
 int run(int config, int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, int64_t sA,
         const float *B, int ldb, int64_t sB, float beta, float *C, int ldc, int64_t sC, const float *bias,
-        int act, int batch, hipStream_t stream)
+        int act, int batch, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     GemmArgs p;
     p.M = M; p.N = N; p.K = K;
@@ -213,20 +318,39 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     }
     const bool vec = vector_ok(opA, opB, M, N, K, A, lda, B, ldb, C, ldc) &&
                      (batch == 1 || (sA % 4 == 0 && sB % 4 == 0 && sC % 4 == 0));
-    const int id = config >= 0 ? config : choose(M, N, vec);
+    const int cus = (ws != nullptr && batch == 1) ? device_cus() : 0;
+    const int id = config >= 0 ? config : choose(M, N, K, vec, ws_bytes, cus);
     const Config &c = kConfigs[id];
     const uint64_t tiles = tile_count(c, M, N);
     if (c.kind == KIND_MFMA && tiles * (uint64_t)c.threads > 0xFFFFFFFFull)
         return SGEMM_ERROR_TOO_LARGE;
     const bool edge = (M % c.bm) != 0 || (N % c.bn) != 0 || (K % c.bk) != 0;
     const bool vec_c = vec && !(c.dma && (lda >= kDmaMaxLd || ldb >= kDmaMaxLd));
+    if (c.kind == KIND_SK) {
+        if (batch != 1 || cus <= 0 || ws_bytes < sk_workspace_bytes(c, cus))
+            return SGEMM_ERROR_WORKSPACE;
+        if (!sk_work_fits(c, M, N, K, cus))
+            return SGEMM_ERROR_TOO_LARGE;
+        StreamK sk;
+        sk.counters = static_cast<unsigned *>(ws);
+        sk.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + kSkCounterBytes);
+        sk.tiles_m = (M + c.bm - 1) / c.bm;
+        sk.tiles_n = (N + c.bn - 1) / c.bn;
+        sk.iters = (K + c.bk - 1) / c.bk;
+        sk.group_m = c.group_m;
+        sk.work = (int)tiles * sk.iters;
+        // At most one workgroup per K-tile step, so every workgroup's range is non-empty.
+        const int grid = sk.work < cus ? sk.work : cus;
+        const hipError_t e = c.launch_sk(p, sk, grid, opA != 0, opB != 0, vec_c, edge, stream);
+        return e == hipSuccess ? 0 : (int)e;
+    }
     const hipError_t e = c.launch(p, batch, opA != 0, opB != 0, vec_c, edge, stream);
     return e == hipSuccess ? 0 : (int)e;
 }
 
 int general(const int *pos, int config, int opA, int opB, int M, int N, int K, float alpha, const float *A,
             int lda, const float *B, int ldb, float beta, float *C, int ldc, const float *bias, int act,
-            void *stream)
+            void *stream, void *ws = nullptr, size_t ws_bytes = 0)
 {
     if (config < -1 || config >= kNumConfigs)
         return SGEMM_ERROR_BAD_CONFIG;
@@ -235,8 +359,8 @@ int general(const int *pos, int config, int opA, int opB, int M, int N, int K, f
         return -pos[bad];
     if (M == 0 || N == 0)
         return SGEMM_SUCCESS;
-    return run(config, opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, bias, act, 1,
-               static_cast<hipStream_t>(stream));
+    return run(config, opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, bias, act, 1, ws,
+               ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -291,7 +415,41 @@ int sgemm_strided_batched(int M, int N, int K, float alpha, const float *A, int 
     if (M == 0 || N == 0 || batch == 0)
         return SGEMM_SUCCESS;
     return run(-1, SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
-               strideC, nullptr, SGEMM_ACT_NONE, batch, static_cast<hipStream_t>(stream));
+               strideC, nullptr, SGEMM_ACT_NONE, batch, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+int sgemm_general_ws(int config, int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+                     const float *B, int ldb, float beta, float *C, int ldc, const float *bias, int act,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (workspace == nullptr ? workspace_bytes != 0 : (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+        return -16;
+    return general(kPosFused, config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream,
+                   workspace, workspace_bytes);
+}
+
+size_t sgemm_workspace_size(int config)
+{
+    const int cus = device_cus();
+    if (cus <= 0)
+        return 0;
+    size_t most = 0;
+    for (int i = 0; i < kNumConfigs; ++i) {
+        if (kConfigs[i].kind != KIND_SK || (config >= 0 && i != config))
+            continue;
+        const size_t b = sk_workspace_bytes(kConfigs[i], cus);
+        most = b > most ? b : most;
+    }
+    return most;
+}
+
+int sgemm_select_config_ws(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+                           const float *C, int ldc, size_t workspace_bytes)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || alpha == 0.0f)
+        return -1;
+    return choose(M, N, K, vector_ok(SGEMM_OP_N, SGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc), workspace_bytes,
+                  workspace_bytes > 0 ? device_cus() : 0);
 }
 
 int sgemm_config_count(void) { return kNumConfigs; }
@@ -306,7 +464,7 @@ int sgemm_select_config(int M, int N, int K, float alpha, const float *A, int ld
 {
     if (M <= 0 || N <= 0 || K <= 0 || alpha == 0.0f)
         return -1;
-    return choose(M, N, vector_ok(SGEMM_OP_N, SGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc));
+    return choose(M, N, K, vector_ok(SGEMM_OP_N, SGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc));
 }
 
 int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3])
@@ -322,6 +480,14 @@ int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3
         return 0;
     }
     const uint64_t tiles = tile_count(c, M, N);
+    if (c.kind == KIND_SK) {
+        // One workgroup per compute unit (MI355X has 256), at most one per K-tile step.
+        if (tiles > (uint64_t)kSkMaxTiles) return SGEMM_ERROR_TOO_LARGE;
+        const uint64_t work = tiles * (uint64_t)((K + c.bk - 1) / c.bk);
+        grid[0] = work < 256 ? (int)work : 256; grid[1] = 1; grid[2] = 1;
+        block[0] = c.threads; block[1] = 1; block[2] = 1;
+        return 0;
+    }
     if (tiles * (uint64_t)c.threads > 0xFFFFFFFFull) return SGEMM_ERROR_TOO_LARGE;
     grid[0] = (int)tiles; grid[1] = 1; grid[2] = 1;
     block[0] = c.threads; block[1] = 1; block[2] = 1;
@@ -334,6 +500,7 @@ const char *sgemm_status_string(int status)
     case 0: return "success";
     case SGEMM_ERROR_TOO_LARGE: return "problem too large: the tile grid exceeds one launch";
     case SGEMM_ERROR_BAD_CONFIG: return "configuration id out of range";
+    case SGEMM_ERROR_WORKSPACE: return "stream-K configuration without a large enough workspace";
     default: break;
     }
     if (status < 0 && status >= -16) {

@@ -107,20 +107,32 @@ __device__ __forceinline__ float finish_value(float acc, float alpha, float beta
 // contiguous range of the logical order. The second walks that order in groups of
 // `group_m` tile rows, column by column, so workgroups that run together share A
 // row panels and B column panels in L2.
-__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int group_m,
-                                            int &tm, int &tn)
+// Workgroup id -> position in a launch order where each of the 8 XCDs (which take ids
+// round-robin) receives one contiguous range.
+__device__ __forceinline__ int xcd_contiguous(int wg, int total)
 {
-    const int total = tiles_m * tiles_n;
     constexpr int XCDS = 8;
     const int per = total / XCDS, rem = total % XCDS;
     const int xcd = wg % XCDS, slot = wg / XCDS;
-    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
+// Position in the launch order -> (tile_m, tile_n), walking bands of `group_m` tile rows
+// column by column.
+__device__ __forceinline__ void band_coords(int logical, int tiles_m, int tiles_n, int group_m, int &tm, int &tn)
+{
     const int band = group_m * tiles_n;
     const int first_m = (logical / band) * group_m;
     const int rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
     const int in_band = logical % band;
     tm = first_m + in_band % rows;
     tn = in_band / rows;
+}
+
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int group_m,
+                                            int &tm, int &tn)
+{
+    band_coords(xcd_contiguous(wg, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 // One operand tile as it sits in memory: TR rows of TC contiguous floats (row stride
@@ -331,382 +343,521 @@ __device__ __forceinline__ void lds_read(const float *p, float (&out)[W])
 //    c*T + b (T blocks), so lane l reads T consecutive values for one k in one read,
 //    and for B writes T consecutive columns of C.
 // ---------------------------------------------------------------------------------
+// One BM x BN tile of op(A) op(B) on matrix cores: the operand loaders, the LDS ring and
+// the MFMA loop over a range of K-tiles (product), and the C update (epilogue). The
+// whole-tile kernel below runs product over all of K; the stream-K kernel runs it over
+// the K-tile ranges its workgroup owns.
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
+          bool EDGE>
+struct MfmaTile {
+    static_assert(PF == 1 || PF == 2, "K-tiles in flight ahead of the one being multiplied");
+    static constexpr bool USE_DMA = DMA && VEC;             // aligned operands: direct HBM -> LDS copies
+    static constexpr int NT = WGM * WGN * WGK * 64;
+    static constexpr int KSLICE = BK / WGK;                    // k per stage handled by one wave group
+    static constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
+    static constexpr int TM = WTM / 32, TN = WTN / 32;         // 32x32 blocks per wave
+    using AIO = typename std::conditional<USE_DMA, TileDMA<TA ? BK : BM, TA ? BM : BK, NT, !TA>,
+                                          TileIO<TA ? BK : BM, TA ? BM : BK, NT>>::type;
+    using BIO = typename std::conditional<USE_DMA, TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB>,
+                                          TileIO<TB ? BN : BK, TB ? BK : BN, NT>>::type;
+    static constexpr int STAGE = AIO::SIZE + BIO::SIZE;
+    static constexpr int NSTAGE = USE_DMA ? PF + 1 : 2;     // LDS stages in the ring
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(!TA || TM == 1 || TM == 2 || TM == 4, "interleaved m blocks read 1, 2 or 4 floats");
+    static_assert(TB || TN == 1 || TN == 2 || TN == 4, "interleaved n blocks read 1, 2 or 4 floats");
+    static_assert(BK % (8 * WGK) == 0, "each wave group consumes k in groups of 8");
+    static constexpr int RED = (WGK - 1) * BM * BN;         // partial sums of groups 1..WGK-1
+    static constexpr int SMEM = NSTAGE * STAGE > RED ? NSTAGE * STAGE : RED;
+    static_assert(SMEM * 4 <= 160 * 1024, "LDS exceeds 160 KiB");
+
+    // Multiply K-tiles [kt0, kt1) of the tile at (m0, n0) into acc, which starts at zero;
+    // tid_in is the thread's index in the workgroup. With WGK > 1 the groups' sums end up
+    // in the waves of group 0; the other waves return false and hold nothing.
+    __device__ __forceinline__ static bool product(const GemmArgs &p, float *smem, int m0, int n0, int kt0,
+                                                   int kt1, floatx16 (&acc)[TM][TN], int tid_in)
+    {
+        const int M = p.M, N = p.N, K = p.K;
+        const float *__restrict__ A = p.A + (int64_t)blockIdx.z * p.strideA;
+        const float *__restrict__ B = p.B + (int64_t)blockIdx.z * p.strideB;
+        const int64_t lda = p.lda, ldb = p.ldb;
+        const int kbase = kt0 * BK;                         // first k of the range
+
+        const int tid = tid_in;
+        const int lane = tid & 63, wave = tid >> 6;
+        const int wk = wave / (WGM * WGN);
+        const int wm = (wave % (WGM * WGN)) / WGN, wn = wave % WGN;
+        const int l32 = lane & 31, half = lane >> 5;
+
+        // PF sets of staging registers: with PF = 2 a K-tile's global loads are issued two
+        // stages before it is multiplied. `slot` is always a compile-time constant after
+        // inlining, so the sets stay in registers.
+        floatx4 ra[USE_DMA ? 1 : PF][AIO::CH], rb[USE_DMA ? 1 : PF][BIO::CH];
+
+        // Global -> registers set `slot` for the K-tile starting kr after the range's first k
+        // (zero outside the matrix).
+        auto load_tile = [&](int kr, int slot) __attribute__((always_inline)) {
+            if constexpr (!USE_DMA) {
+                const int k0 = kbase + kr;
+                if constexpr (TA)
+                    AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, tid);
+                else
+                    AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, tid);
+                if constexpr (TB)
+                    BIO::template load<VEC, EDGE>(rb[slot], B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, tid);
+                else
+                    BIO::template load<VEC, EDGE>(rb[slot], B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, tid);
+            }
+        };
+
+        // Registers set `slot` -> LDS stage `st`.
+        auto store_tile = [&](int st, int slot) __attribute__((always_inline)) {
+            if constexpr (!USE_DMA) {
+                float *As = smem + st * STAGE;
+                AIO::store(ra[slot], As, tid);
+                BIO::store(rb[slot], As + AIO::SIZE, tid);
+            }
+        };
+
+        // Direct copies of the K-tile starting kr after the range's first k into LDS stage `st`
+        // (DMA path).
+        auto copy_tile = [&](int kr, int st) __attribute__((always_inline)) {
+            if constexpr (USE_DMA) {
+                const int k0 = kbase + kr;
+                float *As = smem + st * STAGE;
+                if constexpr (TA)
+                    AIO::template load<EDGE>(A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, As, tid);
+                else
+                    AIO::template load<EDGE>(A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, As, tid);
+                if constexpr (TB)
+                    BIO::template load<EDGE>(B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, As + AIO::SIZE, tid);
+                else
+                    BIO::template load<EDGE>(B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, As + AIO::SIZE, tid);
+            }
+        };
+
+    #pragma unroll
+        for (int a = 0; a < TM; ++a)
+    #pragma unroll
+            for (int b = 0; b < TN; ++b)
+    #pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[a][b][e] = 0.f;
+
+        // This lane's first row of A / column of B inside the tile: plain A rows are
+        // a*32 + l32 (blocks side by side), transposed A rows l32*TM + a (interleaved);
+        // likewise for B columns with the roles swapped.
+        const int a_idx = wm * WTM + (TA ? l32 * TM : l32);
+        const int b_idx = wn * WTN + (TB ? l32 : l32 * TN);
+
+        // One stage: KSLICE/8 groups of 8 k values, 4 matrix steps each.
+        auto compute = [&](int st) __attribute__((always_inline)) {
+            const float *As = smem + st * STAGE;
+            const float *Bs = As + AIO::SIZE;
+    #pragma unroll
+            for (int kk = 0; kk < KSLICE; kk += 8) {
+                const int kg = wk * KSLICE + kk;
+                floatx4 af[TA ? 1 : TM], bf[TB ? TN : 1];
+                if constexpr (!TA) {
+    #pragma unroll
+                    for (int a = 0; a < TM; ++a)
+                        af[a] = *reinterpret_cast<const floatx4 *>(&As[AIO::elem(a_idx + a * 32, kg + 4 * half)]);
+                }
+                if constexpr (TB) {
+    #pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        bf[b] = *reinterpret_cast<const floatx4 *>(&Bs[BIO::elem(b_idx + b * 32, kg + 4 * half)]);
+                }
+    #pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int k = kg + 4 * half + s;
+                    float av[TM], bv[TN];
+                    if constexpr (TA) {
+                        lds_read<TM>(&As[AIO::elem(k, a_idx)], av);
+                    } else {
+    #pragma unroll
+                        for (int a = 0; a < TM; ++a)
+                            av[a] = af[a][s];
+                    }
+                    if constexpr (TB) {
+    #pragma unroll
+                        for (int b = 0; b < TN; ++b)
+                            bv[b] = bf[b][s];
+                    } else {
+                        lds_read<TN>(&Bs[BIO::elem(k, b_idx)], bv);
+                    }
+    #pragma unroll
+                    for (int a = 0; a < TM; ++a)
+    #pragma unroll
+                        for (int b = 0; b < TN; ++b)
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+                }
+            }
+        };
+
+        // Fragment form used by the direct-copy pipeline: the A and B values of one group
+        // of 8 k (4 per lane) for every block, read from LDS in one batch, so the reads of
+        // the next group can be in flight while this one is multiplied.
+        constexpr int NG = KSLICE / 8;                      // groups of 8 k per stage and wave group
+        float fa[USE_DMA ? 2 : 1][4][TM], fb[USE_DMA ? 2 : 1][4][TN];
+        auto read_frag = [&](int st, int g, int buf) __attribute__((always_inline)) {
+            const float *As = smem + st * STAGE;
+            const float *Bs = As + AIO::SIZE;
+            const int kg = wk * KSLICE + 8 * g + 4 * half;
+            if constexpr (TA) {
+    #pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    lds_read<TM>(&As[AIO::elem(kg + s, a_idx)], fa[buf][s]);
+            } else {
+    #pragma unroll
+                for (int a = 0; a < TM; ++a) {
+                    const floatx4 v = *reinterpret_cast<const floatx4 *>(&As[AIO::elem(a_idx + a * 32, kg)]);
+    #pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        fa[buf][s][a] = v[s];
+                }
+            }
+            if constexpr (TB) {
+    #pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    const floatx4 v = *reinterpret_cast<const floatx4 *>(&Bs[BIO::elem(b_idx + b * 32, kg)]);
+    #pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        fb[buf][s][b] = v[s];
+                }
+            } else {
+    #pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    lds_read<TN>(&Bs[BIO::elem(kg + s, b_idx)], fb[buf][s]);
+            }
+        };
+        auto mma_frag = [&](int buf) __attribute__((always_inline)) {
+    #pragma unroll
+            for (int s = 0; s < 4; ++s)
+    #pragma unroll
+                for (int a = 0; a < TM; ++a)
+    #pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[buf][s][a], fb[buf][s][b], acc[a][b],
+                                                                         0, 0, 0);
+        };
+
+        // Pipeline over the range's nk K-tiles, one barrier per K-tile.
+        const int nk = kt1 - kt0;
+        if constexpr (USE_DMA) {
+            // PF + 1 LDS stages. Step t queues the copies of tile t+PF into stage (t+PF) %
+            // NSTAGE (read last during step t-1, so free after that step's barrier),
+            // multiplies stage t % NSTAGE, waits until its own copies of tile t+1 have landed
+            // (the PF-1 newer tiles may stay in flight) and meets the others at the barrier.
+            // Past the end the last tile is copied again, so the count of copies in flight
+            // is the same on every step.
+            // Inside a step, group g+1's fragments are read while group g is multiplied; the
+            // last group is multiplied after the barrier, while group 0 of the next stage
+            // is read (past the last step that read is of a stage nobody uses; harmless).
+            static_assert(NG % 2 == 0, "fragment buffers alternate within a stage");
+            constexpr int COPIES = AIO::CH + BIO::CH;       // copy instructions per thread per tile
+    #pragma unroll
+            for (int q = 0; q < PF; ++q)
+                copy_tile((q < nk ? q : nk - 1) * BK, q);
+            wait_vmcnt<0>();
+            __syncthreads();
+            read_frag(0, 0, 0);
+            for (int t = 0; t < nk; ++t) {
+                const int ahead = t + PF < nk ? t + PF : nk - 1;
+                copy_tile(ahead * BK, (t + PF) % NSTAGE);
+                const int st = t % NSTAGE;
+    #pragma unroll
+                for (int g = 0; g + 1 < NG; ++g) {
+                    read_frag(st, g + 1, (g + 1) & 1);
+                    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+                    mma_frag(g & 1);
+                }
+                copy_barrier<(PF - 1) * COPIES>();
+                read_frag((t + 1) % NSTAGE, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_frag(1);
+            }
+            wait_vmcnt<0>();    // no copy may still write LDS once it is reused or released
+        } else if constexpr (PF == 1) {
+            load_tile(0, 0);
+            store_tile(0, 0);
+            __syncthreads();
+            for (int t = 0; t + 1 < nk; ++t) {
+                load_tile((t + 1) * BK, 0);  // in flight while this stage is multiplied
+                compute(t & 1);
+                store_tile((t + 1) & 1, 0);  // other stage: its last reader finished before the previous barrier
+                __syncthreads();
+            }
+        } else {
+            // Entering step t: stage t%2 holds K-tile t, register set (t+1)%2 holds tile t+1
+            // (loaded during step t-1) and set t%2 is free. Step t loads tile t+2 into set
+            // t%2 (the last tile again once past the end, so the load needs no condition),
+            // multiplies stage t%2, then stores set (t+1)%2 into stage (t+1)%2.
+            auto step = [&](int t, int s) __attribute__((always_inline)) {
+                const int ahead = t + 2 < nk ? t + 2 : nk - 1;
+                load_tile(ahead * BK, s);
+                compute(s);
+                store_tile(1 - s, 1 - s);
+                __syncthreads();
+            };
+            load_tile(0, 0);
+            load_tile((nk > 1 ? 1 : 0) * BK, 1);
+            store_tile(0, 0);
+            __syncthreads();
+            int t = 0;
+            for (; t + 2 < nk; t += 2) {     // steps t and t+1, both before the last tile
+                step(t, 0);
+                step(t + 1, 1);
+            }
+            if (t + 1 < nk) {
+                step(t, 0);
+                ++t;
+            }
+        }
+        if constexpr (!USE_DMA)
+            compute((nk - 1) & 1);
+
+        if constexpr (WGK > 1) {
+            // Groups 1..WGK-1 hand their partial sums to group 0 through LDS (the ring is
+            // free once every wave has passed the barrier); group 0 adds them in group order.
+            constexpr int PER_WAVE = TM * TN * 16 * 64;
+            const int slot = wm * WGN + wn;
+            __syncthreads();
+            if (wk > 0) {
+                float *dst = smem + ((wk - 1) * (WGM * WGN) + slot) * PER_WAVE;
+    #pragma unroll
+                for (int a = 0; a < TM; ++a)
+    #pragma unroll
+                    for (int b = 0; b < TN; ++b)
+    #pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            dst[((a * TN + b) * 16 + e) * 64 + lane] = acc[a][b][e];
+            }
+            __syncthreads();
+            if (wk > 0)
+                return false;
+    #pragma unroll
+            for (int g = 1; g < WGK; ++g) {
+                const float *src = smem + ((g - 1) * (WGM * WGN) + slot) * PER_WAVE;
+    #pragma unroll
+                for (int a = 0; a < TM; ++a)
+    #pragma unroll
+                    for (int b = 0; b < TN; ++b)
+    #pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            acc[a][b][e] += src[((a * TN + b) * 16 + e) * 64 + lane];
+            }
+        }
+        return true;
+    }
+
+    __device__ __forceinline__ static void epilogue(const GemmArgs &p, int m0, int n0,
+                                                    const floatx16 (&acc)[TM][TN], int tid_in)
+    {
+        const int M = p.M, N = p.N;
+        float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
+        const int64_t ldc = p.ldc;
+        const int tid = tid_in;
+        const int lane = tid & 63, wave = tid >> 6;
+        const int wm = (wave % (WGM * WGN)) / WGN, wn = wave % WGN;
+        const int l32 = lane & 31, half = lane >> 5;
+        const int b_idx = wn * WTN + (TB ? l32 : l32 * TN);
+        // Epilogue: C = act(alpha*acc + beta*C + bias), C unread when beta == 0. One 32-row
+        // block at a time: all of the block's reads of C are issued before the first is
+        // used, so the block waits out one memory round trip (two with EB = 8) rather than
+        // one per entry. Lane columns: TN consecutive ones (plain B), or one per 32-column block
+        // (transposed B). Rows: those of accumulator element e, see the mapping above.
+        const float alpha = p.alpha, beta = p.beta;
+        const float *bias = p.bias;
+        const int act = p.act;
+        const bool read_c = beta != 0.f, has_bias = bias != nullptr;
+        const bool full = !EDGE || (m0 + BM <= M && n0 + BN <= N);   // whole tile inside C
+        // 128- or 64-bit accesses of a lane's TN consecutive columns: aligned, and (N % 4 == 0,
+        // first column a multiple of TN) the group is either wholly inside C or wholly out.
+        constexpr bool VCOL = VEC && !TB && (TN == 2 || TN == 4);
+        int gc[TN];
+    #pragma unroll
+        for (int b = 0; b < TN; ++b)
+            gc[b] = n0 + b_idx + (TB ? 32 * b : b);
+        float bj[TN];
+    #pragma unroll
+        for (int b = 0; b < TN; ++b)
+            bj[b] = (has_bias && (full || gc[b] < N)) ? bias[gc[b]] : 0.f;
+        auto row_of = [&](int a, int e) __attribute__((always_inline)) {
+            const int r = 8 * (e / 4) + 4 * half + (e % 4);          // row inside the 32x32 block
+            return m0 + wm * WTM + (TA ? r * TM + a : a * 32 + r);
+        };
+        // Entries per batch of reads: 16 (the whole block), or 8 where four waves share a
+        // SIMD and each has only 128 registers.
+        constexpr int EB = NT >= 1024 ? 8 : 16;
+    #pragma unroll
+        for (int a = 0; a < TM; ++a)
+    #pragma unroll
+        for (int e0 = 0; e0 < 16; e0 += EB) {
+            float cv[16][TN];
+            if (read_c) {
+    #pragma unroll
+                for (int e = e0; e < e0 + EB; ++e) {
+                    const int gr = row_of(a, e);
+                    const float *crow = C + (int64_t)gr * ldc;
+                    if constexpr (VCOL) {
+                        using vec_t = typename std::conditional<TN == 4, floatx4, floatx2>::type;
+                        vec_t v{};
+                        if (full || (gr < M && gc[0] < N))
+                            v = *reinterpret_cast<const vec_t *>(crow + gc[0]);
+    #pragma unroll
+                        for (int b = 0; b < TN; ++b)
+                            cv[e][b] = v[b];
+                    } else {
+    #pragma unroll
+                        for (int b = 0; b < TN; ++b)
+                            cv[e][b] = (full || (gr < M && gc[b] < N)) ? crow[gc[b]] : 0.f;
+                    }
+                }
+            }
+    #pragma unroll
+            for (int e = e0; e < e0 + EB; ++e) {
+                const int gr = row_of(a, e);
+                float *crow = C + (int64_t)gr * ldc;
+                float out[TN];
+    #pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    out[b] = finish_value(acc[a][b][e], alpha, beta, read_c ? cv[e][b] : 0.f, has_bias, bj[b], act);
+                if constexpr (VCOL) {
+                    using vec_t = typename std::conditional<TN == 4, floatx4, floatx2>::type;
+                    vec_t v;
+    #pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        v[b] = out[b];
+                    if (full || (gr < M && gc[0] < N))
+                        *reinterpret_cast<vec_t *>(crow + gc[0]) = v;
+                } else {
+    #pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        if (full || (gr < M && gc[b] < N))
+                            crow[gc[b]] = out[b];
+                }
+            }
+        }
+    }
+};
+
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
           bool EDGE>
 __global__ void __launch_bounds__(WGM * WGN * WGK * 64)
 sgemm_mfma(GemmArgs p, int group_m)
 {
-    static_assert(PF == 1 || PF == 2, "K-tiles in flight ahead of the one being multiplied");
-    constexpr bool USE_DMA = DMA && VEC;                // aligned operands: direct HBM -> LDS copies
-    constexpr int NT = WGM * WGN * WGK * 64;
-    constexpr int KSLICE = BK / WGK;                    // k per stage handled by one wave group
-    constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
-    constexpr int TM = WTM / 32, TN = WTN / 32;         // 32x32 blocks per wave
-    using AIO = typename std::conditional<USE_DMA, TileDMA<TA ? BK : BM, TA ? BM : BK, NT, !TA>,
-                                          TileIO<TA ? BK : BM, TA ? BM : BK, NT>>::type;
-    using BIO = typename std::conditional<USE_DMA, TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB>,
-                                          TileIO<TB ? BN : BK, TB ? BK : BN, NT>>::type;
-    constexpr int STAGE = AIO::SIZE + BIO::SIZE;
-    constexpr int NSTAGE = USE_DMA ? PF + 1 : 2;         // LDS stages in the ring
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(!TA || TM == 1 || TM == 2 || TM == 4, "interleaved m blocks read 1, 2 or 4 floats");
-    static_assert(TB || TN == 1 || TN == 2 || TN == 4, "interleaved n blocks read 1, 2 or 4 floats");
-    static_assert(BK % (8 * WGK) == 0, "each wave group consumes k in groups of 8");
-    constexpr int RED = (WGK - 1) * BM * BN;            // partial sums of groups 1..WGK-1
-    constexpr int SMEM = NSTAGE * STAGE > RED ? NSTAGE * STAGE : RED;
-    static_assert(SMEM * 4 <= 160 * 1024, "LDS exceeds 160 KiB");
-
-    __shared__ __attribute__((aligned(16))) float smem[SMEM];
-
-    const int M = p.M, N = p.N, K = p.K;
-    const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE>;
+    __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    tile_coords(blockIdx.x, ceil_div(p.M, BM), ceil_div(p.N, BN), group_m, tm, tn);
+    floatx16 acc[T::TM][T::TN];
+    if (T::product(p, smem, tm * BM, tn * BN, 0, ceil_div(p.K, BK), acc, threadIdx.x))
+        T::epilogue(p, tm * BM, tn * BN, acc, threadIdx.x);
+}
 
-    const float *__restrict__ A = p.A + (int64_t)blockIdx.z * p.strideA;
-    const float *__restrict__ B = p.B + (int64_t)blockIdx.z * p.strideB;
-    float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
-    const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+// Work split of a stream-K launch (computed on the host).
+struct StreamK {
+    float *partials;        // 2 slots of BM*BN floats per workgroup: its first and its last tile
+    unsigned *counters;     // one per tile; zero before the launch, left zero after it
+    int tiles_m, tiles_n;
+    int iters;              // K-tiles per output tile, I
+    int group_m;
+    int work;               // tiles * I, the K-tile steps of the whole product; (grid+1)*work < 2^31
+};
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wk = wave / (WGM * WGN);
-    const int wm = (wave % (WGM * WGN)) / WGN, wn = wave % WGN;
-    const int l32 = lane & 31, half = lane >> 5;
+// Stream-K: the tiles * I K-tile steps of the product, taken in tile order, are split
+// into gridDim.x equal contiguous ranges, one per workgroup, so every CU does the same
+// amount of work whatever the tile count. The grid is at most the number of steps, so
+// no range is empty and the workgroups whose ranges meet a tile are exactly those
+// between the owners of its first and last step. A workgroup walks its range tile by tile. A
+// tile wholly inside the range gets the ordinary epilogue. A tile the range covers only
+// in part leaves its partial sum in the workgroup's slot and takes a ticket from the
+// tile's counter; the contributor that draws the last ticket adds the partial sums in
+// contributor order (the same order whoever comes last, so results do not depend on
+// timing) and writes C. No workgroup ever waits for another.
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
+          bool EDGE>
+__global__ void __launch_bounds__(WGM * WGN * WGK * 64)
+sgemm_mfma_sk(GemmArgs p, StreamK sk)
+{
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE>;
+    constexpr int TILE = BM * BN;
+    constexpr int PER_WAVE = T::TM * T::TN * 16 * 64;   // one wave's accumulators
+    __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
+    __shared__ unsigned ticket;
 
-    // PF sets of staging registers: with PF = 2 a K-tile's global loads are issued two
-    // stages before it is multiplied. `slot` is always a compile-time constant after
-    // inlining, so the sets stay in registers.
-    floatx4 ra[USE_DMA ? 1 : PF][AIO::CH], rb[USE_DMA ? 1 : PF][BIO::CH];
+    const int G = gridDim.x;
+    const int g = xcd_contiguous(blockIdx.x, G);         // neighbouring ranges share an XCD's L2
+    const int W = sk.work;
+    const int I = sk.iters;
+    auto range_start = [&](int wg) { return wg * W / G; };
+    auto owner = [&](int w) { return ((w + 1) * G - 1) / W; };   // workgroup whose range holds w
+    auto slot_of = [&](int wg, int t) { return t == range_start(wg) / I ? 0 : 1; };
 
-    // Global -> registers set `slot` for the K-tile starting at k0 (zero outside the matrix).
-    auto load_tile = [&](int k0, int slot) __attribute__((always_inline)) {
-        if constexpr (!USE_DMA) {
-            if constexpr (TA)
-                AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, tid);
-            else
-                AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, tid);
-            if constexpr (TB)
-                BIO::template load<VEC, EDGE>(rb[slot], B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, tid);
-            else
-                BIO::template load<VEC, EDGE>(rb[slot], B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, tid);
-        }
-    };
-
-    // Registers set `slot` -> LDS stage `st`.
-    auto store_tile = [&](int st, int slot) __attribute__((always_inline)) {
-        if constexpr (!USE_DMA) {
-            float *As = smem + st * STAGE;
-            AIO::store(ra[slot], As, tid);
-            BIO::store(rb[slot], As + AIO::SIZE, tid);
-        }
-    };
-
-    // Direct copies of the K-tile starting at k0 into LDS stage `st` (DMA path).
-    auto copy_tile = [&](int k0, int st) __attribute__((always_inline)) {
-        if constexpr (USE_DMA) {
-            float *As = smem + st * STAGE;
-            if constexpr (TA)
-                AIO::template load<EDGE>(A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, As, tid);
-            else
-                AIO::template load<EDGE>(A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, As, tid);
-            if constexpr (TB)
-                BIO::template load<EDGE>(B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, As + AIO::SIZE, tid);
-            else
-                BIO::template load<EDGE>(B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, As + AIO::SIZE, tid);
-        }
-    };
-
-    floatx16 acc[TM][TN];
+    const int w_end = range_start(g + 1);
+    for (int w = range_start(g); w < w_end;) {
+        const int t = w / I;
+        const int kt0 = w - t * I;
+        const int kt1 = (w_end - t * I) < I ? (w_end - t * I) : I;
+        int tm, tn;
+        band_coords(t, sk.tiles_m, sk.tiles_n, sk.group_m, tm, tn);
+        floatx16 acc[T::TM][T::TN];
+        // The thread index passes through an empty asm statement on every tile, so the
+        // per-lane addresses are recomputed per tile instead of being hoisted out of
+        // this loop and held (with the accumulators) across the fixup and epilogue.
+        int tid_l = threadIdx.x;
+        asm volatile("" : "+v"(tid_l));
+        const int lane = tid_l & 63, wslot = (tid_l >> 6) % (WGM * WGN);
+        const bool holds = T::product(p, smem, tm * BM, tn * BN, kt0, kt1, acc, tid_l);
+        bool finish = kt0 == 0 && kt1 == I;              // the whole tile is this workgroup's
+        if (!finish) {
+            const int first = owner(t * I), last = owner(t * I + I - 1);
+            // Partial sums travel through device-coherent accesses (device-scope relaxed
+            // atomics, which bypass the XCD's non-coherent L2 copy) rather than fences: a
+            // device-scope fence writes back and invalidates the whole L2 of the XCD.
+            if (holds) {
+                float *dst = sk.partials + ((int64_t)g * 2 + slot_of(g, t)) * TILE + wslot * PER_WAVE;
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+                for (int a = 0; a < T::TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
+                    for (int b = 0; b < T::TN; ++b)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[a][b][e] = 0.f;
-
-    // This lane's first row of A / column of B inside the tile: plain A rows are
-    // a*32 + l32 (blocks side by side), transposed A rows l32*TM + a (interleaved);
-    // likewise for B columns with the roles swapped.
-    const int a_idx = wm * WTM + (TA ? l32 * TM : l32);
-    const int b_idx = wn * WTN + (TB ? l32 : l32 * TN);
-
-    // One stage: KSLICE/8 groups of 8 k values, 4 matrix steps each.
-    auto compute = [&](int st) __attribute__((always_inline)) {
-        const float *As = smem + st * STAGE;
-        const float *Bs = As + AIO::SIZE;
-#pragma unroll
-        for (int kk = 0; kk < KSLICE; kk += 8) {
-            const int kg = wk * KSLICE + kk;
-            floatx4 af[TA ? 1 : TM], bf[TB ? TN : 1];
-            if constexpr (!TA) {
-#pragma unroll
-                for (int a = 0; a < TM; ++a)
-                    af[a] = *reinterpret_cast<const floatx4 *>(&As[AIO::elem(a_idx + a * 32, kg + 4 * half)]);
+                        for (int e = 0; e < 16; ++e)
+                            __hip_atomic_store(&dst[((a * T::TN + b) * 16 + e) * 64 + lane], acc[a][b][e],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            if constexpr (TB) {
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    bf[b] = *reinterpret_cast<const floatx4 *>(&Bs[BIO::elem(b_idx + b * 32, kg + 4 * half)]);
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k = kg + 4 * half + s;
-                float av[TM], bv[TN];
-                if constexpr (TA) {
-                    lds_read<TM>(&As[AIO::elem(k, a_idx)], av);
-                } else {
-#pragma unroll
-                    for (int a = 0; a < TM; ++a)
-                        av[a] = af[a][s];
-                }
-                if constexpr (TB) {
-#pragma unroll
-                    for (int b = 0; b < TN; ++b)
-                        bv[b] = bf[b][s];
-                } else {
-                    lds_read<TN>(&Bs[BIO::elem(k, b_idx)], bv);
-                }
-#pragma unroll
-                for (int a = 0; a < TM; ++a)
-#pragma unroll
-                    for (int b = 0; b < TN; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
-            }
-        }
-    };
-
-    // Fragment form used by the direct-copy pipeline: the A and B values of one group
-    // of 8 k (4 per lane) for every block, read from LDS in one batch, so the reads of
-    // the next group can be in flight while this one is multiplied.
-    constexpr int NG = KSLICE / 8;                      // groups of 8 k per stage and wave group
-    float fa[USE_DMA ? 2 : 1][4][TM], fb[USE_DMA ? 2 : 1][4][TN];
-    auto read_frag = [&](int st, int g, int buf) __attribute__((always_inline)) {
-        const float *As = smem + st * STAGE;
-        const float *Bs = As + AIO::SIZE;
-        const int kg = wk * KSLICE + 8 * g + 4 * half;
-        if constexpr (TA) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                lds_read<TM>(&As[AIO::elem(kg + s, a_idx)], fa[buf][s]);
-        } else {
-#pragma unroll
-            for (int a = 0; a < TM; ++a) {
-                const floatx4 v = *reinterpret_cast<const floatx4 *>(&As[AIO::elem(a_idx + a * 32, kg)]);
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    fa[buf][s][a] = v[s];
-            }
-        }
-        if constexpr (TB) {
-#pragma unroll
-            for (int b = 0; b < TN; ++b) {
-                const floatx4 v = *reinterpret_cast<const floatx4 *>(&Bs[BIO::elem(b_idx + b * 32, kg)]);
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    fb[buf][s][b] = v[s];
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                lds_read<TN>(&Bs[BIO::elem(kg + s, b_idx)], fb[buf][s]);
-        }
-    };
-    auto mma_frag = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[buf][s][a], fb[buf][s][b], acc[a][b], 0, 0, 0);
-    };
-
-    // Pipeline over nk K-tiles, one barrier per K-tile.
-    const int nk = ceil_div(K, BK);
-    if constexpr (USE_DMA) {
-        // PF + 1 LDS stages. Step t queues the copies of tile t+PF into stage (t+PF) %
-        // NSTAGE (read last during step t-1, so free after that step's barrier),
-        // multiplies stage t % NSTAGE, waits until its own copies of tile t+1 have landed
-        // (the PF-1 newer tiles may stay in flight) and meets the others at the barrier.
-        // Past the end the last tile is copied again, so the count of copies in flight
-        // is the same on every step.
-        // Inside a step, group g+1's fragments are read while group g is multiplied; the
-        // last group is multiplied after the barrier, while group 0 of the next stage
-        // is read (past the last step that read is of a stage nobody uses; harmless).
-        static_assert(NG % 2 == 0, "fragment buffers alternate within a stage");
-        constexpr int COPIES = AIO::CH + BIO::CH;       // copy instructions per thread per tile
-#pragma unroll
-        for (int q = 0; q < PF; ++q)
-            copy_tile((q < nk ? q : nk - 1) * BK, q);
-        wait_vmcnt<0>();
-        __syncthreads();
-        read_frag(0, 0, 0);
-        for (int t = 0; t < nk; ++t) {
-            const int ahead = t + PF < nk ? t + PF : nk - 1;
-            copy_tile(ahead * BK, (t + PF) % NSTAGE);
-            const int st = t % NSTAGE;
-#pragma unroll
-            for (int g = 0; g + 1 < NG; ++g) {
-                read_frag(st, g + 1, (g + 1) & 1);
-                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-                mma_frag(g & 1);
-            }
-            copy_barrier<(PF - 1) * COPIES>();
-            read_frag((t + 1) % NSTAGE, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            mma_frag(1);
-        }
-        wait_vmcnt<0>();    // no copy may still write LDS once it is reused or released
-    } else if constexpr (PF == 1) {
-        load_tile(0, 0);
-        store_tile(0, 0);
-        __syncthreads();
-        for (int t = 0; t + 1 < nk; ++t) {
-            load_tile((t + 1) * BK, 0);  // in flight while this stage is multiplied
-            compute(t & 1);
-            store_tile((t + 1) & 1, 0);  // other stage: its last reader finished before the previous barrier
+            // Publish: this wave's stores are acknowledged, then every wave meets, then one
+            // ticket is drawn.
+            wait_vmcnt<0>();
             __syncthreads();
-        }
-    } else {
-        // Entering step t: stage t%2 holds K-tile t, register set (t+1)%2 holds tile t+1
-        // (loaded during step t-1) and set t%2 is free. Step t loads tile t+2 into set
-        // t%2 (the last tile again once past the end, so the load needs no condition),
-        // multiplies stage t%2, then stores set (t+1)%2 into stage (t+1)%2.
-        auto step = [&](int t, int s) __attribute__((always_inline)) {
-            const int ahead = t + 2 < nk ? t + 2 : nk - 1;
-            load_tile(ahead * BK, s);
-            compute(s);
-            store_tile(1 - s, 1 - s);
+            if (tid_l == 0)
+                ticket = __hip_atomic_fetch_add(&sk.counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
-        };
-        load_tile(0, 0);
-        load_tile((nk > 1 ? 1 : 0) * BK, 1);
-        store_tile(0, 0);
-        __syncthreads();
-        int t = 0;
-        for (; t + 2 < nk; t += 2) {     // steps t and t+1, both before the last tile
-            step(t, 0);
-            step(t + 1, 1);
-        }
-        if (t + 1 < nk) {
-            step(t, 0);
-            ++t;
-        }
-    }
-    if constexpr (!USE_DMA)
-        compute((nk - 1) & 1);
-
-    if constexpr (WGK > 1) {
-        // Groups 1..WGK-1 hand their partial sums to group 0 through LDS (the ring is
-        // free once every wave has passed the barrier); group 0 adds them in group order.
-        constexpr int PER_WAVE = TM * TN * 16 * 64;
-        const int slot = wm * WGN + wn;
-        __syncthreads();
-        if (wk > 0) {
-            float *dst = smem + ((wk - 1) * (WGM * WGN) + slot) * PER_WAVE;
+            finish = ticket == (unsigned)(last - first);
+            if (finish) {
+                // Every contributor's partial, this workgroup's included, is in its slot: sum
+                // them in contributor order straight into acc.
+                for (int c = first; holds && c <= last; ++c) {
+                    const float *src = sk.partials + ((int64_t)c * 2 + slot_of(c, t)) * TILE + wslot * PER_WAVE;
 #pragma unroll
-            for (int a = 0; a < TM; ++a)
+                    for (int a = 0; a < T::TM; ++a)
 #pragma unroll
-                for (int b = 0; b < TN; ++b)
+                        for (int b = 0; b < T::TN; ++b)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        dst[((a * TN + b) * 16 + e) * 64 + lane] = acc[a][b][e];
-        }
-        __syncthreads();
-        if (wk > 0)
-            return;
-#pragma unroll
-        for (int g = 1; g < WGK; ++g) {
-            const float *src = smem + ((g - 1) * (WGM * WGN) + slot) * PER_WAVE;
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        acc[a][b][e] += src[((a * TN + b) * 16 + e) * 64 + lane];
-        }
-    }
-
-    // Epilogue: C = act(alpha*acc + beta*C + bias), C unread when beta == 0. One 32-row
-    // block at a time: all of the block's reads of C are issued before the first is
-    // used, so the block waits out one memory round trip (two with EB = 8) rather than
-    // one per entry. Lane columns: TN consecutive ones (plain B), or one per 32-column block
-    // (transposed B). Rows: those of accumulator element e, see the mapping above.
-    const float alpha = p.alpha, beta = p.beta;
-    const float *bias = p.bias;
-    const int act = p.act;
-    const bool read_c = beta != 0.f, has_bias = bias != nullptr;
-    const bool full = !EDGE || (m0 + BM <= M && n0 + BN <= N);   // whole tile inside C
-    // 128- or 64-bit accesses of a lane's TN consecutive columns: aligned, and (N % 4 == 0,
-    // first column a multiple of TN) the group is either wholly inside C or wholly out.
-    constexpr bool VCOL = VEC && !TB && (TN == 2 || TN == 4);
-    int gc[TN];
-#pragma unroll
-    for (int b = 0; b < TN; ++b)
-        gc[b] = n0 + b_idx + (TB ? 32 * b : b);
-    float bj[TN];
-#pragma unroll
-    for (int b = 0; b < TN; ++b)
-        bj[b] = (has_bias && (full || gc[b] < N)) ? bias[gc[b]] : 0.f;
-    auto row_of = [&](int a, int e) __attribute__((always_inline)) {
-        const int r = 8 * (e / 4) + 4 * half + (e % 4);          // row inside the 32x32 block
-        return m0 + wm * WTM + (TA ? r * TM + a : a * 32 + r);
-    };
-    // Entries per batch of reads: 16 (the whole block), or 8 where four waves share a
-    // SIMD and each has only 128 registers.
-    constexpr int EB = NT >= 1024 ? 8 : 16;
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-    for (int e0 = 0; e0 < 16; e0 += EB) {
-        float cv[16][TN];
-        if (read_c) {
-#pragma unroll
-            for (int e = e0; e < e0 + EB; ++e) {
-                const int gr = row_of(a, e);
-                const float *crow = C + (int64_t)gr * ldc;
-                if constexpr (VCOL) {
-                    using vec_t = typename std::conditional<TN == 4, floatx4, floatx2>::type;
-                    vec_t v{};
-                    if (full || (gr < M && gc[0] < N))
-                        v = *reinterpret_cast<const vec_t *>(crow + gc[0]);
-#pragma unroll
-                    for (int b = 0; b < TN; ++b)
-                        cv[e][b] = v[b];
-                } else {
-#pragma unroll
-                    for (int b = 0; b < TN; ++b)
-                        cv[e][b] = (full || (gr < M && gc[b] < N)) ? crow[gc[b]] : 0.f;
+                            for (int e = 0; e < 16; ++e) {
+                                const float v = __hip_atomic_load(&src[((a * T::TN + b) * 16 + e) * 64 + lane],
+                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                acc[a][b][e] = c == first ? v : acc[a][b][e] + v;
+                            }
                 }
+                if (tid_l == 0)                          // ready for the next launch
+                    __hip_atomic_store(&sk.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-#pragma unroll
-        for (int e = e0; e < e0 + EB; ++e) {
-            const int gr = row_of(a, e);
-            float *crow = C + (int64_t)gr * ldc;
-            float out[TN];
-#pragma unroll
-            for (int b = 0; b < TN; ++b)
-                out[b] = finish_value(acc[a][b][e], alpha, beta, read_c ? cv[e][b] : 0.f, has_bias, bj[b], act);
-            if constexpr (VCOL) {
-                using vec_t = typename std::conditional<TN == 4, floatx4, floatx2>::type;
-                vec_t v;
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    v[b] = out[b];
-                if (full || (gr < M && gc[0] < N))
-                    *reinterpret_cast<vec_t *>(crow + gc[0]) = v;
-            } else {
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    if (full || (gr < M && gc[b] < N))
-                        crow[gc[b]] = out[b];
-            }
-        }
+        if (finish && holds)
+            T::epilogue(p, tm * BM, tn * BN, acc, tid_l);
+        w = (t + 1) * I;
+        __syncthreads();                                 // the LDS ring is reused by the next tile
     }
 }
 

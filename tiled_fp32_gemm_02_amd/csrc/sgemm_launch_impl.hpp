@@ -28,4 +28,21 @@ hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, hip
     return hipGetLastError();
 }
 
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, bool TA, bool TB>
+hipError_t launch_mfma_sk_op(const GemmArgs &p, const StreamK &sk, int grid, bool vec, bool edge, hipStream_t s)
+{
+    static_assert(!DMA, "stream-K counts K-tiles of BK in every variant");
+    const dim3 block(WGM * WGN * WGK * 64);
+    if (vec && !edge)
+        hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, false>), dim3(grid),
+                           block, 0, s, p, sk);
+    else if (vec)
+        hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, true>), dim3(grid),
+                           block, 0, s, p, sk);
+    else    // unaligned operands: the data-parallel kernel of the same tile (see launch_mfma_op)
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, 1, false, TA, TB, false, true>),
+                           dim3(sk.tiles_m * sk.tiles_n), block, 0, s, p, GROUP_M);
+    return hipGetLastError();
+}
+
 }  // namespace sgemm_impl
