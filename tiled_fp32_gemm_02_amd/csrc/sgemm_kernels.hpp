@@ -368,6 +368,12 @@ struct MfmaTile {
     static_assert(BK % (8 * WGK) == 0, "each wave group consumes k in groups of 8");
     static constexpr int RED = (WGK - 1) * BM * BN;         // partial sums of groups 1..WGK-1
     static constexpr int SMEM = NSTAGE * STAGE > RED ? NSTAGE * STAGE : RED;
+    // Double-buffered fragment reads (next group's reads in flight while this group is
+    // multiplied). Measured on MI355X: a gain for the direct-copy loop, for one K-tile
+    // in flight and for waves holding a single 32x32 block; with two K-tiles in flight and
+    // larger wave tiles the extra registers cost more than the overlap gains (the 256x256
+    // kernel would spill), so those keep single fragments read next to their use.
+    static constexpr bool FRAG = USE_DMA || PF == 1 || TM * TN == 1;
     static_assert(SMEM * 4 <= 160 * 1024, "LDS exceeds 160 KiB");
 
     // Multiply K-tiles [kt0, kt1) of the tile at (m0, n0) into acc, which starts at zero;
@@ -498,7 +504,7 @@ struct MfmaTile {
         // of 8 k (4 per lane) for every block, read from LDS in one batch, so the reads of
         // the next group can be in flight while this one is multiplied.
         constexpr int NG = KSLICE / 8;                      // groups of 8 k per stage and wave group
-        float fa[USE_DMA ? 2 : 1][4][TM], fb[USE_DMA ? 2 : 1][4][TN];
+        float fa[FRAG ? 2 : 1][4][TM], fb[FRAG ? 2 : 1][4][TN];
         auto read_frag = [&](int st, int g, int buf) __attribute__((always_inline)) {
             const float *As = smem + st * STAGE;
             const float *Bs = As + AIO::SIZE;
@@ -578,31 +584,72 @@ struct MfmaTile {
             }
             wait_vmcnt<0>();    // no copy may still write LDS once it is reused or released
         } else if constexpr (PF == 1) {
+            static_assert(NG % 2 == 0, "fragment buffers alternate within a stage");
             load_tile(0, 0);
             store_tile(0, 0);
             __syncthreads();
+            read_frag(0, 0, 0);
             for (int t = 0; t + 1 < nk; ++t) {
                 load_tile((t + 1) * BK, 0);  // in flight while this stage is multiplied
-                compute(t & 1);
+#pragma unroll
+                for (int g = 0; g + 1 < NG; ++g) {
+                    read_frag(t & 1, g + 1, (g + 1) & 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma_frag(g & 1);
+                }
                 store_tile((t + 1) & 1, 0);  // other stage: its last reader finished before the previous barrier
                 __syncthreads();
+                read_frag((t + 1) & 1, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_frag(1);
             }
+#pragma unroll
+            for (int g = 0; g + 1 < NG; ++g) {
+                read_frag((nk - 1) & 1, g + 1, (g + 1) & 1);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_frag(g & 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mma_frag(1);
         } else {
             // Entering step t: stage t%2 holds K-tile t, register set (t+1)%2 holds tile t+1
             // (loaded during step t-1) and set t%2 is free. Step t loads tile t+2 into set
             // t%2 (the last tile again once past the end, so the load needs no condition),
             // multiplies stage t%2, then stores set (t+1)%2 into stage (t+1)%2.
+            // With FRAG, fragments are double-buffered as in the direct-copy loop: group g+1's
+            // reads are in flight while group g is multiplied, and the next stage's first group
+            // is read right after the barrier, while this stage's last group is multiplied.
+            static_assert(!FRAG || NG % 2 == 0, "fragment buffers alternate within a stage");
+            auto groups = [&](int st) __attribute__((always_inline)) {
+                if constexpr (FRAG) {
+#pragma unroll
+                    for (int g = 0; g + 1 < NG; ++g) {
+                        read_frag(st, g + 1, (g + 1) & 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mma_frag(g & 1);
+                    }
+                } else {
+                    compute(st);
+                }
+            };
             auto step = [&](int t, int s) __attribute__((always_inline)) {
                 const int ahead = t + 2 < nk ? t + 2 : nk - 1;
                 load_tile(ahead * BK, s);
-                compute(s);
+                groups(s);
                 store_tile(1 - s, 1 - s);
                 __syncthreads();
+                if constexpr (FRAG) {
+                    read_frag(1 - s, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma_frag(1);
+                }
             };
             load_tile(0, 0);
             load_tile((nk > 1 ? 1 : 0) * BK, 1);
             store_tile(0, 0);
             __syncthreads();
+            if constexpr (FRAG)
+                read_frag(0, 0, 0);
             int t = 0;
             for (; t + 2 < nk; t += 2) {     // steps t and t+1, both before the last tile
                 step(t, 0);
@@ -612,9 +659,12 @@ struct MfmaTile {
                 step(t, 0);
                 ++t;
             }
+            groups((nk - 1) & 1);            // the last tile: no next stage to read
+            if constexpr (FRAG) {
+                __builtin_amdgcn_sched_barrier(0);
+                mma_frag(1);
+            }
         }
-        if constexpr (!USE_DMA)
-            compute((nk - 1) & 1);
 
         if constexpr (WGK > 1) {
             // Groups 1..WGK-1 hand their partial sums to group 0 through LDS (the ring is
