@@ -156,7 +156,7 @@ def test_auto_choice_with_workspace(ws):
         cid = sg.sgemm_select_config_ws(M, N, K, 1.0, ws.data_ptr(), K, ws.data_ptr(), N, ws.data_ptr(), N,
                                         ws.numel())
         picks[(M, N, K)] = names[cid]
-    assert picks[(4096, 4096, 4096)] == "mfma_256x256x16_w2x4p2"      # one whole tile per CU already
+    assert picks[(4096, 4096, 4096)] == "mfma_256x256x32_w2x4d"       # one whole tile per CU already
     assert picks[(1024, 768, 3072)].startswith("sk_")                # 48..96 tiles for 256 CUs
 
 

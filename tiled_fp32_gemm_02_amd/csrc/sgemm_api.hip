@@ -73,7 +73,7 @@ int device_cus()
 
 // Row strides (floats) from which the direct-copy kernels' 32-bit in-tile offsets
 // could overflow; such calls take the element-wise (unaligned) variant instead.
-constexpr int kDmaMaxLd = 1 << 24;
+constexpr int kDmaMaxLd = 1 << 20;
 
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M>
 hipError_t launch_mfma(const GemmArgs &p, int batch, bool ta, bool tb, bool vec, bool edge, hipStream_t s)
@@ -166,10 +166,11 @@ bool sk_work_fits(const Config &c, int M, int N, int K, int cus)
 // Auto-selection by a small cost model of the kernel time.
 //
 // Data-parallel candidates: the tiles spread over the CUs take L = ceil(tiles / CUs)
-// rounds on the busiest CU, so the time is L tiles of work (one unit is a 64x64 tile,
-// 2 * 64 * 64 * K flop) at the CU's throughput with that many tiles resident.
-// Throughputs (fp32 TFLOP/s per CU) were measured on MI355X with the whole chip busy:
-// rate_one when a CU holds a single workgroup, rate_many when it holds several.
+// rounds on the busiest CU, so the time is a fixed cost (launch, first loads, last
+// epilogue) plus L tiles of work (one unit is a 64x64 tile, 2 * 64 * 64 * K flop) at the
+// CU's throughput with that many tiles resident. Throughputs (fp32 TFLOP/s per CU) were
+// measured on MI355X with the whole chip busy: rate_one when a CU holds a single
+// workgroup, rate_many when it holds several.
 //
 // Stream-K candidates (only with a large enough workspace): every CU gets the same
 // share, tiles * units / CUs, at the one-workgroup rate, plus a fixed cost for the
@@ -180,25 +181,24 @@ struct Candidate {
     int units;          // tile area / (64 * 64)
     double rate_one;    // per-CU rate with one resident workgroup
     double rate_many;   // per-CU rate with two or more
-    double fixed_us;    // stream-K only: cost of combining partial tiles
+    double fixed_us;    // time that does not scale with the work
 };
 
-// Rates measured with every candidate prefetching two K-tiles ahead; fitted to the
-// sweep over 256^3 ... 4096^3, the GPT-2 linear layers and the 1000 x 1537 x 777
-// unaligned case (which the same table serves).
+// Least-squares fit (relative error) of time = fixed + work / rate to a sweep over
+// 256^3 ... 6144^3, 512 x 4096 x 4096 and the GPT-2-small linear layers, all aligned.
+// On every shape of the sweep the model picks the fastest candidate or one within 1%; on
+// the unaligned 1000 x 1537 x 777 product (where the direct-copy candidates run their
+// register-staged variants) it loses 3% to the fastest.
 const Candidate kCandidates[] = {
-    {"mfma_256x256x16_w2x4p2", 16, 0.500, 0.500, 0.0},     // one workgroup per CU
-    {"mfma_128x128x32_w2x2k2p2", 4, 0.484, 0.466, 0.0},    // one per CU
-    {"mfma_64x128x32_w2x2k2p2", 2, 0.459, 0.461, 0.0},     // up to two per CU
-    {"mfma_64x64x64_w2x2k4p2", 1, 0.380, 0.390, 0.0},      // one per CU, 16 waves
-    {"mfma_64x64x32_w2x2k2p2", 1, 0.360, 0.410, 0.0},      // up to four per CU
+    {"mfma_256x256x32_w2x4d", 16, 0.591, 0.580, 7.5},      // one workgroup per CU
+    {"mfma_128x128x32_w2x2k2d", 4, 0.555, 0.573, 5.4},     // up to two per CU
+    {"mfma_64x128x32_w2x2k2d", 2, 0.534, 0.556, 4.3},      // up to three per CU
+    {"mfma_64x64x64_w2x2k4d", 1, 0.539, 0.479, 5.9},       // one per CU, 16 waves
+    {"mfma_64x64x32_w2x2k2d", 1, 0.457, 0.507, 6.1},       // up to four per CU
 };
-// Stream-K rates and fixed costs fitted to 1024^3, 3072^3 and the GPT-2 layers (time =
-// work / (CUs * rate) + fixed): the fixed part covers the per-range pipeline fill, the
-// partial-tile traffic and the last contributor's serial epilogue.
 const Candidate kSkCandidates[] = {
-    {"sk_128x128x32_w2x2k2p2", 4, 0.50, 0.50, 16.0},
-    {"sk_64x128x32_w2x2k2p2", 2, 0.46, 0.46, 9.0},
+    {"sk_128x128x32_w2x2k2p2", 4, 0.534, 0.534, 17.1},
+    {"sk_64x128x32_w2x2k2p2", 2, 0.502, 0.502, 12.2},
 };
 constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
 constexpr int kNumSkCandidates = sizeof(kSkCandidates) / sizeof(kSkCandidates[0]);
@@ -240,7 +240,8 @@ int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0)
             continue;
         const uint64_t tiles = tile_count(kConfigs[ids.id[i]], M, N);
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
-        const double us = (double)rounds * cand.units * unit_mflop / (rounds >= 2 ? cand.rate_many : cand.rate_one);
+        const double us =
+            cand.fixed_us + (double)rounds * cand.units * unit_mflop / (rounds >= 2 ? cand.rate_many : cand.rate_one);
         if (best < 0 || us < best_us) {
             best = ids.id[i];
             best_us = us;

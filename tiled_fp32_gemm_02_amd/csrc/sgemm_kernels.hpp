@@ -197,6 +197,9 @@ struct TileIO {
         }
     }
 
+    struct Lane {};     // register staging keeps no per-lane copy plan
+    __device__ __forceinline__ static Lane plan(int64_t, int) { return Lane{}; }
+
     __device__ __forceinline__ static void store(const floatx4 (&r)[CH], float *lds, int tid)
     {
 #pragma unroll
@@ -223,8 +226,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 //    row, and rows 4 apart (the two half-waves) use opposite halves of each 16-slot window.
 // Chunks outside the matrix are fetched at an offset past the buffer's range, which
 // the hardware answers with zeros, so partial tiles arrive zero-padded as in TileIO.
-// Needs 16-byte aligned rows and pointers (the VEC kernels) and row strides below 2^24
-// floats (the byte offsets inside one instruction's rows stay below 2^30).
+// Needs 16-byte aligned rows and pointers (the VEC kernels) and row strides below 2^20
+// floats (every byte offset from the tile origin stays below 2^31).
 template <int TR, int TC, int NT, bool KCONTIG>
 struct TileDMA {
     static constexpr int CPR = TC / 4;
@@ -246,26 +249,48 @@ struct TileDMA {
         return 4 * (r * CPR + ((col >> 2) ^ swz(r))) + (col & 3);
     }
 
-    // Queue this thread's copies of the tile at src (row stride ld) into lds; rows/cols
-    // are how many rows and columns from the origin lie inside the matrix (EDGE only).
-    template <bool EDGE>
-    __device__ __forceinline__ static void load(const float *src, int64_t ld, int rows, int cols, float *lds,
-                                                int tid)
+    // This lane's share of every copy of the tile, fixed for the whole K loop: per copy
+    // instruction, the byte offset of its global chunk from the tile origin (row stride
+    // ld floats), and that chunk's row and first column inside the tile (for edge checks).
+    // Offsets stay below 2^31 for row strides below 2^20 floats and TR <= 256.
+    struct Lane {
+        unsigned off[CH];
+        int row[CH], col[CH];
+    };
+    __device__ __forceinline__ static Lane plan(int64_t ld, int tid)
     {
-        const int lane = tid & 63;
-        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: resource and LDS base in SGPRs
+        Lane L;
+        const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int s0 = wave * 64 + c * NT;          // first slot of this wave's copy
-            const int r0 = s0 / CPR;                    // its first row (same for the whole wave)
             const int q = s0 % CPR + lane;
-            const int dr = q / CPR, r = r0 + dr, chunk = (q % CPR) ^ swz(r);
-            unsigned off = static_cast<unsigned>((dr * ld + 4 * chunk) * 4);
-            if (EDGE && !(r < rows && 4 * chunk < cols))
+            const int r = s0 / CPR + q / CPR, chunk = (q % CPR) ^ swz(r);
+            L.off[c] = static_cast<unsigned>(((int64_t)r * ld + 4 * chunk) * 4);
+            L.row[c] = r;
+            L.col[c] = 4 * chunk;
+        }
+        return L;
+    }
+
+    // Queue this thread's copies of the tile whose origin is src into lds; rows/cols are
+    // how many rows and columns from the origin lie inside the matrix (EDGE only). The
+    // buffer resource (one per tile, wave-uniform) and the LDS destinations are the only
+    // per-step address work.
+    template <bool EDGE>
+    __device__ __forceinline__ static void load(const Lane &L, const float *src, int rows, int cols, float *lds,
+                                                int tid)
+    {
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS base in M0
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), 0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            unsigned off = L.off[c];
+            if (EDGE && !(L.row[c] < rows && L.col[c] < cols))
                 off = 0x80000000u;                      // past num_records: reads as zeros
-            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<float *>(src + (int64_t)r0 * ld), 0, 0x7fffffff, 0x00020000);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + 4 * s0), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + 4 * (wave * 64 + c * NT)), 16, off,
+                                                     0, 0, 0);
         }
     }
 };
@@ -373,7 +398,11 @@ struct MfmaTile {
     // in flight and for waves holding a single 32x32 block; with two K-tiles in flight and
     // larger wave tiles the extra registers cost more than the overlap gains (the 256x256
     // kernel would spill), so those keep single fragments read next to their use.
-    static constexpr bool FRAG = USE_DMA || PF == 1 || TM * TN == 1;
+    // Waves per SIMD the register budget is sized for: one for waves holding 16 or more
+    // 32x32 blocks (256 accumulators; the wave gets the whole 512-register file), else at
+    // least two, so that two 256-thread workgroups fit on a CU.
+    static constexpr int WPE = TM * TN >= 16 ? 1 : (NT >= 512 ? NT / 256 : 2);
+    static constexpr bool FRAG = USE_DMA || PF == 1 || TM * TN == 1 || WPE == 1;
     static_assert(SMEM * 4 <= 160 * 1024, "LDS exceeds 160 KiB");
 
     // Multiply K-tiles [kt0, kt1) of the tile at (m0, n0) into acc, which starts at zero;
@@ -425,19 +454,21 @@ struct MfmaTile {
         };
 
         // Direct copies of the K-tile starting kr after the range's first k into LDS stage `st`
-        // (DMA path).
+        // (DMA path). Each lane's offsets inside a tile are the same for every K-tile.
+        const typename AIO::Lane a_lane = AIO::plan(lda, tid);
+        const typename BIO::Lane b_lane = BIO::plan(ldb, tid);
         auto copy_tile = [&](int kr, int st) __attribute__((always_inline)) {
             if constexpr (USE_DMA) {
                 const int k0 = kbase + kr;
                 float *As = smem + st * STAGE;
                 if constexpr (TA)
-                    AIO::template load<EDGE>(A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, As, tid);
+                    AIO::template load<EDGE>(a_lane, A + (int64_t)k0 * lda + m0, K - k0, M - m0, As, tid);
                 else
-                    AIO::template load<EDGE>(A + (int64_t)m0 * lda + k0, lda, M - m0, K - k0, As, tid);
+                    AIO::template load<EDGE>(a_lane, A + (int64_t)m0 * lda + k0, M - m0, K - k0, As, tid);
                 if constexpr (TB)
-                    BIO::template load<EDGE>(B + (int64_t)n0 * ldb + k0, ldb, N - n0, K - k0, As + AIO::SIZE, tid);
+                    BIO::template load<EDGE>(b_lane, B + (int64_t)n0 * ldb + k0, N - n0, K - k0, As + AIO::SIZE, tid);
                 else
-                    BIO::template load<EDGE>(B + (int64_t)k0 * ldb + n0, ldb, K - k0, N - n0, As + AIO::SIZE, tid);
+                    BIO::template load<EDGE>(b_lane, B + (int64_t)k0 * ldb + n0, K - k0, N - n0, As + AIO::SIZE, tid);
             }
         };
 
@@ -794,6 +825,7 @@ struct MfmaTile {
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
           bool EDGE>
 __global__ void __launch_bounds__(WGM * WGN * WGK * 64)
+__attribute__((amdgpu_waves_per_eu(MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE>::WPE)))
 sgemm_mfma(GemmArgs p, int group_m)
 {
     using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE>;

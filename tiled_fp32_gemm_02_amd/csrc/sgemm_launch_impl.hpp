@@ -31,7 +31,6 @@ hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, hip
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, bool TA, bool TB>
 hipError_t launch_mfma_sk_op(const GemmArgs &p, const StreamK &sk, int grid, bool vec, bool edge, hipStream_t s)
 {
-    static_assert(!DMA, "stream-K counts K-tiles of BK in every variant");
     const dim3 block(WGM * WGN * WGK * 64);
     if (vec && !edge)
         hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, false>), dim3(grid),
