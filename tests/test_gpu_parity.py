@@ -161,6 +161,23 @@ def test_alignment_and_leading_dimensions(offsets, ld_pad):
         check_against_oracle(M, N, K, 0.75, A, K, B, N, 1.5, C, N, out, checks, f"config {cid}")
 
 
+@pytest.mark.parametrize("lda", [(1 << 20) - 4, 1 << 20])
+def test_long_rows_of_A(lda):
+    """Row strides at the direct-copy limit: just below 2^20 floats the copies' byte offsets
+    inside a 256-row tile reach 2^30; from 2^20 on the call takes the element-wise path.
+    Both must agree with the oracle, on the direct-copy configurations and the auto choice."""
+    import tiled_fp32_gemm_02_amd as sg
+    rng = np.random.default_rng(37)
+    M, N, K = 260, 36, 40
+    A, B, C = draw(rng, (M, K), "normal"), draw(rng, (K, N), "normal"), draw(rng, (M, N), "normal")
+    names = sg.configs()
+    for cid in [-1] + [i for i, n in enumerate(names) if n.startswith("mfma_") and n.endswith("d")]:
+        say(f"long rows lda={lda} config {cid}")
+        st, out, checks = run_gemm(M, N, K, 1.25, A, B, -0.5, C, lda=lda, config=cid)
+        assert st == 0
+        check_against_oracle(M, N, K, 1.25, A, K, B, N, -0.5, C, N, out, checks, f"lda {lda} config {cid}")
+
+
 # ------------------------------------------------------------------ epilogue special cases
 
 def test_beta_zero_ignores_nan_in_C():
