@@ -6,9 +6,10 @@
 // small kernels in sgemm_aux_kernels.hpp (16x16 baseline, quick-return scaling).
 // sgemm_mfma is the hot path. A workgroup owns a BM x BN tile of C; each wave owns
 //    a (BM/WGM) x (BN/WGN) sub-tile made of 32x32 blocks computed with the CDNA fp32
-//    matrix instruction (32x32 outputs, 2 k-steps per issue). A and B tiles move
-//    HBM -> registers -> LDS in 128-bit chunks, into a two-stage LDS ring with one
-//    barrier per K-tile; the next K-tile's global loads are in flight while the
+//    matrix instruction (32x32 outputs, 2 k-steps per issue). A and B tiles reach a
+//    ring of LDS stages with one barrier per K-tile, in 128-bit chunks: copied from HBM
+//    straight into LDS when the operands are 16-byte aligned (TileDMA), else staged
+//    through registers (TileIO). The next K-tile's loads are in flight while the
 //    current one is multiplied.
 //
 // Techniques from the pages and where they come from:
@@ -393,15 +394,16 @@ struct MfmaTile {
     static_assert(BK % (8 * WGK) == 0, "each wave group consumes k in groups of 8");
     static constexpr int RED = (WGK - 1) * BM * BN;         // partial sums of groups 1..WGK-1
     static constexpr int SMEM = NSTAGE * STAGE > RED ? NSTAGE * STAGE : RED;
-    // Double-buffered fragment reads (next group's reads in flight while this group is
-    // multiplied). Measured on MI355X: a gain for the direct-copy loop, for one K-tile
-    // in flight and for waves holding a single 32x32 block; with two K-tiles in flight and
-    // larger wave tiles the extra registers cost more than the overlap gains (the 256x256
-    // kernel would spill), so those keep single fragments read next to their use.
     // Waves per SIMD the register budget is sized for: one for waves holding 16 or more
     // 32x32 blocks (256 accumulators; the wave gets the whole 512-register file), else at
     // least two, so that two 256-thread workgroups fit on a CU.
     static constexpr int WPE = TM * TN >= 16 ? 1 : (NT >= 512 ? NT / 256 : 2);
+    // Double-buffered fragment reads (next group's reads in flight while this group is
+    // multiplied). Measured on MI355X: a gain for the direct-copy loop, for one K-tile
+    // in flight and for waves holding a single 32x32 block; with two K-tiles in flight and
+    // larger wave tiles the extra registers cost more than the overlap gains (the 256x256
+    // kernel would spill), so those keep single fragments read next to their use unless
+    // the wave has the whole register file.
     static constexpr bool FRAG = USE_DMA || PF == 1 || TM * TN == 1 || WPE == 1;
     static_assert(SMEM * 4 <= 160 * 1024, "LDS exceeds 160 KiB");
 
@@ -531,9 +533,9 @@ struct MfmaTile {
             }
         };
 
-        // Fragment form used by the direct-copy pipeline: the A and B values of one group
-        // of 8 k (4 per lane) for every block, read from LDS in one batch, so the reads of
-        // the next group can be in flight while this one is multiplied.
+        // Fragment form (FRAG): the A and B values of one group of 8 k (4 per lane) for every
+        // block, read from LDS in one batch, so the reads of the next group can be in flight
+        // while this one is multiplied.
         constexpr int NG = KSLICE / 8;                      // groups of 8 k per stage and wave group
         float fa[FRAG ? 2 : 1][4][TM], fb[FRAG ? 2 : 1][4][TN];
         auto read_frag = [&](int st, int g, int buf) __attribute__((always_inline)) {
