@@ -280,7 +280,7 @@ def main():
         config = {"workload": args.workload,
                   "sequence": [{"name": p["w"].name, "M": p["w"].M, "N": p["w"].N, "K": p["w"].K,
                                 "kernel": p["cfg_name"]} for p in probs],
-                  "inputs": probs[0]["w"].note, "parallelism": "none (one GPU)"}
+                  "inputs": "; ".join(p["w"].note for p in probs), "parallelism": "none (one GPU)"}
         metric = f"FP32 SGEMM TFLOP/s ({args.workload}: the products in sequence) and fraction of MI355X FP32 peak"
         traffic = None
     line = {
