@@ -49,16 +49,21 @@ def parse_config(name):
 def expected_mfma_kernels(config_names):
     """Template arguments <BM,BN,BK,WGM,WGN,WGK,PF,DMA,TA,TB,VEC,EDGE> of every matrix
     kernel the launcher can start: per configuration and operand form, the aligned
-    whole-tile and edge variants as configured, and the unaligned variant with one
-    K-tile in flight (K-tile 16 * WGK for direct-copy configurations)."""
+    whole-tile and edge variants as configured; the register-staged unaligned variant with
+    one K-tile in flight (K-tile 16 * WGK for direct-copy configurations); and, for
+    direct-copy configurations with at most 16 copies per thread and K-tile, the unaligned
+    variant with 4-byte direct copies."""
     out = set()
     for name in config_names:
         bm, bn, bk, wm, wn, wk, pf, dma = parse_config(name)
+        nt = wm * wn * wk * 64
         for ta in (0, 1):
             for tb in (0, 1):
                 if name.startswith("mfma_"):
                     for edge in (0, 1):
                         out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge))
+                    if dma and (bm * bk + bk * bn) // nt <= 16:
+                        out.add((bm, bn, bk, wm, wn, wk, 1, 1, ta, tb, 0, 1))
                 out.add((bm, bn, 16 * wk if dma else bk, wm, wn, wk, 1, 0, ta, tb, 0, 1))
     return out
 

@@ -161,11 +161,12 @@ def test_alignment_and_leading_dimensions(offsets, ld_pad):
         check_against_oracle(M, N, K, 0.75, A, K, B, N, 1.5, C, N, out, checks, f"config {cid}")
 
 
-@pytest.mark.parametrize("lda", [(1 << 20) - 4, 1 << 20])
+@pytest.mark.parametrize("lda", [(1 << 20) - 4, (1 << 20) - 3, 1 << 20])
 def test_long_rows_of_A(lda):
     """Row strides at the direct-copy limit: just below 2^20 floats the copies' byte offsets
-    inside a 256-row tile reach 2^30; from 2^20 on the call takes the element-wise path.
-    Both must agree with the oracle, on the direct-copy configurations and the auto choice."""
+    inside a 256-row tile reach 2^30 (16-byte copies for the aligned stride, 4-byte copies
+    for the odd one); from 2^20 on the call takes the register-staged element-wise path.
+    All must agree with the oracle, on the direct-copy configurations and the auto choice."""
     import tiled_fp32_gemm_02_amd as sg
     rng = np.random.default_rng(37)
     M, N, K = 260, 36, 40

@@ -24,7 +24,8 @@ using sgemm_impl::StreamK;
 
 enum Kind { KIND_TILE16 = 0, KIND_MFMA = 1, KIND_SK = 2 };
 
-typedef hipError_t (*LaunchFn)(const GemmArgs &, int batch, bool ta, bool tb, bool vec, bool edge, hipStream_t);
+typedef hipError_t (*LaunchFn)(const GemmArgs &, int batch, bool ta, bool tb, bool vec, bool edge, bool dma_ok,
+                               hipStream_t);
 typedef hipError_t (*LaunchSkFn)(const GemmArgs &, const StreamK &, int grid, bool ta, bool tb, bool vec,
                                  bool edge, hipStream_t);
 
@@ -72,19 +73,24 @@ int device_cus()
 }
 
 // Row strides (floats) from which the direct-copy kernels' 32-bit in-tile offsets
-// could overflow; such calls take the element-wise (unaligned) variant instead.
+// could overflow; such calls take the register-staged element-wise variant instead.
 constexpr int kDmaMaxLd = 1 << 20;
 
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M>
-hipError_t launch_mfma(const GemmArgs &p, int batch, bool ta, bool tb, bool vec, bool edge, hipStream_t s)
+hipError_t launch_mfma(const GemmArgs &p, int batch, bool ta, bool tb, bool vec, bool edge, bool dma_ok,
+                       hipStream_t s)
 {
     if (!ta && !tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, false>(p, batch, vec, edge, s);
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, false>(p, batch, vec,
+                                                                                                     edge, dma_ok, s);
     if (!ta && tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, true>(p, batch, vec, edge, s);
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, true>(p, batch, vec,
+                                                                                                    edge, dma_ok, s);
     if (ta && !tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, false>(p, batch, vec, edge, s);
-    return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, true>(p, batch, vec, edge, s);
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, false>(p, batch, vec,
+                                                                                                    edge, dma_ok, s);
+    return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, true>(p, batch, vec, edge,
+                                                                                               dma_ok, s);
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M>
@@ -104,7 +110,7 @@ hipError_t launch_sk(const GemmArgs &p, const StreamK &sk, int grid, bool ta, bo
                                                                                                   edge, s);
 }
 
-hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, bool, hipStream_t s)
+hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, bool, bool, hipStream_t s)
 {
     const dim3 grid((p.N + 15) / 16, (p.M + 15) / 16, batch), block(16, 16);
     if (!ta && !tb)
@@ -326,7 +332,8 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     if (c.kind == KIND_MFMA && tiles * (uint64_t)c.threads > 0xFFFFFFFFull)
         return SGEMM_ERROR_TOO_LARGE;
     const bool edge = (M % c.bm) != 0 || (N % c.bn) != 0 || (K % c.bk) != 0;
-    const bool vec_c = vec && !(c.dma && (lda >= kDmaMaxLd || ldb >= kDmaMaxLd));
+    // Direct copies address a tile with 32-bit offsets, so long rows take the register-staged kernels.
+    const bool dma_ok = lda < kDmaMaxLd && ldb < kDmaMaxLd;
     if (c.kind == KIND_SK) {
         if (batch != 1 || cus <= 0 || ws_bytes < sk_workspace_bytes(c, cus))
             return SGEMM_ERROR_WORKSPACE;
@@ -342,10 +349,10 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
         sk.work = (int)tiles * sk.iters;
         // At most one workgroup per K-tile step, so every workgroup's range is non-empty.
         const int grid = sk.work < cus ? sk.work : cus;
-        const hipError_t e = c.launch_sk(p, sk, grid, opA != 0, opB != 0, vec_c, edge, stream);
+        const hipError_t e = c.launch_sk(p, sk, grid, opA != 0, opB != 0, vec, edge, stream);
         return e == hipSuccess ? 0 : (int)e;
     }
-    const hipError_t e = c.launch(p, batch, opA != 0, opB != 0, vec_c, edge, stream);
+    const hipError_t e = c.launch(p, batch, opA != 0, opB != 0, vec, edge, dma_ok, stream);
     return e == hipSuccess ? 0 : (int)e;
 }
 

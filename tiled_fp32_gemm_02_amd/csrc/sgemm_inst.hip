@@ -12,7 +12,7 @@ namespace sgemm_impl {
 #define SGEMM_INSTANTIATE(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M)                            \
     template hipError_t                                                                                 \
     launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, (SGEMM_TA != 0), (SGEMM_TB != 0)>(         \
-        const GemmArgs &, int, bool, bool, hipStream_t);
+        const GemmArgs &, int, bool, bool, bool, hipStream_t);
 SGEMM_MFMA_CONFIGS(SGEMM_INSTANTIATE)
 #undef SGEMM_INSTANTIATE
 

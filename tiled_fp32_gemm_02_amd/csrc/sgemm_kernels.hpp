@@ -199,7 +199,8 @@ struct TileIO {
     }
 
     struct Lane {};     // register staging keeps no per-lane copy plan
-    __device__ __forceinline__ static Lane plan(int64_t, int) { return Lane{}; }
+    template <bool EDGE>
+    __device__ __forceinline__ static Lane plan(int64_t, int, int) { return Lane{}; }
 
     __device__ __forceinline__ static void store(const floatx4 (&r)[CH], float *lds, int tid)
     {
@@ -216,27 +217,30 @@ struct TileIO {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // The same operand tile copied HBM -> LDS directly, with no staging registers, by
-// 16-byte buffer loads into LDS: one such instruction of one wave fills 64 consecutive
-// 16-byte LDS slots, lane l the l-th. The tile is TR rows of CPR slots with no padding;
-// inside row r, chunk c sits in slot c ^ swz(r). A lane fetches whichever global chunk
-// belongs in its slot, so the copy stays contiguous while the reads stay free of bank
-// conflicts on the 64-bank LDS:
+// buffer loads into LDS: one such instruction of one wave fills 64 consecutive LDS
+// slots of VW floats, lane l the l-th (VW = 4: 16-byte copies, for rows that are
+// 16-byte aligned; VW = 1: 4-byte copies, for rows that are only 4-byte aligned; both
+// lane layouts were checked on the GPU with a probe). The tile is TR rows of TC floats
+// with no padding, in 16-byte chunks; inside row r, chunk c sits in chunk slot
+// c ^ swz(r). A lane fetches whichever global data belongs in its slot, so the copy
+// stays contiguous while the reads stay free of bank conflicts on the 64-bank LDS:
 //  - KCONTIG (rows run along k: plain A, transposed B): 16 consecutive rows read at one
 //    chunk land in 16 distinct 4-bank groups;
 //  - otherwise (rows run along m or n): consecutive lanes read consecutive chunks of one
 //    row, and rows 4 apart (the two half-waves) use opposite halves of each 16-slot window.
-// Chunks outside the matrix are fetched at an offset past the buffer's range, which
-// the hardware answers with zeros, so partial tiles arrive zero-padded as in TileIO.
-// Needs 16-byte aligned rows and pointers (the VEC kernels) and row strides below 2^20
-// floats (every byte offset from the tile origin stays below 2^31).
-template <int TR, int TC, int NT, bool KCONTIG>
+// Data outside the matrix is fetched at an offset past the buffer's range, which the
+// hardware answers with zeros, so partial tiles arrive zero-padded as in TileIO: per
+// chunk for VW = 4 (the extents are then multiples of 4), per float for VW = 1.
+// Needs row strides below 2^20 floats (every byte offset from the tile origin stays
+// below 2^31 for TR <= 256).
+template <int TR, int TC, int NT, bool KCONTIG, int VW>
 struct TileDMA {
     static constexpr int CPR = TC / 4;
-    static constexpr int CHUNKS = TR * CPR;
-    static constexpr int CH = CHUNKS / NT;              // copy instructions per thread
+    static constexpr int SLOTS = TR * TC / VW;
+    static constexpr int CH = SLOTS / NT;               // copy instructions per thread
     static constexpr int SIZE = TR * TC;
-    static_assert(NT % 64 == 0 && CHUNKS % NT == 0, "whole copy instructions per wave");
-    static_assert(CPR <= 64 ? 64 % CPR == 0 : CPR % 64 == 0, "a wave's copy covers whole rows or part of one");
+    static_assert(VW == 4 || VW == 1, "16- or 4-byte copies");
+    static_assert(NT % 64 == 0 && SLOTS % NT == 0, "whole copy instructions per wave");
     static_assert(KCONTIG ? (CPR >= 4) : (CPR >= 16), "slot swizzle needs these row lengths");
 
     __device__ __forceinline__ static int swz(int r)
@@ -250,48 +254,62 @@ struct TileDMA {
         return 4 * (r * CPR + ((col >> 2) ^ swz(r))) + (col & 3);
     }
 
+    // Row and column, inside the tile, of the first float that copy c brings to this lane.
+    __device__ __forceinline__ static void where(int c, int tid, int &r, int &col)
+    {
+        const int f = ((tid >> 6) * 64 + c * NT + (tid & 63)) * VW;   // its LDS position
+        r = f / TC;
+        const int cl = f % TC;
+        col = 4 * ((cl >> 2) ^ swz(r)) + (cl & 3);
+    }
+
     // This lane's share of every copy of the tile, fixed for the whole K loop: per copy
-    // instruction, the byte offset of its global chunk from the tile origin (row stride
-    // ld floats), and that chunk's row and first column inside the tile (for edge checks).
-    // Offsets stay below 2^31 for row strides below 2^20 floats and TR <= 256.
+    // instruction, the byte offset of its data from the tile origin (row stride ld floats).
+    // With EDGE, data beyond `mn` rows (KCONTIG) or columns (otherwise) along m or n gets an
+    // offset past the buffer's range here; the k direction is checked per K-tile.
     struct Lane {
         unsigned off[CH];
-        int row[CH], col[CH];
     };
-    __device__ __forceinline__ static Lane plan(int64_t ld, int tid)
+    template <bool EDGE>
+    __device__ __forceinline__ static Lane plan(int64_t ld, int mn, int tid)
     {
         Lane L;
-        const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int s0 = wave * 64 + c * NT;          // first slot of this wave's copy
-            const int q = s0 % CPR + lane;
-            const int r = s0 / CPR + q / CPR, chunk = (q % CPR) ^ swz(r);
-            L.off[c] = static_cast<unsigned>(((int64_t)r * ld + 4 * chunk) * 4);
-            L.row[c] = r;
-            L.col[c] = 4 * chunk;
+            int r, col;
+            where(c, tid, r, col);
+            L.off[c] = static_cast<unsigned>(((int64_t)r * ld + col) * 4);
+            if (EDGE && !((KCONTIG ? r : col) < mn))
+                L.off[c] = 0x80000000u;                 // past num_records: reads as zeros
         }
         return L;
     }
 
-    // Queue this thread's copies of the tile whose origin is src into lds; rows/cols are
-    // how many rows and columns from the origin lie inside the matrix (EDGE only). The
-    // buffer resource (one per tile, wave-uniform) and the LDS destinations are the only
-    // per-step address work.
+    // Queue this thread's copies of the tile whose origin is src into lds; `k` is how many
+    // of the tile's k indices lie inside the matrix (EDGE only; only a K-tile that ends
+    // past K needs the per-lane check). The buffer resource (one per tile, wave-uniform)
+    // and the LDS destinations are the only per-step address work.
     template <bool EDGE>
-    __device__ __forceinline__ static void load(const Lane &L, const float *src, int rows, int cols, float *lds,
-                                                int tid)
+    __device__ __forceinline__ static void load(const Lane &L, const float *src, int k, float *lds, int tid)
     {
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS base in M0
         const __amdgpu_buffer_rsrc_t rsrc =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), 0, 0x7fffffff, 0x00020000);
+        const bool partial = EDGE && k < (KCONTIG ? TC : TR);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             unsigned off = L.off[c];
-            if (EDGE && !(L.row[c] < rows && L.col[c] < cols))
-                off = 0x80000000u;                      // past num_records: reads as zeros
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + 4 * (wave * 64 + c * NT)), 16, off,
-                                                     0, 0, 0);
+            if (partial) {
+                int r, col;
+                where(c, tid, r, col);
+                if (!((KCONTIG ? col : r) < k))
+                    off = 0x80000000u;
+            }
+            lds_void *dst = (lds_void *)(lds + VW * (wave * 64 + c * NT));
+            if constexpr (VW == 4)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, off, 0, 0, 0);
         }
     }
 };
@@ -377,14 +395,15 @@ template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, b
           bool EDGE>
 struct MfmaTile {
     static_assert(PF == 1 || PF == 2, "K-tiles in flight ahead of the one being multiplied");
-    static constexpr bool USE_DMA = DMA && VEC;             // aligned operands: direct HBM -> LDS copies
+    static constexpr bool USE_DMA = DMA;                    // direct HBM -> LDS copies
+    static constexpr int VW = VEC ? 4 : 1;                  // floats per lane and copy
     static constexpr int NT = WGM * WGN * WGK * 64;
     static constexpr int KSLICE = BK / WGK;                    // k per stage handled by one wave group
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
     static constexpr int TM = WTM / 32, TN = WTN / 32;         // 32x32 blocks per wave
-    using AIO = typename std::conditional<USE_DMA, TileDMA<TA ? BK : BM, TA ? BM : BK, NT, !TA>,
+    using AIO = typename std::conditional<USE_DMA, TileDMA<TA ? BK : BM, TA ? BM : BK, NT, !TA, VW>,
                                           TileIO<TA ? BK : BM, TA ? BM : BK, NT>>::type;
-    using BIO = typename std::conditional<USE_DMA, TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB>,
+    using BIO = typename std::conditional<USE_DMA, TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB, VW>,
                                           TileIO<TB ? BN : BK, TB ? BK : BN, NT>>::type;
     static constexpr int STAGE = AIO::SIZE + BIO::SIZE;
     static constexpr int NSTAGE = USE_DMA ? PF + 1 : 2;     // LDS stages in the ring
@@ -457,20 +476,20 @@ struct MfmaTile {
 
         // Direct copies of the K-tile starting kr after the range's first k into LDS stage `st`
         // (DMA path). Each lane's offsets inside a tile are the same for every K-tile.
-        const typename AIO::Lane a_lane = AIO::plan(lda, tid);
-        const typename BIO::Lane b_lane = BIO::plan(ldb, tid);
+        const typename AIO::Lane a_lane = AIO::template plan<EDGE>(lda, M - m0, tid);
+        const typename BIO::Lane b_lane = BIO::template plan<EDGE>(ldb, N - n0, tid);
         auto copy_tile = [&](int kr, int st) __attribute__((always_inline)) {
             if constexpr (USE_DMA) {
                 const int k0 = kbase + kr;
                 float *As = smem + st * STAGE;
                 if constexpr (TA)
-                    AIO::template load<EDGE>(a_lane, A + (int64_t)k0 * lda + m0, K - k0, M - m0, As, tid);
+                    AIO::template load<EDGE>(a_lane, A + (int64_t)k0 * lda + m0, K - k0, As, tid);
                 else
-                    AIO::template load<EDGE>(a_lane, A + (int64_t)m0 * lda + k0, M - m0, K - k0, As, tid);
+                    AIO::template load<EDGE>(a_lane, A + (int64_t)m0 * lda + k0, K - k0, As, tid);
                 if constexpr (TB)
-                    BIO::template load<EDGE>(b_lane, B + (int64_t)n0 * ldb + k0, N - n0, K - k0, As + AIO::SIZE, tid);
+                    BIO::template load<EDGE>(b_lane, B + (int64_t)n0 * ldb + k0, K - k0, As + AIO::SIZE, tid);
                 else
-                    BIO::template load<EDGE>(b_lane, B + (int64_t)k0 * ldb + n0, K - k0, N - n0, As + AIO::SIZE, tid);
+                    BIO::template load<EDGE>(b_lane, B + (int64_t)k0 * ldb + n0, K - k0, As + AIO::SIZE, tid);
             }
         };
 

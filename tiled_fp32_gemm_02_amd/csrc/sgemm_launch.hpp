@@ -10,7 +10,7 @@
 namespace sgemm_impl {
 
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, bool TA, bool TB>
-hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, hipStream_t s);
+hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, bool dma_ok, hipStream_t s);
 
 // Stream-K launch of the same tile kernel: `grid` workgroups share the work described
 // by sk (batch 1).

@@ -1,9 +1,14 @@
 // Definition of launch_mfma_op (see sgemm_launch.hpp): one workgroup per output tile
 // (1-D grid, blockIdx.z = batch), and the kernel variant for the alignment (VEC) and
-// for whether any tile crosses the matrix edge (EDGE). Unaligned operands (element-wise
-// loads, several times the address registers) always take the register-staged kernel
-// with one K-tile in flight, and with K-tiles of 16 * WGK for direct-copy configurations,
-// so that variant fits the register file for every tile shape.
+// for whether any tile crosses the matrix edge (EDGE).
+//
+// Unaligned operands (rows only 4-byte aligned): a direct-copy configuration copies
+// 4-byte words into the same LDS layout when a thread's share of a K-tile is at most 16
+// copies (the offsets then fit the register budget), with one K-tile in flight. Every
+// other configuration, and every call whose row strides are too long for 32-bit copy
+// offsets (dma_ok false), runs the register-staged kernel with element-wise loads and one
+// K-tile in flight, with K-tiles of 16 * WGK for direct-copy configurations, so that
+// variant fits the register file for every tile shape.
 #pragma once
 
 #include "sgemm_launch.hpp"
@@ -11,20 +16,27 @@
 namespace sgemm_impl {
 
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, bool TA, bool TB>
-hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, hipStream_t s)
+hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, bool dma_ok, hipStream_t s)
 {
-    constexpr int BKU = DMA ? 16 * WGK : BK;            // K-tile of the unaligned variant
+    constexpr int NT = WGM * WGN * WGK * 64;
+    constexpr bool DMA4 = DMA && (BM * BK + BK * BN) / NT <= 16;   // 4-byte copies for unaligned rows
+    constexpr int BKU = DMA ? 16 * WGK : BK;            // K-tile of the register-staged unaligned variant
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    const dim3 grid(tiles, 1, batch), block(WGM * WGN * WGK * 64);
+    const dim3 grid(tiles, 1, batch), block(NT);
+    if (DMA && !dma_ok)
+        vec = false;                                    // only the register-staged variant takes long rows
     if (vec && !edge)
         hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, false>), grid, block, 0, s,
                            p, GROUP_M);
     else if (vec)
         hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, true>), grid, block, 0, s,
                            p, GROUP_M);
-    else
+    else if (!DMA4 || !dma_ok)
         hipLaunchKernelGGL((sgemm_mfma<BM, BN, BKU, WGM, WGN, WGK, 1, false, TA, TB, false, true>), grid, block, 0,
                            s, p, GROUP_M);
+    else if constexpr (DMA4)
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, 1, true, TA, TB, false, true>), grid, block, 0, s,
+                           p, GROUP_M);
     return hipGetLastError();
 }
 
@@ -38,7 +50,7 @@ hipError_t launch_mfma_sk_op(const GemmArgs &p, const StreamK &sk, int grid, boo
     else if (vec)
         hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, true>), dim3(grid),
                            block, 0, s, p, sk);
-    else    // unaligned operands: the data-parallel kernel of the same tile (see launch_mfma_op)
+    else    // unaligned operands: the register-staged data-parallel kernel of the same tile
         hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, 1, false, TA, TB, false, true>),
                            dim3(sk.tiles_m * sk.tiles_n), block, 0, s, p, GROUP_M);
     return hipGetLastError();
