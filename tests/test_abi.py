@@ -146,6 +146,10 @@ def test_select_config():
     sel = lambda M, N, K=64, alpha=1.0: sg.sgemm_select_config(M, N, K, alpha, BAD, K, BAD, N, BAD, N)
     assert sel(0, 5) == -1 and sel(5, 0) == -1 and sel(5, 5, K=0) == -1 and sel(5, 5, alpha=0.0) == -1
     assert names[sel(4096, 4096, 4096)] == "mfma_256x256x32_w2x4d"    # 256 tiles: one per CU
+    # rows only 4-byte aligned: the unaligned table, whose large tile has a 4-byte-copy form
+    assert names[sg.sgemm_select_config(4096, 4096, 4096, 1.0, BAD + 4, 4096, BAD, 4096, BAD, 4096)] == \
+        "mfma_256x256x16_w2x4d"
+    assert names[sel(4095, 4095, 4095)] == "mfma_256x256x16_w2x4d"
     # each choice still gives at least 256 workgroups when the problem allows it
     for M, N in [(1024, 1024), (1024, 2304), (1024, 3072), (1024, 768), (1000, 1537), (256, 256)]:
         name = names[sel(M, N)]

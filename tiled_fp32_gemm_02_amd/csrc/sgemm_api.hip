@@ -190,11 +190,14 @@ struct Candidate {
     double fixed_us;    // time that does not scale with the work
 };
 
-// Least-squares fit (relative error) of time = fixed + work / rate to a sweep over
-// 256^3 ... 6144^3, 512 x 4096 x 4096 and the GPT-2-small linear layers, all aligned.
-// On every shape of the sweep the model picks the fastest candidate or one within 1%; on
-// the unaligned 1000 x 1537 x 777 product (where the direct-copy candidates run their
-// register-staged variants) it loses 3% to the fastest.
+// Least-squares fits (relative error) of time = fixed + work / rate, one per operand
+// alignment. Aligned: a sweep over 256^3 ... 6144^3, 512 x 4096 x 4096 and the GPT-2-small
+// linear layers; on every shape of it the model picks the fastest candidate or one within
+// 1%. Unaligned (rows only 4-byte aligned, 4-byte direct copies): the same kinds of
+// shapes with odd sizes (255^3 ... 6143^3, 511 x 4095 x 4095, 1000 x 1537 x 777 and the
+// GPT-2 layers one short in each dimension); the model picks the fastest on every one.
+// The 256 x 256 x 32 tile has no 4-byte-copy form (its copy offsets would not fit the
+// registers), so the unaligned table has the 256 x 256 x 16 tile instead.
 const Candidate kCandidates[] = {
     {"mfma_256x256x32_w2x4d", 16, 0.591, 0.580, 7.5},      // one workgroup per CU
     {"mfma_128x128x32_w2x2k2d", 4, 0.555, 0.573, 5.4},     // up to two per CU
@@ -202,12 +205,20 @@ const Candidate kCandidates[] = {
     {"mfma_64x64x64_w2x2k4d", 1, 0.539, 0.479, 5.9},       // one per CU, 16 waves
     {"mfma_64x64x32_w2x2k2d", 1, 0.457, 0.507, 6.1},       // up to four per CU
 };
+const Candidate kUnalignedCandidates[] = {
+    {"mfma_256x256x16_w2x4d", 16, 0.519, 0.498, 8.4},
+    {"mfma_128x128x32_w2x2k2d", 4, 0.462, 0.467, 6.7},
+    {"mfma_64x128x32_w2x2k2d", 2, 0.450, 0.472, 5.9},
+    {"mfma_64x64x64_w2x2k4d", 1, 0.421, 0.437, 8.2},
+    {"mfma_64x64x32_w2x2k2d", 1, 0.376, 0.441, 7.4},
+};
 const Candidate kSkCandidates[] = {
     {"sk_128x128x32_w2x2k2p2", 4, 0.534, 0.534, 17.1},
     {"sk_64x128x32_w2x2k2p2", 2, 0.502, 0.502, 12.2},
 };
 constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
 constexpr int kNumSkCandidates = sizeof(kSkCandidates) / sizeof(kSkCandidates[0]);
+static_assert(sizeof(kUnalignedCandidates) == sizeof(kCandidates), "one table length for both alignments");
 
 int find_config(const char *name)
 {
@@ -222,10 +233,11 @@ int find_config(const char *name)
 
 // Table ids of the candidates, looked up once.
 struct CandidateIds {
-    int id[kNumCandidates], sk[kNumSkCandidates];
+    int id[kNumCandidates], un[kNumCandidates], sk[kNumSkCandidates];
     CandidateIds()
     {
         for (int i = 0; i < kNumCandidates; ++i) id[i] = find_config(kCandidates[i].name);
+        for (int i = 0; i < kNumCandidates; ++i) un[i] = find_config(kUnalignedCandidates[i].name);
         for (int i = 0; i < kNumSkCandidates; ++i) sk[i] = find_config(kSkCandidates[i].name);
     }
 };
@@ -234,22 +246,23 @@ struct CandidateIds {
 // only when `ws_bytes` holds their workspace for `cus` compute units (cus > 0).
 int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0)
 {
-    // One data-parallel table serves the 128-bit and the 32-bit paths.
     static const CandidateIds ids;
+    const Candidate *table = vec ? kCandidates : kUnalignedCandidates;
+    const int *table_ids = vec ? ids.id : ids.un;
     const uint64_t kCUs = cus > 0 ? (uint64_t)cus : 256;
     const double unit_mflop = 2.0 * 64 * 64 * (double)K * 1e-6;    // one 64x64 tile, MFLOP
     int best = -1;
     double best_us = 0.0;
     for (int i = 0; i < kNumCandidates; ++i) {
-        const Candidate &cand = kCandidates[i];
-        if (ids.id[i] < 0)
+        const Candidate &cand = table[i];
+        if (table_ids[i] < 0)
             continue;
-        const uint64_t tiles = tile_count(kConfigs[ids.id[i]], M, N);
+        const uint64_t tiles = tile_count(kConfigs[table_ids[i]], M, N);
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
         const double us =
             cand.fixed_us + (double)rounds * cand.units * unit_mflop / (rounds >= 2 ? cand.rate_many : cand.rate_one);
         if (best < 0 || us < best_us) {
-            best = ids.id[i];
+            best = table_ids[i];
             best_us = us;
         }
     }
