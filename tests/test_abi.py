@@ -42,9 +42,9 @@ def test_version_and_configs():
     names = sg.configs()
     assert len(names) == sg.sgemm_config_count() >= 2
     assert names[0] == "tile16"
-    # data-parallel configurations first, then the stream-K ones
+    # matrix-core configurations first, then the stream-K ones, then the vector-ALU micro-tile
     kinds = [n.split("_")[0] for n in names[1:]]
-    assert set(kinds) == {"mfma", "sk"} and kinds == sorted(kinds)
+    assert set(kinds) == {"mfma", "sk", "valu"} and kinds == sorted(kinds)
     assert sg.sgemm_config_name(-1) is None and sg.sgemm_config_name(len(names)) is None
 
 
@@ -120,6 +120,12 @@ def test_launch_shape_tile16_matches_gpt2_post():
     assert sg.sgemm_launch_shape(0, 64, 256, 16) == (0, (16, 4, 1), (16, 16, 1))
     assert sg.sgemm_launch_shape(0, 65, 257, 3) == (0, (17, 5, 1), (16, 16, 1))
     assert sg.sgemm_launch_shape(0, 1, 1, 1) == (0, (1, 1, 1), (16, 16, 1))
+
+
+def test_launch_shape_valu():
+    cid = sg.configs().index("valu_128x128x8_t8x8")
+    for M, N in [(4096, 4096), (1000, 1537), (1, 1), (129, 127)]:
+        assert sg.sgemm_launch_shape(cid, M, N, 64) == (0, (-(-M // 128) * -(-N // 128), 1, 1), (256, 1, 1))
 
 
 def test_launch_shape_mfma():

@@ -83,9 +83,9 @@ def expected_sk_kernels(config_names):
 
 def test_all_kernels_present(kernels):
     names = " ".join(kernels)
-    assert "sgemm_tile16" in names and "sgemm_scale" in names
+    assert "sgemm_tile16" in names and "sgemm_scale" in names and "sgemm_valu" in names
     import tiled_fp32_gemm_02_amd as sg
-    names = sg.configs()[1:]
+    names = [n for n in sg.configs() if n.startswith(("mfma_", "sk_"))]
     for kind, expected in (("sgemm_mfma", expected_mfma_kernels(names)),
                            ("sgemm_mfma_sk", expected_sk_kernels([c for c in names if c.startswith("sk_")]))):
         found = set()
@@ -119,6 +119,18 @@ def test_matrix_kernels_use_fp32_mfma(kernels):
     for name, (k, body) in kernels.items():
         if "sgemm_mfma<" in name or "sgemm_mfma_sk<" in name:
             assert "v_mfma_f32_32x32x2_f32" in body, name
+
+
+def test_vector_kernel_uses_plain_fma(kernels):
+    """The micro-tile reference runs on the vector ALU: fused multiply-adds, no matrix
+    instructions and no packed fp32 forms (the build keeps those off)."""
+    found = 0
+    for name, (k, body) in kernels.items():
+        if "sgemm_valu<" in name:
+            found += 1
+            assert "v_fma_f32" in body or "v_fmac_f32" in body, name
+            assert "v_mfma" not in body and "v_pk_fma_f32" not in body and "v_pk_mul_f32" not in body, name
+    assert found == 4
 
 
 def test_oracle_builds():

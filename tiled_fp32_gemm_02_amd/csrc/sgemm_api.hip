@@ -22,7 +22,7 @@ namespace {
 
 using sgemm_impl::StreamK;
 
-enum Kind { KIND_TILE16 = 0, KIND_MFMA = 1, KIND_SK = 2 };
+enum Kind { KIND_TILE16 = 0, KIND_MFMA = 1, KIND_SK = 2, KIND_VALU = 3 };
 
 typedef hipError_t (*LaunchFn)(const GemmArgs &, int batch, bool ta, bool tb, bool vec, bool edge, bool dma_ok,
                                hipStream_t);
@@ -36,7 +36,7 @@ struct Config {
     int threads;         // threads per workgroup
     bool dma;            // aligned operands are copied HBM -> LDS directly
     int group_m;         // band height of the tile order
-    LaunchFn launch;     // data-parallel launch (KIND_TILE16, KIND_MFMA)
+    LaunchFn launch;     // data-parallel launch (KIND_TILE16, KIND_MFMA, KIND_VALU)
     LaunchSkFn launch_sk;    // stream-K launch (KIND_SK)
 };
 
@@ -110,6 +110,23 @@ hipError_t launch_sk(const GemmArgs &p, const StreamK &sk, int grid, bool ta, bo
                                                                                                   edge, s);
 }
 
+// The vector-ALU micro-tile kernel: one 256-thread workgroup per 128 x 128 tile.
+hipError_t launch_valu(const GemmArgs &p, int batch, bool ta, bool tb, bool, bool, bool, hipStream_t s)
+{
+    constexpr int GROUP_M = 8;
+    const int tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+    const dim3 grid(tiles, 1, batch), block(256);
+    if (!ta && !tb)
+        hipLaunchKernelGGL((sgemm_impl::sgemm_valu<false, false>), grid, block, 0, s, p, GROUP_M);
+    else if (!ta && tb)
+        hipLaunchKernelGGL((sgemm_impl::sgemm_valu<false, true>), grid, block, 0, s, p, GROUP_M);
+    else if (ta && !tb)
+        hipLaunchKernelGGL((sgemm_impl::sgemm_valu<true, false>), grid, block, 0, s, p, GROUP_M);
+    else
+        hipLaunchKernelGGL((sgemm_impl::sgemm_valu<true, true>), grid, block, 0, s, p, GROUP_M);
+    return hipGetLastError();
+}
+
 hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, bool, bool, hipStream_t s)
 {
     const dim3 grid((p.N + 15) / 16, (p.M + 15) / 16, batch), block(16, 16);
@@ -125,9 +142,11 @@ hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, b
 }
 
 // Configuration table: id 0 is the 16x16 baseline kernel, then the MFMA configurations
-// of sgemm_configs.inc in order, then its stream-K configurations. Names encode the tile (BM x BN x BK),
-// the wave grid (WGM x WGN), after "k" the wave groups along k, after "p" the K-tiles
-// prefetched ahead (1 when absent), and a final "d" marks direct HBM -> LDS copies.
+// of sgemm_configs.inc in order, then its stream-K configurations, then the vector-ALU
+// micro-tile kernel (tile 128 x 128 x 8, 8 x 8 outputs per thread). MFMA names encode the
+// tile (BM x BN x BK), the wave grid (WGM x WGN), after "k" the wave groups along k, after
+// "p" the K-tiles prefetched ahead (1 when absent), and a final "d" marks direct HBM -> LDS
+// copies.
 #define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M)                               \
     {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, GROUP_M,                                   \
      launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>, nullptr},
@@ -138,6 +157,7 @@ const Config kConfigs[] = {
     {"tile16", KIND_TILE16, 16, 16, 16, 256, false, 1, launch_tile16, nullptr},
     SGEMM_MFMA_CONFIGS(SGEMM_TABLE_ROW)
     SGEMM_SK_CONFIGS(SGEMM_SK_TABLE_ROW)
+    {"valu_128x128x8_t8x8", KIND_VALU, 128, 128, 8, 256, false, 8, launch_valu, nullptr},
 };
 #undef SGEMM_TABLE_ROW
 #undef SGEMM_SK_TABLE_ROW
@@ -342,7 +362,7 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     const int id = config >= 0 ? config : choose(M, N, K, vec, ws_bytes, cus);
     const Config &c = kConfigs[id];
     const uint64_t tiles = tile_count(c, M, N);
-    if (c.kind == KIND_MFMA && tiles * (uint64_t)c.threads > 0xFFFFFFFFull)
+    if ((c.kind == KIND_MFMA || c.kind == KIND_VALU) && tiles * (uint64_t)c.threads > 0xFFFFFFFFull)
         return SGEMM_ERROR_TOO_LARGE;
     const bool edge = (M % c.bm) != 0 || (N % c.bn) != 0 || (K % c.bk) != 0;
     // Direct copies address a tile with 32-bit offsets, so long rows take the register-staged kernels.
