@@ -14,7 +14,7 @@ the launch stream, against the MI355X fp32 matrix peak of 157.3 TFLOP/s), and
 the CPU oracle timed on a bounded sample of the same product on this host.
 
     python bench.py [--steps K] [--warmup W] [--settle-seconds S] [--workload NAME]
-                    [--config ID] [--no-cpu-baseline] [--copy-probe]
+                    [--config ID|NAME] [--no-cpu-baseline] [--copy-probe]
 
 Before the W warm-up steps the step runs back to back, untimed, for S seconds
 (default 1): the GPU's clock ramps up over the first tens of milliseconds of
@@ -157,7 +157,7 @@ def main():
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed back-to-back steps before the warm-up, for the clock to ramp")
     ap.add_argument("--workload", default="sq4096")
-    ap.add_argument("--config", type=int, default=-1, help="force a kernel configuration id")
+    ap.add_argument("--config", default="-1", help="force a kernel configuration (id or name)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true")
@@ -180,6 +180,12 @@ def main():
     import oracle
     from workloads import WORKLOADS, draw, make, flops
 
+    if args.config.lstrip("-").isdigit():
+        args.config = int(args.config)
+    elif args.config in sg.configs():
+        args.config = sg.configs().index(args.config)
+    else:
+        raise SystemExit(f"bench: no configuration named {args.config!r}; see tiled_fp32_gemm_02_amd.configs()")
     fused = args.workload == "gpt2_mlp_up_gelu"
     names = (["gpt2_qkv", "gpt2_mlp_up", "gpt2_mlp_down"] if args.workload == "gpt2_seq"
              else ["gpt2_mlp_up"] if fused else [args.workload])
