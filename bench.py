@@ -71,14 +71,19 @@ def read_sclk():
     return None
 
 
+# The sources that define the matrix-core kernels and which variant a launch runs: the
+# kernel templates, the launchers, their instantiation and the configuration table. Host
+# dispatch (sgemm_api.hip) and the vector-ALU kernels do not change a matrix-core kernel.
+MFMA_KERNEL_SOURCES = ("sgemm_kernels.hpp", "sgemm_launch.hpp", "sgemm_launch_impl.hpp", "sgemm_inst.hip",
+                       "sgemm_configs.inc")
+
+
 def kernel_source_hash() -> str:
-    """sha256 of the kernel sources with comments and whitespace removed, so the
-    recorded counters stay valid across comment-only edits."""
+    """sha256 of the matrix-core kernel sources with comments and whitespace removed, so
+    the recorded counters stay valid across comment-only edits and host-side changes."""
     import re
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if not name.endswith((".hip", ".hpp", ".inc")):
-            continue
+    for name in MFMA_KERNEL_SOURCES:
         with open(os.path.join(CSRC, name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
