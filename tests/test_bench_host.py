@@ -36,6 +36,7 @@ def test_kernel_source_hash_ignores_comments(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("int f() { return 1; } // one\n/* block */\n")
     monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    monkeypatch.setattr(bench, "MFMA_KERNEL_SOURCES", ("k.hip",))
     h1 = bench.kernel_source_hash()
     src.write_text("int f() {   return 1; }   // a different comment\n")
     assert bench.kernel_source_hash() == h1
