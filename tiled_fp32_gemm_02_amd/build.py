@@ -7,6 +7,10 @@ library next to this file:
 * ``csrc/sgemm_inst.hip`` four times, once per operand form (SGEMM_TA, SGEMM_TB),
   each instantiating every MFMA configuration of ``csrc/sgemm_configs.inc``.
 
+It also builds ``mfma_rate``, a standalone executable that measures the fp32 matrix-core
+rate and the shader clock the chip sustains (no part of the library; a ceiling to read
+the GEMM's timings against).
+
 Flags:
 
 * ``--offload-arch=gfx950``: MI355X only; no other targets, no CUDA.
@@ -29,6 +33,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libsgemm.so")
+RATE_PATH = os.path.join(HERE, "mfma_rate")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -53,7 +58,7 @@ def hipcc() -> str:
 
 
 def _jobs() -> int:
-    return max(1, min(len(UNITS), os.cpu_count() or 1, int(os.environ.get("MAX_JOBS", "16"))))
+    return max(1, min(len(UNITS) + 1, os.cpu_count() or 1, int(os.environ.get("MAX_JOBS", "16"))))
 
 
 def _run(cmd, verbose):
@@ -75,8 +80,11 @@ def build(verbose: bool = False) -> str:
             obj = os.path.join(tmpdir, stem + ".o")
             objs.append(obj)
             cmds.append([hipcc(), *COMMON_FLAGS, "-fPIC", *defs, "-c", os.path.join(CSRC, src), "-o", obj])
+        rate_tmp = RATE_PATH + f".tmp{os.getpid()}"
+        cmds.append([hipcc(), *COMMON_FLAGS, os.path.join(CSRC, "mfma_rate.hip"), "-o", rate_tmp])
         with ThreadPoolExecutor(max_workers=_jobs()) as pool:
             list(pool.map(lambda c: _run(c, verbose), cmds))
+        os.replace(rate_tmp, RATE_PATH)
         tmp = LIB_PATH + f".tmp{os.getpid()}"
         _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
         os.replace(tmp, LIB_PATH)
