@@ -254,6 +254,28 @@ def test_entries_equal_full():
         oracle.sgemm_entries(M, N, K, 1.5, A, K, B, N, 0.5, C, N, [M], [0])
 
 
+def test_alpha_beta_linearity():
+    """With small-integer A, B and C every result is exact in fp64, so the scalars and the
+    operands must act linearly and exactly: alpha = 0, beta = 1 gives C; r(alpha, beta) =
+    alpha * r(1, 0) + beta * C; and the product is additive in A and in B."""
+    rng = np.random.default_rng(23)
+    M, N, K = 11, 13, 17
+    A1, A2 = draw(rng, (M, K), "smallint"), draw(rng, (M, K), "smallint")
+    B1, B2 = draw(rng, (K, N), "smallint"), draw(rng, (K, N), "smallint")
+    C = draw(rng, (M, N), "smallint")
+    c64 = C.astype(np.float64)
+
+    def r(alpha, A, B, beta):
+        return oracle.sgemm(M, N, K, alpha, f32(A), K, f32(B), N, beta, C, N)[0]
+
+    prod = r(1.0, A1, B1, 0.0)
+    assert np.array_equal(r(0.0, A1, B1, 1.0), c64)
+    for alpha, beta in [(3.0, -2.0), (-0.5, 0.25), (2.0, 1.0)]:
+        assert np.array_equal(r(alpha, A1, B1, beta), alpha * prod + beta * c64)
+    assert np.array_equal(r(1.0, A1 + A2, B1, 0.0), prod + r(1.0, A2, B1, 0.0))
+    assert np.array_equal(r(1.0, A1, B1 + B2, 0.0), prod + r(1.0, A1, B2, 0.0))
+
+
 def test_bound_admits_fp32_summation_orders():
     """Results a correct fp32 kernel may produce lie within the bound: forward,
     reverse, pairwise and 16-wide blocked sums, with and without fused multiply-add,
@@ -297,35 +319,51 @@ def test_bound_admits_fp32_summation_orders():
 
 def _pins_pass(call):
     """Run a small battery of pins against `call` (same signature as oracle.sgemm).
-    Returns the list of pins that failed."""
+    Returns the list of pins that failed; a pin whose call raises has failed too."""
     failed = []
-    # sum of squares, non-square: catches transposed operands and dropped terms
-    M, N, K = 5, 7, 11
-    A = f32(np.tile(np.arange(K), (M, 1)))
-    B = f32(np.tile(np.arange(K)[:, None], (1, N)))
-    ref, _ = call(M, N, K, 1.0, A, K, B, N, 0.0, None, N)
-    if not (ref.shape == (M, N) and np.all(ref == (K - 1) * K * (2 * K - 1) / 6)):
-        failed.append("sum_of_squares")
-    # square structured case: a_ik = k, b_kj = j + 1  =>  (AB)_ij = (j+1) K (K-1) / 2
-    K = 9
-    A = f32(np.tile(np.arange(K), (K, 1)))
-    B = f32(np.tile(np.arange(1, K + 1), (K, 1)))
-    ref, _ = call(K, K, K, 1.0, A, K, B, K, 0.0, None, K)
-    jj = np.arange(1, K + 1)[None, :]
-    if not np.array_equal(ref, np.broadcast_to(jj * K * (K - 1) / 2.0, (K, K))):
-        failed.append("square_structured")
-    # golden with alpha/beta
-    g = read_golden("textbook_2x3x2.txt")
-    ref, _ = call(2, 2, 3, g["alpha"][0], f32(g["A"]), 3, f32(g["B"]), 2, g["beta"][0], f32(g["C"]), 2)
-    if ref.reshape(-1).tolist() != g["result"]:
-        failed.append("golden_alpha_beta")
-    # first k alone matters: a_i0 = 1, b_0j = j+1, every other term zero
-    K = 6
-    A = np.zeros((3, K), np.float32); A[:, 0] = 1
-    B = np.zeros((K, 4), np.float32); B[0, :] = np.arange(1, 5)
-    ref, _ = call(3, 4, K, 1.0, A, K, B, 4, 0.0, None, 4)
-    if not np.array_equal(ref, np.tile(np.arange(1.0, 5.0), (3, 1))):
-        failed.append("first_k")
+
+    def pin(name, check):
+        try:
+            ok = check()
+        except (ValueError, IndexError, TypeError):
+            ok = False
+        if not ok:
+            failed.append(name)
+
+    def sum_of_squares():
+        # non-square: catches transposed operands and dropped terms
+        M, N, K = 5, 7, 11
+        A = f32(np.tile(np.arange(K), (M, 1)))
+        B = f32(np.tile(np.arange(K)[:, None], (1, N)))
+        ref, _ = call(M, N, K, 1.0, A, K, B, N, 0.0, None, N)
+        return ref.shape == (M, N) and bool(np.all(ref == (K - 1) * K * (2 * K - 1) / 6))
+
+    def square_structured():
+        # a_ik = k, b_kj = j + 1  =>  (AB)_ij = (j+1) K (K-1) / 2
+        K = 9
+        A = f32(np.tile(np.arange(K), (K, 1)))
+        B = f32(np.tile(np.arange(1, K + 1), (K, 1)))
+        ref, _ = call(K, K, K, 1.0, A, K, B, K, 0.0, None, K)
+        jj = np.arange(1, K + 1)[None, :]
+        return np.array_equal(ref, np.broadcast_to(jj * K * (K - 1) / 2.0, (K, K)))
+
+    def golden_alpha_beta():
+        g = read_golden("textbook_2x3x2.txt")
+        ref, _ = call(2, 2, 3, g["alpha"][0], f32(g["A"]), 3, f32(g["B"]), 2, g["beta"][0], f32(g["C"]), 2)
+        return ref.reshape(-1).tolist() == g["result"]
+
+    def first_k():
+        # a_i0 = 1, b_0j = j+1, every other term zero
+        K = 6
+        A = np.zeros((3, K), np.float32); A[:, 0] = 1
+        B = np.zeros((K, 4), np.float32); B[0, :] = np.arange(1, 5)
+        ref, _ = call(3, 4, K, 1.0, A, K, B, 4, 0.0, None, 4)
+        return np.array_equal(ref, np.tile(np.arange(1.0, 5.0), (3, 1)))
+
+    pin("sum_of_squares", sum_of_squares)
+    pin("square_structured", square_structured)
+    pin("golden_alpha_beta", golden_alpha_beta)
+    pin("first_k", first_k)
     return failed
 
 
@@ -360,6 +398,8 @@ MUTANTS = {
         M, N, K, -al, A, lda, B, ldb, be, C, ldc)),
     "ignores_alpha": _mut(lambda M, N, K, al, A, lda, B, ldb, be, C, ldc: oracle.sgemm(
         M, N, K, 1.0, A, lda, B, ldb, be, C, ldc)),
+    "alpha_beta_swapped": _mut(lambda M, N, K, al, A, lda, B, ldb, be, C, ldc: oracle.sgemm(
+        M, N, K, be, A, lda, B, ldb, al, C, ldc)),
     "ignores_beta": _mut(lambda M, N, K, al, A, lda, B, ldb, be, C, ldc: oracle.sgemm(
         M, N, K, al, A, lda, B, ldb, 0.0, None, ldc)),
     "transposed_A": _mut(lambda M, N, K, al, A, lda, B, ldb, be, C, ldc: oracle.sgemm(
