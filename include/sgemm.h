@@ -48,7 +48,9 @@ extern "C" {
 #endif
 
 #define SGEMM_SUCCESS 0
-/* The tile grid of the problem does not fit one launch (more than 2^31-1 tiles). */
+/* The problem does not fit one launch: the tile count times the configuration's threads
+ * per tile passes 2^32 - 1, or, for a stream-K configuration, the product has more than
+ * 16384 tiles or (compute units + 1) x tiles x K-tiles reaches 2^31. */
 #define SGEMM_ERROR_TOO_LARGE (-100)
 /* sgemm_ex / sgemm_general: the configuration id is not in [-1, sgemm_config_count()). */
 #define SGEMM_ERROR_BAD_CONFIG (-101)

@@ -147,6 +147,39 @@ def test_launch_shape_mfma():
     assert sg.sgemm_launch_shape(99, 4, 4, 4)[0] == sg.SGEMM_ERROR_BAD_CONFIG
 
 
+def test_launch_shape_near_int_max():
+    """Sizes within one tile of 2^31: the ceiling divisions must not overflow. Each
+    launch is either described exactly or rejected as too large."""
+    big = 2**31 - 1
+    # 16x16 kernel: a 2-D grid of 16x16 blocks over N x M
+    assert sg.sgemm_launch_shape(0, big, 1, big) == (0, (1, 2**27, 1), (16, 16, 1))
+    assert sg.sgemm_launch_shape(0, 1, big, 1) == (0, (2**27, 1, 1), (16, 16, 1))
+    valu = sg.configs().index("valu_128x128x8_t8x8")
+    # ceil(big / 128) x 256 threads is 2^32: one more than a launch holds
+    assert sg.sgemm_launch_shape(valu, big, 1, 8)[0] == sg.SGEMM_ERROR_TOO_LARGE
+    m = big - 128
+    assert sg.sgemm_launch_shape(valu, m, 1, 8) == (0, (-(-m // 128), 1, 1), (256, 1, 1))
+    for cid, name in enumerate(sg.configs()):
+        if name.startswith("mfma_"):
+            st, grid, block = sg.sgemm_launch_shape(cid, big, 1, big)
+            bm = int(name.split("_")[1].split("x")[0])
+            fits = -(-big // bm) * block[0] <= 2**32 - 1 if st == 0 else False
+            assert st == (0 if fits else sg.SGEMM_ERROR_TOO_LARGE), (name, st)
+            if st == 0:
+                assert grid == (-(-big // bm), 1, 1)
+        elif name.startswith("sk_"):
+            # K-tile steps x (compute units + 1) pass 2^31
+            assert sg.sgemm_launch_shape(cid, 64, 64, big)[0] == sg.SGEMM_ERROR_TOO_LARGE, name
+
+
+def test_select_config_near_int_max():
+    names = sg.configs()
+    big = 2**31 - 1
+    for M, N, K in [(1, 1, big), (big, 1, 1), (1, big, 1), (big - 128, 1, 4)]:
+        cid = sg.sgemm_select_config(M, N, K, 1.0, BAD, max(K, 1), BAD, N, BAD, N)
+        assert 0 <= cid < len(names), (M, N, K, cid)
+
+
 def test_select_config():
     names = sg.configs()
     sel = lambda M, N, K=64, alpha=1.0: sg.sgemm_select_config(M, N, K, alpha, BAD, K, BAD, N, BAD, N)

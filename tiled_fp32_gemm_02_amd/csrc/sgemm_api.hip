@@ -22,6 +22,9 @@ namespace {
 
 using sgemm_impl::StreamK;
 
+// ceil(a / b) for a >= 0, b >= 1, in 64 bits (a sum like a + b - 1 overflows int for a near 2^31).
+uint64_t cdiv64(int a, int b) { return ((uint64_t)a + (uint64_t)b - 1) / (uint64_t)b; }
+
 enum Kind { KIND_TILE16 = 0, KIND_MFMA = 1, KIND_SK = 2, KIND_VALU = 3 };
 
 typedef hipError_t (*LaunchFn)(const GemmArgs &, int batch, bool ta, bool tb, bool vec, bool edge, bool dma_ok,
@@ -114,7 +117,7 @@ hipError_t launch_sk(const GemmArgs &p, const StreamK &sk, int grid, bool ta, bo
 hipError_t launch_valu(const GemmArgs &p, int batch, bool ta, bool tb, bool, bool, bool, hipStream_t s)
 {
     constexpr int GROUP_M = 8;
-    const int tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+    const unsigned tiles = (unsigned)(cdiv64(p.M, 128) * cdiv64(p.N, 128));   // checked by the caller
     const dim3 grid(tiles, 1, batch), block(256);
     if (!ta && !tb)
         hipLaunchKernelGGL((sgemm_impl::sgemm_valu<false, false>), grid, block, 0, s, p, GROUP_M);
@@ -129,7 +132,7 @@ hipError_t launch_valu(const GemmArgs &p, int batch, bool ta, bool tb, bool, boo
 
 hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, bool, bool, hipStream_t s)
 {
-    const dim3 grid((p.N + 15) / 16, (p.M + 15) / 16, batch), block(16, 16);
+    const dim3 grid((unsigned)cdiv64(p.N, 16), (unsigned)cdiv64(p.M, 16), batch), block(16, 16);
     if (!ta && !tb)
         hipLaunchKernelGGL((sgemm_impl::sgemm_tile16<false, false>), grid, block, 0, s, p);
     else if (!ta && tb)
@@ -178,14 +181,14 @@ bool vector_ok(int opA, int opB, int M, int N, int K, const float *A, int lda, c
 
 uint64_t tile_count(const Config &c, int M, int N)
 {
-    return (uint64_t)((M + c.bm - 1) / c.bm) * (uint64_t)((N + c.bn - 1) / c.bn);
+    return cdiv64(M, c.bm) * cdiv64(N, c.bn);
 }
 
 // The stream-K kernel splits work with 32-bit arithmetic: (CUs + 1) * work < 2^31.
 bool sk_work_fits(const Config &c, int M, int N, int K, int cus)
 {
     const uint64_t tiles = tile_count(c, M, N);
-    const uint64_t work = tiles * (uint64_t)((K + c.bk - 1) / c.bk);
+    const uint64_t work = tiles * cdiv64(K, c.bk);
     return tiles <= (uint64_t)kSkMaxTiles && work * (uint64_t)(cus + 1) < (1ull << 31);
 }
 
@@ -350,7 +353,7 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
 
     if (K == 0 || alpha == 0.0f) {
         // C <- act(beta*C + bias); A and B are not read.
-        const int gx = (N + 255) / 256 < 64 ? (N + 255) / 256 : 64;
+        const int gx = cdiv64(N, 256) < 64 ? (int)cdiv64(N, 256) : 64;
         const int gy = M < 1024 ? M : 1024;
         hipLaunchKernelGGL(sgemm_impl::sgemm_scale, dim3(gx, gy, batch), dim3(256, 1), 0, stream, p);
         const hipError_t e = hipGetLastError();
@@ -375,9 +378,9 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
         StreamK sk;
         sk.counters = static_cast<unsigned *>(ws);
         sk.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + kSkCounterBytes);
-        sk.tiles_m = (M + c.bm - 1) / c.bm;
-        sk.tiles_n = (N + c.bn - 1) / c.bn;
-        sk.iters = (K + c.bk - 1) / c.bk;
+        sk.tiles_m = (int)cdiv64(M, c.bm);
+        sk.tiles_n = (int)cdiv64(N, c.bn);
+        sk.iters = (int)cdiv64(K, c.bk);
         sk.group_m = c.group_m;
         sk.work = (int)tiles * sk.iters;
         // At most one workgroup per K-tile step, so every workgroup's range is non-empty.
@@ -516,15 +519,15 @@ int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3
     if (K < 0) return -3;
     const Config &c = kConfigs[config];
     if (c.kind == KIND_TILE16) {
-        grid[0] = (N + 15) / 16; grid[1] = (M + 15) / 16; grid[2] = 1;
+        grid[0] = (int)cdiv64(N, 16); grid[1] = (int)cdiv64(M, 16); grid[2] = 1;
         block[0] = 16; block[1] = 16; block[2] = 1;
         return 0;
     }
     const uint64_t tiles = tile_count(c, M, N);
     if (c.kind == KIND_SK) {
         // One workgroup per compute unit (MI355X has 256), at most one per K-tile step.
-        if (tiles > (uint64_t)kSkMaxTiles) return SGEMM_ERROR_TOO_LARGE;
-        const uint64_t work = tiles * (uint64_t)((K + c.bk - 1) / c.bk);
+        if (!sk_work_fits(c, M, N, K, 256)) return SGEMM_ERROR_TOO_LARGE;
+        const uint64_t work = tiles * cdiv64(K, c.bk);
         grid[0] = work < 256 ? (int)work : 256; grid[1] = 1; grid[2] = 1;
         block[0] = c.threads; block[1] = 1; block[2] = 1;
         return 0;

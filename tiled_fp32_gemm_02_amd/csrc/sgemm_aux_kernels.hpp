@@ -30,18 +30,22 @@ __global__ void __launch_bounds__(256) sgemm_tile16(GemmArgs p)
     const float *__restrict__ B = p.B + (int64_t)blockIdx.z * p.strideB;
     float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
     float sum = 0.f;
-    for (int k0 = 0; k0 < p.K; k0 += 16) {
+    // K-tiles are counted rather than k advanced past K, and k offsets are compared with
+    // what is left of K, so nothing overflows for K near 2^31.
+    const int nk = ceil_div(p.K, 16);
+    for (int t = 0; t < nk; ++t) {
+        const int k0 = t * 16, kleft = p.K - k0;
         if (TA) {   // thread (ty, tx) stages op(A)(block row + tx, k0 + ty): reads run along m
-            const int ar = blockIdx.y * 16 + tx, ak = k0 + ty;
-            sa[tx][ty] = (ar < p.M && ak < p.K) ? A[(int64_t)ak * p.lda + ar] : 0.f;
+            const int ar = blockIdx.y * 16 + tx;
+            sa[tx][ty] = (ar < p.M && ty < kleft) ? A[(int64_t)(k0 + ty) * p.lda + ar] : 0.f;
         } else {
-            sa[ty][tx] = (row < p.M && k0 + tx < p.K) ? A[(int64_t)row * p.lda + k0 + tx] : 0.f;
+            sa[ty][tx] = (row < p.M && tx < kleft) ? A[(int64_t)row * p.lda + k0 + tx] : 0.f;
         }
         if (TB) {   // thread (ty, tx) stages op(B)(k0 + tx, block col + ty): reads run along k
-            const int bk = k0 + tx, bc = blockIdx.x * 16 + ty;
-            sb[tx][ty] = (bk < p.K && bc < p.N) ? B[(int64_t)bc * p.ldb + bk] : 0.f;
+            const int bc = blockIdx.x * 16 + ty;
+            sb[tx][ty] = (tx < kleft && bc < p.N) ? B[(int64_t)bc * p.ldb + k0 + tx] : 0.f;
         } else {
-            sb[ty][tx] = (k0 + ty < p.K && col < p.N) ? B[(int64_t)(k0 + ty) * p.ldb + col] : 0.f;
+            sb[ty][tx] = (ty < kleft && col < p.N) ? B[(int64_t)(k0 + ty) * p.ldb + col] : 0.f;
         }
         __syncthreads();
 #pragma unroll
@@ -110,7 +114,7 @@ sgemm_valu(GemmArgs p, int group_m)
             int k, m;
             a_coord(tid + NT * i, k, m);
             const int gm = m0 + m, gk = k0 + k;
-            const bool in = gm < M && gk < K;
+            const bool in = gm < M && k < K - k0;          // no k0 + k overflow near K = 2^31
             const float v = A[in ? (TA ? (int64_t)gk * lda + gm : (int64_t)gm * lda + gk) : 0];
             ra[i] = in ? v : 0.f;
         }
@@ -119,7 +123,7 @@ sgemm_valu(GemmArgs p, int group_m)
             int k, n;
             b_coord(tid + NT * i, k, n);
             const int gn = n0 + n, gk = k0 + k;
-            const bool in = gk < K && gn < N;
+            const bool in = k < K - k0 && gn < N;
             const float v = B[in ? (TB ? (int64_t)gn * ldb + gk : (int64_t)gk * ldb + gn) : 0];
             rb[i] = in ? v : 0.f;
         }
@@ -214,10 +218,11 @@ sgemm_valu(GemmArgs p, int group_m)
 __global__ void __launch_bounds__(256) sgemm_scale(GemmArgs p)
 {
     float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
-    for (int i = blockIdx.y * blockDim.y + threadIdx.y; i < p.M; i += gridDim.y * blockDim.y)
-        for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < p.N; j += gridDim.x * blockDim.x) {
-            float *c = C + (int64_t)i * p.ldc + j;
-            *c = finish(0.f, 0.f, p.beta, c, p.bias, j, p.act);
+    // 64-bit indices: the strides would carry a 32-bit index past 2^31 for M or N near it.
+    for (int64_t i = blockIdx.y * blockDim.y + threadIdx.y; i < p.M; i += gridDim.y * blockDim.y)
+        for (int64_t j = blockIdx.x * blockDim.x + threadIdx.x; j < p.N; j += gridDim.x * blockDim.x) {
+            float *c = C + i * p.ldc + j;
+            *c = finish(0.f, 0.f, p.beta, c, p.bias, (int)j, p.act);
         }
 }
 

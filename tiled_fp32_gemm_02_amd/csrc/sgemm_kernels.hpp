@@ -62,7 +62,8 @@ struct GemmArgs {
     int64_t strideA, strideB, strideC;  // per blockIdx.z (batched form); 0 otherwise
 };
 
-__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// ceil(a / b) for a >= 0, b >= 1, in unsigned arithmetic so that a near 2^31 does not overflow.
+__device__ __forceinline__ int ceil_div(int a, int b) { return (int)(((unsigned)a + (unsigned)b - 1u) / (unsigned)b); }
 
 // tanh-form GELU in fp32: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
 __device__ __forceinline__ float gelu_tanh(float x)

@@ -21,7 +21,9 @@ hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, boo
     constexpr int NT = WGM * WGN * WGK * 64;
     constexpr bool DMA4 = DMA && (BM * BK + BK * BN) / NT <= 16;   // 4-byte copies for unaligned rows
     constexpr int BKU = DMA ? 16 * WGK : BK;            // K-tile of the register-staged unaligned variant
-    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    // The caller has checked that tiles x NT fits one launch; the sums are unsigned so that
+    // M or N near 2^31 does not overflow.
+    const unsigned tiles = (((unsigned)p.M + BM - 1) / BM) * (((unsigned)p.N + BN - 1) / BN);
     const dim3 grid(tiles, 1, batch), block(NT);
     if (DMA && !dma_ok)
         vec = false;                                    // only the register-staged variant takes long rows
