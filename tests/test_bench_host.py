@@ -1,9 +1,11 @@
-"""Host-side pieces of bench.py (CPU only): the one-GPU guard, the sysfs clock
-reader and the oracle's bounded CPU sample."""
+"""Host-side pieces of bench.py and the sweep (CPU only): the one-GPU guard, the sysfs
+clock reader, the oracle's bounded CPU sample and the sweep's argument handling."""
 
 import os
 import subprocess
 import sys
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -42,3 +44,12 @@ def test_kernel_source_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() == h1
     src.write_text("int f() { return 2; }\n")
     assert bench.kernel_source_hash() != h1
+
+
+def test_sweep_parses_shapes_and_needs_a_gpu(monkeypatch):
+    from tiled_fp32_gemm_02_amd import sweep
+    assert sweep.parse_shapes("4096,4096,4096;1,2,3") == [(4096, 4096, 4096), (1, 2, 3)]
+    import torch
+    monkeypatch.setattr(torch.cuda, "is_available", lambda: False)
+    with pytest.raises(SystemExit):
+        sweep.main(["--shapes", "64,64,64", "--configs", "0"])
