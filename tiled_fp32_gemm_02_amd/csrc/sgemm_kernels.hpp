@@ -2,15 +2,17 @@
 // gfx950 (MI355X). op is the identity or a transpose; bias (per column) and act (none
 // or tanh-form GELU) are optional and off for the plain product.
 //
-// This header holds the MFMA kernel, sgemm_mfma, and the helpers shared with the
-// small kernels in sgemm_aux_kernels.hpp (16x16 baseline, quick-return scaling).
+// This header holds the matrix-core kernels, sgemm_mfma (one workgroup per output tile)
+// and sgemm_mfma_sk (stream-K: equal shares of the tiles x K-tiles work per compute
+// unit), and the helpers shared with the kernels in sgemm_aux_kernels.hpp (16x16
+// baseline, vector-ALU micro-tile, quick-return scaling).
 // sgemm_mfma is the hot path. A workgroup owns a BM x BN tile of C; each wave owns
 //    a (BM/WGM) x (BN/WGN) sub-tile made of 32x32 blocks computed with the CDNA fp32
 //    matrix instruction (32x32 outputs, 2 k-steps per issue). A and B tiles reach a
-//    ring of LDS stages with one barrier per K-tile, in 128-bit chunks: copied from HBM
-//    straight into LDS when the operands are 16-byte aligned (TileDMA), else staged
-//    through registers (TileIO). The next K-tile's loads are in flight while the
-//    current one is multiplied.
+//    ring of LDS stages with one barrier per K-tile: copied from HBM straight into LDS
+//    (TileDMA; 16-byte copies for 16-byte aligned rows, 4-byte copies otherwise), or
+//    staged through registers (TileIO). The next K-tile's loads (two with register
+//    staging and PF = 2) are in flight while the current one is multiplied.
 //
 // Techniques from the pages and where they come from:
 //  - Tiling through local memory so each global element is fetched once per
