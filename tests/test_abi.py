@@ -194,7 +194,13 @@ def test_select_config():
         name = names[sel(M, N)]
         bm, bn, _ = (int(x) for x in name.split("_")[1].split("x"))
         tiles = -(-M // bm) * -(-N // bn)
-        assert tiles >= 256 or bm == 64, (M, N, name, tiles)
+        assert tiles >= 256 or bm <= 64, (M, N, name, tiles)
+    # the 32-row tiles take the GPT-2 QKV and MLP-up layers and 256^3 (aligned operands only)
+    assert names[sel(1024, 2304, 768)] == "mfma_32x64x64_w1x2k2d"
+    assert names[sel(1024, 3072, 768)] == "mfma_32x128x64_w1x4k2d"
+    assert names[sel(256, 256, 256)] == "mfma_32x64x64_w1x2k2d"
+    assert not names[sg.sgemm_select_config(1024, 2304, 768, 1.0, BAD + 4, 768, BAD, 2304, BAD, 2304)].startswith(
+        "mfma_32x")
 
 
 def test_status_strings():

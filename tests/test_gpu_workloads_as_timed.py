@@ -1,8 +1,8 @@
 """GPU parity of every benchmark workload in the launch the benchmark times.
 
 The benchmark hands each product to sgemm_general_ws with a stream-K workspace, lets
-the library's cost model choose the configuration (stream-K for the GPT-2 QKV and
-MLP-down shapes, tile kernels elsewhere) and launches on a stream of its own. These
+the library's cost model choose the configuration (stream-K for the GPT-2 MLP-down
+shape, tile kernels elsewhere) and launches on a stream of its own. These
 tests make exactly that call on the workloads' own seeded inputs (and the fused
 bias + GELU form of the MLP-up layer) and compare every output entry against the
 oracle's bound, not a sample. Each call also checks that A, B and C outside its window
@@ -79,16 +79,19 @@ def test_workload_as_timed(name, ws):
     say(f"workload {name}: max |err|/bound = {worst:.4f}")
 
 
-def test_gpt2_layers_take_stream_k(ws):
-    """The two GPT-2 shapes with few tiles per compute unit are the ones the workspace
-    changes: their timed launch is a stream-K configuration."""
+def test_timed_configurations(ws):
+    """What the cost model picks for the timed launches: stream-K for the GPT-2 MLP-down
+    layer (96 tiles of 64 x 128 with K = 3072), the 32-row tiles for the QKV and MLP-up
+    layers and 256^3, and the 256 x 256 tile at 4096^3."""
     import tiled_fp32_gemm_02_amd as sg
     picks = {}
-    for name in ["gpt2_qkv", "gpt2_mlp_down", "sq4096"]:
+    for name in ["gpt2_qkv", "gpt2_mlp_up", "gpt2_mlp_down", "sq256", "sq4096"]:
         w = WORKLOADS[name]
         picks[name] = sg.sgemm_config_name(sg.sgemm_select_config_ws(
             w.M, w.N, w.K, w.alpha, ws.data_ptr(), w.lda_, ws.data_ptr(), w.ldb_, ws.data_ptr(), w.ldc_,
             ws.numel()))
     say(f"timed configurations: {picks}")
-    assert picks["gpt2_qkv"].startswith("sk_") and picks["gpt2_mlp_down"].startswith("sk_")
+    assert picks["gpt2_mlp_down"].startswith("sk_")
+    assert picks["gpt2_qkv"] == "mfma_32x64x64_w1x2k2d" and picks["sq256"] == "mfma_32x64x64_w1x2k2d"
+    assert picks["gpt2_mlp_up"] == "mfma_32x128x64_w1x4k2d"
     assert picks["sq4096"] == "mfma_256x256x32_w2x4d"

@@ -207,7 +207,7 @@ bool sk_work_fits(const Config &c, int M, int N, int K, int cus)
 // contributor, and that contributor's epilogue runs after the others').
 struct Candidate {
     const char *name;   // configuration name in the table
-    int units;          // tile area / (64 * 64)
+    double units;       // tile area / (64 * 64)
     double rate_one;    // per-CU rate with one resident workgroup
     double rate_many;   // per-CU rate with two or more
     double fixed_us;    // time that does not scale with the work
@@ -216,17 +216,24 @@ struct Candidate {
 // Least-squares fits (relative error) of time = fixed + work / rate, one per operand
 // alignment. Aligned: a sweep over 256^3 ... 6144^3, 512 x 4096 x 4096 and the GPT-2-small
 // linear layers; on every shape of it the model picks the fastest candidate or one within
-// 1%. Unaligned (rows only 4-byte aligned, 4-byte direct copies): the same kinds of
-// shapes with odd sizes (255^3 ... 6143^3, 511 x 4095 x 4095, 1000 x 1537 x 777 and the
-// GPT-2 layers one short in each dimension); the model picks the fastest on every one.
-// The 256 x 256 x 32 tile has no 4-byte-copy form (its copy offsets would not fit the
-// registers), so the unaligned table has the 256 x 256 x 16 tile instead.
+// 1%. The two 32-row tiles were fitted later on 24 shapes (256^3 ... 6144^3, 3000^3,
+// rectangles, long-K shapes and the GPT-2 layers) with the other rows left as they were;
+// with them the model picks the fastest candidate, or one within 1%, on 23 of the 24, and
+// one within 4.4% on the other (1000 x 1000 x 4000). Unaligned (rows only 4-byte aligned, 4-byte direct copies):
+// the same kinds of shapes with odd sizes (255^3 ... 6143^3, 511 x 4095 x 4095,
+// 1000 x 1537 x 777 and the GPT-2 layers one short in each dimension); the model picks the
+// fastest on every one. The 256 x 256 x 32 tile has no 4-byte-copy form (its copy offsets
+// would not fit the registers), so the unaligned table has the 256 x 256 x 16 tile instead;
+// the 32-row tiles have none either, and their register-staged form is slower than the
+// table's, so they are aligned-only.
 const Candidate kCandidates[] = {
     {"mfma_256x256x32_w2x4d", 16, 0.591, 0.580, 7.5},      // one workgroup per CU
     {"mfma_128x128x32_w2x2k2d", 4, 0.555, 0.573, 5.4},     // up to two per CU
     {"mfma_64x128x32_w2x2k2d", 2, 0.534, 0.556, 4.3},      // up to three per CU
     {"mfma_64x64x64_w2x2k4d", 1, 0.539, 0.479, 5.9},       // one per CU, 16 waves
     {"mfma_64x64x32_w2x2k2d", 1, 0.457, 0.507, 6.1},       // up to four per CU
+    {"mfma_32x64x64_w1x2k2d", 0.5, 0.499, 0.481, 4.8},     // many small tiles (GPT-2 QKV, 256^3)
+    {"mfma_32x128x64_w1x4k2d", 1, 0.449, 0.496, 4.4},      // (GPT-2 MLP-up)
 };
 const Candidate kUnalignedCandidates[] = {
     {"mfma_256x256x16_w2x4d", 16, 0.519, 0.498, 8.4},
@@ -240,8 +247,8 @@ const Candidate kSkCandidates[] = {
     {"sk_64x128x32_w2x2k2p2", 2, 0.502, 0.502, 12.2},
 };
 constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
+constexpr int kNumUnalignedCandidates = sizeof(kUnalignedCandidates) / sizeof(kUnalignedCandidates[0]);
 constexpr int kNumSkCandidates = sizeof(kSkCandidates) / sizeof(kSkCandidates[0]);
-static_assert(sizeof(kUnalignedCandidates) == sizeof(kCandidates), "one table length for both alignments");
 
 int find_config(const char *name)
 {
@@ -256,11 +263,11 @@ int find_config(const char *name)
 
 // Table ids of the candidates, looked up once.
 struct CandidateIds {
-    int id[kNumCandidates], un[kNumCandidates], sk[kNumSkCandidates];
+    int id[kNumCandidates], un[kNumUnalignedCandidates], sk[kNumSkCandidates];
     CandidateIds()
     {
         for (int i = 0; i < kNumCandidates; ++i) id[i] = find_config(kCandidates[i].name);
-        for (int i = 0; i < kNumCandidates; ++i) un[i] = find_config(kUnalignedCandidates[i].name);
+        for (int i = 0; i < kNumUnalignedCandidates; ++i) un[i] = find_config(kUnalignedCandidates[i].name);
         for (int i = 0; i < kNumSkCandidates; ++i) sk[i] = find_config(kSkCandidates[i].name);
     }
 };
@@ -272,11 +279,12 @@ int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0)
     static const CandidateIds ids;
     const Candidate *table = vec ? kCandidates : kUnalignedCandidates;
     const int *table_ids = vec ? ids.id : ids.un;
+    const int table_len = vec ? kNumCandidates : kNumUnalignedCandidates;
     const uint64_t kCUs = cus > 0 ? (uint64_t)cus : 256;
     const double unit_mflop = 2.0 * 64 * 64 * (double)K * 1e-6;    // one 64x64 tile, MFLOP
     int best = -1;
     double best_us = 0.0;
-    for (int i = 0; i < kNumCandidates; ++i) {
+    for (int i = 0; i < table_len; ++i) {
         const Candidate &cand = table[i];
         if (table_ids[i] < 0)
             continue;

@@ -231,6 +231,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 //    chunk land in 16 distinct 4-bank groups;
 //  - otherwise (rows run along m or n): consecutive lanes read consecutive chunks of one
 //    row, and rows 4 apart (the two half-waves) use opposite halves of each 16-slot window.
+//    A row of only 8 chunks (a 32-wide transposed-A tile) swaps its halves instead; there
+//    the two half-waves' rows share banks, a 2-way conflict that only this form pays.
 // Data outside the matrix is fetched at an offset past the buffer's range, which the
 // hardware answers with zeros, so partial tiles arrive zero-padded as in TileIO: per
 // chunk for VW = 4 (the extents are then multiples of 4), per float for VW = 1.
@@ -244,13 +246,13 @@ struct TileDMA {
     static constexpr int SIZE = TR * TC;
     static_assert(VW == 4 || VW == 1, "16- or 4-byte copies");
     static_assert(NT % 64 == 0 && SLOTS % NT == 0, "whole copy instructions per wave");
-    static_assert(KCONTIG ? (CPR >= 4) : (CPR >= 16), "slot swizzle needs these row lengths");
+    static_assert(KCONTIG ? (CPR >= 4) : (CPR >= 8), "slot swizzle needs these row lengths");
 
     __device__ __forceinline__ static int swz(int r)
     {
         if (KCONTIG)
             return CPR >= 16 ? (r & 15) : ((r / (16 / CPR)) & (CPR - 1));
-        return ((r >> 2) & 1) << 3;
+        return ((r >> 2) & 1) << (CPR >= 16 ? 3 : 2);
     }
     __device__ __forceinline__ static int elem(int r, int col)
     {
