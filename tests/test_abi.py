@@ -195,12 +195,15 @@ def test_select_config():
         bm, bn, _ = (int(x) for x in name.split("_")[1].split("x"))
         tiles = -(-M // bm) * -(-N // bn)
         assert tiles >= 256 or bm <= 64, (M, N, name, tiles)
-    # the 32-row tiles take the GPT-2 QKV and MLP-up layers and 256^3 (aligned operands only)
+    # the 32-row tiles take the GPT-2 layers and small squares; only the 32 x 32 one has a
+    # form for unaligned rows
     assert names[sel(1024, 2304, 768)] == "mfma_32x64x64_w1x2k2d"
     assert names[sel(1024, 3072, 768)] == "mfma_32x128x64_w1x4k2d"
-    assert names[sel(256, 256, 256)] == "mfma_32x64x64_w1x2k2d"
-    assert not names[sg.sgemm_select_config(1024, 2304, 768, 1.0, BAD + 4, 768, BAD, 2304, BAD, 2304)].startswith(
-        "mfma_32x")
+    assert names[sel(1024, 768, 3072)] == "mfma_32x32x64_w1x1k4d"
+    assert names[sel(256, 256, 256)] == "mfma_32x32x64_w1x1k4d"
+    assert names[sel(8192, 32, 8192)] == "mfma_32x32x64_w1x1k4d"
+    unaligned = names[sg.sgemm_select_config(1024, 2304, 768, 1.0, BAD + 4, 768, BAD, 2304, BAD, 2304)]
+    assert not unaligned.startswith("mfma_32x64") and not unaligned.startswith("mfma_32x128")
 
 
 def test_status_strings():

@@ -152,26 +152,31 @@ def test_auto_choice_with_workspace(ws):
     import tiled_fp32_gemm_02_amd as sg
     names = sg.configs()
     picks = {}
-    for M, N, K in [(1024, 2304, 768), (1024, 768, 3072), (4096, 4096, 4096)]:
+    for M, N, K in [(1536, 1536, 1536), (2560, 2560, 2560), (4096, 4096, 4096)]:
         cid = sg.sgemm_select_config_ws(M, N, K, 1.0, ws.data_ptr(), K, ws.data_ptr(), N, ws.data_ptr(), N,
                                         ws.numel())
         picks[(M, N, K)] = names[cid]
     assert picks[(4096, 4096, 4096)] == "mfma_256x256x32_w2x4d"       # one whole tile per CU already
-    assert picks[(1024, 768, 3072)].startswith("sk_")                # 48..96 tiles for 256 CUs
+    assert picks[(2560, 2560, 2560)].startswith("sk_")               # 400 tiles of 128^2, K long
+    assert picks[(1536, 1536, 1536)].startswith("sk_")               # 288 tiles of 64x128
 
 
 def test_tensor_form_uses_the_workspace():
+    """The tensor form passes its cached workspace, so a shape the cost model sends to
+    stream-K (1536^3) gets it; without the workspace the same call runs a tile kernel."""
     import torch
     import tiled_fp32_gemm_02_amd as sg
     rng = np.random.default_rng(17)
-    a, b = draw(rng, (1024, 3072), "normal"), draw(rng, (3072, 768), "normal002")
+    n = 1536
+    a, b = draw(rng, (n, n), "normal"), draw(rng, (n, n), "normal002")
     A, B = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    ws = sg.workspace_for(A.device)
+    assert sg.sgemm_config_name(sg.sgemm_select_config_ws(n, n, n, 1.0, A, n, B, n, A, n, ws.numel())).startswith("sk_")
     say("stream-K through the tensor form")
     C = sg.gemm(A, B)
     C2 = sg.gemm(A, B, workspace=None)
     torch.cuda.synchronize()
-    ref, bound = oracle.gemm(0, 0, 1024, 768, 3072, 1.0, a, 3072, b, 768, 0.0, None, 768)
+    ref, bound = oracle.gemm(0, 0, n, n, n, 1.0, a, n, b, n, 0.0, None, n)
     assert oracle.within_bound(C.cpu().numpy(), ref, bound)[0]
     assert oracle.within_bound(C2.cpu().numpy(), ref, bound)[0]
-    ws = sg.workspace_for(A.device)
     assert counters_clear(ws)

@@ -1,8 +1,8 @@
 """GPU parity of every benchmark workload in the launch the benchmark times.
 
 The benchmark hands each product to sgemm_general_ws with a stream-K workspace, lets
-the library's cost model choose the configuration (stream-K for the GPT-2 MLP-down
-shape, tile kernels elsewhere) and launches on a stream of its own. These
+the library's cost model choose the configuration (it may pick stream-K; for these
+shapes it picks tile kernels) and launches on a stream of its own. These
 tests make exactly that call on the workloads' own seeded inputs (and the fused
 bias + GELU form of the MLP-up layer) and compare every output entry against the
 oracle's bound, not a sample. Each call also checks that A, B and C outside its window
@@ -80,18 +80,19 @@ def test_workload_as_timed(name, ws):
 
 
 def test_timed_configurations(ws):
-    """What the cost model picks for the timed launches: stream-K for the GPT-2 MLP-down
-    layer (96 tiles of 64 x 128 with K = 3072), the 32-row tiles for the QKV and MLP-up
-    layers and 256^3, and the 256 x 256 tile at 4096^3."""
+    """What the cost model picks for the timed launches, with a workspace: the 32-row tiles
+    for the three GPT-2 layers and 256^3, the 64 x 64 x 64 tile at 1024^3 and the
+    256 x 256 tile at 4096^3 (no stream-K: each of these beats it)."""
     import tiled_fp32_gemm_02_amd as sg
     picks = {}
-    for name in ["gpt2_qkv", "gpt2_mlp_up", "gpt2_mlp_down", "sq256", "sq4096"]:
+    for name in ["gpt2_qkv", "gpt2_mlp_up", "gpt2_mlp_down", "sq256", "sq1024", "sq4096"]:
         w = WORKLOADS[name]
         picks[name] = sg.sgemm_config_name(sg.sgemm_select_config_ws(
             w.M, w.N, w.K, w.alpha, ws.data_ptr(), w.lda_, ws.data_ptr(), w.ldb_, ws.data_ptr(), w.ldc_,
             ws.numel()))
     say(f"timed configurations: {picks}")
-    assert picks["gpt2_mlp_down"].startswith("sk_")
-    assert picks["gpt2_qkv"] == "mfma_32x64x64_w1x2k2d" and picks["sq256"] == "mfma_32x64x64_w1x2k2d"
+    assert picks["gpt2_qkv"] == "mfma_32x64x64_w1x2k2d"
     assert picks["gpt2_mlp_up"] == "mfma_32x128x64_w1x4k2d"
+    assert picks["gpt2_mlp_down"] == "mfma_32x32x64_w1x1k4d" and picks["sq256"] == "mfma_32x32x64_w1x1k4d"
+    assert picks["sq1024"] == "mfma_64x64x64_w2x2k4d"
     assert picks["sq4096"] == "mfma_256x256x32_w2x4d"

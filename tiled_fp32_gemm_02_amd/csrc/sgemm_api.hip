@@ -211,40 +211,51 @@ struct Candidate {
     double rate_one;    // per-CU rate with one resident workgroup
     double rate_many;   // per-CU rate with two or more
     double fixed_us;    // time that does not scale with the work
+    double round_us;    // time per round of tiles on a CU beyond its work (a tile's first
+                        // loads and epilogue), where short K-loops do not hide it
 };
 
 // Least-squares fits (relative error) of time = fixed + work / rate, one per operand
 // alignment. Aligned: a sweep over 256^3 ... 6144^3, 512 x 4096 x 4096 and the GPT-2-small
 // linear layers; on every shape of it the model picks the fastest candidate or one within
-// 1%. The two 32-row tiles were fitted later on 24 shapes (256^3 ... 6144^3, 3000^3,
-// rectangles, long-K shapes and the GPT-2 layers) with the other rows left as they were;
-// with them the model picks the fastest candidate, or one within 1%, on 23 of the 24, and
-// one within 4.4% on the other (1000 x 1000 x 4000). Unaligned (rows only 4-byte aligned, 4-byte direct copies):
+// 1%. The 32-row tiles were fitted later, with the other rows left as they were, on 40
+// shapes: the 24 of a second sweep (256^3 ... 6144^3, 3000^3, rectangles, 1000 x 1000 x 4000
+// and the GPT-2 layers) and 16 skinny or long-K ones (128 x 4096 x 4096, 8192 x 32 x 8192,
+// 16384 x 16 x 16384, 2048 x 256 x 16384, 512 x 512 x 8192 and the like). The 32 x 64 and
+// 32 x 32 rows carry a cost per round of tiles (a tile's first loads and epilogue, which
+// short K-loops do not hide); without it the QKV layer (9 rounds of 12 K-tiles) went to the
+// 32 x 32 tile, 5% slower. With a workspace the picks then average 1.008 of the fastest
+// candidate on the 40 shapes, every benchmark shape gets its fastest, and the worst is
+// 1.135 (8192 x 128 x 8192 on the 64x64x64 tile, as before the 32-row tiles). Unaligned (rows only 4-byte aligned, 4-byte direct copies):
 // the same kinds of shapes with odd sizes (255^3 ... 6143^3, 511 x 4095 x 4095,
 // 1000 x 1537 x 777 and the GPT-2 layers one short in each dimension); the model picks the
 // fastest on every one. The 256 x 256 x 32 tile has no 4-byte-copy form (its copy offsets
 // would not fit the registers), so the unaligned table has the 256 x 256 x 16 tile instead;
-// the 32-row tiles have none either, and their register-staged form is slower than the
-// table's, so they are aligned-only.
+// the 32 x 64 and 32 x 128 tiles have none either, and their register-staged form is slower
+// than the table's, so they are aligned-only. The 32 x 32 tile has a 4-byte-copy form; its
+// unaligned row, fitted on 24 odd-sized shapes (skinny and long-K ones included), makes the
+// model pick the fastest candidate on all of them.
 const Candidate kCandidates[] = {
-    {"mfma_256x256x32_w2x4d", 16, 0.591, 0.580, 7.5},      // one workgroup per CU
-    {"mfma_128x128x32_w2x2k2d", 4, 0.555, 0.573, 5.4},     // up to two per CU
-    {"mfma_64x128x32_w2x2k2d", 2, 0.534, 0.556, 4.3},      // up to three per CU
-    {"mfma_64x64x64_w2x2k4d", 1, 0.539, 0.479, 5.9},       // one per CU, 16 waves
-    {"mfma_64x64x32_w2x2k2d", 1, 0.457, 0.507, 6.1},       // up to four per CU
-    {"mfma_32x64x64_w1x2k2d", 0.5, 0.499, 0.481, 4.8},     // many small tiles (GPT-2 QKV, 256^3)
-    {"mfma_32x128x64_w1x4k2d", 1, 0.449, 0.496, 4.4},      // (GPT-2 MLP-up)
+    {"mfma_256x256x32_w2x4d", 16, 0.591, 0.580, 7.5, 0},      // one workgroup per CU
+    {"mfma_128x128x32_w2x2k2d", 4, 0.555, 0.573, 5.4, 0},     // up to two per CU
+    {"mfma_64x128x32_w2x2k2d", 2, 0.534, 0.556, 4.3, 0},      // up to three per CU
+    {"mfma_64x64x64_w2x2k4d", 1, 0.539, 0.479, 5.9, 0},       // one per CU, 16 waves
+    {"mfma_64x64x32_w2x2k2d", 1, 0.457, 0.507, 6.1, 0},       // up to four per CU
+    {"mfma_32x64x64_w1x2k2d", 0.5, 0.405, 0.507, 2.9, 1.12},  // many small tiles (GPT-2 QKV)
+    {"mfma_32x128x64_w1x4k2d", 1, 0.449, 0.496, 4.4, 0},      // (GPT-2 MLP-up)
+    {"mfma_32x32x64_w1x1k4d", 0.25, 0.215, 0.442, 2.4, 0.67}, // (GPT-2 MLP-down, up to 768^3, skinny)
 };
 const Candidate kUnalignedCandidates[] = {
-    {"mfma_256x256x16_w2x4d", 16, 0.519, 0.498, 8.4},
-    {"mfma_128x128x32_w2x2k2d", 4, 0.462, 0.467, 6.7},
-    {"mfma_64x128x32_w2x2k2d", 2, 0.450, 0.472, 5.9},
-    {"mfma_64x64x64_w2x2k4d", 1, 0.421, 0.437, 8.2},
-    {"mfma_64x64x32_w2x2k2d", 1, 0.376, 0.441, 7.4},
+    {"mfma_256x256x16_w2x4d", 16, 0.519, 0.498, 8.4, 0},
+    {"mfma_128x128x32_w2x2k2d", 4, 0.462, 0.467, 6.7, 0},
+    {"mfma_64x128x32_w2x2k2d", 2, 0.450, 0.472, 5.9, 0},
+    {"mfma_64x64x64_w2x2k4d", 1, 0.421, 0.437, 8.2, 0},
+    {"mfma_64x64x32_w2x2k2d", 1, 0.376, 0.441, 7.4, 0},
+    {"mfma_32x32x64_w1x1k4d", 0.25, 0.360, 0.360, 6.8, 1.04},
 };
 const Candidate kSkCandidates[] = {
-    {"sk_128x128x32_w2x2k2p2", 4, 0.534, 0.534, 17.1},
-    {"sk_64x128x32_w2x2k2p2", 2, 0.502, 0.502, 12.2},
+    {"sk_128x128x32_w2x2k2p2", 4, 0.534, 0.534, 17.1, 0},
+    {"sk_64x128x32_w2x2k2p2", 2, 0.502, 0.502, 12.2, 0},
 };
 constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
 constexpr int kNumUnalignedCandidates = sizeof(kUnalignedCandidates) / sizeof(kUnalignedCandidates[0]);
@@ -290,8 +301,8 @@ int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0)
             continue;
         const uint64_t tiles = tile_count(kConfigs[table_ids[i]], M, N);
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
-        const double us =
-            cand.fixed_us + (double)rounds * cand.units * unit_mflop / (rounds >= 2 ? cand.rate_many : cand.rate_one);
+        const double us = cand.fixed_us + (double)rounds * cand.round_us +
+                          (double)rounds * cand.units * unit_mflop / (rounds >= 2 ? cand.rate_many : cand.rate_one);
         if (best < 0 || us < best_us) {
             best = table_ids[i];
             best_us = us;

@@ -231,8 +231,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 //    chunk land in 16 distinct 4-bank groups;
 //  - otherwise (rows run along m or n): consecutive lanes read consecutive chunks of one
 //    row, and rows 4 apart (the two half-waves) use opposite halves of each 16-slot window.
-//    A row of only 8 chunks (a 32-wide transposed-A tile) swaps its halves instead; there
-//    the two half-waves' rows share banks, a 2-way conflict that only this form pays.
+//    A row of only 8 chunks (a 32-wide tile) fills half the banks, so there the rows
+//    themselves are permuted instead: logical row r sits at row r ^ ((r >> 2) & 1), which
+//    puts rows 4 apart in opposite halves of the banks.
 // Data outside the matrix is fetched at an offset past the buffer's range, which the
 // hardware answers with zeros, so partial tiles arrive zero-padded as in TileIO: per
 // chunk for VW = 4 (the extents are then multiples of 4), per float for VW = 1.
@@ -248,22 +249,26 @@ struct TileDMA {
     static_assert(NT % 64 == 0 && SLOTS % NT == 0, "whole copy instructions per wave");
     static_assert(KCONTIG ? (CPR >= 4) : (CPR >= 8), "slot swizzle needs these row lengths");
 
+    static constexpr bool ROWPERM = !KCONTIG && CPR == 8;
+    static_assert(!ROWPERM || TR % 2 == 0, "row pairs");
     __device__ __forceinline__ static int swz(int r)
     {
         if (KCONTIG)
             return CPR >= 16 ? (r & 15) : ((r / (16 / CPR)) & (CPR - 1));
-        return ((r >> 2) & 1) << (CPR >= 16 ? 3 : 2);
+        return ROWPERM ? 0 : ((r >> 2) & 1) << 3;
     }
+    // Physical row of logical row r (an involution: it also maps physical to logical).
+    __device__ __forceinline__ static int prow(int r) { return ROWPERM ? (r ^ ((r >> 2) & 1)) : r; }
     __device__ __forceinline__ static int elem(int r, int col)
     {
-        return 4 * (r * CPR + ((col >> 2) ^ swz(r))) + (col & 3);
+        return 4 * (prow(r) * CPR + ((col >> 2) ^ swz(r))) + (col & 3);
     }
 
     // Row and column, inside the tile, of the first float that copy c brings to this lane.
     __device__ __forceinline__ static void where(int c, int tid, int &r, int &col)
     {
         const int f = ((tid >> 6) * 64 + c * NT + (tid & 63)) * VW;   // its LDS position
-        r = f / TC;
+        r = prow(f / TC);
         const int cl = f % TC;
         col = 4 * ((cl >> 2) ^ swz(r)) + (cl & 3);
     }
