@@ -81,8 +81,8 @@ def test_workload_as_timed(name, ws):
 
 def test_timed_configurations(ws):
     """What the cost model picks for the timed launches, with a workspace: the 32-row tiles
-    for the three GPT-2 layers and 256^3, the 64 x 64 x 64 tile at 1024^3 and the
-    256 x 256 tile at 4096^3 (no stream-K: each of these beats it)."""
+    for the three GPT-2 layers, 256^3 and 1024^3, and the 256 x 256 tile at 4096^3 (no
+    stream-K: each of these beats it)."""
     import tiled_fp32_gemm_02_amd as sg
     picks = {}
     for name in ["gpt2_qkv", "gpt2_mlp_up", "gpt2_mlp_down", "sq256", "sq1024", "sq4096"]:
@@ -94,5 +94,5 @@ def test_timed_configurations(ws):
     assert picks["gpt2_qkv"] == "mfma_32x64x64_w1x2k2d"
     assert picks["gpt2_mlp_up"] == "mfma_32x128x64_w1x4k2d"
     assert picks["gpt2_mlp_down"] == "mfma_32x32x64_w1x1k4d" and picks["sq256"] == "mfma_32x32x64_w1x1k4d"
-    assert picks["sq1024"] == "mfma_64x64x64_w2x2k4d"
+    assert picks["sq1024"] == "mfma_32x64x64_w1x2k2d"
     assert picks["sq4096"] == "mfma_256x256x32_w2x4d"

@@ -224,9 +224,11 @@ struct Candidate {
 // 16384 x 16 x 16384, 2048 x 256 x 16384, 512 x 512 x 8192 and the like). The 32 x 64 and
 // 32 x 32 rows carry a cost per round of tiles (a tile's first loads and epilogue, which
 // short K-loops do not hide); without it the QKV layer (9 rounds of 12 K-tiles) went to the
-// 32 x 32 tile, 5% slower. With a workspace the picks then average 1.008 of the fastest
-// candidate on the 40 shapes, every benchmark shape gets its fastest, and the worst is
-// 1.135 (8192 x 128 x 8192 on the 64x64x64 tile, as before the 32-row tiles). Unaligned (rows only 4-byte aligned, 4-byte direct copies):
+// 32 x 32 tile, 5% slower. The 64x64x64 row was refit the same way on the 40 shapes; its
+// first fit assumed the rate of short K-loops, which long ones (latency-bound with one
+// K-tile in flight) do not reach. With a workspace the picks then average 1.004 of the
+// fastest candidate on the 40 shapes and the worst is 1.043 (32 x 8192 x 8192); every
+// benchmark shape gets its fastest but 1024^3, where the 32 x 64 pick is within 0.5%. Unaligned (rows only 4-byte aligned, 4-byte direct copies):
 // the same kinds of shapes with odd sizes (255^3 ... 6143^3, 511 x 4095 x 4095,
 // 1000 x 1537 x 777 and the GPT-2 layers one short in each dimension); the model picks the
 // fastest on every one. The 256 x 256 x 32 tile has no 4-byte-copy form (its copy offsets
@@ -239,7 +241,7 @@ const Candidate kCandidates[] = {
     {"mfma_256x256x32_w2x4d", 16, 0.591, 0.580, 7.5, 0},      // one workgroup per CU
     {"mfma_128x128x32_w2x2k2d", 4, 0.555, 0.573, 5.4, 0},     // up to two per CU
     {"mfma_64x128x32_w2x2k2d", 2, 0.534, 0.556, 4.3, 0},      // up to three per CU
-    {"mfma_64x64x64_w2x2k4d", 1, 0.539, 0.479, 5.9, 0},       // one per CU, 16 waves
+    {"mfma_64x64x64_w2x2k4d", 1, 0.491, 0.518, 0.6, 4.10},    // one per CU, 16 waves
     {"mfma_64x64x32_w2x2k2d", 1, 0.457, 0.507, 6.1, 0},       // up to four per CU
     {"mfma_32x64x64_w1x2k2d", 0.5, 0.405, 0.507, 2.9, 1.12},  // many small tiles (GPT-2 QKV)
     {"mfma_32x128x64_w1x4k2d", 1, 0.449, 0.496, 4.4, 0},      // (GPT-2 MLP-up)
