@@ -176,8 +176,8 @@ int sgemm_strided_batched(int M, int N, int K, float alpha,
  * sgemm_general with a workspace, which lets the library use stream-K configurations
  * (names starting "sk_"). Those split the product's tiles x K-tiles work into one equal
  * contiguous share per compute unit, so the chip stays full when the tile count does
- * not divide evenly over the compute units (for example the GPT-2-small MLP-down layer,
- * 1536^3, 2560^3 and 3072^3).
+ * not divide evenly over the compute units and K is long enough to pay for the fixup
+ * (for example 1536^3, 2560^3 and 3072^3).
  * A tile shared by several workgroups is finished by the one that arrives last, which
  * adds the partial sums in a fixed order: results stay bitwise reproducible from run
  * to run, and within the same error bound as every other configuration. Stream-K runs
