@@ -7,9 +7,14 @@ library next to this file:
 * ``csrc/sgemm_inst.hip`` four times, once per operand form (SGEMM_TA, SGEMM_TB),
   each instantiating every MFMA configuration of ``csrc/sgemm_configs.inc``.
 
-It also builds ``mfma_rate``, a standalone executable that measures the fp32 matrix-core
-rate and the shader clock the chip sustains (no part of the library; a ceiling to read
-the GEMM's timings against).
+It also builds two standalone executables, no part of the library:
+
+* ``mfma_rate`` measures the fp32 matrix-core rate and the shader clock the chip
+  sustains (a ceiling to read the GEMM's timings against);
+* ``layout_check`` checks on the host, without a GPU, the LDS layouts of the
+  direct-copy kernels with the kernels' own index functions: every copy lands where
+  the layout puts its data, the tile is covered once, and the fragment reads are free
+  of bank conflicts in a model of the LDS.
 
 Flags:
 
@@ -34,6 +39,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libsgemm.so")
 RATE_PATH = os.path.join(HERE, "mfma_rate")
+LAYOUT_CHECK_PATH = os.path.join(HERE, "layout_check")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -58,7 +64,7 @@ def hipcc() -> str:
 
 
 def _jobs() -> int:
-    return max(1, min(len(UNITS) + 1, os.cpu_count() or 1, int(os.environ.get("MAX_JOBS", "16"))))
+    return max(1, min(len(UNITS) + 2, os.cpu_count() or 1, int(os.environ.get("MAX_JOBS", "16"))))
 
 
 def _run(cmd, verbose):
@@ -82,9 +88,12 @@ def build(verbose: bool = False) -> str:
             cmds.append([hipcc(), *COMMON_FLAGS, "-fPIC", *defs, "-c", os.path.join(CSRC, src), "-o", obj])
         rate_tmp = RATE_PATH + f".tmp{os.getpid()}"
         cmds.append([hipcc(), *COMMON_FLAGS, os.path.join(CSRC, "mfma_rate.hip"), "-o", rate_tmp])
+        check_tmp = LAYOUT_CHECK_PATH + f".tmp{os.getpid()}"
+        cmds.append(_layout_check_cmd(check_tmp))
         with ThreadPoolExecutor(max_workers=_jobs()) as pool:
             list(pool.map(lambda c: _run(c, verbose), cmds))
         os.replace(rate_tmp, RATE_PATH)
+        os.replace(check_tmp, LAYOUT_CHECK_PATH)
         tmp = LIB_PATH + f".tmp{os.getpid()}"
         _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
         os.replace(tmp, LIB_PATH)
@@ -107,6 +116,20 @@ def device_asm(out_path: str) -> str:
                 f.write(open(out).read())
                 f.write("\n")
     return out_path
+
+
+def _layout_check_cmd(out):
+    return [hipcc(), *COMMON_FLAGS, os.path.join(CSRC, "layout_check.hip"), "-o", out]
+
+
+def ensure_layout_check() -> str:
+    """Build layout_check if it is missing or older than any kernel source."""
+    if not os.path.exists(LAYOUT_CHECK_PATH) or \
+            os.path.getmtime(LAYOUT_CHECK_PATH) < max(os.path.getmtime(f) for f in SOURCES):
+        tmp = LAYOUT_CHECK_PATH + f".tmp{os.getpid()}"
+        _run(_layout_check_cmd(tmp), False)
+        os.replace(tmp, LAYOUT_CHECK_PATH)
+    return LAYOUT_CHECK_PATH
 
 
 def ensure_built() -> str:

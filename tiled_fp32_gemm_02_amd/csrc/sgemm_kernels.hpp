@@ -247,25 +247,26 @@ struct TileDMA {
     static constexpr int SIZE = TR * TC;
     static_assert(VW == 4 || VW == 1, "16- or 4-byte copies");
     static_assert(NT % 64 == 0 && SLOTS % NT == 0, "whole copy instructions per wave");
-    static_assert(KCONTIG ? (CPR >= 4) : (CPR >= 8), "slot swizzle needs these row lengths");
+    static_assert(KCONTIG ? (CPR == 4 || CPR == 8 || CPR % 16 == 0) : (CPR == 8 || CPR % 16 == 0),
+                  "slot swizzle needs these row lengths");
 
     static constexpr bool ROWPERM = !KCONTIG && CPR == 8;
     static_assert(!ROWPERM || TR % 2 == 0, "row pairs");
-    __device__ __forceinline__ static int swz(int r)
+    __host__ __device__ __forceinline__ static int swz(int r)
     {
         if (KCONTIG)
             return CPR >= 16 ? (r & 15) : ((r / (16 / CPR)) & (CPR - 1));
         return ROWPERM ? 0 : ((r >> 2) & 1) << 3;
     }
     // Physical row of logical row r (an involution: it also maps physical to logical).
-    __device__ __forceinline__ static int prow(int r) { return ROWPERM ? (r ^ ((r >> 2) & 1)) : r; }
-    __device__ __forceinline__ static int elem(int r, int col)
+    __host__ __device__ __forceinline__ static int prow(int r) { return ROWPERM ? (r ^ ((r >> 2) & 1)) : r; }
+    __host__ __device__ __forceinline__ static int elem(int r, int col)
     {
         return 4 * (prow(r) * CPR + ((col >> 2) ^ swz(r))) + (col & 3);
     }
 
     // Row and column, inside the tile, of the first float that copy c brings to this lane.
-    __device__ __forceinline__ static void where(int c, int tid, int &r, int &col)
+    __host__ __device__ __forceinline__ static void where(int c, int tid, int &r, int &col)
     {
         const int f = ((tid >> 6) * 64 + c * NT + (tid & 63)) * VW;   // its LDS position
         r = prow(f / TC);
