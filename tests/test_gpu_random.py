@@ -1,4 +1,5 @@
-"""GPU parity on seeded random cases: the automatic configuration choice, with a
+"""GPU parity on seeded random cases: the automatic configuration choice (and, in a second
+test, a configuration drawn at random per case), with a
 stream-K workspace, over random shapes, operand forms, base offsets, leading-dimension
 padding, alpha/beta, bias and activation.
 
@@ -49,34 +50,53 @@ def draw_case(rng):
     return M, N, K, opA, opB, offsets, pads, alpha, beta, with_bias, act
 
 
-@pytest.mark.parametrize("seed", range(8))
-def test_random_cases(seed, ws):
+def run_case(rng, seed, case, ws, config=-1):
+    """Draw one case, run it through sgemm_general_ws with `config` (-1: the automatic
+    choice) and check it against the oracle, the guard bands and the tile counters."""
     import torch
     import tiled_fp32_gemm_02_amd as sg
+    M, N, K, opA, opB, offsets, pads, alpha, beta, with_bias, act = draw_case(rng)
+    a, b = draw(rng, (M, K), "normal"), draw(rng, (K, N), "normal")
+    c = draw(rng, (M, N), "uniform")
+    bias = draw(rng, (N,), "normal") if with_bias else None
+    As = np.ascontiguousarray(a.T if opA else a)
+    Bs = np.ascontiguousarray(b.T if opB else b)
+    lda, ldb, ldc = As.shape[1] + pads[0], Bs.shape[1] + pads[1], N + pads[2]
+    say(f"random seed {seed} case {case} config {config}: {M}x{N}x{K} op {opA}{opB} offsets {offsets} "
+        f"pads {pads} alpha {alpha} beta {beta} bias {with_bias} act {act}")
+    dA = DevMatrix(As, As.shape[0], As.shape[1], lda, offsets[0])
+    dB = DevMatrix(Bs, Bs.shape[0], Bs.shape[1], ldb, offsets[1])
+    dC = DevMatrix(c, M, N, ldc, offsets[2])
+    dbias = torch.from_numpy(bias).cuda() if bias is not None else None
+    st = sg.sgemm_general_ws(config, opA, opB, M, N, K, alpha, dA.ptr, lda, dB.ptr, ldb, beta, dC.ptr, ldc,
+                             dbias, act, ws, ws.numel(), torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == 0, (seed, case, config, st)
+    flat = dC.fetch()
+    assert dA.unchanged() and dB.unchanged() and dC.outside_unchanged(flat)
+    ref, bound = oracle.gemm(opA, opB, M, N, K, alpha, As, As.shape[1], Bs, Bs.shape[1], beta, c, N,
+                             bias, act)
+    ok, worst, idx = oracle.within_bound(dC.window(flat), ref, bound)
+    assert ok, (seed, case, config, worst, idx)
+    counters = ws[:4 * COUNTER_WORDS].view(dtype=torch.int32)
+    assert int(counters.abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_cases(seed, ws):
     rng = np.random.default_rng(1000 + seed)
     for case in range(16):
-        M, N, K, opA, opB, offsets, pads, alpha, beta, with_bias, act = draw_case(rng)
-        a, b = draw(rng, (M, K), "normal"), draw(rng, (K, N), "normal")
-        c = draw(rng, (M, N), "uniform")
-        bias = draw(rng, (N,), "normal") if with_bias else None
-        As = np.ascontiguousarray(a.T if opA else a)
-        Bs = np.ascontiguousarray(b.T if opB else b)
-        lda, ldb, ldc = As.shape[1] + pads[0], Bs.shape[1] + pads[1], N + pads[2]
-        say(f"random seed {seed} case {case}: {M}x{N}x{K} op {opA}{opB} offsets {offsets} pads {pads} "
-            f"alpha {alpha} beta {beta} bias {with_bias} act {act}")
-        dA = DevMatrix(As, As.shape[0], As.shape[1], lda, offsets[0])
-        dB = DevMatrix(Bs, Bs.shape[0], Bs.shape[1], ldb, offsets[1])
-        dC = DevMatrix(c, M, N, ldc, offsets[2])
-        dbias = torch.from_numpy(bias).cuda() if bias is not None else None
-        st = sg.sgemm_general_ws(-1, opA, opB, M, N, K, alpha, dA.ptr, lda, dB.ptr, ldb, beta, dC.ptr, ldc,
-                                 dbias, act, ws, ws.numel(), torch.cuda.current_stream())
-        torch.cuda.synchronize()
-        assert st == 0, st
-        flat = dC.fetch()
-        assert dA.unchanged() and dB.unchanged() and dC.outside_unchanged(flat)
-        ref, bound = oracle.gemm(opA, opB, M, N, K, alpha, As, As.shape[1], Bs, Bs.shape[1], beta, c, N,
-                                 bias, act)
-        ok, worst, idx = oracle.within_bound(dC.window(flat), ref, bound)
-        assert ok, (seed, case, worst, idx)
-        counters = ws[:4 * COUNTER_WORDS].view(dtype=torch.int32)
-        assert int(counters.abs().sum().item()) == 0
+        run_case(rng, seed, case, ws)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_cases_every_config(seed, ws):
+    """The same random cases with the configuration forced, drawn uniformly over every
+    configuration (the 16x16 rung, the vector-ALU micro-tile, each matrix-core tile and
+    stream-K), so each kernel meets random offsets, padding, operand forms and epilogues."""
+    import tiled_fp32_gemm_02_amd as sg
+    n = len(sg.configs())
+    rng = np.random.default_rng(2000 + seed)
+    for case in range(32):
+        config = int(rng.integers(n))
+        run_case(rng, seed, case, ws, config)
