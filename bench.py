@@ -321,7 +321,7 @@ def main():
                    "step_us_p90": round(float(np.percentile(per_step, 90)) * 1e3, 2),
                    "sclk_mhz_before": sclk_before, "sclk_mhz_after": sclk_after},
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
+                   "arch": getattr(props, "gcnArchName", ""), "hip": torch.version.hip},
         "check": {"sampled_entries": int(checked), "max_err_over_bound": round(worst_all, 4)},
     }
     if not args.no_cpu_baseline:
