@@ -92,6 +92,27 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def tile_dims(config_name: str):
+    """(BM, BN) of a configuration from its name (e.g. mfma_256x256x32_w2x4d -> (256, 256);
+    tile16 -> (16, 16))."""
+    import re
+    if config_name == "tile16":
+        return 16, 16
+    m = re.search(r"_(\d+)x(\d+)x\d+", config_name)
+    if not m:
+        raise ValueError(f"no tile shape in configuration name {config_name!r}")
+    return int(m.group(1)), int(m.group(2))
+
+
+def lds_fill_bytes(M: int, N: int, K: int, config_name: str) -> float:
+    """Bytes the tiles copy from memory into LDS (or registers) per launch: each BM x BN tile
+    reads a BM-row panel of A and a BN-column panel of B over all of K, so
+    4 M N K (1/BM + 1/BN) in total. The L2 caches serve what HBM does not (the measured
+    FETCH_SIZE is the part that misses)."""
+    bm, bn = tile_dims(config_name)
+    return 4.0 * M * N * K * (1.0 / bm + 1.0 / bn)
+
+
 def recorded_traffic(workload: str, config_name: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on
     the current kernel source and the same workload and configuration; else None."""
@@ -323,6 +344,9 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", ""), "hip": torch.version.hip},
         "check": {"sampled_entries": int(checked), "max_err_over_bound": round(worst_all, 4)},
+        "tile_traffic": {"global_to_lds_bytes": round(sum(lds_fill_bytes(p["w"].M, p["w"].N, p["w"].K, p["cfg_name"])
+                                                          for p in probs)),
+                         "model": "4*M*N*K*(1/BM + 1/BN) per step, the tiles' operand panels"},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")

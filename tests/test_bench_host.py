@@ -53,3 +53,20 @@ def test_sweep_parses_shapes_and_needs_a_gpu(monkeypatch):
     monkeypatch.setattr(torch.cuda, "is_available", lambda: False)
     with pytest.raises(SystemExit):
         sweep.main(["--shapes", "64,64,64", "--configs", "0"])
+
+
+def test_tile_traffic_model():
+    """The tiles' operand-panel bytes: 4 M N K (1/BM + 1/BN), from the configuration's name."""
+    import bench
+    assert bench.tile_dims("mfma_256x256x32_w2x4d") == (256, 256)
+    assert bench.tile_dims("mfma_32x128x64_w1x4k2d") == (32, 128)
+    assert bench.tile_dims("sk_64x128x32_w2x2k2p2") == (64, 128)
+    assert bench.tile_dims("valu_128x128x8_t8x8") == (128, 128)
+    assert bench.tile_dims("tile16") == (16, 16)
+    # 4096^3 on 256 x 256 tiles: 2 * 4096^3 * 4 / 256 bytes
+    assert bench.lds_fill_bytes(4096, 4096, 4096, "mfma_256x256x32_w2x4d") == 2 * 4 * 4096 ** 3 / 256
+    # the pages' 16 x 16 tile reads MNK/8 floats
+    assert bench.lds_fill_bytes(64, 64, 64, "tile16") == 4 * 64 ** 3 / 8
+    import tiled_fp32_gemm_02_amd as sg
+    for name in sg.configs():
+        bench.tile_dims(name)
