@@ -65,7 +65,7 @@ def test_tile_traffic_model():
     assert bench.tile_dims("tile16") == (16, 16)
     # 4096^3 on 256 x 256 tiles: 2 * 4096^3 * 4 / 256 bytes
     assert bench.lds_fill_bytes(4096, 4096, 4096, "mfma_256x256x32_w2x4d") == 2 * 4 * 4096 ** 3 / 256
-    # the pages' 16 x 16 tile reads MNK/8 floats
+    # 16 x 16 tiles read MNK/8 floats (AutoMine++ #4, section "current algorithm")
     assert bench.lds_fill_bytes(64, 64, 64, "tile16") == 4 * 64 ** 3 / 8
     import tiled_fp32_gemm_02_amd as sg
     for name in sg.configs():
