@@ -92,6 +92,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo), or ''."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def tile_dims(config_name: str):
     """(BM, BN) of a configuration from its name (e.g. mfma_256x256x32_w2x4d -> (256, 256);
     tile16 -> (16, 16))."""
@@ -342,7 +354,8 @@ def main():
                    "step_us_p90": round(float(np.percentile(per_step, 90)) * 1e3, 2),
                    "sclk_mhz_before": sclk_before, "sclk_mhz_after": sclk_after},
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", ""), "hip": torch.version.hip},
+                   "arch": getattr(props, "gcnArchName", ""), "hip": torch.version.hip,
+                   "host_cpu": host_cpu_model(), "host_threads": len(os.sched_getaffinity(0))},
         "check": {"sampled_entries": int(checked), "max_err_over_bound": round(worst_all, 4)},
         "tile_traffic": {"global_to_lds_bytes": round(sum(lds_fill_bytes(p["w"].M, p["w"].N, p["w"].K, p["cfg_name"])
                                                           for p in probs)),
