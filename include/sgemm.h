@@ -233,6 +233,32 @@ int sgemm_config_count(void);
 const char *sgemm_config_name(int config);
 
 /*
+ * One static line of space-separated key=value fields describing configuration
+ * `config`, or NULL if it is out of range. The fields are the tile parameters that a
+ * tiled kernel is built from ("Micro_gemm_4x4 - cuBLAS micro GEMM skeleton", section
+ * "Tile parameters"), as this library sizes them:
+ *   name          as sgemm_config_name
+ *   kind          tile16 (one output per thread), mfma (one workgroup per tile),
+ *                 streamk (equal shares of tiles x K-tiles per compute unit), valu
+ *                 (register micro-tile on vector FMAs)
+ *   tile          BMxBNxBK: the workgroup's output tile and the k depth of one LDS stage
+ *   waves         WGMxWGN: waves over the tile (1x1 for the non-matrix kinds)
+ *   kgroups       wave groups splitting each stage's k range
+ *   threads       threads per workgroup
+ *   ahead         K-tiles whose loads run ahead of the one being multiplied
+ *   loader        direct-16B (HBM -> LDS copies), staged-16B (through registers), or the
+ *                 element-wise forms of tile16 and valu
+ *   lds_bytes     static LDS per workgroup
+ *   band          tile rows per band of the workgroup order
+ *   unaligned     the form run when rows are only 4-byte aligned: direct-4B, staged-4B,
+ *                 or for streamk the data-parallel kernel of its tile, register-staged
+ *   unaligned_bk  the K-tile of that form
+ *   compute       the instruction that does the multiply-adds
+ * The string is owned by the library and valid for the life of the process.
+ */
+const char *sgemm_config_describe(int config);
+
+/*
  * The configuration sgemm would use for these arguments (host logic only; no GPU
  * call). Returns an id in [0, sgemm_config_count()), or -1 when no kernel would
  * run (M == 0 or N == 0) or the quick-return scaling kernel would (K == 0 or alpha == 0

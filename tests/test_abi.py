@@ -206,6 +206,48 @@ def test_select_config():
     assert not unaligned.startswith("mfma_32x64") and not unaligned.startswith("mfma_32x128")
 
 
+def test_config_describe_every_id():
+    """Every configuration has one description line whose fields agree with its name,
+    its launch shape and the limits of the hardware; ids out of range give NULL."""
+    names = sg.configs()
+    kinds = {"tile16": "tile16", "mfma": "mfma", "sk": "streamk", "valu": "valu"}
+    for cid, name in enumerate(names):
+        d = sg.describe(cid)
+        assert set(d) == {"name", "kind", "tile", "waves", "kgroups", "threads", "ahead", "loader", "lds_bytes",
+                          "band", "unaligned", "unaligned_bk", "compute"}, d
+        assert d["name"] == name and d["kind"] == kinds[name.split("_")[0]]
+        bm, bn, bk = (int(x) for x in d["tile"].split("x"))
+        wm, wn = (int(x) for x in d["waves"].split("x"))
+        wk, threads, lds = int(d["kgroups"]), int(d["threads"]), int(d["lds_bytes"])
+        assert 0 < lds <= 160 * 1024 and int(d["band"]) >= 1 and int(d["unaligned_bk"]) >= 1
+        if d["kind"] in ("mfma", "streamk"):
+            m = re.fullmatch(r"(?:mfma|sk)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
+            assert m, name
+            assert (bm, bn, bk, wm, wn) == tuple(int(x) for x in m.groups()[:5])
+            assert wk == int(m.group(6) or 1) and int(d["ahead"]) == int(m.group(7) or 1)
+            assert threads == wm * wn * wk * 64
+            assert d["loader"] == ("direct-16B" if m.group(8) else "staged-16B")
+            assert d["compute"] == "v_mfma_f32_32x32x2_f32"
+            # the stages hold A and B tiles: at least BK * (BM + BN) floats per stage
+            assert lds >= 4 * bk * (bm + bn)
+        if d["kind"] == "streamk":
+            assert d["unaligned"] == "data-parallel-staged-4B"
+        elif d["kind"] == "mfma":
+            assert d["unaligned"] in ("direct-4B", "staged-4B")
+            if d["unaligned"] == "direct-4B":
+                assert d["loader"] == "direct-16B" and (bm * bk + bk * bn) // threads <= 16
+        if d["kind"] != "streamk":
+            st, grid, block = sg.sgemm_launch_shape(cid, 1000, 1537, 777)
+            assert st == 0 and block[0] * block[1] * block[2] == threads
+    for bad in (-1, -2, len(names), len(names) + 7, 2**31 - 1):
+        assert sg.sgemm_config_describe(bad) is None
+        with pytest.raises(ValueError):
+            sg.describe(bad)
+    # the direct-copy large tile: 2 stages of (256 + 256) x 32 floats
+    d = sg.describe(names.index("mfma_256x256x32_w2x4d"))
+    assert d["lds_bytes"] == str(2 * 32 * 512 * 4) and d["unaligned"] == "staged-4B"
+
+
 def test_status_strings():
     assert sg.sgemm_status_string(0) == "success"
     assert "too large" in sg.sgemm_status_string(sg.SGEMM_ERROR_TOO_LARGE)
@@ -333,7 +375,13 @@ def test_workspace_cache_does_not_deadlock(monkeypatch):
     torch = pytest.importorskip("torch")
     real_zeros = torch.zeros
     monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
-    monkeypatch.setattr(torch.cuda, "current_stream", lambda device=None: None)
+    class _Stream:                           # the current stream: fills are waited for on it
+        cuda_stream = 0
+        synced = 0
+
+        def synchronize(self):
+            _Stream.synced += 1
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda device=None: _Stream())
     monkeypatch.setattr(torch.cuda, "device", lambda dev: contextlib.nullcontext())
     monkeypatch.setattr(torch, "zeros", lambda *a, **k: real_zeros(*a, dtype=k.get("dtype")))
     monkeypatch.setattr(sg, "_workspaces", {})
@@ -343,4 +391,6 @@ def test_workspace_cache_does_not_deadlock(monkeypatch):
     th.join(timeout=20)
     assert not th.is_alive(), "workspace_for() deadlocked"
     assert out and out[0].numel() >= 16 and int(out[0].sum()) == 0
+    assert _Stream.synced == 1               # the zero fill is complete before the buffer is used
     assert sg.workspace_for() is out[0]      # cached
+    assert _Stream.synced == 1

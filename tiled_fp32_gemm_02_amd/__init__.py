@@ -34,7 +34,8 @@ import threading
 
 __all__ = [
     "load", "lib_path", "sgemm", "sgemm_ex", "sgemm_strided_batched", "sgemm_config_count",
-    "sgemm_config_name", "sgemm_select_config", "sgemm_launch_shape", "sgemm_status_string",
+    "sgemm_config_name", "sgemm_config_describe", "describe", "sgemm_select_config", "sgemm_launch_shape",
+    "sgemm_status_string",
     "sgemm_version", "sgemm_op", "sgemm_bias_act", "sgemm_general", "configs", "gemm", "gemm_batched",
     "check", "SgemmError", "SGEMM_ERROR_TOO_LARGE", "SGEMM_ERROR_BAD_CONFIG", "SGEMM_OP_N", "SGEMM_OP_T",
     "SGEMM_ACT_NONE", "SGEMM_ACT_GELU_TANH", "SGEMM_ERROR_WORKSPACE", "sgemm_general_ws", "sgemm_workspace_size",
@@ -82,6 +83,7 @@ _SIGS = {
         ctypes.c_int, _fp]),
     "sgemm_config_count": (ctypes.c_int, []),
     "sgemm_config_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "sgemm_config_describe": (ctypes.c_char_p, [ctypes.c_int]),
     "sgemm_select_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp,
                                            ctypes.c_int, _fp, ctypes.c_int, _fp, ctypes.c_int]),
     "sgemm_launch_shape": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -196,6 +198,19 @@ def sgemm_config_name(config: int):
     return name.decode() if name is not None else None
 
 
+def sgemm_config_describe(config: int):
+    line = load().sgemm_config_describe(config)
+    return line.decode() if line is not None else None
+
+
+def describe(config: int) -> dict:
+    """The fields of sgemm_config_describe(config) as a dict (ValueError if out of range)."""
+    line = sgemm_config_describe(config)
+    if line is None:
+        raise ValueError(f"no configuration {config}")
+    return dict(field.split("=", 1) for field in line.split())
+
+
 def sgemm_select_config(M, N, K, alpha, A, lda, B, ldb, C, ldc) -> int:
     return load().sgemm_select_config(M, N, K, alpha, _addr(A), lda, _addr(B), ldb, _addr(C), ldc)
 
@@ -269,7 +284,11 @@ _ws_lock = threading.Lock()      # guards _workspaces only; never held while cal
 def workspace_for(device=None, stream=None):
     """The stream-K workspace for (device, stream): a zero-filled uint8 GPU tensor of
     sgemm_workspace_size() bytes, made once and reused. Calls on one stream run in
-    order, so they can share it; each stream gets its own."""
+    order, so they can share it; each stream gets its own.
+
+    The zero fill is queued on the device's current stream, which need not be
+    `stream`; the fill is waited for before the buffer is handed out, so the first
+    launch on `stream` (or on any stream) cannot overtake it."""
     import torch
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     if stream is None:
@@ -281,7 +300,8 @@ def workspace_for(device=None, stream=None):
         return ws
     with torch.cuda.device(dev):
         nbytes = sgemm_workspace_size(-1)   # loads the library: not under _ws_lock
-    fresh = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        fresh = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        torch.cuda.current_stream(dev).synchronize()
     with _ws_lock:
         return _workspaces.setdefault(key, fresh)
 

@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cstddef>
 #include <cstdint>
+#include <cstdio>
 
 #include "sgemm.h"
 #include "sgemm_configs.inc"
@@ -41,6 +42,22 @@ struct Config {
     int group_m;         // band height of the tile order
     LaunchFn launch;     // data-parallel launch (KIND_TILE16, KIND_MFMA, KIND_VALU)
     LaunchSkFn launch_sk;    // stream-K launch (KIND_SK)
+    int wgm, wgn, wgk;   // wave grid over the tile and wave groups along k (MFMA kinds)
+    int pf;              // K-tiles whose loads run ahead of the one being multiplied
+    int lds_bytes;       // static LDS per workgroup (aligned form)
+    int unaligned_bk;    // K-tile of the form run for 4-byte aligned rows
+    bool unaligned_dma;  // that form copies 4-byte words HBM -> LDS directly (else register-staged)
+};
+
+// LDS bytes and the unaligned form of an MFMA configuration, from the kernel's own
+// constants (the same selection launch_mfma_op makes).
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA>
+struct MfmaFacts {
+    static constexpr int NT = WGM * WGN * WGK * 64;
+    static constexpr int LDS =
+        4 * sgemm_impl::MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, false, false, true, false>::SMEM;
+    static constexpr bool DMA4 = DMA && (BM * BK + BK * BN) / NT <= 16;
+    static constexpr int UBK = DMA4 ? BK : (DMA ? 16 * WGK : BK);
 };
 
 // Stream-K workspace: per-tile counters at a fixed offset (so a call with more tiles
@@ -152,15 +169,22 @@ hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, b
 // copies.
 #define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M)                               \
     {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, GROUP_M,                                   \
-     launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>, nullptr},
+     launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>, nullptr, WGM, WGN, WGK, PF,                    \
+     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA>::LDS, MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA>::UBK,  \
+     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA>::DMA4},
 #define SGEMM_SK_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M)                            \
     {name, KIND_SK, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, GROUP_M, nullptr,                            \
-     launch_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>},
+     launch_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>, WGM, WGN, WGK, PF,                              \
+     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA>::LDS, BK, false},
+// LDS of the two kernels outside the MFMA template: tile16 stages two 16 x 17 tiles; the
+// vector-ALU kernel two k-major 8 x 132 tiles per stage, two stages.
 const Config kConfigs[] = {
-    {"tile16", KIND_TILE16, 16, 16, 16, 256, false, 1, launch_tile16, nullptr},
+    {"tile16", KIND_TILE16, 16, 16, 16, 256, false, 1, launch_tile16, nullptr, 1, 1, 1, 0, 2 * 16 * 17 * 4, 16,
+     false},
     SGEMM_MFMA_CONFIGS(SGEMM_TABLE_ROW)
     SGEMM_SK_CONFIGS(SGEMM_SK_TABLE_ROW)
-    {"valu_128x128x8_t8x8", KIND_VALU, 128, 128, 8, 256, false, 8, launch_valu, nullptr},
+    {"valu_128x128x8_t8x8", KIND_VALU, 128, 128, 8, 256, false, 8, launch_valu, nullptr, 1, 1, 1, 1,
+     2 * 2 * 8 * 132 * 4, 8, false},
 };
 #undef SGEMM_TABLE_ROW
 #undef SGEMM_SK_TABLE_ROW
@@ -522,6 +546,38 @@ int sgemm_config_count(void) { return kNumConfigs; }
 const char *sgemm_config_name(int config)
 {
     return (config >= 0 && config < kNumConfigs) ? kConfigs[config].name : nullptr;
+}
+
+const char *sgemm_config_describe(int config)
+{
+    // One line per configuration, written once (thread-safe static initialisation).
+    struct Lines {
+        char text[kNumConfigs][320];
+        Lines()
+        {
+            static const char *const kinds[] = {"tile16", "mfma", "streamk", "valu"};
+            for (int i = 0; i < kNumConfigs; ++i) {
+                const Config &c = kConfigs[i];
+                const bool mfma = c.kind == KIND_MFMA || c.kind == KIND_SK;
+                const char *loader = c.kind == KIND_TILE16 ? "staged-elementwise"
+                                     : c.kind == KIND_VALU ? "staged-k-major"
+                                     : c.dma               ? "direct-16B"
+                                                           : "staged-16B";
+                const char *unaligned = c.kind == KIND_SK  ? "data-parallel-staged-4B"
+                                        : !mfma            ? loader
+                                        : c.unaligned_dma  ? "direct-4B"
+                                                           : "staged-4B";
+                snprintf(text[i], sizeof(text[i]),
+                         "name=%s kind=%s tile=%dx%dx%d waves=%dx%d kgroups=%d threads=%d ahead=%d loader=%s "
+                         "lds_bytes=%d band=%d unaligned=%s unaligned_bk=%d compute=%s",
+                         c.name, kinds[c.kind], c.bm, c.bn, c.bk, c.wgm, c.wgn, c.wgk, c.threads, c.pf, loader,
+                         c.lds_bytes, c.group_m, unaligned, c.unaligned_bk,
+                         mfma ? "v_mfma_f32_32x32x2_f32" : "v_fma_f32");
+            }
+        }
+    };
+    static const Lines lines;
+    return (config >= 0 && config < kNumConfigs) ? lines.text[config] : nullptr;
 }
 
 int sgemm_select_config(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
