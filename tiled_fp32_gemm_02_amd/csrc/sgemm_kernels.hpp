@@ -926,9 +926,29 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
         bool finish = kt0 == 0 && kt1 == I;              // the whole tile is this workgroup's
         if (!finish) {
             const int first = owner(t * I), last = owner(t * I + I - 1);
-            // Partial sums travel through device-coherent accesses (device-scope relaxed
-            // atomics, which bypass the XCD's non-coherent L2 copy) rather than fences: a
-            // device-scope fence writes back and invalidates the whole L2 of the XCD.
+            // Ordering of the hand-off. The accesses are relaxed, so the C++/HIP memory
+            // model alone does not order them; the argument rests on how gfx950 executes
+            // agent-scope accesses (the code sequences of the AMDGPU backend's memory model
+            // for this target family):
+            //  1. An agent-scope store is issued with sc1 and written through the XCD's L2
+            //     to the device coherence point (memory side, shared by all XCDs). Stores
+            //     count in vmcnt, and the counter drops only when the store is
+            //     acknowledged there, so after wait_vmcnt<0>() every partial this wave
+            //     stored is visible to an agent-scope access from any XCD.
+            //  2. s_barrier (inside __syncthreads) makes thread 0's ticket RMW issue after
+            //     every wave of the workgroup has passed step 1.
+            //  3. The agent-scope fetch_add is atomic at the coherence point, so the
+            //     counter's values are totally ordered; the contributor that reads
+            //     last - first saw every other contributor's increment, each issued after
+            //     that contributor's step 1.
+            //  4. The winner's waves issue their partial loads after the barrier that
+            //     follows the ticket's return. An agent-scope load (sc1) is served from the
+            //     coherence point, never from a stale line in the XCD's L2, so it returns
+            //     the stored partials.
+            // A release/acquire pair (__threadfence, or release RMW + acquire load) would
+            // make this follow from the language model, but on this target it is compiled
+            // to buffer_wbl2 / buffer_inv of the whole XCD L2; with it the GPT-2 QKV layer
+            // took 143 us instead of 41 us, so the per-access form is kept.
             if (holds) {
                 float *dst = sk.partials + ((int64_t)g * 2 + slot_of(g, t)) * TILE + wslot * PER_WAVE;
 #pragma unroll
