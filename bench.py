@@ -125,6 +125,40 @@ def lds_fill_bytes(M: int, N: int, K: int, config_name: str) -> float:
     return 4.0 * M * N * K * (1.0 / bm + 1.0 / bn)
 
 
+def register_tile(config_name: str):
+    """(TM, TN): the register tile whose rows and columns each LDS read feeds, from the
+    configuration's name. For the matrix-core kernels it is the wave's tile
+    (BM/WGM x BN/WGN); for the vector-ALU kernel the thread's 8 x 8 micro-tile; for the
+    16x16 kernel one output per thread."""
+    import re
+    if config_name == "tile16":
+        return 1, 1
+    m = re.search(r"_t(\d+)x(\d+)$", config_name)
+    if m:
+        return int(m.group(1)), int(m.group(2))
+    m = re.search(r"_(\d+)x(\d+)x\d+_w(\d+)x(\d+)", config_name)
+    if not m:
+        raise ValueError(f"no wave grid in configuration name {config_name!r}")
+    bm, bn, wm, wn = (int(x) for x in m.groups())
+    return bm // wm, bn // wn
+
+
+def lds_read_bytes(M: int, N: int, K: int, config_name: str) -> float:
+    """Bytes read from LDS into registers per launch: for every k, each TM x TN register
+    tile reads its TM values of op(A) and TN values of op(B), so 4 M N K (1/TM + 1/TN) in
+    total (AutoMine++ #4's count for its register tile, "Let's use registers")."""
+    tm, tn = register_tile(config_name)
+    return 4.0 * M * N * K * (1.0 / tm + 1.0 / tn)
+
+
+def peak_at_clock(cus, sclk_mhz):
+    """The fp32 matrix peak at a measured shader clock: CUs x 256 flop/clk x sclk, in TFLOP/s
+    (None when the clock was not readable)."""
+    if not cus or not sclk_mhz:
+        return None
+    return cus * 256 * sclk_mhz * 1e6 / 1e12
+
+
 def recorded_traffic(workload: str, config_name: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on
     the current kernel source and the same workload and configuration; else None."""
@@ -311,6 +345,9 @@ def main():
         f"mean step {kernel_ms * 1e3:.1f} us (events)")
 
     props = torch.cuda.get_device_properties(dev)
+    clocks = [c for c in (sclk_before, sclk_after) if c]
+    sclk_mean = sum(clocks) / len(clocks) if clocks else None
+    peak_sclk = peak_at_clock(props.multi_processor_count, sclk_mean)
     w0 = probs[0]["w"]
     if len(probs) == 1:
         config = {"workload": args.workload, "M": w0.M, "N": w0.N, "K": w0.K, "alpha": w0.alpha, "beta": w0.beta,
@@ -348,6 +385,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
             "traffic": traffic,
+            "peak_at_sclk": round(peak_sclk, 2) if peak_sclk else None,
+            "frac_at_sclk": round(achieved / peak_sclk, 4) if peak_sclk else None,
+            "sclk_mhz": round(sclk_mean, 1) if sclk_mean else None,
         },
         "timing": {"settle_steps": settle, "step_us_median": round(float(np.median(per_step)) * 1e3, 2),
                    "step_us_min": round(float(per_step.min()) * 1e3, 2),
@@ -359,7 +399,10 @@ def main():
         "check": {"sampled_entries": int(checked), "max_err_over_bound": round(worst_all, 4)},
         "tile_traffic": {"global_to_lds_bytes": round(sum(lds_fill_bytes(p["w"].M, p["w"].N, p["w"].K, p["cfg_name"])
                                                           for p in probs)),
-                         "model": "4*M*N*K*(1/BM + 1/BN) per step, the tiles' operand panels"},
+                         "lds_to_register_bytes": round(sum(lds_read_bytes(p["w"].M, p["w"].N, p["w"].K,
+                                                                           p["cfg_name"]) for p in probs)),
+                         "model": "per step: 4*M*N*K*(1/BM + 1/BN) for the tiles' operand panels into LDS; "
+                                  "4*M*N*K*(1/TM + 1/TN) from LDS into each TM x TN wave (or thread) tile"},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")

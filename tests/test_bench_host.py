@@ -70,3 +70,23 @@ def test_tile_traffic_model():
     import tiled_fp32_gemm_02_amd as sg
     for name in sg.configs():
         bench.tile_dims(name)
+
+
+def test_register_tile_and_clock_peak():
+    """The LDS -> register model uses the wave tile (matrix cores) or the thread's micro-tile;
+    the clock-adjusted peak is CUs x 256 flop/clk x sclk."""
+    assert bench.register_tile("mfma_256x256x32_w2x4d") == (128, 64)
+    assert bench.register_tile("mfma_32x128x64_w1x4k2d") == (32, 32)
+    assert bench.register_tile("sk_64x128x32_w2x2k2p2") == (32, 64)
+    assert bench.register_tile("valu_128x128x8_t8x8") == (8, 8)
+    assert bench.register_tile("tile16") == (1, 1)
+    # one output per thread: two LDS reads per multiply-add
+    assert bench.lds_read_bytes(64, 64, 64, "tile16") == 4 * 2 * 64 ** 3
+    assert bench.lds_read_bytes(4096, 4096, 4096, "mfma_256x256x32_w2x4d") == 4 * 4096 ** 3 * (1 / 128 + 1 / 64)
+    # 256 CUs at 2.4 GHz: the published 157.3 TFLOP/s
+    assert abs(bench.peak_at_clock(256, 2400) - 157.2864) < 1e-9
+    assert bench.peak_at_clock(256, None) is None
+    import tiled_fp32_gemm_02_amd as sg
+    for name in sg.configs():
+        tm, tn = bench.register_tile(name)
+        assert tm >= 1 and tn >= 1

@@ -180,3 +180,30 @@ def test_tensor_form_uses_the_workspace():
     assert oracle.within_bound(C.cpu().numpy(), ref, bound)[0]
     assert oracle.within_bound(C2.cpu().numpy(), ref, bound)[0]
     assert counters_clear(ws)
+
+
+def test_tensor_form_on_a_side_stream_with_a_fresh_workspace(monkeypatch):
+    """gemm(..., stream=s) on a stream other than the current one, with the workspace
+    cache empty: the buffer's zero fill is queued on the current stream, and must be
+    complete before the stream-K kernel on s reads its counters. Checked elementwise
+    against the oracle, and the counters are zero again afterwards."""
+    import torch
+    import tiled_fp32_gemm_02_amd as sg
+    monkeypatch.setattr(sg, "_workspaces", {})
+    rng = np.random.default_rng(23)
+    n = 1536
+    a, b = draw(rng, (n, n), "normal"), draw(rng, (n, n), "normal002")
+    A, B = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    # reuse of a freed allocation: leave nonzero bytes where the workspace may land
+    junk = torch.full((sg.sgemm_workspace_size(-1) // 4 + 16,), -1, dtype=torch.int32, device="cuda")
+    del junk
+    say("stream-K through the tensor form on a side stream, fresh workspace")
+    C = sg.gemm(A, B, stream=side)
+    side.synchronize()
+    ref, bound = oracle.gemm(0, 0, n, n, n, 1.0, a, n, b, n, 0.0, None, n)
+    ok, worst, idx = oracle.within_bound(C.cpu().numpy(), ref, bound)
+    assert ok, (worst, idx)
+    ws = sg._workspaces[(A.device.index, int(side.cuda_stream))]
+    assert counters_clear(ws)
