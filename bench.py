@@ -26,6 +26,9 @@ read from sysfs before and after the timed steps where the driver exposes it.
 
 ``--workload gpt2_seq`` times the three GPT-2-small linears (QKV, MLP up, MLP
 down) in that order as one step: total flops over total time.
+``--workload gpt2_attn`` times attention's two per-head batched products (12 heads
+of Q K^T / 8 with K transposed in place, then P V with the heads side by side), as
+one step.
 ``--workload gpt2_mlp_up_gelu`` is the MLP-up layer with its bias and tanh GELU
 fused into the product's final write (bias ~ 0.02 N(0,1), drawn from seed 4 + 1000);
 flops are counted as 2MNK, as for the plain product.
@@ -180,26 +183,150 @@ def recorded_traffic(workload: str, config_name: str):
         return None
 
 
+class LinearProblem:
+    """One plain product of the workload table (optionally with bias + tanh GELU), with
+    its host inputs, device copies and the configuration the library picks."""
+
+    def __init__(self, sg, torch, dev, w, config, ws, fused):
+        from workloads import draw, make
+        self.sg, self.w, self.name, self.note = sg, w, w.name, w.note
+        self.M, self.N, self.K, self.batch = w.M, w.N, w.K, 1
+        self.A, self.B, self.C = make(w)
+        self.dA = torch.from_numpy(self.A).to(dev)
+        self.dB = torch.from_numpy(self.B).to(dev)
+        self.dC = (torch.from_numpy(self.C).to(dev) if self.C is not None
+                   else torch.empty((w.M, w.ldc_), device=dev))
+        self.C0 = self.dC.clone()
+        self.config, self.ws = config, ws
+        self.cfg = config if config >= 0 else sg.sgemm_select_config_ws(
+            w.M, w.N, w.K, w.alpha, self.dA, w.lda_, self.dB, w.ldb_, self.dC, w.ldc_, ws.numel())
+        self.cfg_name = sg.sgemm_config_name(self.cfg)
+        self.bias = draw(np.random.default_rng(w.seed + 1000), (w.N,), "normal002") if fused else None
+        self.dbias = torch.from_numpy(self.bias).to(dev) if fused else None
+        self.act = sg.SGEMM_ACT_GELU_TANH if fused else sg.SGEMM_ACT_NONE
+
+    def launch(self, stream_handle):
+        w, sg = self.w, self.sg
+        st = sg.sgemm_general_ws(self.config, sg.SGEMM_OP_N, sg.SGEMM_OP_N, w.M, w.N, w.K, w.alpha,
+                                 self.dA.data_ptr(), w.lda_, self.dB.data_ptr(), w.ldb_, w.beta,
+                                 self.dC.data_ptr(), w.ldc_, self.dbias, self.act, self.ws.data_ptr(),
+                                 self.ws.numel(), stream_handle)
+        if st != 0:
+            raise RuntimeError(f"sgemm failed: {sg.sgemm_status_string(st)}")
+
+    def check(self, oracle):
+        """256 sampled entries (the corners included) against the oracle: (worst, count)."""
+        w = self.w
+        out = self.dC.cpu().numpy()
+        rng = np.random.default_rng(12345)
+        rows = np.concatenate([[0, w.M - 1], rng.integers(0, w.M, 254)])
+        cols = np.concatenate([[0, w.N - 1], rng.integers(0, w.N, 254)])
+        ref, bound = oracle.gemm_entries(0, 0, w.M, w.N, w.K, w.alpha, self.A, w.lda_, self.B, w.ldb_, w.beta,
+                                         self.C, w.ldc_, rows, cols, bias=self.bias, act=self.act)
+        ok, worst, _ = oracle.within_bound(out[rows, cols], ref, bound)
+        if not ok:
+            raise SystemExit(f"bench: {w.name} outside the oracle bound (max |err|/bound = {worst})")
+        self.dC.copy_(self.C0)
+        return worst, rows.size
+
+    def cpu(self, oracle, rows):
+        """Seconds for the oracle on the first `rows` rows of the product."""
+        w = self.w
+        t0 = time.perf_counter()
+        oracle.gemm(0, 0, rows, w.N, w.K, w.alpha, self.A, w.lda_, self.B, w.ldb_, w.beta, self.C, w.ldc_,
+                    self.bias, self.act, with_bound=False)
+        return time.perf_counter() - t0
+
+    def describe(self):
+        return {"name": self.name, "M": self.M, "N": self.N, "K": self.K, "kernel": self.cfg_name}
+
+
+class BatchedProblem:
+    """One strided-batched product (workloads.BatchedGemm) over shared device buffers, with
+    the operand forms read in place."""
+
+    def __init__(self, sg, torch, dev, prob, bufs, dbufs, config):
+        self.sg, self.p, self.name, self.note = sg, prob, prob.name, prob.note
+        self.M, self.N, self.K, self.batch = prob.M, prob.N, prob.K, prob.batch
+        self.bufs, self.dbufs = bufs, dbufs
+        self.dC = torch.zeros(prob.c_rows * prob.c_cols, device=dev)
+        self.config = config
+        self.cfg = config if config >= 0 else sg.sgemm_select_config_general(
+            prob.opA, prob.opB, prob.M, prob.N, prob.K, prob.alpha, self._ptr(prob.a, prob.a_off), prob.lda,
+            prob.sA, self._ptr(prob.b, prob.b_off), prob.ldb, prob.sB, self.dC.data_ptr() + 4 * prob.c_off,
+            prob.ldc, prob.sC, prob.batch)
+        self.cfg_name = sg.sgemm_config_name(self.cfg)
+
+    def _ptr(self, name, off):
+        return self.dbufs[name].data_ptr() + 4 * off
+
+    def launch(self, stream_handle):
+        p, sg = self.p, self.sg
+        st = sg.sgemm_strided_batched_general(self.config, p.opA, p.opB, p.M, p.N, p.K, p.alpha,
+                                              self._ptr(p.a, p.a_off), p.lda, p.sA, self._ptr(p.b, p.b_off),
+                                              p.ldb, p.sB, 0.0, self.dC.data_ptr() + 4 * p.c_off, p.ldc, p.sC,
+                                              None, sg.SGEMM_ACT_NONE, p.batch, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"sgemm_strided_batched_general failed: {sg.sgemm_status_string(st)}")
+
+    def _operands(self, b):
+        p = self.p
+        a = self.bufs[p.a].reshape(-1)[p.a_off + b * p.sA:]
+        bb = self.bufs[p.b].reshape(-1)[p.b_off + b * p.sB:]
+        return a, bb
+
+    def check(self, oracle):
+        """256 sampled entries, spread over the batches (the first and last batch's corners
+        included), against the oracle: (worst, count)."""
+        p = self.p
+        out = self.dC.cpu().numpy()
+        rng = np.random.default_rng(12345)
+        bs = np.concatenate([[0, p.batch - 1], rng.integers(0, p.batch, 254)])
+        rows = np.concatenate([[0, p.M - 1], rng.integers(0, p.M, 254)])
+        cols = np.concatenate([[0, p.N - 1], rng.integers(0, p.N, 254)])
+        worst = 0.0
+        for b in np.unique(bs):
+            sel = bs == b
+            a, bb = self._operands(int(b))
+            ref, bound = oracle.gemm_entries(p.opA, p.opB, p.M, p.N, p.K, p.alpha, a, p.lda, bb, p.ldb, 0.0, None,
+                                             p.ldc, rows[sel], cols[sel])
+            got = out[p.c_off + int(b) * p.sC + rows[sel] * p.ldc + cols[sel]]
+            ok, wb, _ = oracle.within_bound(got, ref, bound)
+            if not ok:
+                raise SystemExit(f"bench: {p.name} batch {b} outside the oracle bound (max |err|/bound = {wb})")
+            worst = max(worst, wb)
+        return worst, bs.size
+
+    def cpu(self, oracle, rows):
+        """Seconds for the oracle on the first `rows` rows of every batch."""
+        p = self.p
+        t0 = time.perf_counter()
+        for b in range(p.batch):
+            a, bb = self._operands(b)
+            oracle.gemm(p.opA, p.opB, rows, p.N, p.K, p.alpha, a, p.lda, bb, p.ldb, 0.0, None, p.ldc,
+                        with_bound=False)
+        return time.perf_counter() - t0
+
+    def describe(self):
+        p = self.p
+        return {"name": p.name, "batch": p.batch, "M": p.M, "N": p.N, "K": p.K, "opA": "NT"[p.opA],
+                "opB": "NT"[p.opB], "kernel": self.cfg_name}
+
+
 def cpu_baseline(probs, target_s: float):
     """Time the CPU oracle on the first rows of each product of the step (the same
     fraction of every product's rows, chosen from a pilot run so that the sample
     takes about `target_s` seconds). Returns the JSON object."""
     import oracle
 
-    def run(p, rows):
-        w = p["w"]
-        t0 = time.perf_counter()
-        oracle.gemm(0, 0, rows, w.N, w.K, w.alpha, p["A"], w.lda_, p["B"], w.ldb_, w.beta, p["C"], w.ldc_,
-                    p.get("bias"), p.get("act", oracle.ACT_NONE), with_bound=False)
-        return time.perf_counter() - t0
-
-    pilot = [min(p["w"].M, 16) for p in probs]
-    t_pilot = sum(run(p, r) for p, r in zip(probs, pilot))
-    frac = min(1.0, target_s / max(t_pilot, 1e-6) * sum(pilot) / sum(p["w"].M for p in probs))
-    rows = [int(min(p["w"].M, max(r, round(frac * p["w"].M)))) for p, r in zip(probs, pilot)]
-    t = sum(run(p, r) for p, r in zip(probs, rows))
-    flops = sum(2.0 * r * p["w"].N * p["w"].K for p, r in zip(probs, rows))
-    what = "; ".join(f"rows 0..{r - 1} of the {p['w'].M}x{p['w'].N}x{p['w'].K} product" for p, r in zip(probs, rows))
+    pilot = [min(p.M, 16) for p in probs]
+    t_pilot = sum(p.cpu(oracle, r) for p, r in zip(probs, pilot))
+    frac = min(1.0, target_s / max(t_pilot, 1e-6) * sum(pilot) / sum(p.M for p in probs))
+    rows = [int(min(p.M, max(r, round(frac * p.M)))) for p, r in zip(probs, pilot)]
+    t = sum(p.cpu(oracle, r) for p, r in zip(probs, rows))
+    flops = sum(2.0 * r * p.N * p.K * p.batch for p, r in zip(probs, rows))
+    what = "; ".join(f"rows 0..{r - 1} of {'each of the %d ' % p.batch if p.batch > 1 else 'the '}"
+                     f"{p.M}x{p.N}x{p.K} product{'s' if p.batch > 1 else ''}" for p, r in zip(probs, rows))
     return {
         "value": round(flops / t / 1e12, 6),
         "unit": "TFLOP/s",
@@ -250,7 +377,7 @@ def main():
     sgbuild.ensure_built()
     import tiled_fp32_gemm_02_amd as sg
     import oracle
-    from workloads import WORKLOADS, draw, make, flops
+    from workloads import WORKLOADS, flops
 
     if args.config.lstrip("-").isdigit():
         args.config = int(args.config)
@@ -259,58 +386,37 @@ def main():
     else:
         raise SystemExit(f"bench: no configuration named {args.config!r}; see tiled_fp32_gemm_02_amd.configs()")
     fused = args.workload == "gpt2_mlp_up_gelu"
-    names = (["gpt2_qkv", "gpt2_mlp_up", "gpt2_mlp_down"] if args.workload == "gpt2_seq"
-             else ["gpt2_mlp_up"] if fused else [args.workload])
     dev = torch.device("cuda:0")
     # The stream-K workspace (zero-filled once, outside the timed region): the library
     # picks stream-K configurations where its cost model favours them.
     ws = torch.zeros(max(sg.sgemm_workspace_size(-1), 16), dtype=torch.uint8, device=dev)
-    probs = []
-    for name in names:
-        w = WORKLOADS[name]
-        A, B, C = make(w)
-        dA = torch.from_numpy(A).to(dev)
-        dB = torch.from_numpy(B).to(dev)
-        dC = torch.from_numpy(C).to(dev) if C is not None else torch.empty((w.M, w.ldc_), device=dev)
-        cfg = args.config if args.config >= 0 else sg.sgemm_select_config_ws(
-            w.M, w.N, w.K, w.alpha, dA, w.lda_, dB, w.ldb_, dC, w.ldc_, ws.numel())
-        bias = draw(np.random.default_rng(w.seed + 1000), (w.N,), "normal002") if fused else None
-        probs.append({"w": w, "A": A, "B": B, "C": C, "dA": dA, "dB": dB, "dC": dC, "C0": dC.clone(),
-                      "cfg": cfg, "cfg_name": sg.sgemm_config_name(cfg), "bias": bias,
-                      "dbias": torch.from_numpy(bias).to(dev) if fused else None,
-                      "act": sg.SGEMM_ACT_GELU_TANH if fused else sg.SGEMM_ACT_NONE})
+    if args.workload == "gpt2_attn":
+        from workloads import attention_products, gpt2_attention_set
+        bufs = gpt2_attention_set()
+        dbufs = {k: torch.from_numpy(v).to(dev) for k, v in bufs.items()}
+        probs = [BatchedProblem(sg, torch, dev, pr, bufs, dbufs, args.config) for pr in attention_products()]
+    else:
+        names = (["gpt2_qkv", "gpt2_mlp_up", "gpt2_mlp_down"] if args.workload == "gpt2_seq"
+                 else ["gpt2_mlp_up"] if fused else [args.workload])
+        if any(n not in WORKLOADS for n in names):
+            raise SystemExit(f"bench: unknown workload {args.workload!r}")
+        probs = [LinearProblem(sg, torch, dev, WORKLOADS[n], args.config, ws, fused) for n in names]
     stream = torch.cuda.Stream(device=dev)
     s_handle = int(stream.cuda_stream)
 
     def step():
         for p in probs:
-            w = p["w"]
-            st = sg.sgemm_general_ws(args.config, sg.SGEMM_OP_N, sg.SGEMM_OP_N, w.M, w.N, w.K, w.alpha,
-                                     p["dA"].data_ptr(), w.lda_, p["dB"].data_ptr(), w.ldb_, w.beta,
-                                     p["dC"].data_ptr(), w.ldc_, p["dbias"], p["act"], ws.data_ptr(),
-                                     ws.numel(), s_handle)
-            if st != 0:
-                raise RuntimeError(f"sgemm failed: {sg.sgemm_status_string(st)}")
+            p.launch(s_handle)
 
     # One checked call on a fresh C: sampled entries against the oracle.
     for p in probs:
-        log(f"bench: workload {p['w'].name} {p['w'].M}x{p['w'].N}x{p['w'].K} config {p['cfg']} {p['cfg_name']}")
+        log(f"bench: workload {p.name} {p.batch} x {p.M}x{p.N}x{p.K} config {p.cfg} {p.cfg_name}")
     step()
     torch.cuda.synchronize()
     worst_all, checked = 0.0, 0
     for p in probs:
-        w = p["w"]
-        out = p["dC"].cpu().numpy()
-        rng = np.random.default_rng(12345)
-        rows = np.concatenate([[0, w.M - 1], rng.integers(0, w.M, 254)])
-        cols = np.concatenate([[0, w.N - 1], rng.integers(0, w.N, 254)])
-        ref, bound = oracle.gemm_entries(0, 0, w.M, w.N, w.K, w.alpha, p["A"], w.lda_, p["B"], w.ldb_, w.beta,
-                                         p["C"], w.ldc_, rows, cols, bias=p["bias"], act=p["act"])
-        ok, worst, _ = oracle.within_bound(out[rows, cols], ref, bound)
-        if not ok:
-            raise SystemExit(f"bench: {w.name} outside the oracle bound (max |err|/bound = {worst})")
-        worst_all, checked = max(worst_all, worst), checked + rows.size
-        p["dC"].copy_(p["C0"])
+        worst, n = p.check(oracle)
+        worst_all, checked = max(worst_all, worst), checked + n
     log(f"bench: checked {checked} sampled entries, max |err|/bound = {worst_all:.3f}")
     torch.cuda.synchronize()
 
@@ -338,7 +444,7 @@ def main():
     wall_s = t1 - t0
     per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])    # ms
     kernel_ms = evs[0].elapsed_time(evs[-1]) / args.steps
-    fl = sum(flops(p["w"].M, p["w"].N, p["w"].K) for p in probs)
+    fl = sum(flops(p.M, p.N, p.K) * p.batch for p in probs)
     value = fl * args.steps / wall_s / 1e12
     achieved = fl / (kernel_ms * 1e-3) / 1e12
     log(f"bench: {settle} settle steps, {args.warmup} warm-up; {args.steps} steps in {wall_s * 1e3:.2f} ms wall; "
@@ -348,20 +454,18 @@ def main():
     clocks = [c for c in (sclk_before, sclk_after) if c]
     sclk_mean = sum(clocks) / len(clocks) if clocks else None
     peak_sclk = peak_at_clock(props.multi_processor_count, sclk_mean)
-    w0 = probs[0]["w"]
     if len(probs) == 1:
+        p0, w0 = probs[0], probs[0].w
         config = {"workload": args.workload, "M": w0.M, "N": w0.N, "K": w0.K, "alpha": w0.alpha, "beta": w0.beta,
-                  "inputs": w0.note, "kernel": probs[0]["cfg_name"], "parallelism": "none (one GPU)"}
+                  "inputs": w0.note, "kernel": p0.cfg_name, "parallelism": "none (one GPU)"}
         if fused:
             config["epilogue"] = "bias + tanh GELU"
         metric = ("FP32 SGEMM TFLOP/s at M=N=K=4096 and fraction of MI355X FP32 peak" if w0.name == "sq4096"
                   else f"FP32 SGEMM TFLOP/s ({args.workload}) and fraction of MI355X FP32 peak")
-        traffic = recorded_traffic(args.workload, probs[0]["cfg_name"])
+        traffic = recorded_traffic(args.workload, p0.cfg_name)
     else:
-        config = {"workload": args.workload,
-                  "sequence": [{"name": p["w"].name, "M": p["w"].M, "N": p["w"].N, "K": p["w"].K,
-                                "kernel": p["cfg_name"]} for p in probs],
-                  "inputs": "; ".join(p["w"].note for p in probs), "parallelism": "none (one GPU)"}
+        config = {"workload": args.workload, "sequence": [p.describe() for p in probs],
+                  "inputs": "; ".join(p.note for p in probs), "parallelism": "none (one GPU)"}
         metric = f"FP32 SGEMM TFLOP/s ({args.workload}: the products in sequence) and fraction of MI355X FP32 peak"
         traffic = None
     line = {
@@ -397,10 +501,10 @@ def main():
                    "arch": getattr(props, "gcnArchName", ""), "hip": torch.version.hip,
                    "host_cpu": host_cpu_model(), "host_threads": len(os.sched_getaffinity(0))},
         "check": {"sampled_entries": int(checked), "max_err_over_bound": round(worst_all, 4)},
-        "tile_traffic": {"global_to_lds_bytes": round(sum(lds_fill_bytes(p["w"].M, p["w"].N, p["w"].K, p["cfg_name"])
+        "tile_traffic": {"global_to_lds_bytes": round(sum(p.batch * lds_fill_bytes(p.M, p.N, p.K, p.cfg_name)
                                                           for p in probs)),
-                         "lds_to_register_bytes": round(sum(lds_read_bytes(p["w"].M, p["w"].N, p["w"].K,
-                                                                           p["cfg_name"]) for p in probs)),
+                         "lds_to_register_bytes": round(sum(p.batch * lds_read_bytes(p.M, p.N, p.K, p.cfg_name)
+                                                            for p in probs)),
                          "model": "per step: 4*M*N*K*(1/BM + 1/BN) for the tiles' operand panels into LDS; "
                                   "4*M*N*K*(1/TM + 1/TN) from LDS into each TM x TN wave (or thread) tile"},
     }

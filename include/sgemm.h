@@ -163,14 +163,65 @@ int sgemm_general(int config, int opA, int opB, int M, int N, int K, float alpha
  * Arguments by position: 1 M, 2 N, 3 K, 4 alpha, 5 A, 6 lda, 7 strideA, 8 B, 9 ldb,
  * 10 strideB, 11 beta, 12 C, 13 ldc, 14 strideC, 15 batch, 16 stream.
  * batch >= 0 and at most 65535; batch == 0 returns 0. strideA, strideB >= 0 (0 reuses
- * one matrix for all batches). strideC must be >= (M-1)*ldc + N so the C windows do
- * not overlap, unless batch == 1. Other rules as for sgemm.
+ * one matrix for all batches). The C windows must not overlap, unless batch == 1:
+ * strideC >= (M-1)*ldc + N (stacked), or N <= strideC and (batch-1)*strideC + N <= ldc
+ * (side by side within each row). Other rules as for sgemm.
  */
 int sgemm_strided_batched(int M, int N, int K, float alpha,
                           const float *A, int lda, long long strideA,
                           const float *B, int ldb, long long strideB,
                           float beta, float *C, int ldc, long long strideC,
                           int batch, void *stream);
+
+/*
+ * Strided-batched form with operand forms: for b in [0, batch),
+ *   C_b <- alpha * op(A_b) * op(B_b) + beta * C_b,
+ * A_b = A + b*strideA, B_b = B + b*strideB, C_b = C + b*strideC (strides in floats), op
+ * as for sgemm_op (a transposed operand is read in place). This is the per-head product of
+ * attention in the GPT-2 post: its batched kernel adds a grid dimension indexed by batch,
+ * and takes strided and transposed views without copies ("GPU Target - GPT-2 on the GPU",
+ * section "Tiled matrix multiplication"). With Q, K and V the three 768-column blocks of a
+ * 1024 x 2304 row-major QKV matrix (12 heads of 64 columns):
+ *   scores_h = Q_h K_h^T / 8:  opA = N, opB = T, M = N = 1024, K = 64, alpha = 0.125,
+ *       A = QKV, lda = 2304, strideA = 64; B = QKV + 768, ldb = 2304, strideB = 64;
+ *       C = S (12 x 1024 x 1024), ldc = 1024, strideC = 1024 * 1024;
+ *   out_h = P_h V_h:           opA = opB = N, M = 1024, N = 64, K = 1024,
+ *       A = P, lda = 1024, strideA = 1024 * 1024; B = QKV + 1536, ldb = 2304, strideB = 64;
+ *       C = O (1024 x 768), ldc = 768, strideC = 64 (heads side by side in each row).
+ *
+ * Arguments by position: 1 opA, 2 opB, 3 M, 4 N, 5 K, 6 alpha, 7 A, 8 lda, 9 strideA, 10 B,
+ * 11 ldb, 12 strideB, 13 beta, 14 C, 15 ldc, 16 strideC, 17 batch, 18 stream.
+ *  - strideA, strideB >= 0 (0 reuses one matrix for every batch); lda and ldb follow op.
+ *  - batch in [0, 65535]; batch == 0 returns 0.
+ *  - The C windows must not overlap (unless batch == 1): either stacked,
+ *    strideC >= (M-1)*ldc + N, or side by side within each row, N <= strideC and
+ *    (batch-1)*strideC + N <= ldc. Otherwise -16.
+ *  - The 128-bit path needs the strides to be multiples of 4, besides the rules of sgemm_op.
+ * The library never picks a stream-K configuration for a batched call.
+ */
+int sgemm_strided_batched_op(int opA, int opB, int M, int N, int K, float alpha,
+                             const float *A, int lda, long long strideA,
+                             const float *B, int ldb, long long strideB,
+                             float beta, float *C, int ldc, long long strideC,
+                             int batch, void *stream);
+
+/*
+ * sgemm_strided_batched_op with a forced configuration (config as for sgemm_ex, not
+ * counted in argument positions; a stream-K configuration returns SGEMM_ERROR_WORKSPACE),
+ * a bias and an activation applied to every batch as in sgemm_bias_act (bias has N
+ * entries, shared by all batches, or is NULL):
+ *   C_b <- act(alpha * op(A_b) * op(B_b) + beta * C_b + bias).
+ * Used by tests and sweeps, and by batched linear layers.
+ *
+ * Arguments by position: 1 opA, 2 opB, 3 M, 4 N, 5 K, 6 alpha, 7 A, 8 lda, 9 strideA, 10 B,
+ * 11 ldb, 12 strideB, 13 beta, 14 C, 15 ldc, 16 strideC, 17 bias, 18 act, 19 batch, 20 stream.
+ */
+int sgemm_strided_batched_general(int config, int opA, int opB, int M, int N, int K, float alpha,
+                                  const float *A, int lda, long long strideA,
+                                  const float *B, int ldb, long long strideB,
+                                  float beta, float *C, int ldc, long long strideC,
+                                  const float *bias, int act,
+                                  int batch, void *stream);
 
 /*
  * sgemm_general with a workspace, which lets the library use stream-K configurations
@@ -225,6 +276,20 @@ int sgemm_select_config_ws(int M, int N, int K, float alpha,
                            const float *B, int ldb,
                            const float *C, int ldc,
                            size_t workspace_bytes);
+
+/*
+ * The configuration the library would pick for any call form (host logic only): opA/opB
+ * as for sgemm_op, strides and batch as for sgemm_strided_batched_op (batch == 1 for the
+ * single-matrix entry points, strides then ignored), and the workspace size as for
+ * sgemm_general_ws (used only when batch == 1; it queries the current device's
+ * compute-unit count when nonzero). Arguments are not validated. Returns -1 when no
+ * matrix kernel would run (M, N, K or batch <= 0, or alpha == 0).
+ */
+int sgemm_select_config_general(int opA, int opB, int M, int N, int K, float alpha,
+                                const float *A, int lda, long long strideA,
+                                const float *B, int ldb, long long strideB,
+                                const float *C, int ldc, long long strideC,
+                                int batch, size_t workspace_bytes);
 
 /* Number of kernel configurations compiled into the library. */
 int sgemm_config_count(void);

@@ -108,6 +108,62 @@ def test_batched_invalid_arguments(args, code):
     assert sg.sgemm_strided_batched(*args) == code
 
 
+@pytest.mark.parametrize("args,code", [
+    # (opA, opB, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch)
+    ((2, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, 2), -1),
+    ((0, 3, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, 2), -2),
+    ((0, 0, -1, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, 2), -3),
+    ((0, 0, 4, 4, 4, 1.0, None, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, 2), -7),
+    ((1, 0, 6, 4, 8, 1.0, BAD, 5, 48, BAD, 4, 32, 0.0, BAD, 4, 24, 2), -8),      # transposed A: lda >= M
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, -4, BAD, 4, 16, 0.0, BAD, 4, 16, 2), -9),
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, 16, None, 4, 16, 0.0, BAD, 4, 16, 2), -10),
+    ((0, 1, 4, 6, 8, 1.0, BAD, 8, 32, BAD, 7, 48, 0.0, BAD, 6, 24, 2), -11),     # transposed B: ldb >= K
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, -1, 0.0, BAD, 4, 16, 2), -12),
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, None, 4, 16, 2), -14),
+    ((0, 0, 4, 5, 4, 1.0, BAD, 4, 16, BAD, 5, 20, 0.0, BAD, 4, 20, 2), -15),
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 15, 2), -16),     # C windows overlap
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, -16, 2), -16),
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 12, 4, 4), -16),     # side by side: 4 x 4 > 12
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 12, 3, 3), -16),     # side by side, overlapping
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, -1), -17),
+    ((0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, 65536), -17),
+])
+def test_batched_op_invalid_arguments(args, code):
+    assert sg.sgemm_strided_batched_op(*args) == code
+    # the general form: same positions up to C's stride; bias and act come before batch
+    gen = args[:16] + (None, sg.SGEMM_ACT_NONE, args[16])
+    expect = code if code > -17 else -19
+    assert sg.sgemm_strided_batched_general(-1, *gen) == expect
+    assert sg.sgemm_status_string(code) == f"invalid argument {-code}"
+
+
+def test_batched_general_checks():
+    ok = (0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16)
+    assert sg.sgemm_strided_batched_general(-1, *ok, None, 2, 2) == -18          # act
+    assert sg.sgemm_strided_batched_general(-2, *ok, None, 0, 2) == sg.SGEMM_ERROR_BAD_CONFIG
+    sk = [i for i, n in enumerate(sg.configs()) if n.startswith("sk_")]
+    assert sg.sgemm_strided_batched_general(sk[0], *ok, None, 0, 2) == sg.SGEMM_ERROR_WORKSPACE
+    # quick returns: nothing launched, unread pointers may be anything
+    assert sg.sgemm_strided_batched_general(-1, *ok, None, 0, 0) == 0
+    assert sg.sgemm_strided_batched_op(0, 0, 0, 4, 4, 1.0, None, 4, 0, None, 4, 0, 0.0, None, 4, 0, 9) == 0
+    assert sg.sgemm_status_string(-20) == "invalid argument 20"
+
+
+def test_batched_side_by_side_windows_accepted():
+    """Heads written side by side into the rows of one matrix (attention's output): each
+    window N wide, all within ldc. Accepted by the plain batched form too; the call here
+    stops before any launch because batch == 0 after the checks would launch nothing, so
+    the acceptance is seen through the quick return of M == 0."""
+    # 12 heads of 64 columns in a 768-wide row: accepted (the M == 0 quick return follows)
+    assert sg.sgemm_strided_batched(0, 64, 1024, 1.0, None, 1024, 0, None, 64, 0, 0.0, None, 768, 64, 12) == 0
+    assert sg.sgemm_strided_batched_op(0, 0, 0, 64, 1024, 1.0, None, 1024, 0, None, 64, 0, 0.0, None, 768, 64,
+                                       12) == 0
+    # one column too many for the row: rejected before the quick return is reached
+    args = (5, 64, 16, 1.0, BAD, 16, 0, BAD, 64, 0, 0.0, BAD, 767, 64, 12)
+    assert sg.sgemm_strided_batched(*args) == -14
+    assert sg.sgemm_strided_batched_op(0, 0, *args) == -16
+
+
 def test_batched_quick_returns():
     assert sg.sgemm_strided_batched(4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16, 0) == 0
     assert sg.sgemm_strided_batched(0, 4, 4, 1.0, None, 4, 0, None, 4, 0, 0.0, None, 4, 0, 9) == 0
@@ -246,6 +302,29 @@ def test_config_describe_every_id():
     # the direct-copy large tile: 2 stages of (256 + 256) x 32 floats
     d = sg.describe(names.index("mfma_256x256x32_w2x4d"))
     assert d["lds_bytes"] == str(2 * 32 * 512 * 4) and d["unaligned"] == "staged-4B"
+
+
+def test_select_config_general_agrees_with_the_plain_query():
+    """batch == 1 with plain operands: the same pick as sgemm_select_config; the batch
+    multiplies the tile count the cost model spreads over the compute units."""
+    names = sg.configs()
+    for M, N, K in [(4096, 4096, 4096), (1024, 2304, 768), (1000, 1537, 777), (256, 256, 256), (1, 1, 1)]:
+        for a in (BAD, BAD + 4):
+            plain = sg.sgemm_select_config(M, N, K, 1.0, a, K, BAD, N, BAD, N)
+            assert sg.sgemm_select_config_general(0, 0, M, N, K, 1.0, a, K, 0, BAD, N, 0, BAD, N, 0, 1, 0) == plain
+    assert sg.sgemm_select_config_general(0, 0, 64, 64, 64, 0.0, BAD, 64, 0, BAD, 64, 0, BAD, 64, 0, 4, 0) == -1
+    assert sg.sgemm_select_config_general(0, 0, 64, 64, 64, 1.0, BAD, 64, 0, BAD, 64, 0, BAD, 64, 0, 0, 0) == -1
+    # 12 heads of 1024 x 1024 x 64: enough tiles to fill the chip with a larger tile than one head alone gets
+    one = names[sg.sgemm_select_config_general(0, 1, 1024, 1024, 64, 0.125, BAD, 2304, 64, BAD, 2304, 64, BAD,
+                                               1024, 1 << 20, 1, 0)]
+    twelve = names[sg.sgemm_select_config_general(0, 1, 1024, 1024, 64, 0.125, BAD, 2304, 64, BAD, 2304, 64, BAD,
+                                                  1024, 1 << 20, 12, 0)]
+    area = lambda n: int(n.split("_")[1].split("x")[0]) * int(n.split("_")[1].split("x")[1])
+    assert area(twelve) >= area(one), (one, twelve)
+    # odd strides take the unaligned table (no 32 x 64 tile there)
+    odd = names[sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD, 768, 3, BAD, 2304, 0, BAD, 2304,
+                                               1 << 22, 2, 0)]
+    assert not odd.startswith("mfma_32x64")
 
 
 def test_status_strings():

@@ -23,16 +23,32 @@ def test_read_sclk_is_an_int_or_none():
     v = bench.read_sclk()
     assert v is None or (isinstance(v, int) and v > 0)
 
+def _host_linear(w):
+    """A LinearProblem's host half (inputs, oracle leg) without device copies."""
+    p = bench.LinearProblem.__new__(bench.LinearProblem)
+    p.w, p.name, p.M, p.N, p.K, p.batch = w, w.name, w.M, w.N, w.K, 1
+    p.A, p.B, p.C = make(w)
+    p.bias, p.act = None, 0
+    return p
+
+
+def _host_batched(prob, bufs):
+    p = bench.BatchedProblem.__new__(bench.BatchedProblem)
+    p.p, p.name, p.M, p.N, p.K, p.batch, p.bufs = prob, prob.name, prob.M, prob.N, prob.K, prob.batch, bufs
+    return p
+
+
 def test_cpu_baseline_samples_every_product():
-    probs = []
-    for name, (M, N, K) in {"p1": (64, 48, 40), "p2": (32, 80, 24)}.items():
-        w = Gemm(name, M, N, K, alpha=1.5, beta=0.5, seed=7)
-        A, B, C = make(w)
-        probs.append({"w": w, "A": A, "B": B, "C": C})
+    from workloads import attention_products, gpt2_attention_set
+    probs = [_host_linear(Gemm(name, M, N, K, alpha=1.5, beta=0.5, seed=7))
+             for name, (M, N, K) in {"p1": (64, 48, 40), "p2": (32, 80, 24)}.items()]
     out = bench.cpu_baseline(probs, 0.05)
     assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s" and out["value"] > 0
     assert out["cores"] >= 1
     assert "64x48x40" in out["sample"] and "32x80x24" in out["sample"]
+    bufs = gpt2_attention_set(seed=3, T=64, heads=3, hd=16)
+    out = bench.cpu_baseline([_host_batched(p, bufs) for p in attention_products(T=64, heads=3, hd=16)], 0.05)
+    assert out["value"] > 0 and "each of the 3 64x64x16 products" in out["sample"]
 
 def test_kernel_source_hash_ignores_comments(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"

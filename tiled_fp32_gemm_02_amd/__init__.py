@@ -16,6 +16,9 @@ Raw entry points take device addresses as Python ints (or CUDA tensors, whose
     sgemm_general_ws(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
                      workspace, workspace_bytes, stream)
     sgemm_strided_batched(M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch, stream)
+    sgemm_strided_batched_op(opA, opB, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch, stream)
+    sgemm_strided_batched_general(config, opA, opB, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC,
+                                  bias, act, batch, stream)
 
 ``gemm(A, B, C=None, alpha=1, beta=0, bias=None, act=None)`` is the tensor-level
 form: it checks shapes, dtypes and devices, reads a transposed view (unit row
@@ -39,7 +42,8 @@ __all__ = [
     "sgemm_version", "sgemm_op", "sgemm_bias_act", "sgemm_general", "configs", "gemm", "gemm_batched",
     "check", "SgemmError", "SGEMM_ERROR_TOO_LARGE", "SGEMM_ERROR_BAD_CONFIG", "SGEMM_OP_N", "SGEMM_OP_T",
     "SGEMM_ACT_NONE", "SGEMM_ACT_GELU_TANH", "SGEMM_ERROR_WORKSPACE", "sgemm_general_ws", "sgemm_workspace_size",
-    "sgemm_select_config_ws", "workspace_for",
+    "sgemm_select_config_ws", "workspace_for", "sgemm_strided_batched_op", "sgemm_strided_batched_general",
+    "sgemm_select_config_general",
 ]
 
 SGEMM_ERROR_TOO_LARGE = -100
@@ -81,6 +85,18 @@ _SIGS = {
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, ctypes.c_longlong,
         _fp, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, _fp, ctypes.c_int, ctypes.c_longlong,
         ctypes.c_int, _fp]),
+    "sgemm_strided_batched_op": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int,
+        ctypes.c_longlong, _fp, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, _fp, ctypes.c_int,
+        ctypes.c_longlong, ctypes.c_int, _fp]),
+    "sgemm_strided_batched_general": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp,
+        ctypes.c_int, ctypes.c_longlong, _fp, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, _fp, ctypes.c_int,
+        ctypes.c_longlong, _fp, ctypes.c_int, ctypes.c_int, _fp]),
+    "sgemm_select_config_general": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int,
+        ctypes.c_longlong, _fp, ctypes.c_int, ctypes.c_longlong, _fp, ctypes.c_int, ctypes.c_longlong,
+        ctypes.c_int, ctypes.c_size_t]),
     "sgemm_config_count": (ctypes.c_int, []),
     "sgemm_config_name": (ctypes.c_char_p, [ctypes.c_int]),
     "sgemm_config_describe": (ctypes.c_char_p, [ctypes.c_int]),
@@ -187,6 +203,25 @@ def sgemm_strided_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta
                           batch, stream=None) -> int:
     return load().sgemm_strided_batched(M, N, K, alpha, _addr(A), lda, strideA, _addr(B), ldb, strideB,
                                         beta, _addr(C), ldc, strideC, batch, _stream(stream))
+
+
+def sgemm_strided_batched_op(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
+                             batch, stream=None) -> int:
+    return load().sgemm_strided_batched_op(opA, opB, M, N, K, alpha, _addr(A), lda, strideA, _addr(B), ldb,
+                                           strideB, beta, _addr(C), ldc, strideC, batch, _stream(stream))
+
+
+def sgemm_strided_batched_general(config, opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C,
+                                  ldc, strideC, bias, act, batch, stream=None) -> int:
+    return load().sgemm_strided_batched_general(config, opA, opB, M, N, K, alpha, _addr(A), lda, strideA,
+                                                _addr(B), ldb, strideB, beta, _addr(C), ldc, strideC, _addr(bias),
+                                                act, batch, _stream(stream))
+
+
+def sgemm_select_config_general(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                                batch, workspace_bytes=0) -> int:
+    return load().sgemm_select_config_general(opA, opB, M, N, K, alpha, _addr(A), lda, strideA, _addr(B), ldb,
+                                              strideB, _addr(C), ldc, strideC, batch, workspace_bytes)
 
 
 def sgemm_config_count() -> int:
@@ -349,32 +384,64 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None, confi
     return C
 
 
-def gemm_batched(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None):
-    """Batched C[b] <- alpha*A[b]@B[b] + beta*C[b] on 3-D GPU float32 tensors.
+def _batched_operand(t, name, allow_transposed=True):
+    """(op, ld, batch stride) of a batch x rows x cols view. The last two dimensions are
+    read as for gemm(): unit column stride -> as stored, unit row stride -> a transpose
+    read in place (only if allow_transposed)."""
+    if t.dim() != 3:
+        raise ValueError(f"Dimension error: {name} must be 3-D (batch, rows, cols), got {t.dim()} dimensions")
+    if str(t.dtype) != "torch.float32":
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    bsz, rows, cols = t.shape
+    s0, s1, s2 = t.stride()
+    sb = s0 if bsz > 1 else 0
+    if cols <= 1 or s2 == 1:
+        ld = s1 if rows > 1 else max(cols, 1)
+        return SGEMM_OP_N, max(ld, cols, 1), sb
+    if allow_transposed and (rows <= 1 or s1 == 1):
+        ld = s2 if cols > 1 else max(rows, 1)
+        return SGEMM_OP_T, max(ld, rows, 1), sb
+    what = "a unit stride in one of its last two dimensions" if allow_transposed else "unit column stride"
+    raise ValueError(f"{name} needs {what} (got strides {tuple(t.stride())})")
 
-    Each operand is batch x rows x cols with unit column stride; the batch stride
-    and row stride come from the tensor. Returns C.
+
+def gemm_batched(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None, config: int = -1, bias=None,
+                 act=None):
+    """Batched C[b] <- act(alpha*A[b]@B[b] + beta*C[b] + bias) on 3-D GPU float32 tensors.
+
+    Each operand is batch x rows x cols. A and B may be views whose last two dimensions
+    are row-major or transposed (``x.transpose(1, 2)``), read in place; C needs unit
+    column stride. The batch and row strides come from the tensors, so per-head views of
+    one matrix (e.g. ``qkv[:, :768].view(T, 12, 64).transpose(0, 1)``) need no copies,
+    and C may be heads side by side in one matrix. bias (length N, shared by all
+    batches) and act as for gemm(). Returns C.
     """
     import torch
 
-    for name, t in (("A", A), ("B", B)):
-        if t.dim() != 3:
-            raise ValueError(f"Dimension error: {name} must be 3-D (batch, rows, cols)")
+    opA, lda, sA = _batched_operand(A, "A")
+    opB, ldb, sB = _batched_operand(B, "B")
     bsz, M, K = A.shape
     if B.shape[0] != bsz or B.shape[1] != K:
         raise ValueError(f"Size error: A is {tuple(A.shape)} and B is {tuple(B.shape)}")
     N = B.shape[2]
+    if act not in _ACTS:
+        raise ValueError(f"act must be one of {sorted(k for k in _ACTS if k)} or None, got {act!r}")
+    if bias is not None:
+        if bias.dim() != 1 or bias.shape[0] != N or str(bias.dtype) != "torch.float32" or not bias.is_cuda:
+            raise ValueError(f"bias must be a float32 GPU vector of length {N}")
+        if bias.stride(0) != 1 and N > 1:
+            raise ValueError("bias must be contiguous")
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an input C")
         C = torch.empty((bsz, M, N), dtype=torch.float32, device=A.device)
     if tuple(C.shape) != (bsz, M, N):
         raise ValueError(f"Size error: C is {tuple(C.shape)}, expected {(bsz, M, N)}")
-    lda = _row_major_ld(A[0], "A[b]") if bsz else max(K, 1)
-    ldb = _row_major_ld(B[0], "B[b]") if bsz else max(N, 1)
-    ldc = _row_major_ld(C[0], "C[b]") if bsz else max(N, 1)
+    _, ldc, sC = _batched_operand(C, "C", allow_transposed=False)
     if stream is None:
         stream = torch.cuda.current_stream(A.device)
-    check(sgemm_strided_batched(M, N, K, alpha, A, lda, A.stride(0), B, ldb, B.stride(0), beta, C, ldc,
-                                C.stride(0), bsz, stream), "sgemm_strided_batched")
+    check(sgemm_strided_batched_general(config, opA, opB, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc,
+                                        sC, bias, _ACTS[act], bsz, stream), "sgemm_strided_batched_general")
     return C

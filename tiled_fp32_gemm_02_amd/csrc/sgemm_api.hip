@@ -311,7 +311,7 @@ struct CandidateIds {
 
 // The configuration with the least modelled time. Stream-K candidates are considered
 // only when `ws_bytes` holds their workspace for `cus` compute units (cus > 0).
-int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0)
+int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0, int batch = 1)
 {
     static const CandidateIds ids;
     const Candidate *table = vec ? kCandidates : kUnalignedCandidates;
@@ -325,7 +325,7 @@ int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0)
         const Candidate &cand = table[i];
         if (table_ids[i] < 0)
             continue;
-        const uint64_t tiles = tile_count(kConfigs[table_ids[i]], M, N);
+        const uint64_t tiles = tile_count(kConfigs[table_ids[i]], M, N) * (uint64_t)batch;
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
         const double us = cand.fixed_us + (double)rounds * cand.round_us +
                           (double)rounds * cand.units * unit_mflop / (rounds >= 2 ? cand.rate_many : cand.rate_one);
@@ -334,7 +334,7 @@ int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0)
             best_us = us;
         }
     }
-    for (int i = 0; vec && cus > 0 && i < kNumSkCandidates; ++i) {   // stream-K kernels: aligned operands
+    for (int i = 0; vec && cus > 0 && batch == 1 && i < kNumSkCandidates; ++i) {   // stream-K: aligned, one matrix
         const Candidate &cand = kSkCandidates[i];
         if (ids.sk[i] < 0)
             continue;
@@ -383,6 +383,27 @@ const int kPosPlain[] = {0, 0, 0, 1, 2, 3, 5, 6, 7, 8, 10, 11, 0};     // sgemm,
 const int kPosOp[] = {0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 12, 13, 0};       // sgemm_op
 const int kPosFused[] = {0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 12, 13, 15};   // sgemm_bias_act, sgemm_general
 const int kPosBatched[] = {0, 0, 0, 1, 2, 3, 5, 6, 8, 9, 12, 13, 0};   // sgemm_strided_batched
+const int kPosBatchedOp[] = {0, 1, 2, 3, 4, 5, 7, 8, 10, 11, 14, 15, 18};  // sgemm_strided_batched_op/general
+
+// Batched calls: strides and count valid, and the batches' C windows disjoint. Windows are
+// disjoint when they are stacked (each starts past the previous one's last entry) or side by
+// side inside the rows of one matrix (each N wide, all of them within ldc), as when attention
+// heads write their columns of one output. Returns 0, or the position of the bad argument
+// given the positions of strideA, strideB, strideC and batch.
+int check_batch(int M, int N, int ldc, long long sA, long long sB, long long sC, int batch, int pA, int pB,
+                int pC, int pBatch)
+{
+    if (sA < 0) return pA;
+    if (sB < 0) return pB;
+    if (sC < 0) return pC;
+    if (batch < 0 || batch > 65535) return pBatch;
+    if (batch > 1 && M > 0 && N > 0) {
+        const bool stacked = sC >= (long long)(M - 1) * ldc + N;
+        const bool side_by_side = sC >= N && (long long)(batch - 1) * sC + N <= ldc;
+        if (!stacked && !side_by_side) return pC;
+    }
+    return 0;
+}
 
 int run(int config, int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, int64_t sA,
         const float *B, int ldb, int64_t sB, float beta, float *C, int ldc, int64_t sC, const float *bias,
@@ -407,7 +428,7 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     const bool vec = vector_ok(opA, opB, M, N, K, A, lda, B, ldb, C, ldc) &&
                      (batch == 1 || (sA % 4 == 0 && sB % 4 == 0 && sC % 4 == 0));
     const int cus = (ws != nullptr && batch == 1) ? device_cus() : 0;
-    const int id = config >= 0 ? config : choose(M, N, K, vec, ws_bytes, cus);
+    const int id = config >= 0 ? config : choose(M, N, K, vec, ws_bytes, cus, batch);
     const Config &c = kConfigs[id];
     const uint64_t tiles = tile_count(c, M, N);
     if ((c.kind == KIND_MFMA || c.kind == KIND_VALU) && tiles * (uint64_t)c.threads > 0xFFFFFFFFull)
@@ -450,6 +471,28 @@ int general(const int *pos, int config, int opA, int opB, int M, int N, int K, f
         return SGEMM_SUCCESS;
     return run(config, opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, bias, act, 1, ws,
                ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// The batched entry points with operand forms. Arguments keep the positions of
+// sgemm_strided_batched_general up to strideC (16); `batch_pos` is where batch sits in the
+// caller's signature (17 without bias and act, 19 with them).
+int batched(int batch_pos, int config, int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+            long long strideA, const float *B, int ldb, long long strideB, float beta, float *C, int ldc,
+            long long strideC, const float *bias, int act, int batch, void *stream)
+{
+    if (config < -1 || config >= kNumConfigs)
+        return SGEMM_ERROR_BAD_CONFIG;
+    const Arg bad = check_args(opA, opB, M, N, K, alpha, A, lda, B, ldb, C, ldc, act);
+    if (bad != ARG_OK)
+        return -kPosBatchedOp[bad];
+    if (const int pos = check_batch(M, N, ldc, strideA, strideB, strideC, batch, 9, 12, 16, batch_pos))
+        return -pos;
+    if (M == 0 || N == 0 || batch == 0)
+        return SGEMM_SUCCESS;
+    if (config >= 0 && kConfigs[config].kind == KIND_SK)
+        return SGEMM_ERROR_WORKSPACE;
+    return run(config, opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, bias,
+               act, batch, nullptr, 0, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -497,14 +540,29 @@ int sgemm_strided_batched(int M, int N, int K, float alpha, const float *A, int 
     const Arg bad = check_args(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, C, ldc, SGEMM_ACT_NONE);
     if (bad != ARG_OK)
         return -kPosBatched[bad];
-    if (strideA < 0) return -7;
-    if (strideB < 0) return -10;
-    if (batch < 0 || batch > 65535) return -15;
-    if (batch > 1 && M > 0 && N > 0 && strideC < (long long)(M - 1) * ldc + N) return -14;
+    if (const int pos = check_batch(M, N, ldc, strideA, strideB, strideC, batch, 7, 10, 14, 15))
+        return -pos;
     if (M == 0 || N == 0 || batch == 0)
         return SGEMM_SUCCESS;
     return run(-1, SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
                strideC, nullptr, SGEMM_ACT_NONE, batch, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+int sgemm_strided_batched_general(int config, int opA, int opB, int M, int N, int K, float alpha, const float *A,
+                                  int lda, long long strideA, const float *B, int ldb, long long strideB,
+                                  float beta, float *C, int ldc, long long strideC, const float *bias, int act,
+                                  int batch, void *stream)
+{
+    return batched(19, config, opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
+                   bias, act, batch, stream);
+}
+
+int sgemm_strided_batched_op(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+                             long long strideA, const float *B, int ldb, long long strideB, float beta, float *C,
+                             int ldc, long long strideC, int batch, void *stream)
+{
+    return batched(17, -1, opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
+                   nullptr, SGEMM_ACT_NONE, batch, stream);
 }
 
 int sgemm_general_ws(int config, int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
@@ -539,6 +597,18 @@ int sgemm_select_config_ws(int M, int N, int K, float alpha, const float *A, int
         return -1;
     return choose(M, N, K, vector_ok(SGEMM_OP_N, SGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc), workspace_bytes,
                   workspace_bytes > 0 ? device_cus() : 0);
+}
+
+int sgemm_select_config_general(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+                                long long strideA, const float *B, int ldb, long long strideB, const float *C,
+                                int ldc, long long strideC, int batch, size_t workspace_bytes)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || alpha == 0.0f || batch <= 0)
+        return -1;
+    const bool vec = vector_ok(opA != 0, opB != 0, M, N, K, A, lda, B, ldb, C, ldc) &&
+                     (batch == 1 || (strideA % 4 == 0 && strideB % 4 == 0 && strideC % 4 == 0));
+    return choose(M, N, K, vec, batch == 1 ? workspace_bytes : 0,
+                  batch == 1 && workspace_bytes > 0 ? device_cus() : 0, batch);
 }
 
 int sgemm_config_count(void) { return kNumConfigs; }
@@ -624,12 +694,13 @@ const char *sgemm_status_string(int status)
     case SGEMM_ERROR_WORKSPACE: return "stream-K configuration without a large enough workspace";
     default: break;
     }
-    if (status < 0 && status >= -16) {
-        static const char *const msgs[17] = {
+    if (status < 0 && status >= -20) {
+        static const char *const msgs[21] = {
             "", "invalid argument 1", "invalid argument 2", "invalid argument 3", "invalid argument 4",
             "invalid argument 5", "invalid argument 6", "invalid argument 7", "invalid argument 8",
             "invalid argument 9", "invalid argument 10", "invalid argument 11", "invalid argument 12",
-            "invalid argument 13", "invalid argument 14", "invalid argument 15", "invalid argument 16"};
+            "invalid argument 13", "invalid argument 14", "invalid argument 15", "invalid argument 16",
+            "invalid argument 17", "invalid argument 18", "invalid argument 19", "invalid argument 20"};
         return msgs[-status];
     }
     if (status > 0)

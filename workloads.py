@@ -16,6 +16,9 @@ row-major, float32:
 * ``normal``: ``rng.standard_normal(shape, float32)``.
 * ``normal002``: ``0.02 * rng.standard_normal(shape, float32)`` (the usual
   init scale of a GPT-2 linear weight).
+* ``prob1024``: ``rng.random(shape, float32) * 2**-9``: non-negative entries whose
+  rows of 1024 sum to about 1, standing in for attention probabilities after the
+  softmax (exact in fp32: a power-of-two scale of multiples of 2**-24).
 
 Draw order within one workload is A, then B, then C (C only when beta != 0).
 The GPT-2-small linear set draws X1, W1, W2, X3, W3 from one generator; X1
@@ -28,7 +31,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Gemm", "WORKLOADS", "draw", "make", "gpt2_linear_set", "flops"]
+__all__ = ["Gemm", "WORKLOADS", "draw", "make", "gpt2_linear_set", "flops", "BatchedGemm", "gpt2_attention_set",
+           "ATTENTION"]
 
 
 @dataclass(frozen=True)
@@ -76,6 +80,8 @@ def draw(rng: np.random.Generator, shape, dist: str) -> np.ndarray:
         x = rng.standard_normal(shape, dtype=np.float32)
     elif dist == "normal002":
         x = np.float32(0.02) * rng.standard_normal(shape, dtype=np.float32)
+    elif dist == "prob1024":
+        x = rng.random(shape, dtype=np.float32) * np.float32(2.0 ** -9)
     elif dist == "smallint":
         # integers in [-8, 8]: every partial sum of K <= 2**17 products stays exact in fp32
         x = rng.integers(-8, 9, size=shape).astype(np.float32)
@@ -145,3 +151,66 @@ WORKLOADS = {
     "gpt2_mlp_down": Gemm("gpt2_mlp_down", 1024, 768, 3072, dist_a="normal", dist_b="normal002", seed=4,
                           note="GPT-2-small MLP down, 1024 tokens: X[1024x3072] W[3072x768]"),
 }
+
+
+@dataclass(frozen=True)
+class BatchedGemm:
+    """One strided-batched product over shared buffers: for b in [0, batch),
+    C_b = alpha * op(A_b) op(B_b) with A_b at float offset a_off + b*sA of buffer `a`
+    (leading dimension lda), likewise B_b and C_b. op = 1 reads the stored matrix
+    transposed. Names the buffers of ``gpt2_attention_set``."""
+
+    name: str
+    batch: int
+    M: int
+    N: int
+    K: int
+    alpha: float
+    opA: int
+    opB: int
+    a: str
+    a_off: int
+    lda: int
+    sA: int
+    b: str
+    b_off: int
+    ldb: int
+    sB: int
+    c_rows: int
+    c_cols: int
+    c_off: int
+    ldc: int
+    sC: int
+    note: str = field(default="", compare=False)
+
+
+def gpt2_attention_set(seed: int = 5, T: int = 1024, heads: int = 12, hd: int = 64):
+    """Inputs of one GPT-2-small attention layer's two per-head products at batch 1 x T
+    tokens: the QKV projection output X[T x 3*heads*hd] ~ N(0, 1) (Q, K, V are its three
+    column blocks, head h at columns h*hd of each) and probabilities P[heads x T x T]
+    (``prob1024``), drawn in that order from one generator. P is drawn, not computed from
+    the scores, so that each product's inputs are independent of the other's result."""
+    rng = np.random.default_rng(seed)
+    qkv = draw(rng, (T, 3 * heads * hd), "normal")
+    p = draw(rng, (heads, T, T), "prob1024")
+    return {"qkv": qkv, "p": p}
+
+
+def attention_products(T: int = 1024, heads: int = 12, hd: int = 64):
+    """The two batched products of attention over ``gpt2_attention_set`` buffers:
+    scores_h = Q_h K_h^T / sqrt(hd) into S[heads x T x T], and out_h = P_h V_h written
+    side by side into O[T x heads*hd] (head h at columns h*hd)."""
+    w = 3 * heads * hd
+    return [
+        BatchedGemm("gpt2_attn_scores", heads, T, T, hd, 1.0 / float(np.sqrt(hd)), 0, 1,
+                    "qkv", 0, w, hd, "qkv", heads * hd, w, hd, heads * T, T, 0, T, T * T,
+                    note=f"{heads} heads x Q_h K_h^T / sqrt({hd}): {T}x{T}x{hd}, Q and K read in place from "
+                         f"QKV[{T}x{w}] (K transposed)"),
+        BatchedGemm("gpt2_attn_values", heads, T, hd, T, 1.0, 0, 0,
+                    "p", 0, T, T * T, "qkv", 2 * heads * hd, w, hd, T, heads * hd, 0, heads * hd, hd,
+                    note=f"{heads} heads x P_h V_h: {T}x{hd}x{T}, V read in place from QKV, heads side by side "
+                         f"in O[{T}x{heads * hd}]"),
+    ]
+
+
+ATTENTION = {b.name: b for b in attention_products()}
