@@ -258,6 +258,37 @@ int sgemm_general_ws(int config, int opA, int opB, int M, int N, int K, float al
                      void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/* Bytes of the scratch array that sgemm_general_noalloc uses on each GPU: 64 KiB of tile
+ * counters plus two 128 x 128 fp32 partial tiles for each of 256 compute units. */
+#define SGEMM_NOALLOC_SCRATCH_BYTES (65536ull + 2ull * 256ull * 128ull * 128ull * 4ull)
+
+/*
+ * sgemm_general_ws for callers that cannot allocate device memory or pass a workspace:
+ * code under HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * It calls no hipMalloc, hipFree or allocating routine. The stream-K configurations use a
+ * scratch array of SGEMM_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on, from the first call on that GPU until the process ends; everything else is as for
+ * sgemm_general_ws with that array as the workspace.
+ *  - Every call on a GPU shares that GPU's array. Calls that may overlap on one GPU (on
+ *    different streams, or from several threads) race on it and must not be issued; calls
+ *    queued in order on one stream are fine.
+ *  - The first call on a GPU looks up the array's address and queues a small kernel on
+ *    `stream` that zeroes its tile counters; every later call leaves them at zero again.
+ *  - A forced stream-K configuration whose workspace (sgemm_workspace_size) exceeds the
+ *    array returns SGEMM_ERROR_WORKSPACE; with config == -1 only stream-K configurations
+ *    that fit are considered.
+ *  - A failure to look up the array returns a positive hipError_t.
+ *
+ * Arguments by position, as sgemm_general: 1 opA, 2 opB, 3 M, 4 N, 5 K, 6 alpha, 7 A, 8 lda,
+ * 9 B, 10 ldb, 11 beta, 12 C, 13 ldc, 14 bias, 15 act, 16 stream (config is not counted).
+ */
+int sgemm_general_noalloc(int config, int opA, int opB, int M, int N, int K, float alpha,
+                          const float *A, int lda,
+                          const float *B, int ldb,
+                          float beta, float *C, int ldc,
+                          const float *bias, int act,
+                          void *stream);
+
 /*
  * Workspace bytes that stream-K configuration `config` needs on the current device
  * (64 KiB of counters plus two partial tiles per compute unit), or with config == -1

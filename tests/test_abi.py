@@ -408,6 +408,21 @@ def test_workspace_argument_checks():
     assert sg.sgemm_general_ws(-1, 0, 0, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, None, 0, None, 0) == 0
 
 
+def test_noalloc_validates_before_touching_the_device():
+    """The allocation-free entry point numbers its arguments as sgemm_general and rejects
+    bad ones, or returns early on an empty result, before it looks up its scratch array."""
+    assert sg.sgemm_general_noalloc(-1, 0, 0, 4, 4, 8, 1.0, BAD, 7, BAD, 4, 0.0, BAD, 4, None, 0) == -8  # lda < K
+    assert sg.sgemm_general_noalloc(-1, 2, *WS_ARGS[1:]) == -1
+    assert sg.sgemm_general_noalloc(-1, *WS_ARGS[:14], 5) == -15                      # act
+    assert sg.sgemm_general_noalloc(-2, *WS_ARGS) == sg.SGEMM_ERROR_BAD_CONFIG
+    assert sg.sgemm_general_noalloc(sg.sgemm_config_count(), *WS_ARGS) == sg.SGEMM_ERROR_BAD_CONFIG
+    assert sg.sgemm_general_noalloc(-1, 0, 0, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, None, 0) == 0
+    # the array holds the counters and two 128 x 128 partial tiles for each of 256 compute units
+    assert sg.SGEMM_NOALLOC_SCRATCH_BYTES == 65536 + 2 * 256 * 128 * 128 * 4
+    text = open(HEADER).read()
+    assert "#define SGEMM_NOALLOC_SCRATCH_BYTES (65536ull + 2ull * 256ull * 128ull * 128ull * 4ull)" in text
+
+
 def test_forced_stream_k_needs_a_workspace():
     for cid in sk_ids():
         assert sg.sgemm_general_ws(cid, *WS_ARGS, None, 0) == sg.SGEMM_ERROR_WORKSPACE

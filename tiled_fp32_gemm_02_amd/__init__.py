@@ -15,6 +15,7 @@ Raw entry points take device addresses as Python ints (or CUDA tensors, whose
     sgemm_general(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream)
     sgemm_general_ws(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
                      workspace, workspace_bytes, stream)
+    sgemm_general_noalloc(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream)
     sgemm_strided_batched(M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch, stream)
     sgemm_strided_batched_op(opA, opB, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch, stream)
     sgemm_strided_batched_general(config, opA, opB, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC,
@@ -43,7 +44,7 @@ __all__ = [
     "check", "SgemmError", "SGEMM_ERROR_TOO_LARGE", "SGEMM_ERROR_BAD_CONFIG", "SGEMM_OP_N", "SGEMM_OP_T",
     "SGEMM_ACT_NONE", "SGEMM_ACT_GELU_TANH", "SGEMM_ERROR_WORKSPACE", "sgemm_general_ws", "sgemm_workspace_size",
     "sgemm_select_config_ws", "workspace_for", "sgemm_strided_batched_op", "sgemm_strided_batched_general",
-    "sgemm_select_config_general",
+    "sgemm_select_config_general", "sgemm_general_noalloc", "SGEMM_NOALLOC_SCRATCH_BYTES",
 ]
 
 SGEMM_ERROR_TOO_LARGE = -100
@@ -78,6 +79,9 @@ _SIGS = {
                                         ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int,
                                         ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int, _fp,
                                         ctypes.c_size_t, _fp]),
+    "sgemm_general_noalloc": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int,
+                                             ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int, _fp]),
     "sgemm_workspace_size": (ctypes.c_size_t, [ctypes.c_int]),
     "sgemm_select_config_ws": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp,
                                               ctypes.c_int, _fp, ctypes.c_int, _fp, ctypes.c_int, ctypes.c_size_t]),
@@ -188,6 +192,15 @@ def sgemm_general_ws(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, 
     return load().sgemm_general_ws(config, opA, opB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta,
                                    _addr(C), ldc, _addr(bias), act, _addr(workspace), workspace_bytes,
                                    _stream(stream))
+
+
+def sgemm_general_noalloc(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
+                          stream=None) -> int:
+    return load().sgemm_general_noalloc(config, opA, opB, M, N, K, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                                        _addr(C), ldc, _addr(bias), act, _stream(stream))
+
+
+SGEMM_NOALLOC_SCRATCH_BYTES = 65536 + 2 * 256 * 128 * 128 * 4
 
 
 def sgemm_workspace_size(config: int = -1) -> int:

@@ -11,6 +11,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "sgemm.h"
 #include "sgemm_configs.inc"
@@ -18,6 +19,11 @@
 #include "sgemm_launch.hpp"
 
 using sgemm_impl::GemmArgs;
+
+// Scratch of the allocation-free entry point (sgemm_general_noalloc): the stream-K workspace
+// (tile counters, then partial-tile slots) as a file-scope device array, one copy per GPU,
+// held until the process ends. Sized for both stream-K configurations on 256 compute units.
+static __device__ __align__(256) unsigned char scratch[SGEMM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -473,6 +479,49 @@ int general(const int *pos, int config, int opA, int opB, int M, int N, int K, f
                ws_bytes, static_cast<hipStream_t>(stream));
 }
 
+static_assert(SGEMM_NOALLOC_SCRATCH_BYTES == kSkCounterBytes + 2ull * 256 * 128 * 128 * sizeof(float),
+              "scratch holds the counters and two 128 x 128 partial tiles per compute unit");
+
+__global__ void __launch_bounds__(256) zero_words(unsigned *p, int n)
+{
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256)
+        p[i] = 0u;
+}
+
+// Device address of this device's copy of `scratch`. Host code must never pass the array's
+// name to a kernel (on the host it is a stand-in, not a device address); the address comes
+// from hipGetSymbolAddress, once per device with that device current. The first call on a
+// device also queues a kernel on `stream` that zeroes the tile counters, ahead of any
+// kernel that reads them (every stream-K call leaves them at zero again). Returns 0 or a
+// positive hipError_t.
+int scratch_for_current_device(void **out, hipStream_t stream)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mtx;
+    static void *addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return (int)e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mtx);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return e != hipSuccess ? (int)e : (int)hipErrorInvalidSymbol;
+        hipLaunchKernelGGL(zero_words, dim3(64), dim3(256), 0, stream, static_cast<unsigned *>(p),
+                           (int)(kSkCounterBytes / sizeof(unsigned)));
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return (int)e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return 0;
+}
+
 // The batched entry points with operand forms. Arguments keep the positions of
 // sgemm_strided_batched_general up to strideC (16); `batch_pos` is where batch sits in the
 // caller's signature (17 without bias and act, 19 with them).
@@ -573,6 +622,27 @@ int sgemm_general_ws(int config, int opA, int opB, int M, int N, int K, float al
         return -16;
     return general(kPosFused, config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream,
                    workspace, workspace_bytes);
+}
+
+int sgemm_general_noalloc(int config, int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+                          const float *B, int ldb, float beta, float *C, int ldc, const float *bias, int act,
+                          void *stream)
+{
+    if (config < -1 || config >= kNumConfigs)
+        return SGEMM_ERROR_BAD_CONFIG;
+    const Arg bad = check_args(opA, opB, M, N, K, alpha, A, lda, B, ldb, C, ldc, act);
+    if (bad != ARG_OK)
+        return -kPosFused[bad];
+    if (M == 0 || N == 0)
+        return SGEMM_SUCCESS;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if (const int e = scratch_for_current_device(&ws, s))
+        return e;
+    // A forced stream-K configuration whose workspace exceeds the array returns
+    // SGEMM_ERROR_WORKSPACE from run(); the automatic choice only considers those that fit.
+    return run(config, opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, bias, act, 1, ws,
+               SGEMM_NOALLOC_SCRATCH_BYTES, s);
 }
 
 size_t sgemm_workspace_size(int config)
