@@ -49,10 +49,11 @@ def parse_config(name):
 def expected_mfma_kernels(config_names):
     """Template arguments <BM,BN,BK,WGM,WGN,WGK,PF,DMA,TA,TB,VEC,EDGE> of every matrix
     kernel the launcher can start: per configuration and operand form, the aligned
-    whole-tile and edge variants as configured; the register-staged unaligned variant with
-    one K-tile in flight (K-tile 16 * WGK for direct-copy configurations); and, for
-    direct-copy configurations with at most 16 copies per thread and K-tile, the unaligned
-    variant with 4-byte direct copies."""
+    whole-tile and edge variants as configured; for register-staged configurations
+    (stream-K ones included) the unaligned variant with their own K-tile and loads in
+    flight; for direct-copy ones the register-staged unaligned variant with one K-tile in
+    flight and K-tiles of 16 * WGK, and, with at most 16 copies per thread and K-tile, the
+    unaligned variant with 4-byte direct copies and the configured K-tiles in flight."""
     out = set()
     for name in config_names:
         bm, bn, bk, wm, wn, wk, pf, dma = parse_config(name)
@@ -63,21 +64,33 @@ def expected_mfma_kernels(config_names):
                     for edge in (0, 1):
                         out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge))
                     if dma and (bm * bk + bk * bn) // nt <= 16:
-                        out.add((bm, bn, bk, wm, wn, wk, 1, 1, ta, tb, 0, 1))
-                out.add((bm, bn, 16 * wk if dma else bk, wm, wn, wk, 1, 0, ta, tb, 0, 1))
+                        out.add((bm, bn, bk, wm, wn, wk, pf, 1, ta, tb, 0, 1))
+                    if dma:
+                        out.add((bm, bn, 16 * wk, wm, wn, wk, 1, 0, ta, tb, 0, 1))
+                    else:
+                        out.add((bm, bn, bk, wm, wn, wk, pf, 0, ta, tb, 0, 1))
+                else:
+                    # stream-K: the register-staged tile kernel for operands it cannot take (unaligned
+                    # without a 4-byte-copy form, or rows too long for direct copies)
+                    out.add((bm, bn, bk, wm, wn, wk, pf, 0, ta, tb, 0, 1))
     return out
 
 
 def expected_sk_kernels(config_names):
     """Stream-K kernels: the aligned whole-tile and edge variants of each stream-K
-    configuration (unaligned operands run the data-parallel kernel of the tile)."""
+    configuration, and for direct-copy ones with at most 16 copies per thread and K-tile
+    the unaligned variant with 4-byte copies (other configurations run the data-parallel
+    kernel of the tile on unaligned operands)."""
     out = set()
     for name in config_names:
         bm, bn, bk, wm, wn, wk, pf, dma = parse_config(name)
+        nt = wm * wn * wk * 64
         for ta in (0, 1):
             for tb in (0, 1):
                 for edge in (0, 1):
                     out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge))
+                if dma and (bm * bk + bk * bn) // nt <= 16:
+                    out.add((bm, bn, bk, wm, wn, wk, pf, 1, ta, tb, 0, 1))
     return out
 
 

@@ -37,7 +37,7 @@ enum Kind { KIND_TILE16 = 0, KIND_MFMA = 1, KIND_SK = 2, KIND_VALU = 3 };
 typedef hipError_t (*LaunchFn)(const GemmArgs &, int batch, bool ta, bool tb, bool vec, bool edge, bool dma_ok,
                                hipStream_t);
 typedef hipError_t (*LaunchSkFn)(const GemmArgs &, const StreamK &, int grid, bool ta, bool tb, bool vec,
-                                 bool edge, hipStream_t);
+                                 bool edge, bool dma_ok, hipStream_t);
 
 struct Config {
     const char *name;
@@ -121,19 +121,19 @@ hipError_t launch_mfma(const GemmArgs &p, int batch, bool ta, bool tb, bool vec,
 
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M>
 hipError_t launch_sk(const GemmArgs &p, const StreamK &sk, int grid, bool ta, bool tb, bool vec, bool edge,
-                     hipStream_t s)
+                     bool dma_ok, hipStream_t s)
 {
     if (!ta && !tb)
-        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, false>(p, sk, grid,
-                                                                                                        vec, edge, s);
+        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, false>(
+            p, sk, grid, vec, edge, dma_ok, s);
     if (!ta && tb)
-        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, true>(p, sk, grid,
-                                                                                                       vec, edge, s);
+        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, true>(
+            p, sk, grid, vec, edge, dma_ok, s);
     if (ta && !tb)
-        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, false>(p, sk, grid,
-                                                                                                       vec, edge, s);
-    return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, true>(p, sk, grid, vec,
-                                                                                                  edge, s);
+        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, false>(
+            p, sk, grid, vec, edge, dma_ok, s);
+    return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, true>(
+        p, sk, grid, vec, edge, dma_ok, s);
 }
 
 // The vector-ALU micro-tile kernel: one 256-thread workgroup per 128 x 128 tile.
@@ -457,7 +457,7 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
         sk.work = (int)tiles * sk.iters;
         // At most one workgroup per K-tile step, so every workgroup's range is non-empty.
         const int grid = sk.work < cus ? sk.work : cus;
-        const hipError_t e = c.launch_sk(p, sk, grid, opA != 0, opB != 0, vec, edge, stream);
+        const hipError_t e = c.launch_sk(p, sk, grid, opA != 0, opB != 0, vec, edge, dma_ok, stream);
         return e == hipSuccess ? 0 : (int)e;
     }
     const hipError_t e = c.launch(p, batch, opA != 0, opB != 0, vec, edge, dma_ok, stream);

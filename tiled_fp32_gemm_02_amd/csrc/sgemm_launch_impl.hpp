@@ -4,11 +4,15 @@
 //
 // Unaligned operands (rows only 4-byte aligned): a direct-copy configuration copies
 // 4-byte words into the same LDS layout when a thread's share of a K-tile is at most 16
-// copies (the offsets then fit the register budget), with one K-tile in flight. Every
-// other configuration, and every call whose row strides are too long for 32-bit copy
-// offsets (dma_ok false), runs the register-staged kernel with element-wise loads and one
-// K-tile in flight, with K-tiles of 16 * WGK for direct-copy configurations, so that
-// variant fits the register file for every tile shape.
+// copies (the offsets then fit the register budget), with its K-tiles in flight. A
+// register-staged configuration keeps its own K-tile and loads in flight, with 16-byte
+// loads of the chunks wholly inside a row and element-wise ones for the chunk that
+// straddles its end. Every other direct-copy configuration, and every call whose row
+// strides are too long for 32-bit copy offsets (dma_ok false), runs the register-staged
+// kernel with one K-tile in flight and K-tiles of 16 * WGK, so that variant fits the
+// register file for every tile shape. A stream-K configuration (register-staged) runs the
+// data-parallel kernel of its tile on unaligned operands: stream-K itself was measured
+// slower there on every odd-sized shape swept.
 #pragma once
 
 #include "sgemm_launch.hpp"
@@ -33,28 +37,40 @@ hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, boo
     else if (vec)
         hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, true>), grid, block, 0, s,
                            p, GROUP_M);
+    else if constexpr (!DMA)    // register-staged configuration: its own K-tile and loads in flight
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, false, TA, TB, false, true>), grid, block, 0,
+                           s, p, GROUP_M);
     else if (!DMA4 || !dma_ok)
         hipLaunchKernelGGL((sgemm_mfma<BM, BN, BKU, WGM, WGN, WGK, 1, false, TA, TB, false, true>), grid, block, 0,
                            s, p, GROUP_M);
     else if constexpr (DMA4)
-        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, 1, true, TA, TB, false, true>), grid, block, 0, s,
-                           p, GROUP_M);
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, true, TA, TB, false, true>), grid, block, 0,
+                           s, p, GROUP_M);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, bool TA, bool TB>
-hipError_t launch_mfma_sk_op(const GemmArgs &p, const StreamK &sk, int grid, bool vec, bool edge, hipStream_t s)
+hipError_t launch_mfma_sk_op(const GemmArgs &p, const StreamK &sk, int grid, bool vec, bool edge, bool dma_ok,
+                             hipStream_t s)
 {
-    const dim3 block(WGM * WGN * WGK * 64);
-    if (vec && !edge)
+    constexpr int NT = WGM * WGN * WGK * 64;
+    constexpr bool DMA4 = DMA && (BM * BK + BK * BN) / NT <= 16;   // 4-byte copies for unaligned rows
+    const dim3 block(NT);
+    // Direct copies address a tile with 32-bit offsets: long rows run the register-staged
+    // data-parallel kernel of the tile, like unaligned operands without a 4-byte-copy form.
+    const bool staged = (DMA && !dma_ok) || (!vec && !DMA4);
+    if (staged)
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, false, TA, TB, false, true>),
+                           dim3(sk.tiles_m * sk.tiles_n), block, 0, s, p, GROUP_M);
+    else if (vec && !edge)
         hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, false>), dim3(grid),
                            block, 0, s, p, sk);
     else if (vec)
         hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, true>), dim3(grid),
                            block, 0, s, p, sk);
-    else    // unaligned operands: the register-staged data-parallel kernel of the same tile
-        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, 1, false, TA, TB, false, true>),
-                           dim3(sk.tiles_m * sk.tiles_n), block, 0, s, p, GROUP_M);
+    else if constexpr (DMA4)    // rows only 4-byte aligned: 4-byte direct copies into the same LDS layout
+        hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, true, TA, TB, false, true>), dim3(grid),
+                           block, 0, s, p, sk);
     return hipGetLastError();
 }
 
