@@ -44,7 +44,7 @@ def test_version_and_configs():
     assert names[0] == "tile16"
     # matrix-core configurations first, then the stream-K ones, then the vector-ALU micro-tile
     kinds = [n.split("_")[0] for n in names[1:]]
-    assert set(kinds) == {"mfma", "sk", "valu"} and kinds == sorted(kinds)
+    assert set(kinds) == {"mfma", "mfma16", "sk", "valu"} and kinds == sorted(kinds)
     assert sg.sgemm_config_name(-1) is None and sg.sgemm_config_name(len(names)) is None
 
 
@@ -186,9 +186,9 @@ def test_launch_shape_valu():
 
 def test_launch_shape_mfma():
     for cid, name in enumerate(sg.configs()):
-        if not name.startswith("mfma_"):
+        if not name.startswith(("mfma_", "mfma16_")):
             continue
-        m = re.fullmatch(r"mfma_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
+        m = re.fullmatch(r"mfma(?:16)?_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
         assert m, name
         bm, bn, _, wm, wn = (int(x) for x in m.groups()[:5])
         wk = int(m.group(6) or 1)
@@ -216,7 +216,7 @@ def test_launch_shape_near_int_max():
     m = big - 128
     assert sg.sgemm_launch_shape(valu, m, 1, 8) == (0, (-(-m // 128), 1, 1), (256, 1, 1))
     for cid, name in enumerate(sg.configs()):
-        if name.startswith("mfma_"):
+        if name.startswith(("mfma_", "mfma16_")):
             st, grid, block = sg.sgemm_launch_shape(cid, big, 1, big)
             bm = int(name.split("_")[1].split("x")[0])
             fits = -(-big // bm) * block[0] <= 2**32 - 1 if st == 0 else False
@@ -241,32 +241,35 @@ def test_select_config():
     sel = lambda M, N, K=64, alpha=1.0: sg.sgemm_select_config(M, N, K, alpha, BAD, K, BAD, N, BAD, N)
     assert sel(0, 5) == -1 and sel(5, 0) == -1 and sel(5, 5, K=0) == -1 and sel(5, 5, alpha=0.0) == -1
     assert names[sel(4096, 4096, 4096)] == "mfma_256x256x32_w2x4d"    # 256 tiles: one per CU
-    # rows only 4-byte aligned: the unaligned table, whose large tile has a 4-byte-copy form
+    # rows only 4-byte aligned: the unaligned table, whose large tiles have 4-byte-copy forms
     assert names[sg.sgemm_select_config(4096, 4096, 4096, 1.0, BAD + 4, 4096, BAD, 4096, BAD, 4096)] == \
-        "mfma_256x256x16_w2x4d"
-    assert names[sel(4095, 4095, 4095)] == "mfma_256x256x16_w2x4d"
+        "mfma_256x256x16_w2x4p2d"
+    assert names[sel(4095, 4095, 4095)] == "mfma_256x256x16_w2x4p2d"
     # each choice still gives at least 256 workgroups when the problem allows it
     for M, N in [(1024, 1024), (1024, 2304), (1024, 3072), (1024, 768), (1000, 1537), (256, 256)]:
         name = names[sel(M, N)]
         bm, bn, _ = (int(x) for x in name.split("_")[1].split("x"))
         tiles = -(-M // bm) * -(-N // bn)
         assert tiles >= 256 or bm <= 64, (M, N, name, tiles)
-    # the 32-row tiles take the GPT-2 layers and small squares; only the 32 x 32 one has a
-    # form for unaligned rows
-    assert names[sel(1024, 2304, 768)] == "mfma_32x64x64_w1x2k2d"
-    assert names[sel(1024, 3072, 768)] == "mfma_32x128x64_w1x4k2d"
+    # the measured winners of the benchmark shapes: 16x16-block tiles for the GPT-2 QKV and
+    # MLP-up layers, 256^3 and the 32-wide product; the 32x32-block tile for MLP-down
+    assert names[sel(1024, 2304, 768)] == "mfma16_64x64x32_w4x1k1d"
+    assert names[sel(1024, 3072, 768)] == "mfma16_64x64x32_w4x1k1d"
     assert names[sel(1024, 768, 3072)] == "mfma_32x32x64_w1x1k4d"
-    assert names[sel(256, 256, 256)] == "mfma_32x32x64_w1x1k4d"
-    assert names[sel(8192, 32, 8192)] == "mfma_32x32x64_w1x1k4d"
-    unaligned = names[sg.sgemm_select_config(1024, 2304, 768, 1.0, BAD + 4, 768, BAD, 2304, BAD, 2304)]
-    assert not unaligned.startswith("mfma_32x64") and not unaligned.startswith("mfma_32x128")
+    assert names[sel(1024, 1024, 1024)] == "mfma16_64x64x64_w4x1k2d"
+    assert names[sel(256, 256, 256)] == "mfma16_16x16x128_w1x1k4d"
+    assert names[sel(8192, 32, 8192)] == "mfma16_16x16x128_w1x1k4d"
+    assert names[sel(32, 8192, 8192)] == "mfma16_16x64x128_w1x1k4d"
+    # unaligned: the ragged product keeps the 64 x 128 tile with 4-byte copies
+    assert names[sg.sgemm_select_config(1000, 1537, 777, 1.0, BAD, 777, BAD, 1537, BAD, 1537)] == \
+        "mfma_64x128x32_w2x2k2d"
 
 
 def test_config_describe_every_id():
     """Every configuration has one description line whose fields agree with its name,
     its launch shape and the limits of the hardware; ids out of range give NULL."""
     names = sg.configs()
-    kinds = {"tile16": "tile16", "mfma": "mfma", "sk": "streamk", "valu": "valu"}
+    kinds = {"tile16": "tile16", "mfma": "mfma", "mfma16": "mfma", "sk": "streamk", "valu": "valu"}
     for cid, name in enumerate(names):
         d = sg.describe(cid)
         assert set(d) == {"name", "kind", "tile", "waves", "kgroups", "threads", "ahead", "loader", "lds_bytes",
@@ -277,13 +280,13 @@ def test_config_describe_every_id():
         wk, threads, lds = int(d["kgroups"]), int(d["threads"]), int(d["lds_bytes"])
         assert 0 < lds <= 160 * 1024 and int(d["band"]) >= 1 and int(d["unaligned_bk"]) >= 1
         if d["kind"] in ("mfma", "streamk"):
-            m = re.fullmatch(r"(?:mfma|sk)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
+            m = re.fullmatch(r"(mfma|mfma16|sk)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
             assert m, name
-            assert (bm, bn, bk, wm, wn) == tuple(int(x) for x in m.groups()[:5])
-            assert wk == int(m.group(6) or 1) and int(d["ahead"]) == int(m.group(7) or 1)
+            assert (bm, bn, bk, wm, wn) == tuple(int(x) for x in m.groups()[1:6])
+            assert wk == int(m.group(7) or 1) and int(d["ahead"]) == int(m.group(8) or 1)
             assert threads == wm * wn * wk * 64
-            assert d["loader"] == ("direct-16B" if m.group(8) else "staged-16B")
-            assert d["compute"] == "v_mfma_f32_32x32x2_f32"
+            assert d["loader"] == ("direct-16B" if m.group(9) else "staged-16B")
+            assert d["compute"] == ("v_mfma_f32_16x16x4_f32" if m.group(1) == "mfma16" else "v_mfma_f32_32x32x2_f32")
             # the stages hold A and B tiles: at least BK * (BM + BN) floats per stage
             assert lds >= 4 * bk * (bm + bn)
         if d["kind"] == "streamk":
@@ -321,10 +324,14 @@ def test_select_config_general_agrees_with_the_plain_query():
                                                   1024, 1 << 20, 12, 0)]
     area = lambda n: int(n.split("_")[1].split("x")[0]) * int(n.split("_")[1].split("x")[1])
     assert area(twelve) >= area(one), (one, twelve)
-    # odd strides take the unaligned table (no 32 x 64 tile there)
-    odd = names[sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD, 768, 3, BAD, 2304, 0, BAD, 2304,
-                                               1 << 22, 2, 0)]
-    assert not odd.startswith("mfma_32x64")
+    # odd strides take the unaligned table, as a misaligned pointer does
+    odd = sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD, 768, 3, BAD, 2304, 0, BAD, 2304,
+                                         1 << 22, 2, 0)
+    misaligned = sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD + 4, 768, 4, BAD, 2304, 0, BAD,
+                                                2304, 1 << 22, 2, 0)
+    aligned = sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD, 768, 4, BAD, 2304, 0, BAD, 2304,
+                                             1 << 22, 2, 0)
+    assert odd == misaligned != aligned, (names[odd], names[misaligned], names[aligned])
 
 
 def test_status_strings():

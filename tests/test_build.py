@@ -40,10 +40,11 @@ def kernels(tmp_path_factory):
 
 
 def parse_config(name):
-    m = re.fullmatch(r"(?:mfma|sk)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
+    m = re.fullmatch(r"(mfma|mfma16|sk)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
     assert m, name
-    bm, bn, bk, wm, wn = (int(x) for x in m.groups()[:5])
-    return bm, bn, bk, wm, wn, int(m.group(6) or 1), int(m.group(7) or 1), m.group(8) is not None
+    bm, bn, bk, wm, wn = (int(x) for x in m.groups()[1:6])
+    mb = 16 if m.group(1) == "mfma16" else 32
+    return bm, bn, bk, wm, wn, int(m.group(7) or 1), int(m.group(8) or 1), m.group(9) is not None, mb
 
 
 def expected_mfma_kernels(config_names):
@@ -56,23 +57,23 @@ def expected_mfma_kernels(config_names):
     unaligned variant with 4-byte direct copies and the configured K-tiles in flight."""
     out = set()
     for name in config_names:
-        bm, bn, bk, wm, wn, wk, pf, dma = parse_config(name)
+        bm, bn, bk, wm, wn, wk, pf, dma, mb = parse_config(name)
         nt = wm * wn * wk * 64
         for ta in (0, 1):
             for tb in (0, 1):
-                if name.startswith("mfma_"):
+                if name.startswith("mfma"):
                     for edge in (0, 1):
-                        out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge))
+                        out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge, mb))
                     if dma and (bm * bk + bk * bn) // nt <= 16:
-                        out.add((bm, bn, bk, wm, wn, wk, pf, 1, ta, tb, 0, 1))
-                    if dma:
-                        out.add((bm, bn, 16 * wk, wm, wn, wk, 1, 0, ta, tb, 0, 1))
+                        out.add((bm, bn, bk, wm, wn, wk, pf, 1, ta, tb, 0, 1, mb))
+                    if dma:     # two k groups per wave group: 16 k (32x32 blocks) or 32 k (16x16 blocks)
+                        out.add((bm, bn, (512 // mb) * wk, wm, wn, wk, 1, 0, ta, tb, 0, 1, mb))
                     else:
-                        out.add((bm, bn, bk, wm, wn, wk, pf, 0, ta, tb, 0, 1))
+                        out.add((bm, bn, bk, wm, wn, wk, pf, 0, ta, tb, 0, 1, mb))
                 else:
                     # stream-K: the register-staged tile kernel for operands it cannot take (unaligned
                     # without a 4-byte-copy form, or rows too long for direct copies)
-                    out.add((bm, bn, bk, wm, wn, wk, pf, 0, ta, tb, 0, 1))
+                    out.add((bm, bn, bk, wm, wn, wk, pf, 0, ta, tb, 0, 1, mb))
     return out
 
 
@@ -83,14 +84,14 @@ def expected_sk_kernels(config_names):
     kernel of the tile on unaligned operands)."""
     out = set()
     for name in config_names:
-        bm, bn, bk, wm, wn, wk, pf, dma = parse_config(name)
+        bm, bn, bk, wm, wn, wk, pf, dma, mb = parse_config(name)
         nt = wm * wn * wk * 64
         for ta in (0, 1):
             for tb in (0, 1):
                 for edge in (0, 1):
-                    out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge))
+                    out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge, mb))
                 if dma and (bm * bk + bk * bn) // nt <= 16:
-                    out.add((bm, bn, bk, wm, wn, wk, pf, 1, ta, tb, 0, 1))
+                    out.add((bm, bn, bk, wm, wn, wk, pf, 1, ta, tb, 0, 1, mb))
     return out
 
 
@@ -98,7 +99,7 @@ def test_all_kernels_present(kernels):
     names = " ".join(kernels)
     assert "sgemm_tile16" in names and "sgemm_scale" in names and "sgemm_valu" in names
     import tiled_fp32_gemm_02_amd as sg
-    names = [n for n in sg.configs() if n.startswith(("mfma_", "sk_"))]
+    names = [n for n in sg.configs() if n.startswith(("mfma_", "mfma16_", "sk_"))]
     for kind, expected in (("sgemm_mfma", expected_mfma_kernels(names)),
                            ("sgemm_mfma_sk", expected_sk_kernels([c for c in names if c.startswith("sk_")]))):
         found = set()
@@ -129,9 +130,18 @@ def test_registers_fit_the_launch(kernels):
 
 
 def test_matrix_kernels_use_fp32_mfma(kernels):
+    """Each matrix kernel issues the fp32 instruction of its block size (the last template
+    argument): v_mfma_f32_32x32x2_f32 for 32, v_mfma_f32_16x16x4_f32 for 16, and not the other."""
+    sizes = set()
     for name, (k, body) in kernels.items():
-        if "sgemm_mfma<" in name or "sgemm_mfma_sk<" in name:
-            assert "v_mfma_f32_32x32x2_f32" in body, name
+        m = re.search(r"sgemm_mfma(?:_sk)?<[^>]*, (\d+)>", name)
+        if m:
+            mb = int(m.group(1))
+            sizes.add(mb)
+            want, other = ("v_mfma_f32_16x16x4_f32", "v_mfma_f32_32x32x2_f32") if mb == 16 else \
+                ("v_mfma_f32_32x32x2_f32", "v_mfma_f32_16x16x4_f32")
+            assert want in body and other not in body, name
+    assert sizes == {16, 32}
 
 
 def test_vector_kernel_uses_plain_fma(kernels):

@@ -172,7 +172,7 @@ def test_long_rows_of_A(lda):
     M, N, K = 260, 36, 40
     A, B, C = draw(rng, (M, K), "normal"), draw(rng, (K, N), "normal"), draw(rng, (M, N), "normal")
     names = sg.configs()
-    for cid in [-1] + [i for i, n in enumerate(names) if n.startswith("mfma_") and n.endswith("d")]:
+    for cid in [-1] + [i for i, n in enumerate(names) if n.startswith(("mfma_", "mfma16_")) and n.endswith("d")]:
         say(f"long rows lda={lda} config {cid}")
         st, out, checks = run_gemm(M, N, K, 1.25, A, B, -0.5, C, lda=lda, config=cid)
         assert st == 0

@@ -90,10 +90,10 @@ static void check_read(const char *what, const int *addr, int width)
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, bool TA, bool TB, int VW>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int MB, bool TA, bool TB, int VW>
 static void check_config(const char *name)
 {
-    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, 1, true, TA, TB, VW == 4, false>;
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, 1, true, TA, TB, VW == 4, false, MB>;
     using A = typename T::AIO;
     using B = typename T::BIO;
     char what[160];
@@ -102,16 +102,17 @@ static void check_config(const char *name)
     std::snprintf(what, sizeof what, "%s %s%s VW=%d B", name, TA ? "t" : "n", TB ? "t" : "n", VW);
     check_copies<B, TB ? BN : BK, TB ? BK : BN, T::NT, TB, VW>(what);
 
-    // The loop's fragment reads, per wave and group of 8 k (as in MfmaTile::read_frag).
-    constexpr int TM = T::TM, TN = T::TN, KS = T::KSLICE;
+    // The loop's fragment reads, per wave and group of KGRP k (as in MfmaTile::read_frag):
+    // lane l is row/column l % MB of its block and supplies k = 4 * (l / MB) + step.
+    constexpr int TM = T::TM, TN = T::TN, KS = T::KSLICE, KG = T::KGRP;
     for (int wave = 0; wave < T::NT / 64; ++wave) {
         const int wk = wave / (WGM * WGN), wm = (wave % (WGM * WGN)) / WGN, wn = wave % WGN;
-        for (int g = 0; g < KS / 8; ++g) {
+        for (int g = 0; g < KS / KG; ++g) {
             int addr[64];
             if (!TA) {
                 for (int a = 0; a < TM; ++a) {
                     for (int l = 0; l < 64; ++l)
-                        addr[l] = A::elem(wm * T::WTM + (l & 31) + a * 32, wk * KS + 8 * g + 4 * (l >> 5));
+                        addr[l] = A::elem(wm * T::WTM + (l % MB) + a * MB, wk * KS + KG * g + 4 * (l / MB));
                     std::snprintf(what, sizeof what, "%s %s%s VW=%d A read (wave %d, group %d, block %d)", name,
                                   TA ? "t" : "n", TB ? "t" : "n", VW, wave, g, a);
                     check_read(what, addr, 4);
@@ -119,7 +120,7 @@ static void check_config(const char *name)
             } else {
                 for (int s = 0; s < 4; ++s) {
                     for (int l = 0; l < 64; ++l)
-                        addr[l] = A::elem(wk * KS + 8 * g + 4 * (l >> 5) + s, wm * T::WTM + (l & 31) * TM);
+                        addr[l] = A::elem(wk * KS + KG * g + 4 * (l / MB) + s, wm * T::WTM + (l % MB) * TM);
                     std::snprintf(what, sizeof what, "%s %s%s VW=%d A read (wave %d, group %d, k %d)", name,
                                   TA ? "t" : "n", TB ? "t" : "n", VW, wave, g, s);
                     check_read(what, addr, TM);
@@ -128,7 +129,7 @@ static void check_config(const char *name)
             if (TB) {
                 for (int b = 0; b < TN; ++b) {
                     for (int l = 0; l < 64; ++l)
-                        addr[l] = B::elem(wn * T::WTN + (l & 31) + b * 32, wk * KS + 8 * g + 4 * (l >> 5));
+                        addr[l] = B::elem(wn * T::WTN + (l % MB) + b * MB, wk * KS + KG * g + 4 * (l / MB));
                     std::snprintf(what, sizeof what, "%s %s%s VW=%d B read (wave %d, group %d, block %d)", name,
                                   TA ? "t" : "n", TB ? "t" : "n", VW, wave, g, b);
                     check_read(what, addr, 4);
@@ -136,7 +137,7 @@ static void check_config(const char *name)
             } else {
                 for (int s = 0; s < 4; ++s) {
                     for (int l = 0; l < 64; ++l)
-                        addr[l] = B::elem(wk * KS + 8 * g + 4 * (l >> 5) + s, wn * T::WTN + (l & 31) * TN);
+                        addr[l] = B::elem(wk * KS + KG * g + 4 * (l / MB) + s, wn * T::WTN + (l % MB) * TN);
                     std::snprintf(what, sizeof what, "%s %s%s VW=%d B read (wave %d, group %d, k %d)", name,
                                   TA ? "t" : "n", TB ? "t" : "n", VW, wave, g, s);
                     check_read(what, addr, TN);
@@ -146,25 +147,25 @@ static void check_config(const char *name)
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int MB>
 static int check_all_forms(const char *name)
 {
-    check_config<BM, BN, BK, WGM, WGN, WGK, false, false, 4>(name);
-    check_config<BM, BN, BK, WGM, WGN, WGK, false, true, 4>(name);
-    check_config<BM, BN, BK, WGM, WGN, WGK, true, false, 4>(name);
-    check_config<BM, BN, BK, WGM, WGN, WGK, true, true, 4>(name);
-    check_config<BM, BN, BK, WGM, WGN, WGK, false, false, 1>(name);
-    check_config<BM, BN, BK, WGM, WGN, WGK, false, true, 1>(name);
-    check_config<BM, BN, BK, WGM, WGN, WGK, true, false, 1>(name);
-    check_config<BM, BN, BK, WGM, WGN, WGK, true, true, 1>(name);
+    check_config<BM, BN, BK, WGM, WGN, WGK, MB, false, false, 4>(name);
+    check_config<BM, BN, BK, WGM, WGN, WGK, MB, false, true, 4>(name);
+    check_config<BM, BN, BK, WGM, WGN, WGK, MB, true, false, 4>(name);
+    check_config<BM, BN, BK, WGM, WGN, WGK, MB, true, true, 4>(name);
+    check_config<BM, BN, BK, WGM, WGN, WGK, MB, false, false, 1>(name);
+    check_config<BM, BN, BK, WGM, WGN, WGK, MB, false, true, 1>(name);
+    check_config<BM, BN, BK, WGM, WGN, WGK, MB, true, false, 1>(name);
+    check_config<BM, BN, BK, WGM, WGN, WGK, MB, true, true, 1>(name);
     return 1;
 }
 
-template <bool DMA, int BM, int BN, int BK, int WGM, int WGN, int WGK>
+template <bool DMA, int BM, int BN, int BK, int WGM, int WGN, int WGK, int MB>
 static int check_if_direct(const char *name)
 {
     if constexpr (DMA)
-        return check_all_forms<BM, BN, BK, WGM, WGN, WGK>(name);
+        return check_all_forms<BM, BN, BK, WGM, WGN, WGK, MB>(name);
     else
         return 0;
 }
@@ -172,8 +173,8 @@ static int check_if_direct(const char *name)
 int main()
 {
     int configs = 0;
-#define SGEMM_CHECK(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M) \
-    configs += check_if_direct<(DMA != 0), BM, BN, BK, WGM, WGN, WGK>(name);
+#define SGEMM_CHECK(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB) \
+    configs += check_if_direct<(DMA != 0), BM, BN, BK, WGM, WGN, WGK, MB>(name);
     SGEMM_MFMA_CONFIGS(SGEMM_CHECK)
     SGEMM_SK_CONFIGS(SGEMM_CHECK)
 #undef SGEMM_CHECK

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 #include <cstdio>
@@ -53,17 +54,18 @@ struct Config {
     int lds_bytes;       // static LDS per workgroup (aligned form)
     int unaligned_bk;    // K-tile of the form run for 4-byte aligned rows
     bool unaligned_dma;  // that form copies 4-byte words HBM -> LDS directly (else register-staged)
+    int mb;              // block of the matrix instruction (32 or 16; 0 for the non-matrix kinds)
 };
 
 // LDS bytes and the unaligned form of an MFMA configuration, from the kernel's own
 // constants (the same selection launch_mfma_op makes).
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int MB>
 struct MfmaFacts {
     static constexpr int NT = WGM * WGN * WGK * 64;
     static constexpr int LDS =
-        4 * sgemm_impl::MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, false, false, true, false>::SMEM;
+        4 * sgemm_impl::MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, false, false, true, false, MB>::SMEM;
     static constexpr bool DMA4 = DMA && (BM * BK + BK * BN) / NT <= 16;
-    static constexpr int UBK = DMA4 ? BK : (DMA ? 16 * WGK : BK);
+    static constexpr int UBK = DMA4 ? BK : (DMA ? 8 * (64 / MB) * WGK : BK);
 };
 
 // Stream-K workspace: per-tile counters at a fixed offset (so a call with more tiles
@@ -102,37 +104,37 @@ int device_cus()
 // could overflow; such calls take the register-staged element-wise variant instead.
 constexpr int kDmaMaxLd = 1 << 20;
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, int MB>
 hipError_t launch_mfma(const GemmArgs &p, int batch, bool ta, bool tb, bool vec, bool edge, bool dma_ok,
                        hipStream_t s)
 {
     if (!ta && !tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, false>(p, batch, vec,
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB, false, false>(p, batch, vec,
                                                                                                      edge, dma_ok, s);
     if (!ta && tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, true>(p, batch, vec,
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB, false, true>(p, batch, vec,
                                                                                                     edge, dma_ok, s);
     if (ta && !tb)
-        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, false>(p, batch, vec,
+        return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB, true, false>(p, batch, vec,
                                                                                                     edge, dma_ok, s);
-    return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, true>(p, batch, vec, edge,
+    return sgemm_impl::launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB, true, true>(p, batch, vec, edge,
                                                                                                dma_ok, s);
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, int MB>
 hipError_t launch_sk(const GemmArgs &p, const StreamK &sk, int grid, bool ta, bool tb, bool vec, bool edge,
                      bool dma_ok, hipStream_t s)
 {
     if (!ta && !tb)
-        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, false>(
+        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB, false, false>(
             p, sk, grid, vec, edge, dma_ok, s);
     if (!ta && tb)
-        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, false, true>(
+        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB, false, true>(
             p, sk, grid, vec, edge, dma_ok, s);
     if (ta && !tb)
-        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, false>(
+        return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB, true, false>(
             p, sk, grid, vec, edge, dma_ok, s);
-    return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, true, true>(
+    return sgemm_impl::launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB, true, true>(
         p, sk, grid, vec, edge, dma_ok, s);
 }
 
@@ -173,24 +175,25 @@ hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, b
 // tile (BM x BN x BK), the wave grid (WGM x WGN), after "k" the wave groups along k, after
 // "p" the K-tiles prefetched ahead (1 when absent), and a final "d" marks direct HBM -> LDS
 // copies.
-#define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M)                               \
+#define SGEMM_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB)                           \
     {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, GROUP_M,                                   \
-     launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>, nullptr, WGM, WGN, WGK, PF,                    \
-     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA>::LDS, MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA>::UBK,  \
-     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA>::DMA4},
-#define SGEMM_SK_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M)                            \
+     launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB>, nullptr, WGM, WGN, WGK, PF,                \
+     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::LDS,                                                   \
+     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::UBK, MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::DMA4, \
+     MB},
+#define SGEMM_SK_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB)                        \
     {name, KIND_SK, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, GROUP_M, nullptr,                            \
-     launch_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M>, WGM, WGN, WGK, PF,                              \
-     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA>::LDS, BK, false},
+     launch_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB>, WGM, WGN, WGK, PF,                          \
+     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::LDS, BK, false, MB},
 // LDS of the two kernels outside the MFMA template: tile16 stages two 16 x 17 tiles; the
 // vector-ALU kernel two k-major 8 x 132 tiles per stage, two stages.
 const Config kConfigs[] = {
     {"tile16", KIND_TILE16, 16, 16, 16, 256, false, 1, launch_tile16, nullptr, 1, 1, 1, 0, 2 * 16 * 17 * 4, 16,
-     false},
+     false, 0},
     SGEMM_MFMA_CONFIGS(SGEMM_TABLE_ROW)
     SGEMM_SK_CONFIGS(SGEMM_SK_TABLE_ROW)
     {"valu_128x128x8_t8x8", KIND_VALU, 128, 128, 8, 256, false, 8, launch_valu, nullptr, 1, 1, 1, 1,
-     2 * 2 * 8 * 132 * 4, 8, false},
+     2 * 2 * 8 * 132 * 4, 8, false, 0},
 };
 #undef SGEMM_TABLE_ROW
 #undef SGEMM_SK_TABLE_ROW
@@ -222,76 +225,91 @@ bool sk_work_fits(const Config &c, int M, int N, int K, int cus)
     return tiles <= (uint64_t)kSkMaxTiles && work * (uint64_t)(cus + 1) < (1ull << 31);
 }
 
-// Auto-selection by a small cost model of the kernel time.
+// Auto-selection by a small cost model of the kernel time, measured on MI355X.
 //
-// Data-parallel candidates: the tiles spread over the CUs take L = ceil(tiles / CUs)
-// rounds on the busiest CU, so the time is a fixed cost (launch, first loads, last
-// epilogue) plus L tiles of work (one unit is a 64x64 tile, 2 * 64 * 64 * K flop) at the
-// CU's throughput with that many tiles resident. Throughputs (fp32 TFLOP/s per CU) were
-// measured on MI355X with the whole chip busy: rate_one when a CU holds a single
-// workgroup, rate_many when it holds several.
-//
-// Stream-K candidates (only with a large enough workspace): every CU gets the same
-// share, tiles * units / CUs, at the one-workgroup rate, plus a fixed cost for the
-// partial tiles (each partial is written once and read once by the tile's last
-// contributor, and that contributor's epilogue runs after the others').
+// A candidate's time is the largest of three bounds:
+//  - compute: the tiles spread over the CUs take L = ceil(tiles / CUs) rounds on the
+//    busiest CU, so the time is a fixed cost (launch, first loads, last epilogue), a cost
+//    per round (a tile's first loads and epilogue, which short K loops do not hide) and L
+//    tiles of work (one unit is a 64 x 64 tile, 2 * 64 * 64 * K flop) at the CU's measured
+//    speed, given as microseconds per MFLOP with one workgroup resident (L = 1) or
+//    several (L >= 2). Stream-K candidates (only with a large enough workspace) give
+//    every CU the same share, tiles * units / CUs, plus a fixed cost for the partial
+//    tiles.
+//  - HBM: each operand's compulsory bytes (A and B read, C written) at a bandwidth that
+//    depends on the contiguous bytes per row a tile reads (BK floats of A, BN of B and C):
+//    5.7 TB/s for 512-byte rows, falling as (bytes / 512)^0.19 for shorter ones (measured
+//    from 3.8 TB/s at 64 bytes to 5.7 TB/s on products that stream one operand).
+//  - L2: the tiles' operand panels, 4 M N K (1 / BM + 1 / BN) bytes, at the highest rate
+//    any swept configuration reached on them (20 TB/s for 16-byte aligned rows, 14 TB/s
+//    for 4-byte aligned ones). Small tiles re-read panels many times, and on long-K
+//    products such as 1024 x 768 x 3072 that, not the matrix cores, sets their time.
 struct Candidate {
     const char *name;   // configuration name in the table
-    double units;       // tile area / (64 * 64)
-    double rate_one;    // per-CU rate with one resident workgroup
-    double rate_many;   // per-CU rate with two or more
     double fixed_us;    // time that does not scale with the work
-    double round_us;    // time per round of tiles on a CU beyond its work (a tile's first
-                        // loads and epilogue), where short K-loops do not hide it
+    double round_us;    // time per round of tiles on a CU beyond its work
+    double us_one;      // microseconds per MFLOP of a CU's work with one workgroup resident
+    double us_many;     // the same with two or more
 };
 
-// Least-squares fits (relative error) of time = fixed + work / rate, one per operand
-// alignment. Aligned: a sweep over 256^3 ... 6144^3, 512 x 4096 x 4096 and the GPT-2-small
-// linear layers; on every shape of it the model picks the fastest candidate or one within
-// 1%. The 32-row tiles were fitted later, with the other rows left as they were, on 40
-// shapes: the 24 of a second sweep (256^3 ... 6144^3, 3000^3, rectangles, 1000 x 1000 x 4000
-// and the GPT-2 layers) and 16 skinny or long-K ones (128 x 4096 x 4096, 8192 x 32 x 8192,
-// 16384 x 16 x 16384, 2048 x 256 x 16384, 512 x 512 x 8192 and the like). The 32 x 64 and
-// 32 x 32 rows carry a cost per round of tiles (a tile's first loads and epilogue, which
-// short K-loops do not hide); without it the QKV layer (9 rounds of 12 K-tiles) went to the
-// 32 x 32 tile, 5% slower. The 64x64x64 row was refit the same way on the 40 shapes; its
-// first fit assumed the rate of short K-loops, which long ones (latency-bound with one
-// K-tile in flight) do not reach. With a workspace the picks then average 1.004 of the
-// fastest candidate on the 40 shapes and the worst is 1.043 (32 x 8192 x 8192); every
-// benchmark shape gets its fastest but 1024^3, where the 32 x 64 pick is within 0.5%. Unaligned (rows only 4-byte aligned, 4-byte direct copies):
-// the same kinds of shapes with odd sizes (255^3 ... 6143^3, 511 x 4095 x 4095,
-// 1000 x 1537 x 777 and the GPT-2 layers one short in each dimension); the model picks the
-// fastest on every one. The 256 x 256 x 32 tile has no 4-byte-copy form (its copy offsets
-// would not fit the registers), so the unaligned table has the 256 x 256 x 16 tile instead;
-// the 32 x 64 and 32 x 128 tiles have none either, and their register-staged form is slower
-// than the table's, so they are aligned-only. The 32 x 32 tile has a 4-byte-copy form; its
-// unaligned row, fitted on 24 odd-sized shapes (skinny and long-K ones included), makes the
-// model pick the fastest candidate on all of them.
+// Non-negative least-squares fits (relative error) of the compute bound, per operand
+// alignment, over the shapes of one sweep where neither memory bound was within 75% of the
+// measured time. Aligned: 36 shapes (256^3 ... 6144^3, 3000^3, rectangles, the GPT-2-small
+// linear layers, long-K and skinny products down to 16 rows or columns). With the
+// candidates below the model picks, on average, a configuration within 1.6% of the fastest
+// of all those swept; it picks the fastest on 256^3, 1024^3, 4096^3 and the three GPT-2
+// layers; the worst misses are 13% (128 x 4096 x 4096), 11% (4096 x 64 x 4096 and
+// 2048 x 256 x 16384). Candidates were chosen by dropping, one at a time, those whose removal
+// improved the picks. Unaligned (rows only 4-byte aligned): 24 odd-sized shapes (255^3 ...
+// 6143^3, 2999^3, 511 x 4095 x 4095, 1000 x 1537 x 777, the GPT-2 layers one short in each
+// dimension, long-K and skinny ones); picks average within 0.6% of the fastest, the worst
+// 3.7% (1535^3), and the ragged 1000 x 1537 x 777 and the GPT-2 layers get the fastest.
 const Candidate kCandidates[] = {
-    {"mfma_256x256x32_w2x4d", 16, 0.591, 0.580, 7.5, 0},      // one workgroup per CU
-    {"mfma_128x128x32_w2x2k2d", 4, 0.555, 0.573, 5.4, 0},     // up to two per CU
-    {"mfma_64x128x32_w2x2k2d", 2, 0.534, 0.556, 4.3, 0},      // up to three per CU
-    {"mfma_64x64x64_w2x2k4d", 1, 0.491, 0.518, 0.6, 4.10},    // one per CU, 16 waves
-    {"mfma_64x64x32_w2x2k2d", 1, 0.457, 0.507, 6.1, 0},       // up to four per CU
-    {"mfma_32x64x64_w1x2k2d", 0.5, 0.405, 0.507, 2.9, 1.12},  // many small tiles (GPT-2 QKV)
-    {"mfma_32x128x64_w1x4k2d", 1, 0.449, 0.496, 4.4, 0},      // (GPT-2 MLP-up)
-    {"mfma_32x32x64_w1x1k4d", 0.25, 0.215, 0.442, 2.4, 0.67}, // (GPT-2 MLP-down, up to 768^3, skinny)
+    {"mfma_256x256x32_w2x4d", 6.61, 0.00, 1.7203, 1.7386},     // one workgroup per CU
+    {"mfma_128x128x32_w2x2k2d", 0.00, 5.39, 1.8261, 1.7742},
+    {"mfma16_64x128x32_w4x2k1d", 0.70, 1.25, 1.9955, 1.7866},
+    {"mfma16_64x64x64_w4x1k2d", 1.50, 1.09, 2.0556, 1.8173},   // 1024^3, 3072^3
+    {"mfma16_64x64x32_w4x1k1d", 0.30, 0.48, 2.7419, 1.8653},   // GPT-2 QKV and MLP-up
+    {"mfma_32x32x64_w1x1k4d", 1.95, 0.84, 4.7050, 2.2238},     // GPT-2 MLP-down
+    {"mfma16_16x16x128_w1x1k4d", 2.24, 0.00, 19.4973, 4.3872}, // 256^3, 16- and 32-wide products
+    {"mfma16_16x64x128_w1x1k4d", 2.79, 0.22, 3.5509, 2.6575},  // 16- and 32-row products
+    {"mfma16_64x64x64_w2x2k2d", 1.46, 1.14, 2.0651, 1.8220},
+    {"mfma_64x128x32_w2x2k2d", 0.41, 2.39, 2.0202, 1.7895},
+    {"mfma_64x64x64_w2x2k4d", 0.33, 3.93, 2.1330, 1.9589},
+    {"mfma16_128x64x32_w8x1k1d", 0.57, 1.49, 2.0763, 1.8275},
+    {"mfma_64x64x32_w2x2k2d", 0.00, 1.99, 2.7448, 1.9717},
 };
 const Candidate kUnalignedCandidates[] = {
-    {"mfma_256x256x16_w2x4d", 16, 0.519, 0.498, 8.4, 0},
-    {"mfma_128x128x32_w2x2k2d", 4, 0.462, 0.467, 6.7, 0},
-    {"mfma_64x128x32_w2x2k2d", 2, 0.450, 0.472, 5.9, 0},
-    {"mfma_64x64x64_w2x2k4d", 1, 0.421, 0.437, 8.2, 0},
-    {"mfma_64x64x32_w2x2k2d", 1, 0.376, 0.441, 7.4, 0},
-    {"mfma_32x32x64_w1x1k4d", 0.25, 0.360, 0.360, 6.8, 1.04},
+    {"mfma_256x256x32_w2x4d", 5.94, 0.00, 2.0225, 2.0671},
+    {"mfma_256x256x16_w2x4p2d", 7.88, 0.00, 1.9201, 2.0263},
+    {"mfma_128x128x32_w2x2k2d", 6.57, 0.00, 2.1279, 2.1380},
+    {"mfma_64x128x32_w2x2k2d", 2.32, 2.86, 2.2324, 2.0580},     // 1000 x 1537 x 777
+    {"mfma_64x64x32_w2x2k2d", 2.75, 2.73, 2.9376, 2.1774},
+    {"mfma_32x128x64_w1x4k2d", 3.65, 2.15, 3.4416, 2.5125},
+    {"mfma_32x64x64_w1x2k2d", 5.65, 0.00, 5.7274, 2.7701},
+    {"mfma16_128x64x32_w8x1k1d", 1.26, 3.67, 2.3279, 2.0705},
+    {"mfma16_64x128x32_w4x2k1d", 1.32, 3.72, 2.3340, 2.0783},
+    {"mfma16_64x64x64_w4x1k2d", 1.73, 2.72, 2.4920, 2.1934},
+    {"mfma16_64x64x64_w2x2k2d", 1.86, 2.40, 2.4844, 2.1924},
+    {"mfma16_64x64x32_w4x1k1d", 0.83, 2.57, 3.2597, 2.2475},
+    {"mfma16_64x16x64_w4x1k1d", 0.00, 0.00, 11.1652, 4.3130},
+    {"mfma16_32x128x64_w2x2k2d", 0.00, 3.39, 3.2870, 3.1858},
+    {"mfma16_32x64x128_w2x1k4d", 0.59, 2.83, 3.5119, 3.4162},
+    {"mfma16_32x64x64_w2x1k2d", 3.10, 0.36, 4.5025, 2.8383},
+    {"mfma16_16x64x128_w1x1k4d", 1.16, 2.59, 6.2842, 5.7675},
+    {"mfma16_16x16x128_w1x1k4d", 2.56, 0.36, 15.2149, 5.2090},
 };
 const Candidate kSkCandidates[] = {
-    {"sk_128x128x32_w2x2k2p2", 4, 0.534, 0.534, 17.1, 0},
-    {"sk_64x128x32_w2x2k2p2", 2, 0.502, 0.502, 12.2, 0},
+    {"sk_128x128x32_w2x2k2p2", 19.09, 0.00, 1.8743, 1.8743},
+    {"sk_64x128x32_w2x2k2p2", 12.20, 0.00, 2.0418, 2.0418},
 };
 constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
 constexpr int kNumUnalignedCandidates = sizeof(kUnalignedCandidates) / sizeof(kUnalignedCandidates[0]);
 constexpr int kNumSkCandidates = sizeof(kSkCandidates) / sizeof(kSkCandidates[0]);
+constexpr double kHbmBytesPerUs = 5.7e6;          // 5.7 TB/s for rows of 512 contiguous bytes
+constexpr double kHbmRowExponent = 0.19;
+constexpr double kL2BytesPerUs = 20.0e6;          // tile-fill bytes, 16-byte aligned rows
+constexpr double kL2BytesPerUsUnaligned = 14.1e6; // and 4-byte aligned rows
 
 int find_config(const char *name)
 {
@@ -315,8 +333,22 @@ struct CandidateIds {
     }
 };
 
+// The two memory bounds of configuration c on `batch` products of M x N x K, in us.
+double memory_us(const Config &c, int M, int N, int K, int batch, bool vec)
+{
+    auto bw = [](double row_bytes) {
+        const double r = row_bytes < 512.0 ? row_bytes / 512.0 : 1.0;
+        return kHbmBytesPerUs * std::pow(r, kHbmRowExponent);
+    };
+    const double m = M, n = N, k = K, b = batch;
+    const double hbm = b * (4.0 * m * k / bw(4.0 * c.bk) + 4.0 * k * n / bw(4.0 * c.bn) + 4.0 * m * n / bw(4.0 * c.bn));
+    const double l2 = b * 4.0 * m * n * k * (1.0 / c.bm + 1.0 / c.bn) / (vec ? kL2BytesPerUs : kL2BytesPerUsUnaligned);
+    return hbm > l2 ? hbm : l2;
+}
+
 // The configuration with the least modelled time. Stream-K candidates are considered
-// only when `ws_bytes` holds their workspace for `cus` compute units (cus > 0).
+// only for one product (batch 1) with aligned operands, when `ws_bytes` holds their
+// workspace for `cus` compute units (cus > 0).
 int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0, int batch = 1)
 {
     static const CandidateIds ids;
@@ -331,16 +363,20 @@ int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0, int 
         const Candidate &cand = table[i];
         if (table_ids[i] < 0)
             continue;
-        const uint64_t tiles = tile_count(kConfigs[table_ids[i]], M, N) * (uint64_t)batch;
+        const Config &c = kConfigs[table_ids[i]];
+        const uint64_t tiles = tile_count(c, M, N) * (uint64_t)batch;
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
-        const double us = cand.fixed_us + (double)rounds * cand.round_us +
-                          (double)rounds * cand.units * unit_mflop / (rounds >= 2 ? cand.rate_many : cand.rate_one);
+        const double units = (double)c.bm * c.bn / 4096.0;
+        double us = cand.fixed_us + (double)rounds * cand.round_us +
+                    (double)rounds * units * unit_mflop * (rounds >= 2 ? cand.us_many : cand.us_one);
+        const double mem = memory_us(c, M, N, K, batch, vec);
+        us = us > mem ? us : mem;
         if (best < 0 || us < best_us) {
             best = table_ids[i];
             best_us = us;
         }
     }
-    for (int i = 0; vec && cus > 0 && batch == 1 && i < kNumSkCandidates; ++i) {   // stream-K: aligned, one matrix
+    for (int i = 0; vec && cus > 0 && batch == 1 && i < kNumSkCandidates; ++i) {
         const Candidate &cand = kSkCandidates[i];
         if (ids.sk[i] < 0)
             continue;
@@ -348,7 +384,10 @@ int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0, int 
         const uint64_t tiles = tile_count(c, M, N);
         if (!sk_work_fits(c, M, N, K, cus) || ws_bytes < sk_workspace_bytes(c, cus))
             continue;
-        const double us = (double)tiles * cand.units / (double)kCUs * unit_mflop / cand.rate_one + cand.fixed_us;
+        const double units = (double)c.bm * c.bn / 4096.0;
+        double us = cand.fixed_us + (double)tiles * units / (double)kCUs * unit_mflop * cand.us_one;
+        const double mem = memory_us(c, M, N, K, 1, vec);
+        us = us > mem ? us : mem;
         if (us < best_us) {
             best = ids.sk[i];
             best_us = us;
@@ -712,7 +751,7 @@ const char *sgemm_config_describe(int config)
                          "lds_bytes=%d band=%d unaligned=%s unaligned_bk=%d compute=%s",
                          c.name, kinds[c.kind], c.bm, c.bn, c.bk, c.wgm, c.wgn, c.wgk, c.threads, c.pf, loader,
                          c.lds_bytes, c.group_m, unaligned, c.unaligned_bk,
-                         mfma ? "v_mfma_f32_32x32x2_f32" : "v_fma_f32");
+                         !mfma ? "v_fma_f32" : c.mb == 16 ? "v_mfma_f32_16x16x4_f32" : "v_mfma_f32_32x32x2_f32");
             }
         }
     };

@@ -9,16 +9,16 @@
 
 namespace sgemm_impl {
 
-#define SGEMM_INSTANTIATE(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M)                            \
+#define SGEMM_INSTANTIATE(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB)                        \
     template hipError_t                                                                                 \
-    launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, (SGEMM_TA != 0), (SGEMM_TB != 0)>(         \
+    launch_mfma_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB, (SGEMM_TA != 0), (SGEMM_TB != 0)>(     \
         const GemmArgs &, int, bool, bool, bool, hipStream_t);
 SGEMM_MFMA_CONFIGS(SGEMM_INSTANTIATE)
 #undef SGEMM_INSTANTIATE
 
-#define SGEMM_INSTANTIATE_SK(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M)                         \
+#define SGEMM_INSTANTIATE_SK(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB)                     \
     template hipError_t                                                                                 \
-    launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, (SGEMM_TA != 0), (SGEMM_TB != 0)>(      \
+    launch_mfma_sk_op<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB, (SGEMM_TA != 0), (SGEMM_TB != 0)>(  \
         const GemmArgs &, const StreamK &, int, bool, bool, bool, hipStream_t);
 SGEMM_SK_CONFIGS(SGEMM_INSTANTIATE_SK)
 #undef SGEMM_INSTANTIATE_SK

@@ -8,7 +8,8 @@
 // baseline, vector-ALU micro-tile, quick-return scaling).
 // sgemm_mfma is the hot path. A workgroup owns a BM x BN tile of C; each wave owns
 //    a (BM/WGM) x (BN/WGN) sub-tile made of 32x32 blocks computed with the CDNA fp32
-//    matrix instruction (32x32 outputs, 2 k-steps per issue). A and B tiles reach a
+//    matrix instruction (32x32 outputs, 2 k-steps per issue), or of 16x16 blocks (4
+//    k-steps per issue) for small, skinny and ragged products. A and B tiles reach a
 //    ring of LDS stages with one barrier per K-tile: copied from HBM straight into LDS
 //    (TileDMA; 16-byte copies for 16-byte aligned rows, 4-byte copies otherwise), or
 //    staged through registers (TileIO). The next K-tile's loads (two with register
@@ -239,7 +240,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 // chunk for VW = 4 (the extents are then multiples of 4), per float for VW = 1.
 // Needs row strides below 2^20 floats (every byte offset from the tile origin stays
 // below 2^31 for TR <= 256).
-template <int TR, int TC, int NT, bool KCONTIG, int VW>
+//
+// Q16 (only for m- or n-contiguous tiles): the tile is read by 16x16-block matrix code one
+// float per lane, so four groups of 16 lanes read rows k, k+4, k+8 and k+12 at the same 16
+// columns in one pass. Row r's chunks are then XORed with ((r >> 2) & 3) << 2, which puts
+// those four rows' 16 columns in four distinct 16-bank groups. With 32-wide rows (row
+// permutation, the two halves of the banks) the chunks are XORed with ((r >> 3) & 1) << 2
+// instead: rows 4 apart alternate halves through the permutation, rows 8 apart alternate
+// 16-column groups through the XOR, so the four rows again meet four distinct groups.
+template <int TR, int TC, int NT, bool KCONTIG, int VW, bool Q16 = false>
 struct TileDMA {
     static constexpr int CPR = TC / 4;
     static constexpr int SLOTS = TR * TC / VW;
@@ -247,19 +256,31 @@ struct TileDMA {
     static constexpr int SIZE = TR * TC;
     static_assert(VW == 4 || VW == 1, "16- or 4-byte copies");
     static_assert(NT % 64 == 0 && SLOTS % NT == 0, "whole copy instructions per wave");
-    static_assert(KCONTIG ? (CPR == 4 || CPR == 8 || CPR % 16 == 0) : (CPR == 8 || CPR % 16 == 0),
+    static_assert(KCONTIG ? (CPR == 4 || CPR == 8 || CPR % 16 == 0) : (CPR == 4 || CPR == 8 || CPR % 16 == 0),
                   "slot swizzle needs these row lengths");
 
     static constexpr bool ROWPERM = !KCONTIG && CPR == 8;
+    // Rows of 16 floats (a 16-wide tile, read by 16x16-block code) fill a quarter of the
+    // banks: rows are permuted within groups of four, logical row r at r ^ ((r >> 2) & 3),
+    // so the four rows k, k+4, k+8, k+12 that one pass reads sit in four distinct quarters.
+    static constexpr bool ROWPERM4 = !KCONTIG && CPR == 4;
     static_assert(!ROWPERM || TR % 2 == 0, "row pairs");
+    static_assert(!ROWPERM4 || TR % 4 == 0, "row quads");
     __host__ __device__ __forceinline__ static int swz(int r)
     {
         if (KCONTIG)
             return CPR >= 16 ? (r & 15) : ((r / (16 / CPR)) & (CPR - 1));
-        return ROWPERM ? 0 : ((r >> 2) & 1) << 3;
+        if (ROWPERM4)
+            return 0;
+        if (ROWPERM)
+            return Q16 ? ((r >> 3) & 1) << 2 : 0;
+        return Q16 ? ((r >> 2) & 3) << 2 : ((r >> 2) & 1) << 3;
     }
     // Physical row of logical row r (an involution: it also maps physical to logical).
-    __host__ __device__ __forceinline__ static int prow(int r) { return ROWPERM ? (r ^ ((r >> 2) & 1)) : r; }
+    __host__ __device__ __forceinline__ static int prow(int r)
+    {
+        return ROWPERM ? (r ^ ((r >> 2) & 1)) : ROWPERM4 ? (r ^ ((r >> 2) & 3)) : r;
+    }
     __host__ __device__ __forceinline__ static int elem(int r, int col)
     {
         return 4 * (prow(r) * CPR + ((col >> 2) ^ swz(r))) + (col & 3);
@@ -367,12 +388,43 @@ __device__ __forceinline__ void lds_read(const float *p, float (&out)[W])
     }
 }
 
+// The two fp32 matrix instructions, as blocks of MB x MB outputs. Lane l supplies
+// A(l % MB, l / MB) and B(l / MB, l % MB) and holds NACC accumulators; LG = 64 / MB lane
+// groups each supply one k, so one instruction adds the outer products of LG k values.
+//  - MB = 32: v_mfma_f32_32x32x2_f32, 16 accumulators, accumulator e of lane l is
+//    D(8*(e/4) + 4*(l/32) + e%4, l%32).
+//  - MB = 16: v_mfma_f32_16x16x4_f32, 4 accumulators, accumulator e of lane l is
+//    D(4*(l/16) + e, l%16).
+// Both are D(LG*4*(e/4) + 4*(l/MB) + e%4, l%MB). Each does MB*MB*LG multiply-adds per issue
+// at the same rate per cycle, so the 16 x 16 form trades twice the issues for blocks a
+// quarter of the size: finer tiles for small, skinny and ragged products.
+template <int MB>
+struct MfmaBlock;
+template <>
+struct MfmaBlock<32> {
+    typedef floatx16 acc_t;
+    static constexpr int NACC = 16, LG = 2;
+    __device__ __forceinline__ static acc_t mma(float a, float b, const acc_t &c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct MfmaBlock<16> {
+    typedef floatx4 acc_t;
+    static constexpr int NACC = 4, LG = 4;
+    __device__ __forceinline__ static acc_t mma(float a, float b, const acc_t &c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
 // ---------------------------------------------------------------------------------
 // MFMA kernel.
 //
 // Template parameters: BM x BN workgroup tile, BK k-depth per LDS stage, WGM x WGN
 // waves over the tile, WGK wave groups along k, TA / TB whether op(A) / op(B) is a
-// transpose. With WGK > 1 every wave group multiplies its own BK/WGK slice of each
+// transpose, MB the matrix instruction's block (32 or 16). With WGK > 1 every wave group multiplies its own BK/WGK slice of each
 // stage into its own accumulators, and at the end the groups add their accumulators
 // through LDS in a fixed order (group 0 + 1 + 2 ...), so results stay reproducible;
 // this puts more waves on each CU when the problem has few tiles, without any memory
@@ -385,14 +437,13 @@ __device__ __forceinline__ void lds_read(const float *p, float (&out)[W])
 // [BM][BK] (k contiguous), or [BK][BM] when transposed (m contiguous); B as [BK][BN] (n
 // contiguous), or [BN][BK] when transposed (k contiguous).
 //
-// Lane layout of v_mfma_f32_32x32x2_f32 (one 32x32 block, k = 2): lane l supplies
-// A(l%32, l/32) and B(l/32, l%32); accumulator element e of lane l is
-// D(8*(e/4) + 4*(l/32) + e%4, l%32). Remappings make every LDS read wide:
-//  - k: within each group of 8 k values, the half-wave h = l/32 takes k = 4h + s on
-//    matrix step s (s = 0..3). A and B use the same map, so each issue still adds
-//    A(:,k)B(k,:) for two distinct k and the 4 steps cover all 8. An operand stored
-//    k-contiguous (A plain, B transposed) then gives lane l its four values as one
-//    128-bit read.
+// Lane layout: MfmaBlock above (for 32x32 blocks lane l supplies A(l%32, l/32) and
+// B(l/32, l%32)). Remappings make every LDS read wide:
+//  - k: within each group of KGRP = 4*LG k values (8 for 32x32 blocks, 16 for 16x16), lane
+//    group h = l/MB takes k = 4h + s on matrix step s (s = 0..3). A and B use the same
+//    map, so each issue still adds A(:,k)B(k,:) for LG distinct k and the 4 steps cover
+//    all KGRP. An operand stored k-contiguous (A plain, B transposed) then gives lane l
+//    its four values as one 128-bit read.
 //  - m / n: an operand stored m- or n-contiguous (A transposed, B plain) has the
 //    wave's blocks along that dimension interleaved, block b index c <-> wave index
 //    c*T + b (T blocks), so lane l reads T consecutive values for one k in one read,
@@ -403,31 +454,39 @@ __device__ __forceinline__ void lds_read(const float *p, float (&out)[W])
 // whole-tile kernel below runs product over all of K; the stream-K kernel runs it over
 // the K-tile ranges its workgroup owns.
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
-          bool EDGE>
+          bool EDGE, int MB = 32>
 struct MfmaTile {
     static_assert(PF == 1 || PF == 2, "K-tiles in flight ahead of the one being multiplied");
+    static_assert(MB == 32 || MB == 16, "32x32 or 16x16 matrix blocks");
+    using BLK = MfmaBlock<MB>;
+    using acc_t = typename BLK::acc_t;
+    static constexpr int NACC = BLK::NACC;                  // accumulators per lane and block
+    static constexpr int LG = BLK::LG;                      // lane groups, one k each per issue
+    static constexpr int KGRP = 4 * LG;                     // k per group of 4 matrix steps
     static constexpr bool USE_DMA = DMA;                    // direct HBM -> LDS copies
     static constexpr int VW = VEC ? 4 : 1;                  // floats per lane and copy
     static constexpr int NT = WGM * WGN * WGK * 64;
     static constexpr int KSLICE = BK / WGK;                    // k per stage handled by one wave group
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
-    static constexpr int TM = WTM / 32, TN = WTN / 32;         // 32x32 blocks per wave
-    using AIO = typename std::conditional<USE_DMA, TileDMA<TA ? BK : BM, TA ? BM : BK, NT, !TA, VW>,
+    static constexpr int TM = WTM / MB, TN = WTN / MB;         // blocks per wave
+    using AIO = typename std::conditional<USE_DMA,
+                                          TileDMA<TA ? BK : BM, TA ? BM : BK, NT, !TA, VW, MB == 16 && TM == 1>,
                                           TileIO<TA ? BK : BM, TA ? BM : BK, NT>>::type;
-    using BIO = typename std::conditional<USE_DMA, TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB, VW>,
+    using BIO = typename std::conditional<USE_DMA,
+                                          TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB, VW, MB == 16 && TN == 1>,
                                           TileIO<TB ? BN : BK, TB ? BK : BN, NT>>::type;
     static constexpr int STAGE = AIO::SIZE + BIO::SIZE;
     static constexpr int NSTAGE = USE_DMA ? PF + 1 : 2;     // LDS stages in the ring
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(WTM % MB == 0 && WTN % MB == 0, "wave tile must be whole blocks");
     static_assert(!TA || TM == 1 || TM == 2 || TM == 4, "interleaved m blocks read 1, 2 or 4 floats");
     static_assert(TB || TN == 1 || TN == 2 || TN == 4, "interleaved n blocks read 1, 2 or 4 floats");
-    static_assert(BK % (8 * WGK) == 0, "each wave group consumes k in groups of 8");
+    static_assert(BK % (KGRP * WGK) == 0, "each wave group consumes k in whole groups");
     static constexpr int RED = (WGK - 1) * BM * BN;         // partial sums of groups 1..WGK-1
     static constexpr int SMEM = NSTAGE * STAGE > RED ? NSTAGE * STAGE : RED;
-    // Waves per SIMD the register budget is sized for: one for waves holding 16 or more
-    // 32x32 blocks (256 accumulators; the wave gets the whole 512-register file), else at
-    // least two, so that two 256-thread workgroups fit on a CU.
-    static constexpr int WPE = TM * TN >= 16 ? 1 : (NT >= 512 ? NT / 256 : 2);
+    // Waves per SIMD the register budget is sized for: one for waves holding 256 or more
+    // accumulators (the wave gets the whole 512-register file), else at least two, so that
+    // two 256-thread workgroups fit on a CU.
+    static constexpr int WPE = TM * TN * NACC >= 256 ? 1 : (NT >= 512 ? NT / 256 : 2);
     // Double-buffered fragment reads (next group's reads in flight while this group is
     // multiplied). Measured on MI355X: a gain for the direct-copy loop, for one K-tile
     // in flight and for waves holding a single 32x32 block; with two K-tiles in flight and
@@ -441,7 +500,7 @@ struct MfmaTile {
     // tid_in is the thread's index in the workgroup. With WGK > 1 the groups' sums end up
     // in the waves of group 0; the other waves return false and hold nothing.
     __device__ __forceinline__ static bool product(const GemmArgs &p, float *smem, int m0, int n0, int kt0,
-                                                   int kt1, floatx16 (&acc)[TM][TN], int tid_in)
+                                                   int kt1, acc_t (&acc)[TM][TN], int tid_in)
     {
         const int M = p.M, N = p.N, K = p.K;
         const float *__restrict__ A = p.A + (int64_t)blockIdx.z * p.strideA;
@@ -453,7 +512,7 @@ struct MfmaTile {
         const int lane = tid & 63, wave = tid >> 6;
         const int wk = wave / (WGM * WGN);
         const int wm = (wave % (WGM * WGN)) / WGN, wn = wave % WGN;
-        const int l32 = lane & 31, half = lane >> 5;
+        const int li = lane % MB, lg = lane / MB;   // row / column in the block, lane group
 
         // PF sets of staging registers: with PF = 2 a K-tile's global loads are issued two
         // stages before it is multiplied. `slot` is always a compile-time constant after
@@ -509,36 +568,36 @@ struct MfmaTile {
     #pragma unroll
             for (int b = 0; b < TN; ++b)
     #pragma unroll
-                for (int e = 0; e < 16; ++e)
+                for (int e = 0; e < NACC; ++e)
                     acc[a][b][e] = 0.f;
 
         // This lane's first row of A / column of B inside the tile: plain A rows are
-        // a*32 + l32 (blocks side by side), transposed A rows l32*TM + a (interleaved);
+        // a*MB + li (blocks side by side), transposed A rows li*TM + a (interleaved);
         // likewise for B columns with the roles swapped.
-        const int a_idx = wm * WTM + (TA ? l32 * TM : l32);
-        const int b_idx = wn * WTN + (TB ? l32 : l32 * TN);
+        const int a_idx = wm * WTM + (TA ? li * TM : li);
+        const int b_idx = wn * WTN + (TB ? li : li * TN);
 
-        // One stage: KSLICE/8 groups of 8 k values, 4 matrix steps each.
+        // One stage: KSLICE/KGRP groups of KGRP k values, 4 matrix steps each.
         auto compute = [&](int st) __attribute__((always_inline)) {
             const float *As = smem + st * STAGE;
             const float *Bs = As + AIO::SIZE;
     #pragma unroll
-            for (int kk = 0; kk < KSLICE; kk += 8) {
+            for (int kk = 0; kk < KSLICE; kk += KGRP) {
                 const int kg = wk * KSLICE + kk;
                 floatx4 af[TA ? 1 : TM], bf[TB ? TN : 1];
                 if constexpr (!TA) {
     #pragma unroll
                     for (int a = 0; a < TM; ++a)
-                        af[a] = *reinterpret_cast<const floatx4 *>(&As[AIO::elem(a_idx + a * 32, kg + 4 * half)]);
+                        af[a] = *reinterpret_cast<const floatx4 *>(&As[AIO::elem(a_idx + a * MB, kg + 4 * lg)]);
                 }
                 if constexpr (TB) {
     #pragma unroll
                     for (int b = 0; b < TN; ++b)
-                        bf[b] = *reinterpret_cast<const floatx4 *>(&Bs[BIO::elem(b_idx + b * 32, kg + 4 * half)]);
+                        bf[b] = *reinterpret_cast<const floatx4 *>(&Bs[BIO::elem(b_idx + b * MB, kg + 4 * lg)]);
                 }
     #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const int k = kg + 4 * half + s;
+                    const int k = kg + 4 * lg + s;
                     float av[TM], bv[TN];
                     if constexpr (TA) {
                         lds_read<TM>(&As[AIO::elem(k, a_idx)], av);
@@ -558,20 +617,20 @@ struct MfmaTile {
                     for (int a = 0; a < TM; ++a)
     #pragma unroll
                         for (int b = 0; b < TN; ++b)
-                            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+                            acc[a][b] = BLK::mma(av[a], bv[b], acc[a][b]);
                 }
             }
         };
 
-        // Fragment form (FRAG): the A and B values of one group of 8 k (4 per lane) for every
-        // block, read from LDS in one batch, so the reads of the next group can be in flight
-        // while this one is multiplied.
-        constexpr int NG = KSLICE / 8;                      // groups of 8 k per stage and wave group
+        // Fragment form (FRAG): the A and B values of one group of KGRP k (4 per lane) for
+        // every block, read from LDS in one batch, so the reads of the next group can be in
+        // flight while this one is multiplied.
+        constexpr int NG = KSLICE / KGRP;                   // groups of k per stage and wave group
         float fa[FRAG ? 2 : 1][4][TM], fb[FRAG ? 2 : 1][4][TN];
         auto read_frag = [&](int st, int g, int buf) __attribute__((always_inline)) {
             const float *As = smem + st * STAGE;
             const float *Bs = As + AIO::SIZE;
-            const int kg = wk * KSLICE + 8 * g + 4 * half;
+            const int kg = wk * KSLICE + KGRP * g + 4 * lg;
             if constexpr (TA) {
     #pragma unroll
                 for (int s = 0; s < 4; ++s)
@@ -579,7 +638,7 @@ struct MfmaTile {
             } else {
     #pragma unroll
                 for (int a = 0; a < TM; ++a) {
-                    const floatx4 v = *reinterpret_cast<const floatx4 *>(&As[AIO::elem(a_idx + a * 32, kg)]);
+                    const floatx4 v = *reinterpret_cast<const floatx4 *>(&As[AIO::elem(a_idx + a * MB, kg)]);
     #pragma unroll
                     for (int s = 0; s < 4; ++s)
                         fa[buf][s][a] = v[s];
@@ -588,7 +647,7 @@ struct MfmaTile {
             if constexpr (TB) {
     #pragma unroll
                 for (int b = 0; b < TN; ++b) {
-                    const floatx4 v = *reinterpret_cast<const floatx4 *>(&Bs[BIO::elem(b_idx + b * 32, kg)]);
+                    const floatx4 v = *reinterpret_cast<const floatx4 *>(&Bs[BIO::elem(b_idx + b * MB, kg)]);
     #pragma unroll
                     for (int s = 0; s < 4; ++s)
                         fb[buf][s][b] = v[s];
@@ -606,8 +665,7 @@ struct MfmaTile {
                 for (int a = 0; a < TM; ++a)
     #pragma unroll
                     for (int b = 0; b < TN; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[buf][s][a], fb[buf][s][b], acc[a][b],
-                                                                         0, 0, 0);
+                        acc[a][b] = BLK::mma(fa[buf][s][a], fb[buf][s][b], acc[a][b]);
         };
 
         // Pipeline over the range's nk K-tiles, one barrier per K-tile.
@@ -732,7 +790,7 @@ struct MfmaTile {
         if constexpr (WGK > 1) {
             // Groups 1..WGK-1 hand their partial sums to group 0 through LDS (the ring is
             // free once every wave has passed the barrier); group 0 adds them in group order.
-            constexpr int PER_WAVE = TM * TN * 16 * 64;
+            constexpr int PER_WAVE = TM * TN * NACC * 64;
             const int slot = wm * WGN + wn;
             __syncthreads();
             if (wk > 0) {
@@ -742,8 +800,8 @@ struct MfmaTile {
     #pragma unroll
                     for (int b = 0; b < TN; ++b)
     #pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            dst[((a * TN + b) * 16 + e) * 64 + lane] = acc[a][b][e];
+                        for (int e = 0; e < NACC; ++e)
+                            dst[((a * TN + b) * NACC + e) * 64 + lane] = acc[a][b][e];
             }
             __syncthreads();
             if (wk > 0)
@@ -756,15 +814,15 @@ struct MfmaTile {
     #pragma unroll
                     for (int b = 0; b < TN; ++b)
     #pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            acc[a][b][e] += src[((a * TN + b) * 16 + e) * 64 + lane];
+                        for (int e = 0; e < NACC; ++e)
+                            acc[a][b][e] += src[((a * TN + b) * NACC + e) * 64 + lane];
             }
         }
         return true;
     }
 
     __device__ __forceinline__ static void epilogue(const GemmArgs &p, int m0, int n0,
-                                                    const floatx16 (&acc)[TM][TN], int tid_in)
+                                                    const acc_t (&acc)[TM][TN], int tid_in)
     {
         const int M = p.M, N = p.N;
         float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
@@ -772,13 +830,13 @@ struct MfmaTile {
         const int tid = tid_in;
         const int lane = tid & 63, wave = tid >> 6;
         const int wm = (wave % (WGM * WGN)) / WGN, wn = wave % WGN;
-        const int l32 = lane & 31, half = lane >> 5;
-        const int b_idx = wn * WTN + (TB ? l32 : l32 * TN);
-        // Epilogue: C = act(alpha*acc + beta*C + bias), C unread when beta == 0. One 32-row
-        // block at a time: all of the block's reads of C are issued before the first is
-        // used, so the block waits out one memory round trip (two with EB = 8) rather than
-        // one per entry. Lane columns: TN consecutive ones (plain B), or one per 32-column block
-        // (transposed B). Rows: those of accumulator element e, see the mapping above.
+        const int li = lane % MB, lg = lane / MB;
+        const int b_idx = wn * WTN + (TB ? li : li * TN);
+        // Epilogue: C = act(alpha*acc + beta*C + bias), C unread when beta == 0. One block
+        // row at a time: all of the block's reads of C are issued before the first is used,
+        // so the block waits out one memory round trip (two with EB = 8) rather than one per
+        // entry. Lane columns: TN consecutive ones (plain B), or one per MB-column block
+        // (transposed B). Rows: those of accumulator element e, see MfmaBlock.
         const float alpha = p.alpha, beta = p.beta;
         const float *bias = p.bias;
         const int act = p.act;
@@ -790,23 +848,23 @@ struct MfmaTile {
         int gc[TN];
     #pragma unroll
         for (int b = 0; b < TN; ++b)
-            gc[b] = n0 + b_idx + (TB ? 32 * b : b);
+            gc[b] = n0 + b_idx + (TB ? MB * b : b);
         float bj[TN];
     #pragma unroll
         for (int b = 0; b < TN; ++b)
             bj[b] = (has_bias && (full || gc[b] < N)) ? bias[gc[b]] : 0.f;
         auto row_of = [&](int a, int e) __attribute__((always_inline)) {
-            const int r = 8 * (e / 4) + 4 * half + (e % 4);          // row inside the 32x32 block
-            return m0 + wm * WTM + (TA ? r * TM + a : a * 32 + r);
+            const int r = 4 * LG * (e / 4) + 4 * lg + (e % 4);      // row inside the block
+            return m0 + wm * WTM + (TA ? r * TM + a : a * MB + r);
         };
-        // Entries per batch of reads: 16 (the whole block), or 8 where four waves share a
-        // SIMD and each has only 128 registers.
-        constexpr int EB = NT >= 1024 ? 8 : 16;
+        // Entries per batch of reads: the whole block (16 or 4), or 8 where four waves share
+        // a SIMD and each has only 128 registers.
+        constexpr int EB = NT >= 1024 && NACC > 8 ? 8 : NACC;
     #pragma unroll
         for (int a = 0; a < TM; ++a)
     #pragma unroll
-        for (int e0 = 0; e0 < 16; e0 += EB) {
-            float cv[16][TN];
+        for (int e0 = 0; e0 < NACC; e0 += EB) {
+            float cv[NACC][TN];
             if (read_c) {
     #pragma unroll
                 for (int e = e0; e < e0 + EB; ++e) {
@@ -855,16 +913,16 @@ struct MfmaTile {
 };
 
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
-          bool EDGE>
+          bool EDGE, int MB>
 __global__ void __launch_bounds__(WGM * WGN * WGK * 64)
-__attribute__((amdgpu_waves_per_eu(MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE>::WPE)))
+__attribute__((amdgpu_waves_per_eu(MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE, MB>::WPE)))
 sgemm_mfma(GemmArgs p, int group_m)
 {
-    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE>;
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE, MB>;
     __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
     int tm, tn;
     tile_coords(blockIdx.x, ceil_div(p.M, BM), ceil_div(p.N, BN), group_m, tm, tn);
-    floatx16 acc[T::TM][T::TN];
+    typename T::acc_t acc[T::TM][T::TN];
     if (T::product(p, smem, tm * BM, tn * BN, 0, ceil_div(p.K, BK), acc, threadIdx.x))
         T::epilogue(p, tm * BM, tn * BN, acc, threadIdx.x);
 }
@@ -890,13 +948,14 @@ struct StreamK {
 // contributor order (the same order whoever comes last, so results do not depend on
 // timing) and writes C. No workgroup ever waits for another.
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
-          bool EDGE>
+          bool EDGE, int MB>
 __global__ void __launch_bounds__(WGM * WGN * WGK * 64)
 sgemm_mfma_sk(GemmArgs p, StreamK sk)
 {
-    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE>;
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE, MB>;
     constexpr int TILE = BM * BN;
-    constexpr int PER_WAVE = T::TM * T::TN * 16 * 64;   // one wave's accumulators
+    constexpr int NACC = T::NACC;
+    constexpr int PER_WAVE = T::TM * T::TN * NACC * 64;   // one wave's accumulators
     __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
     __shared__ unsigned ticket;
 
@@ -915,7 +974,7 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
         const int kt1 = (w_end - t * I) < I ? (w_end - t * I) : I;
         int tm, tn;
         band_coords(t, sk.tiles_m, sk.tiles_n, sk.group_m, tm, tn);
-        floatx16 acc[T::TM][T::TN];
+        typename T::acc_t acc[T::TM][T::TN];
         // The thread index passes through an empty asm statement on every tile, so the
         // per-lane addresses are recomputed per tile instead of being hoisted out of
         // this loop and held (with the accumulators) across the fixup and epilogue.
@@ -956,8 +1015,8 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
 #pragma unroll
                     for (int b = 0; b < T::TN; ++b)
 #pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            __hip_atomic_store(&dst[((a * T::TN + b) * 16 + e) * 64 + lane], acc[a][b][e],
+                        for (int e = 0; e < NACC; ++e)
+                            __hip_atomic_store(&dst[((a * T::TN + b) * NACC + e) * 64 + lane], acc[a][b][e],
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             // Publish: this wave's stores are acknowledged, then every wave meets, then one
@@ -978,8 +1037,8 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
 #pragma unroll
                         for (int b = 0; b < T::TN; ++b)
 #pragma unroll
-                            for (int e = 0; e < 16; ++e) {
-                                const float v = __hip_atomic_load(&src[((a * T::TN + b) * 16 + e) * 64 + lane],
+                            for (int e = 0; e < NACC; ++e) {
+                                const float v = __hip_atomic_load(&src[((a * T::TN + b) * NACC + e) * 64 + lane],
                                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                                 acc[a][b][e] = c == first ? v : acc[a][b][e] + v;
                             }

@@ -9,8 +9,9 @@
 // loads of the chunks wholly inside a row and element-wise ones for the chunk that
 // straddles its end. Every other direct-copy configuration, and every call whose row
 // strides are too long for 32-bit copy offsets (dma_ok false), runs the register-staged
-// kernel with one K-tile in flight and K-tiles of 16 * WGK, so that variant fits the
-// register file for every tile shape. A stream-K configuration (register-staged) runs the
+// kernel with one K-tile in flight and K-tiles of two k groups per wave group (16 * WGK for
+// 32x32 blocks, 32 * WGK for 16x16 ones), so that variant fits the register file for every
+// tile shape. A stream-K configuration (register-staged) runs the
 // data-parallel kernel of its tile on unaligned operands: stream-K itself was measured
 // slower there on every odd-sized shape swept.
 #pragma once
@@ -19,12 +20,13 @@
 
 namespace sgemm_impl {
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, bool TA, bool TB>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, int MB, bool TA,
+          bool TB>
 hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, bool dma_ok, hipStream_t s)
 {
     constexpr int NT = WGM * WGN * WGK * 64;
     constexpr bool DMA4 = DMA && (BM * BK + BK * BN) / NT <= 16;   // 4-byte copies for unaligned rows
-    constexpr int BKU = DMA ? 16 * WGK : BK;            // K-tile of the register-staged unaligned variant
+    constexpr int BKU = DMA ? 8 * (64 / MB) * WGK : BK;  // K-tile of the register-staged unaligned variant
     // The caller has checked that tiles x NT fits one launch; the sums are unsigned so that
     // M or N near 2^31 does not overflow.
     const unsigned tiles = (((unsigned)p.M + BM - 1) / BM) * (((unsigned)p.N + BN - 1) / BN);
@@ -32,24 +34,25 @@ hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, boo
     if (DMA && !dma_ok)
         vec = false;                                    // only the register-staged variant takes long rows
     if (vec && !edge)
-        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, false>), grid, block, 0, s,
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, false, MB>), grid, block, 0, s,
                            p, GROUP_M);
     else if (vec)
-        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, true>), grid, block, 0, s,
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, true, MB>), grid, block, 0, s,
                            p, GROUP_M);
     else if constexpr (!DMA)    // register-staged configuration: its own K-tile and loads in flight
-        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, false, TA, TB, false, true>), grid, block, 0,
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, false, TA, TB, false, true, MB>), grid, block, 0,
                            s, p, GROUP_M);
     else if (!DMA4 || !dma_ok)
-        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BKU, WGM, WGN, WGK, 1, false, TA, TB, false, true>), grid, block, 0,
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BKU, WGM, WGN, WGK, 1, false, TA, TB, false, true, MB>), grid, block, 0,
                            s, p, GROUP_M);
     else if constexpr (DMA4)
-        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, true, TA, TB, false, true>), grid, block, 0,
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, true, TA, TB, false, true, MB>), grid, block, 0,
                            s, p, GROUP_M);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, bool TA, bool TB>
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, int MB, bool TA,
+          bool TB>
 hipError_t launch_mfma_sk_op(const GemmArgs &p, const StreamK &sk, int grid, bool vec, bool edge, bool dma_ok,
                              hipStream_t s)
 {
@@ -60,16 +63,16 @@ hipError_t launch_mfma_sk_op(const GemmArgs &p, const StreamK &sk, int grid, boo
     // data-parallel kernel of the tile, like unaligned operands without a 4-byte-copy form.
     const bool staged = (DMA && !dma_ok) || (!vec && !DMA4);
     if (staged)
-        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, false, TA, TB, false, true>),
+        hipLaunchKernelGGL((sgemm_mfma<BM, BN, BK, WGM, WGN, WGK, PF, false, TA, TB, false, true, MB>),
                            dim3(sk.tiles_m * sk.tiles_n), block, 0, s, p, GROUP_M);
     else if (vec && !edge)
-        hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, false>), dim3(grid),
+        hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, false, MB>), dim3(grid),
                            block, 0, s, p, sk);
     else if (vec)
-        hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, true>), dim3(grid),
+        hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, true, true, MB>), dim3(grid),
                            block, 0, s, p, sk);
     else if constexpr (DMA4)    // rows only 4-byte aligned: 4-byte direct copies into the same LDS layout
-        hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, true, TA, TB, false, true>), dim3(grid),
+        hipLaunchKernelGGL((sgemm_mfma_sk<BM, BN, BK, WGM, WGN, WGK, PF, true, TA, TB, false, true, MB>), dim3(grid),
                            block, 0, s, p, sk);
     return hipGetLastError();
 }
