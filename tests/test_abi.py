@@ -252,14 +252,15 @@ def test_select_config():
         tiles = -(-M // bm) * -(-N // bn)
         assert tiles >= 256 or bm <= 64, (M, N, name, tiles)
     # the measured winners of the benchmark shapes: 16x16-block tiles for the GPT-2 QKV and
-    # MLP-up layers, 256^3 and the 32-wide product; the 32x32-block tile for MLP-down
+    # MLP-up layers, 1024^3, 256^3 (whole K in one 256-deep K-tile) and the 32-wide and
+    # 32-row products; the 32x32-block tile for MLP-down
     assert names[sel(1024, 2304, 768)] == "mfma16_64x64x32_w4x1k1d"
     assert names[sel(1024, 3072, 768)] == "mfma16_64x64x32_w4x1k1d"
     assert names[sel(1024, 768, 3072)] == "mfma_32x32x64_w1x1k4d"
     assert names[sel(1024, 1024, 1024)] == "mfma16_64x64x64_w4x1k2d"
-    assert names[sel(256, 256, 256)] == "mfma16_16x16x128_w1x1k4d"
-    assert names[sel(8192, 32, 8192)] == "mfma16_16x16x128_w1x1k4d"
-    assert names[sel(32, 8192, 8192)] == "mfma16_16x64x128_w1x1k4d"
+    assert names[sel(256, 256, 256)] == "mfma16_16x16x256_w1x1k4d"
+    assert names[sel(8192, 32, 8192)] == "mfma16_32x32x128_w2x2k2d"
+    assert names[sel(32, 8192, 8192)] == "mfma16_32x32x128_w2x2k2d"
     # unaligned: the ragged product keeps the 64 x 128 tile with 4-byte copies
     assert names[sg.sgemm_select_config(1000, 1537, 777, 1.0, BAD, 777, BAD, 1537, BAD, 1537)] == \
         "mfma_64x128x32_w2x2k2d"

@@ -82,7 +82,7 @@ def test_workload_as_timed(name, ws):
 def test_timed_configurations(ws):
     """What the cost model picks for the timed launches, with a workspace: the measured
     winners of the sweep. 16x16-block tiles for GPT-2 QKV and MLP-up (64 x 64, wave tiles of
-    16 x 64), 1024^3 (64 x 64 x 64) and 256^3 (16 x 16); the 32 x 32 tile of 32x32 blocks for
+    16 x 64), 1024^3 (64 x 64 x 64) and 256^3 (16 x 16, all of K in one K-tile); the 32 x 32 tile of 32x32 blocks for
     MLP-down; the 256 x 256 tile at 4096^3 (no stream-K: each of these beats it)."""
     import tiled_fp32_gemm_02_amd as sg
     picks = {}
@@ -94,6 +94,6 @@ def test_timed_configurations(ws):
     say(f"timed configurations: {picks}")
     assert picks["gpt2_qkv"] == "mfma16_64x64x32_w4x1k1d"
     assert picks["gpt2_mlp_up"] == "mfma16_64x64x32_w4x1k1d"
-    assert picks["gpt2_mlp_down"] == "mfma_32x32x64_w1x1k4d" and picks["sq256"] == "mfma16_16x16x128_w1x1k4d"
+    assert picks["gpt2_mlp_down"] == "mfma_32x32x64_w1x1k4d" and picks["sq256"] == "mfma16_16x16x256_w1x1k4d"
     assert picks["sq1024"] == "mfma16_64x64x64_w4x1k2d"
     assert picks["sq4096"] == "mfma_256x256x32_w2x4d"

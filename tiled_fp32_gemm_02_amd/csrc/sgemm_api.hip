@@ -256,34 +256,40 @@ struct Candidate {
 // alignment, over the shapes of one sweep where neither memory bound was within 75% of the
 // measured time. Aligned: 36 shapes (256^3 ... 6144^3, 3000^3, rectangles, the GPT-2-small
 // linear layers, long-K and skinny products down to 16 rows or columns). With the
-// candidates below the model picks, on average, a configuration within 1.6% of the fastest
-// of all those swept; it picks the fastest on 256^3, 1024^3, 4096^3 and the three GPT-2
-// layers; the worst misses are 13% (128 x 4096 x 4096), 11% (4096 x 64 x 4096 and
-// 2048 x 256 x 16384). Candidates were chosen by dropping, one at a time, those whose removal
-// improved the picks. Unaligned (rows only 4-byte aligned): 24 odd-sized shapes (255^3 ...
-// 6143^3, 2999^3, 511 x 4095 x 4095, 1000 x 1537 x 777, the GPT-2 layers one short in each
-// dimension, long-K and skinny ones); picks average within 0.6% of the fastest, the worst
-// 3.7% (1535^3), and the ragged 1000 x 1537 x 777 and the GPT-2 layers get the fastest.
+// candidates below the model picks, on average, a configuration within 1.3% of the fastest
+// of all those swept, and the fastest on 256^3, 1024^3, 4096^3 and the three GPT-2 layers;
+// the worst misses are skinny products: 16384 x 16 x 16384 (19%), 16 x 16384 x 16384 (8%)
+// and 8192 x 128 x 8192 (6%). Candidates were chosen by dropping, one at a time, those whose
+// removal improved the picks. Unaligned (rows only 4-byte aligned): 24 odd-sized shapes
+// (255^3 ... 6143^3, 2999^3, 511 x 4095 x 4095, 1000 x 1537 x 777, the GPT-2 layers one
+// short in each dimension, long-K and skinny ones); picks average within 0.6% of the
+// fastest, the worst 3.7% (1535^3), and the ragged 1000 x 1537 x 777 and the GPT-2 layers
+// get the fastest.
 const Candidate kCandidates[] = {
-    {"mfma_256x256x32_w2x4d", 6.61, 0.00, 1.7203, 1.7386},     // one workgroup per CU
+    {"mfma_256x256x32_w2x4d", 6.61, 0.00, 1.7203, 1.7386}, // one workgroup per CU (4096^3)
     {"mfma_128x128x32_w2x2k2d", 0.00, 5.39, 1.8261, 1.7742},
     {"mfma16_64x128x32_w4x2k1d", 0.70, 1.25, 1.9955, 1.7866},
-    {"mfma16_64x64x64_w4x1k2d", 1.50, 1.09, 2.0556, 1.8173},   // 1024^3, 3072^3
-    {"mfma16_64x64x32_w4x1k1d", 0.30, 0.48, 2.7419, 1.8653},   // GPT-2 QKV and MLP-up
-    {"mfma_32x32x64_w1x1k4d", 1.95, 0.84, 4.7050, 2.2238},     // GPT-2 MLP-down
-    {"mfma16_16x16x128_w1x1k4d", 2.24, 0.00, 19.4973, 4.3872}, // 256^3, 16- and 32-wide products
-    {"mfma16_16x64x128_w1x1k4d", 2.79, 0.22, 3.5509, 2.6575},  // 16- and 32-row products
+    {"mfma16_64x64x64_w4x1k2d", 1.50, 1.09, 2.0556, 1.8173}, // 1024^3, 3072^3
+    {"mfma16_64x64x32_w4x1k1d", 0.30, 0.48, 2.7419, 1.8653}, // GPT-2 QKV and MLP-up
+    {"mfma_32x32x64_w1x1k4d", 1.95, 0.84, 4.7050, 2.2238}, // GPT-2 MLP-down
+    {"mfma16_16x16x128_w1x1k4d", 2.24, 0.00, 19.4973, 4.3872}, // 256^3
+    {"mfma16_16x64x128_w1x1k4d", 2.79, 0.22, 3.5509, 2.6575}, // 16- and 32-row products
+    {"mfma16_32x64x128_w2x1k4d", 1.35, 2.04, 2.0422, 2.0440},
     {"mfma16_64x64x64_w2x2k2d", 1.46, 1.14, 2.0651, 1.8220},
     {"mfma_64x128x32_w2x2k2d", 0.41, 2.39, 2.0202, 1.7895},
     {"mfma_64x64x64_w2x2k4d", 0.33, 3.93, 2.1330, 1.9589},
     {"mfma16_128x64x32_w8x1k1d", 0.57, 1.49, 2.0763, 1.8275},
     {"mfma_64x64x32_w2x2k2d", 0.00, 1.99, 2.7448, 1.9717},
+    {"mfma16_64x16x64_w4x1k1d", 2.31, 0.00, 4.5801, 2.7833},
+    {"mfma16_16x16x256_w1x1k4d", 2.36, 0.71, 9.3849, 3.8645}, // 16-wide products
+    {"mfma16_16x16x128_w1x1k4p2d", 2.98, 0.25, 8.9629, 3.9316},
+    {"mfma16_32x32x128_w2x2k2d", 2.16, 0.81, 2.8215, 2.2516}, // 512^3, 32- and 64-wide products
 };
 const Candidate kUnalignedCandidates[] = {
     {"mfma_256x256x32_w2x4d", 5.94, 0.00, 2.0225, 2.0671},
     {"mfma_256x256x16_w2x4p2d", 7.88, 0.00, 1.9201, 2.0263},
     {"mfma_128x128x32_w2x2k2d", 6.57, 0.00, 2.1279, 2.1380},
-    {"mfma_64x128x32_w2x2k2d", 2.32, 2.86, 2.2324, 2.0580},     // 1000 x 1537 x 777
+    {"mfma_64x128x32_w2x2k2d", 2.32, 2.86, 2.2324, 2.0580}, // 1000 x 1537 x 777
     {"mfma_64x64x32_w2x2k2d", 2.75, 2.73, 2.9376, 2.1774},
     {"mfma_32x128x64_w1x4k2d", 3.65, 2.15, 3.4416, 2.5125},
     {"mfma_32x64x64_w1x2k2d", 5.65, 0.00, 5.7274, 2.7701},
@@ -292,12 +298,16 @@ const Candidate kUnalignedCandidates[] = {
     {"mfma16_64x64x64_w4x1k2d", 1.73, 2.72, 2.4920, 2.1934},
     {"mfma16_64x64x64_w2x2k2d", 1.86, 2.40, 2.4844, 2.1924},
     {"mfma16_64x64x32_w4x1k1d", 0.83, 2.57, 3.2597, 2.2475},
-    {"mfma16_64x16x64_w4x1k1d", 0.00, 0.00, 11.1652, 4.3130},
+    {"mfma16_64x16x64_w4x1k1d", 0.07, 0.00, 11.1018, 4.1094},
     {"mfma16_32x128x64_w2x2k2d", 0.00, 3.39, 3.2870, 3.1858},
     {"mfma16_32x64x128_w2x1k4d", 0.59, 2.83, 3.5119, 3.4162},
     {"mfma16_32x64x64_w2x1k2d", 3.10, 0.36, 4.5025, 2.8383},
+    {"mfma16_32x32x128_w2x2k2d", 2.49, 1.29, 4.4149, 3.0238},
+    {"mfma16_32x32x64_w2x2k1d", 3.13, 0.38, 5.9164, 3.1477},
     {"mfma16_16x64x128_w1x1k4d", 1.16, 2.59, 6.2842, 5.7675},
-    {"mfma16_16x16x128_w1x1k4d", 2.56, 0.36, 15.2149, 5.2090},
+    {"mfma16_16x16x256_w1x1k4d", 2.06, 0.19, 17.2871, 5.6646},
+    {"mfma16_16x16x128_w1x1k4p2d", 3.91, 0.51, 4.4454, 5.5433},
+    {"mfma16_16x16x128_w1x1k4d", 2.77, 0.21, 14.6886, 5.5336},
 };
 const Candidate kSkCandidates[] = {
     {"sk_128x128x32_w2x2k2p2", 19.09, 0.00, 1.8743, 1.8743},
@@ -309,7 +319,7 @@ constexpr int kNumSkCandidates = sizeof(kSkCandidates) / sizeof(kSkCandidates[0]
 constexpr double kHbmBytesPerUs = 5.7e6;          // 5.7 TB/s for rows of 512 contiguous bytes
 constexpr double kHbmRowExponent = 0.19;
 constexpr double kL2BytesPerUs = 20.0e6;          // tile-fill bytes, 16-byte aligned rows
-constexpr double kL2BytesPerUsUnaligned = 14.1e6; // and 4-byte aligned rows
+constexpr double kL2BytesPerUsUnaligned = 14.75e6; // and 4-byte aligned rows
 
 int find_config(const char *name)
 {
