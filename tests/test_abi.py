@@ -251,10 +251,11 @@ def test_select_config():
         bm, bn, _ = (int(x) for x in name.split("_")[1].split("x"))
         tiles = -(-M // bm) * -(-N // bn)
         assert tiles >= 256 or bm <= 64, (M, N, name, tiles)
-    # the measured winners of the benchmark shapes: 16x16-block tiles for the GPT-2 QKV and
-    # MLP-up layers, 1024^3, 256^3 (whole K in one 256-deep K-tile) and the 32-wide and
-    # 32-row products; the 32x32-block tile for MLP-down
-    assert names[sel(1024, 2304, 768)] == "mfma16_64x64x32_w4x1k1d"
+    # the measured winners of the benchmark shapes: 16x16-block tiles for the GPT-2 QKV layer
+    # (32 x 96: 768 tiles, three per CU) and MLP-up layer, 1024^3, 1536^3, 256^3 (whole K in
+    # one 256-deep K-tile) and the 32-wide and 32-row products; the 32x32-block tile for MLP-down
+    assert names[sel(1024, 2304, 768)] == "mfma16_32x96x32_w2x2k1d"
+    assert names[sel(1536, 1536, 1536)] == "mfma16_32x96x32_w2x2k1d"
     assert names[sel(1024, 3072, 768)] == "mfma16_64x64x32_w4x1k1d"
     assert names[sel(1024, 768, 3072)] == "mfma_32x32x64_w1x1k4d"
     assert names[sel(1024, 1024, 1024)] == "mfma16_64x64x64_w4x1k2d"

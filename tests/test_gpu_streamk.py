@@ -158,25 +158,27 @@ def test_auto_choice_with_workspace(ws):
         picks[(M, N, K)] = names[cid]
     assert picks[(4096, 4096, 4096)] == "mfma_256x256x32_w2x4d"       # one whole tile per CU already
     assert picks[(2560, 2560, 2560)].startswith("sk_")               # 400 tiles of 128^2, K long
-    assert picks[(1536, 1536, 1536)].startswith("sk_")               # 288 tiles of 64x128
+    # 768 tiles of 32 x 96, three per CU: balanced without stream-K (66 against 71 us measured)
+    assert picks[(1536, 1536, 1536)] == "mfma16_32x96x32_w2x2k1d"
 
 
 def test_tensor_form_uses_the_workspace():
     """The tensor form passes its cached workspace, so a shape the cost model sends to
-    stream-K (1536^3) gets it; without the workspace the same call runs a tile kernel."""
+    stream-K (512 x 512 x 8192: 16 tiles of 128 x 128, K long) gets it; without the workspace
+    the same call runs a tile kernel."""
     import torch
     import tiled_fp32_gemm_02_amd as sg
     rng = np.random.default_rng(17)
-    n = 1536
-    a, b = draw(rng, (n, n), "normal"), draw(rng, (n, n), "normal002")
+    M, N, K = 512, 512, 8192
+    a, b = draw(rng, (M, K), "normal"), draw(rng, (K, N), "normal002")
     A, B = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
     ws = sg.workspace_for(A.device)
-    assert sg.sgemm_config_name(sg.sgemm_select_config_ws(n, n, n, 1.0, A, n, B, n, A, n, ws.numel())).startswith("sk_")
+    assert sg.sgemm_config_name(sg.sgemm_select_config_ws(M, N, K, 1.0, A, K, B, N, A, N, ws.numel())).startswith("sk_")
     say("stream-K through the tensor form")
     C = sg.gemm(A, B)
     C2 = sg.gemm(A, B, workspace=None)
     torch.cuda.synchronize()
-    ref, bound = oracle.gemm(0, 0, n, n, n, 1.0, a, n, b, n, 0.0, None, n)
+    ref, bound = oracle.gemm(0, 0, M, N, K, 1.0, a, K, b, N, 0.0, None, N)
     assert oracle.within_bound(C.cpu().numpy(), ref, bound)[0]
     assert oracle.within_bound(C2.cpu().numpy(), ref, bound)[0]
     assert counters_clear(ws)
@@ -191,10 +193,12 @@ def test_tensor_form_on_a_side_stream_with_a_fresh_workspace(monkeypatch):
     import tiled_fp32_gemm_02_amd as sg
     monkeypatch.setattr(sg, "_workspaces", {})
     rng = np.random.default_rng(23)
-    n = 1536
-    a, b = draw(rng, (n, n), "normal"), draw(rng, (n, n), "normal002")
+    M, N, K = 512, 512, 8192
+    a, b = draw(rng, (M, K), "normal"), draw(rng, (K, N), "normal002")
     A, B = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
     torch.cuda.synchronize()
+    ws_bytes = sg.sgemm_workspace_size(-1)
+    assert sg.sgemm_config_name(sg.sgemm_select_config_ws(M, N, K, 1.0, A, K, B, N, A, N, ws_bytes)).startswith("sk_")
     side = torch.cuda.Stream()
     # reuse of a freed allocation: leave nonzero bytes where the workspace may land
     junk = torch.full((sg.sgemm_workspace_size(-1) // 4 + 16,), -1, dtype=torch.int32, device="cuda")
@@ -202,7 +206,7 @@ def test_tensor_form_on_a_side_stream_with_a_fresh_workspace(monkeypatch):
     say("stream-K through the tensor form on a side stream, fresh workspace")
     C = sg.gemm(A, B, stream=side)
     side.synchronize()
-    ref, bound = oracle.gemm(0, 0, n, n, n, 1.0, a, n, b, n, 0.0, None, n)
+    ref, bound = oracle.gemm(0, 0, M, N, K, 1.0, a, K, b, N, 0.0, None, N)
     ok, worst, idx = oracle.within_bound(C.cpu().numpy(), ref, bound)
     assert ok, (worst, idx)
     ws = sg._workspaces[(A.device.index, int(side.cuda_stream))]

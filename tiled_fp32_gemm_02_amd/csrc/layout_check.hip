@@ -7,7 +7,8 @@
 //  - the copies together cover every element of the tile exactly once;
 //  - the layout maps the tile one-to-one onto its SIZE floats of LDS;
 //  - the fragment reads of the matrix-core loop (16-byte reads of k-contiguous rows,
-//    1-, 2- or 4-float reads of m- or n-contiguous rows) meet no LDS bank conflict in a
+//    1-, 2- or 4-float reads of m- or n-contiguous rows, one float per block where plain
+//    B's blocks sit side by side) meet no LDS bank conflict in a
 //    model of the 64-bank LDS that serves 64 dwords per pass (64 lanes of a 4-byte read,
 //    32 of an 8-byte one, 16 of a 16-byte one). The hardware counters are the final
 //    word on conflicts; this catches a layout that cannot be conflict-free.
@@ -134,6 +135,15 @@ static void check_config(const char *name)
                                   TA ? "t" : "n", TB ? "t" : "n", VW, wave, g, b);
                     check_read(what, addr, 4);
                 }
+            } else if (T::BSIDE) {
+                for (int s = 0; s < 4; ++s)
+                    for (int b = 0; b < TN; ++b) {
+                        for (int l = 0; l < 64; ++l)
+                            addr[l] = B::elem(wk * KS + KG * g + 4 * (l / MB) + s, wn * T::WTN + (l % MB) + b * MB);
+                        std::snprintf(what, sizeof what, "%s %s%s VW=%d B read (wave %d, group %d, k %d, block %d)",
+                                      name, TA ? "t" : "n", TB ? "t" : "n", VW, wave, g, s, b);
+                        check_read(what, addr, 1);
+                    }
             } else {
                 for (int s = 0; s < 4; ++s) {
                     for (int l = 0; l < 64; ++l)

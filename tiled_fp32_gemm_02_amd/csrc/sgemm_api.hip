@@ -254,36 +254,43 @@ struct Candidate {
 
 // Non-negative least-squares fits (relative error) of the compute bound, per operand
 // alignment, over the shapes of one sweep where neither memory bound was within 75% of the
-// measured time. Aligned: 36 shapes (256^3 ... 6144^3, 3000^3, rectangles, the GPT-2-small
-// linear layers, long-K and skinny products down to 16 rows or columns). With the
-// candidates below the model picks, on average, a configuration within 1.3% of the fastest
-// of all those swept, and the fastest on 256^3, 1024^3, 4096^3 and the three GPT-2 layers;
-// the worst misses are skinny products: 16384 x 16 x 16384 (19%), 16 x 16384 x 16384 (8%)
-// and 8192 x 128 x 8192 (6%). Candidates were chosen by dropping, one at a time, those whose
-// removal improved the picks. Unaligned (rows only 4-byte aligned): 24 odd-sized shapes
+// measured time. Aligned: 36 single products (256^3 ... 6144^3, 3000^3, rectangles, the
+// GPT-2-small linear layers, long-K and skinny products down to 16 rows or columns) and 10
+// batched ones at half weight (attention's 12-head products 1024 x 1024 x 64 and
+// 1024 x 64 x 1024, the first with K from 16 to 256, and 48 or 3 heads of other sizes),
+// whose short K loops set the per-round costs. With the candidates below the model picks,
+// on average, a configuration within 1.1% of the fastest of all those swept, and the
+// fastest on 256^3, 1024^3, 1536^3, 4096^3, the three GPT-2 layers and the attention
+// scores (the attention values product 3.6% off); the worst misses are skinny products:
+// 16384 x 16 x 16384 (19%), 16 x 16384 x 16384 (8%) and 8192 x 128 x 8192 (6%). Candidates were chosen by dropping, one at a time, those
+// whose removal improved the picks. Unaligned (rows only 4-byte aligned): 24 odd-sized shapes
 // (255^3 ... 6143^3, 2999^3, 511 x 4095 x 4095, 1000 x 1537 x 777, the GPT-2 layers one
-// short in each dimension, long-K and skinny ones); picks average within 0.6% of the
-// fastest, the worst 3.7% (1535^3), and the ragged 1000 x 1537 x 777 and the GPT-2 layers
-// get the fastest.
+// short in each dimension, long-K and skinny ones); picks average within 0.5% of the
+// fastest, the worst 3.3% (2559^3), and the ragged 1000 x 1537 x 777 and the first two
+// GPT-2 layers get the fastest (the third is 2.8% off).
 const Candidate kCandidates[] = {
-    {"mfma_256x256x32_w2x4d", 6.61, 0.00, 1.7203, 1.7386}, // one workgroup per CU (4096^3)
-    {"mfma_128x128x32_w2x2k2d", 0.00, 5.39, 1.8261, 1.7742},
-    {"mfma16_64x128x32_w4x2k1d", 0.70, 1.25, 1.9955, 1.7866},
-    {"mfma16_64x64x64_w4x1k2d", 1.50, 1.09, 2.0556, 1.8173}, // 1024^3, 3072^3
-    {"mfma16_64x64x32_w4x1k1d", 0.30, 0.48, 2.7419, 1.8653}, // GPT-2 QKV and MLP-up
-    {"mfma_32x32x64_w1x1k4d", 1.95, 0.84, 4.7050, 2.2238}, // GPT-2 MLP-down
-    {"mfma16_16x16x128_w1x1k4d", 2.24, 0.00, 19.4973, 4.3872}, // 256^3
-    {"mfma16_16x64x128_w1x1k4d", 2.79, 0.22, 3.5509, 2.6575}, // 16- and 32-row products
-    {"mfma16_32x64x128_w2x1k4d", 1.35, 2.04, 2.0422, 2.0440},
-    {"mfma16_64x64x64_w2x2k2d", 1.46, 1.14, 2.0651, 1.8220},
-    {"mfma_64x128x32_w2x2k2d", 0.41, 2.39, 2.0202, 1.7895},
-    {"mfma_64x64x64_w2x2k4d", 0.33, 3.93, 2.1330, 1.9589},
-    {"mfma16_128x64x32_w8x1k1d", 0.57, 1.49, 2.0763, 1.8275},
-    {"mfma_64x64x32_w2x2k2d", 0.00, 1.99, 2.7448, 1.9717},
-    {"mfma16_64x16x64_w4x1k1d", 2.31, 0.00, 4.5801, 2.7833},
-    {"mfma16_16x16x256_w1x1k4d", 2.36, 0.71, 9.3849, 3.8645}, // 16-wide products
-    {"mfma16_16x16x128_w1x1k4p2d", 2.98, 0.25, 8.9629, 3.9316},
-    {"mfma16_32x32x128_w2x2k2d", 2.16, 0.81, 2.8215, 2.2516}, // 512^3, 32- and 64-wide products
+    {"mfma_256x256x32_w2x4d", 0.00, 10.68, 1.7024, 1.7316}, // one workgroup per CU (4096^3)
+    {"mfma_128x128x32_w2x2k2d", 0.00, 5.53, 1.8246, 1.7719},
+    {"mfma16_64x128x32_w4x2k1d", 0.56, 1.63, 1.9927, 1.7666},
+    {"mfma16_64x64x64_w4x1k2d", 1.28, 1.32, 2.0562, 1.8045}, // 1024^3, 3072^3
+    {"mfma16_64x64x32_w4x1k1d", 0.08, 0.86, 2.7331, 1.8368}, // GPT-2 MLP-up
+    {"mfma_32x32x64_w1x1k4d", 2.02, 0.84, 4.6692, 2.1984}, // GPT-2 MLP-down
+    {"mfma16_16x16x128_w1x1k4d", 2.15, 0.50, 16.3796, 2.7659},
+    {"mfma16_16x64x128_w1x1k4d", 2.34, 0.70, 3.5422, 2.4972}, // 16- and 32-row products
+    {"mfma16_32x64x128_w2x1k4d", 0.99, 2.40, 2.0417, 2.0110},
+    {"mfma16_64x64x64_w2x2k2d", 1.26, 1.35, 2.0657, 1.8103},
+    {"mfma_64x128x32_w2x2k2d", 0.70, 2.33, 2.0154, 1.7883},
+    {"mfma_64x64x64_w2x2k4d", 0.20, 4.07, 2.1338, 1.9515},
+    {"mfma16_128x64x32_w8x1k1d", 0.45, 1.61, 2.0761, 1.8242},
+    {"mfma_64x64x32_w2x2k2d", 0.00, 2.00, 2.7466, 1.9709},
+    {"mfma16_64x16x64_w4x1k1d", 2.09, 0.27, 4.5657, 2.7117},
+    {"mfma16_16x16x256_w1x1k4d", 1.99, 0.87, 10.9830, 3.5898}, // 256^3, 16-wide products
+    {"mfma16_16x16x128_w1x1k4p2d", 2.66, 0.49, 9.5499, 3.4119},
+    {"mfma16_32x32x128_w2x2k2d", 1.99, 0.99, 2.8169, 2.2152}, // 512^3, 32- and 64-wide products
+    {"mfma_32x96x64_w1x1k4d", 3.32, 2.26, 2.5438, 2.1241},
+    {"mfma16_32x96x32_w2x2k1d", 1.70, 0.36, 3.8224, 2.3231}, // GPT-2 QKV, 1536^3
+    {"mfma16_32x96x64_w2x2k2d", 2.09, 1.14, 2.8095, 2.2418},
+    {"mfma16_64x96x64_w4x2k1d", 2.02, 1.26, 2.4321, 2.1043},
 };
 const Candidate kUnalignedCandidates[] = {
     {"mfma_256x256x32_w2x4d", 5.94, 0.00, 2.0225, 2.0671},
@@ -308,6 +315,10 @@ const Candidate kUnalignedCandidates[] = {
     {"mfma16_16x16x256_w1x1k4d", 2.06, 0.19, 17.2871, 5.6646},
     {"mfma16_16x16x128_w1x1k4p2d", 3.91, 0.51, 4.4454, 5.5433},
     {"mfma16_16x16x128_w1x1k4d", 2.77, 0.21, 14.6886, 5.5336},
+    {"mfma_32x96x64_w1x1k4d", 2.30, 4.28, 4.0505, 2.8843},
+    {"mfma16_32x96x32_w2x2k1d", 2.87, 0.49, 4.2756, 2.6846}, // GPT-2 QKV one short, 1535^3
+    {"mfma16_32x96x64_w2x2k2d", 1.90, 1.94, 3.1783, 2.5940},
+    {"mfma16_64x96x64_w4x2k1d", 0.00, 1.21, 3.5439, 2.5614},
 };
 const Candidate kSkCandidates[] = {
     {"sk_128x128x32_w2x2k2p2", 19.09, 0.00, 1.8743, 1.8743},

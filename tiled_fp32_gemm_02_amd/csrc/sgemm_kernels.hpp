@@ -248,16 +248,23 @@ typedef __attribute__((address_space(3))) void lds_void;
 // permutation, the two halves of the banks) the chunks are XORed with ((r >> 3) & 1) << 2
 // instead: rows 4 apart alternate halves through the permutation, rows 8 apart alternate
 // 16-column groups through the XOR, so the four rows again meet four distinct groups.
-template <int TR, int TC, int NT, bool KCONTIG, int VW, bool Q16 = false>
+//
+// Panels (PW < TC, m- or n-contiguous tiles only): rows of 3 * 2^j floats (48, 96) have no
+// such swizzle, so the tile is kept as TC / PW panels of TR rows x PW columns, one after
+// the other, each laid out as a TR x PW tile of its own. A read of 16 or 32 consecutive
+// columns that stays inside one panel then meets the banks exactly as in a PW-wide tile.
+template <int TR, int TC, int NT, bool KCONTIG, int VW, bool Q16 = false, int PW = TC>
 struct TileDMA {
-    static constexpr int CPR = TC / 4;
+    static constexpr int NP = TC / PW;                  // panels
+    static constexpr int CPR = PW / 4;                  // chunks per row of a panel
+    static constexpr int PSIZE = TR * PW;
     static constexpr int SLOTS = TR * TC / VW;
     static constexpr int CH = SLOTS / NT;               // copy instructions per thread
     static constexpr int SIZE = TR * TC;
     static_assert(VW == 4 || VW == 1, "16- or 4-byte copies");
     static_assert(NT % 64 == 0 && SLOTS % NT == 0, "whole copy instructions per wave");
-    static_assert(KCONTIG ? (CPR == 4 || CPR == 8 || CPR % 16 == 0) : (CPR == 4 || CPR == 8 || CPR % 16 == 0),
-                  "slot swizzle needs these row lengths");
+    static_assert(TC % PW == 0 && (NP == 1 || !KCONTIG), "whole panels, along m or n only");
+    static_assert(CPR == 4 || CPR == 8 || CPR % 16 == 0, "slot swizzle needs these row lengths");
 
     static constexpr bool ROWPERM = !KCONTIG && CPR == 8;
     // Rows of 16 floats (a 16-wide tile, read by 16x16-block code) fill a quarter of the
@@ -283,16 +290,22 @@ struct TileDMA {
     }
     __host__ __device__ __forceinline__ static int elem(int r, int col)
     {
-        return 4 * (prow(r) * CPR + ((col >> 2) ^ swz(r))) + (col & 3);
+        if constexpr (NP == 1) {
+            return 4 * (prow(r) * CPR + ((col >> 2) ^ swz(r))) + (col & 3);
+        } else {
+            const int p = col / PW, c = col % PW;
+            return p * PSIZE + 4 * (prow(r) * CPR + ((c >> 2) ^ swz(r))) + (c & 3);
+        }
     }
 
     // Row and column, inside the tile, of the first float that copy c brings to this lane.
     __host__ __device__ __forceinline__ static void where(int c, int tid, int &r, int &col)
     {
         const int f = ((tid >> 6) * 64 + c * NT + (tid & 63)) * VW;   // its LDS position
-        r = prow(f / TC);
-        const int cl = f % TC;
-        col = 4 * ((cl >> 2) ^ swz(r)) + (cl & 3);
+        const int p = NP == 1 ? 0 : f / PSIZE, fp = NP == 1 ? f : f % PSIZE;
+        r = prow(fp / PW);
+        const int cl = fp % PW;
+        col = p * PW + 4 * ((cl >> 2) ^ swz(r)) + (cl & 3);
     }
 
     // This lane's share of every copy of the tile, fixed for the whole K loop: per copy
@@ -447,7 +460,9 @@ struct MfmaBlock<16> {
 //  - m / n: an operand stored m- or n-contiguous (A transposed, B plain) has the
 //    wave's blocks along that dimension interleaved, block b index c <-> wave index
 //    c*T + b (T blocks), so lane l reads T consecutive values for one k in one read,
-//    and for B writes T consecutive columns of C.
+//    and for B writes T consecutive columns of C. For plain B with T = 3 or 6 (wave
+//    tiles 48 or 96 wide) the blocks stay side by side and each is read one float per
+//    lane, from a B tile kept in 32- or 16-wide panels (TileDMA).
 // ---------------------------------------------------------------------------------
 // One BM x BN tile of op(A) op(B) on matrix cores: the operand loaders, the LDS ring and
 // the MFMA loop over a range of K-tiles (product), and the C update (epilogue). The
@@ -469,17 +484,23 @@ struct MfmaTile {
     static constexpr int KSLICE = BK / WGK;                    // k per stage handled by one wave group
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
     static constexpr int TM = WTM / MB, TN = WTN / MB;         // blocks per wave
+    // B's blocks side by side in the wave tile (lane column li of block b is wave column
+    // b*MB + li): always for transposed B, and for plain B when a lane's TN columns cannot
+    // be one 1-, 2- or 4-float read (TN = 3 or 6); otherwise they are interleaved.
+    static constexpr bool BSIDE = TB || !(TN == 1 || TN == 2 || TN == 4);
+    // Panel width of a plain B tile in LDS: rows of 3 * 2^j floats are split into 32- or
+    // 16-wide panels (TileDMA), which the side-by-side blocks read one panel at a time.
+    static constexpr int BPW = (TB || BN % 64 == 0 || BN == 16 || BN == 32) ? (TB ? BK : BN) : (BN % 32 == 0 ? 32 : 16);
     using AIO = typename std::conditional<USE_DMA,
                                           TileDMA<TA ? BK : BM, TA ? BM : BK, NT, !TA, VW, MB == 16 && TM == 1>,
                                           TileIO<TA ? BK : BM, TA ? BM : BK, NT>>::type;
     using BIO = typename std::conditional<USE_DMA,
-                                          TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB, VW, MB == 16 && TN == 1>,
+                                          TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB, VW, MB == 16 && (TN == 1 || BSIDE), BPW>,
                                           TileIO<TB ? BN : BK, TB ? BK : BN, NT>>::type;
     static constexpr int STAGE = AIO::SIZE + BIO::SIZE;
     static constexpr int NSTAGE = USE_DMA ? PF + 1 : 2;     // LDS stages in the ring
     static_assert(WTM % MB == 0 && WTN % MB == 0, "wave tile must be whole blocks");
     static_assert(!TA || TM == 1 || TM == 2 || TM == 4, "interleaved m blocks read 1, 2 or 4 floats");
-    static_assert(TB || TN == 1 || TN == 2 || TN == 4, "interleaved n blocks read 1, 2 or 4 floats");
     static_assert(BK % (KGRP * WGK) == 0, "each wave group consumes k in whole groups");
     static constexpr int RED = (WGK - 1) * BM * BN;         // partial sums of groups 1..WGK-1
     static constexpr int SMEM = NSTAGE * STAGE > RED ? NSTAGE * STAGE : RED;
@@ -575,7 +596,7 @@ struct MfmaTile {
         // a*MB + li (blocks side by side), transposed A rows li*TM + a (interleaved);
         // likewise for B columns with the roles swapped.
         const int a_idx = wm * WTM + (TA ? li * TM : li);
-        const int b_idx = wn * WTN + (TB ? li : li * TN);
+        const int b_idx = wn * WTN + (BSIDE ? li : li * TN);
 
         // One stage: KSLICE/KGRP groups of KGRP k values, 4 matrix steps each.
         auto compute = [&](int st) __attribute__((always_inline)) {
@@ -610,6 +631,10 @@ struct MfmaTile {
     #pragma unroll
                         for (int b = 0; b < TN; ++b)
                             bv[b] = bf[b][s];
+                    } else if constexpr (BSIDE) {
+    #pragma unroll
+                        for (int b = 0; b < TN; ++b)
+                            bv[b] = Bs[BIO::elem(k, b_idx + b * MB)];
                     } else {
                         lds_read<TN>(&Bs[BIO::elem(k, b_idx)], bv);
                     }
@@ -652,6 +677,12 @@ struct MfmaTile {
                     for (int s = 0; s < 4; ++s)
                         fb[buf][s][b] = v[s];
                 }
+            } else if constexpr (BSIDE) {
+    #pragma unroll
+                for (int s = 0; s < 4; ++s)
+    #pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        fb[buf][s][b] = Bs[BIO::elem(kg + s, b_idx + b * MB)];
             } else {
     #pragma unroll
                 for (int s = 0; s < 4; ++s)
@@ -831,12 +862,12 @@ struct MfmaTile {
         const int lane = tid & 63, wave = tid >> 6;
         const int wm = (wave % (WGM * WGN)) / WGN, wn = wave % WGN;
         const int li = lane % MB, lg = lane / MB;
-        const int b_idx = wn * WTN + (TB ? li : li * TN);
+        const int b_idx = wn * WTN + (BSIDE ? li : li * TN);
         // Epilogue: C = act(alpha*acc + beta*C + bias), C unread when beta == 0. One block
         // row at a time: all of the block's reads of C are issued before the first is used,
         // so the block waits out one memory round trip (two with EB = 8) rather than one per
-        // entry. Lane columns: TN consecutive ones (plain B), or one per MB-column block
-        // (transposed B). Rows: those of accumulator element e, see MfmaBlock.
+        // entry. Lane columns: TN consecutive ones (interleaved blocks), or one per MB-column
+        // block (side by side). Rows: those of accumulator element e, see MfmaBlock.
         const float alpha = p.alpha, beta = p.beta;
         const float *bias = p.bias;
         const int act = p.act;
@@ -844,11 +875,11 @@ struct MfmaTile {
         const bool full = !EDGE || (m0 + BM <= M && n0 + BN <= N);   // whole tile inside C
         // 128- or 64-bit accesses of a lane's TN consecutive columns: aligned, and (N % 4 == 0,
         // first column a multiple of TN) the group is either wholly inside C or wholly out.
-        constexpr bool VCOL = VEC && !TB && (TN == 2 || TN == 4);
+        constexpr bool VCOL = VEC && !BSIDE && (TN == 2 || TN == 4);
         int gc[TN];
     #pragma unroll
         for (int b = 0; b < TN; ++b)
-            gc[b] = n0 + b_idx + (TB ? MB * b : b);
+            gc[b] = n0 + b_idx + (BSIDE ? MB * b : b);
         float bj[TN];
     #pragma unroll
         for (int b = 0; b < TN; ++b)
