@@ -265,9 +265,9 @@ struct Candidate {
 // 16384 x 16 x 16384 (19%), 16 x 16384 x 16384 (8%) and 8192 x 128 x 8192 (6%). Candidates were chosen by dropping, one at a time, those
 // whose removal improved the picks. Unaligned (rows only 4-byte aligned): 24 odd-sized shapes
 // (255^3 ... 6143^3, 2999^3, 511 x 4095 x 4095, 1000 x 1537 x 777, the GPT-2 layers one
-// short in each dimension, long-K and skinny ones); picks average within 0.5% of the
-// fastest, the worst 3.3% (2559^3), and the ragged 1000 x 1537 x 777 and the first two
-// GPT-2 layers get the fastest (the third is 2.8% off).
+// short in each dimension, long-K and skinny ones); picks average within 0.4% of the
+// fastest, the worst 3.3% (2559^3), and the ragged 1000 x 1537 x 777 and the three GPT-2
+// layers get the fastest.
 const Candidate kCandidates[] = {
     {"mfma_256x256x32_w2x4d", 0.00, 10.68, 1.7024, 1.7316}, // one workgroup per CU (4096^3)
     {"mfma_128x128x32_w2x2k2d", 0.00, 5.53, 1.8246, 1.7719},
@@ -319,6 +319,7 @@ const Candidate kUnalignedCandidates[] = {
     {"mfma16_32x96x32_w2x2k1d", 2.87, 0.49, 4.2756, 2.6846}, // GPT-2 QKV one short, 1535^3
     {"mfma16_32x96x64_w2x2k2d", 1.90, 1.94, 3.1783, 2.5940},
     {"mfma16_64x96x64_w4x2k1d", 0.00, 1.21, 3.5439, 2.5614},
+    {"mfma16_32x96x128_w2x2k4d", 0.41, 4.50, 2.6868, 2.6500}, // GPT-2 MLP-down one short
 };
 const Candidate kSkCandidates[] = {
     {"sk_128x128x32_w2x2k2p2", 19.09, 0.00, 1.8743, 1.8743},
