@@ -594,7 +594,7 @@ struct MfmaTile {
 
         // This lane's first row of A / column of B inside the tile: plain A rows are
         // a*MB + li (blocks side by side), transposed A rows li*TM + a (interleaved);
-        // likewise for B columns with the roles swapped.
+        // B columns likewise, side by side or interleaved (BSIDE).
         const int a_idx = wm * WTM + (TA ? li * TM : li);
         const int b_idx = wn * WTN + (BSIDE ? li : li * TN);
 
@@ -711,28 +711,46 @@ struct MfmaTile {
             // Inside a step, group g+1's fragments are read while group g is multiplied; the
             // last group is multiplied after the barrier, while group 0 of the next stage
             // is read (past the last step that read is of a stage nobody uses; harmless).
-            static_assert(NG % 2 == 0, "fragment buffers alternate within a stage");
+            // The two fragment buffers alternate group by group across the steps: a step whose
+            // group 0 sits in buffer P leaves the next step's group 0 in buffer (NG + P) % 2, so
+            // with an odd number of groups per stage the steps alternate P = 0, 1 (the loop is
+            // unrolled by two to keep the buffer indices compile-time constants).
             constexpr int COPIES = AIO::CH + BIO::CH;       // copy instructions per thread per tile
+            auto step = [&](int t, auto parity) __attribute__((always_inline)) {
+                constexpr int P = decltype(parity)::value;
+                const int ahead = t + PF < nk ? t + PF : nk - 1;
+                copy_tile(ahead * BK, (t + PF) % NSTAGE);
+                const int st = t % NSTAGE;
+    #pragma unroll
+                for (int g = 0; g + 1 < NG; ++g) {
+                    read_frag(st, g + 1, (g + 1 + P) & 1);
+                    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+                    mma_frag((g + P) & 1);
+                }
+                copy_barrier<(PF - 1) * COPIES>();
+                read_frag((t + 1) % NSTAGE, 0, (NG + P) & 1);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_frag((NG - 1 + P) & 1);
+            };
+            using even = std::integral_constant<int, 0>;
+            using odd = std::integral_constant<int, 1>;
     #pragma unroll
             for (int q = 0; q < PF; ++q)
                 copy_tile((q < nk ? q : nk - 1) * BK, q);
             wait_vmcnt<0>();
             __syncthreads();
             read_frag(0, 0, 0);
-            for (int t = 0; t < nk; ++t) {
-                const int ahead = t + PF < nk ? t + PF : nk - 1;
-                copy_tile(ahead * BK, (t + PF) % NSTAGE);
-                const int st = t % NSTAGE;
-    #pragma unroll
-                for (int g = 0; g + 1 < NG; ++g) {
-                    read_frag(st, g + 1, (g + 1) & 1);
-                    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-                    mma_frag(g & 1);
+            if constexpr (NG % 2 == 0) {
+                for (int t = 0; t < nk; ++t)
+                    step(t, even{});
+            } else {
+                int t = 0;
+                for (; t + 1 < nk; t += 2) {
+                    step(t, even{});
+                    step(t + 1, odd{});
                 }
-                copy_barrier<(PF - 1) * COPIES>();
-                read_frag((t + 1) % NSTAGE, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-                mma_frag(1);
+                if (t < nk)
+                    step(t, even{});
             }
             wait_vmcnt<0>();    // no copy may still write LDS once it is reused or released
         } else if constexpr (PF == 1) {
