@@ -153,6 +153,34 @@ int sgemm_general(int config, int opA, int opB, int M, int N, int K, float alpha
                   void *stream);
 
 /*
+ * General-stride form: C <- act(alpha * A * B + beta * C + bias) on operands given by a row
+ * and a column stride each (in floats):
+ *   A(i,k) = A[i*rsA + k*csA], B(k,j) = B[k*rsB + j*csB], C(i,j) = C[i*rsC + j*csC].
+ * The GPT-2 post's kernel takes operands with dynamic sizes, strides and offsets, so that
+ * sliced and transposed views run without copies ("GPU Target - GPT-2 on the GPU",
+ * section "Tiled matrix multiplication"); this is that form. Strides of A and B may be any
+ * value >= 0 (0 repeats a row or column); C's must give distinct entries distinct
+ * addresses (csC >= 1 and rsC >= (N-1)*csC + 1, or rsC >= 1 and csC >= (M-1)*rsC + 1).
+ * Layouts with a unit stride in one dimension (the other at least the extent it spans)
+ * run the stored-matrix kernels with the automatic choice, as sgemm_bias_act would; a
+ * column-major C with no bias runs as the transposed product; every other layout runs a
+ * register-staged tile kernel that reads and writes float by float. C must not overlap A
+ * or B. No stream-K; nothing is allocated; results within the same bound as
+ * sgemm_bias_act.
+ *
+ * Arguments by position: 1 M, 2 N, 3 K, 4 alpha, 5 A, 6 rsA, 7 csA, 8 B, 9 rsB, 10 csB,
+ * 11 beta, 12 C, 13 rsC, 14 csC, 15 bias, 16 act, 17 stream. Returns -i for invalid
+ * argument i (a C window whose entries would share addresses is reported as 13), 0 on
+ * success, SGEMM_ERROR_TOO_LARGE past the launch limits, or a positive hipError_t.
+ */
+int sgemm_strided(int M, int N, int K, float alpha,
+                  const float *A, long long rsA, long long csA,
+                  const float *B, long long rsB, long long csB,
+                  float beta, float *C, long long rsC, long long csC,
+                  const float *bias, int act,
+                  void *stream);
+
+/*
  * Strided-batched form: for b in [0, batch), C_b <- alpha * A_b * B_b + beta * C_b with
  * A_b = A + b*strideA, B_b = B + b*strideB, C_b = C + b*strideC (strides in floats).
  * All batches share M, N, K, the leading dimensions and the scalars. The batched

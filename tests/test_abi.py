@@ -497,3 +497,38 @@ def test_workspace_cache_does_not_deadlock(monkeypatch):
     assert _Stream.synced == 1               # the zero fill is complete before the buffer is used
     assert sg.workspace_for() is out[0]      # cached
     assert _Stream.synced == 1
+
+
+# sgemm_strided: M N K alpha A rsA csA B rsB csB beta C rsC csC bias act stream
+_STRIDED_OK = (4, 5, 3, 1.0, BAD, 7, 2, BAD, 11, 3, 0.5, BAD, 20, 2, None, 0, None)
+
+
+@pytest.mark.parametrize("pos,value,code", [
+    (0, -1, -1), (1, -1, -2), (2, -1, -3),
+    (4, None, -5), (5, -1, -6), (6, -2, -7), (7, None, -8), (8, -1, -9), (9, -3, -10),
+    (11, None, -12), (12, -1, -13), (13, -1, -14), (15, 2, -16),
+    # C windows whose entries would share addresses: rows 2 floats apart with 5 columns 2 apart
+    (12, 8, -13),
+    # a column stride of 0 for C with N > 1
+    (13, 0, -13),
+])
+def test_strided_invalid_arguments(pos, value, code):
+    args = list(_STRIDED_OK)
+    args[pos] = value
+    assert sg.sgemm_strided(*args) == code
+
+
+def test_strided_checks_and_quick_returns():
+    ok = list(_STRIDED_OK)
+    # unread operands may be anything on the quick returns; M or N zero launches nothing
+    assert sg.sgemm_strided(0, 5, 3, 1.0, None, -0, 0, None, 0, 0, 0.0, None, 0, 0, None, 0, None) == 0
+    assert sg.sgemm_strided(4, 0, 3, 1.0, None, 0, 0, None, 0, 0, 0.0, None, 0, 0, None, 0, None) == 0
+    # strides of 0 are valid for A and B (a repeated row or column); column-major C is valid
+    a = [4, 5, 3, 1.0, BAD, 0, 1, BAD, 1, 0, 0.0, None, 1, 4, None, 0, None]
+    assert sg.sgemm_strided(*a) == -12    # C null with M, N > 0: rejected after A's and B's strides passed
+    ok[12], ok[13] = 1, 4             # column-major C (rows 1 apart, columns M = 4 apart): accepted
+    ok[11] = None
+    assert sg.sgemm_strided(*ok) == -12
+    # M == 1 or N == 1: only the stride that walks the window must be positive
+    assert sg.sgemm_strided(1, 5, 3, 1.0, BAD, 0, 0, BAD, 0, 0, 0.0, BAD, 0, 0, None, 0, None) == -14
+    assert sg.sgemm_strided(4, 1, 3, 1.0, BAD, 0, 0, BAD, 0, 0, 0.0, BAD, 0, 7, None, 0, None) == -13

@@ -44,7 +44,7 @@ __all__ = [
     "check", "SgemmError", "SGEMM_ERROR_TOO_LARGE", "SGEMM_ERROR_BAD_CONFIG", "SGEMM_OP_N", "SGEMM_OP_T",
     "SGEMM_ACT_NONE", "SGEMM_ACT_GELU_TANH", "SGEMM_ERROR_WORKSPACE", "sgemm_general_ws", "sgemm_workspace_size",
     "sgemm_select_config_ws", "workspace_for", "sgemm_strided_batched_op", "sgemm_strided_batched_general",
-    "sgemm_select_config_general", "sgemm_general_noalloc", "SGEMM_NOALLOC_SCRATCH_BYTES",
+    "sgemm_select_config_general", "sgemm_general_noalloc", "SGEMM_NOALLOC_SCRATCH_BYTES", "sgemm_strided",
 ]
 
 SGEMM_ERROR_TOO_LARGE = -100
@@ -82,6 +82,10 @@ _SIGS = {
     "sgemm_general_noalloc": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int,
                                              ctypes.c_float, _fp, ctypes.c_int, _fp, ctypes.c_int, _fp]),
+    "sgemm_strided": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp, ctypes.c_longlong, ctypes.c_longlong,
+        _fp, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_float, _fp, ctypes.c_longlong, ctypes.c_longlong,
+        _fp, ctypes.c_int, _fp]),
     "sgemm_workspace_size": (ctypes.c_size_t, [ctypes.c_int]),
     "sgemm_select_config_ws": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, _fp,
                                               ctypes.c_int, _fp, ctypes.c_int, _fp, ctypes.c_int, ctypes.c_size_t]),
@@ -203,6 +207,12 @@ def sgemm_general_noalloc(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta
 SGEMM_NOALLOC_SCRATCH_BYTES = 65536 + 2 * 256 * 128 * 128 * 4
 
 
+def sgemm_strided(M, N, K, alpha, A, rsA, csA, B, rsB, csB, beta, C, rsC, csC, bias=None, act=SGEMM_ACT_NONE,
+                  stream=None) -> int:
+    return load().sgemm_strided(M, N, K, alpha, _addr(A), rsA, csA, _addr(B), rsB, csB, beta, _addr(C), rsC, csC,
+                                _addr(bias), act, _stream(stream))
+
+
 def sgemm_workspace_size(config: int = -1) -> int:
     return load().sgemm_workspace_size(config)
 
@@ -300,28 +310,33 @@ def _check_matrix(t, name):
         raise ValueError(f"{name} must be a GPU tensor")
 
 
-def _row_major_ld(t, name):
-    """Leading dimension of a row-major matrix view (unit column stride)."""
-    _check_matrix(t, name)
+def _stored_form(t):
+    """(op, ld) when an operand view is a stored row-major matrix read as stored
+    (SGEMM_OP_N: unit column stride, row stride at least the row length) or in place as a
+    transpose (SGEMM_OP_T: unit row stride, column stride at least the column length);
+    None for any other layout (no unit stride, or rows that overlap in memory)."""
     rows, cols = t.shape
-    if cols > 1 and t.stride(1) != 1:
-        raise ValueError(f"{name} must be row-major with unit column stride (got strides {tuple(t.stride())})")
-    ld = t.stride(0) if rows > 1 else max(cols, 1)
-    return max(ld, cols, 1)
+    s0, s1 = t.stride()
+    if cols <= 1 or s1 == 1:
+        if rows <= 1:
+            return SGEMM_OP_N, max(cols, 1)
+        if s0 >= max(cols, 1):
+            return SGEMM_OP_N, s0
+    if rows <= 1 or s0 == 1:
+        if cols <= 1:
+            return SGEMM_OP_T, max(rows, 1)
+        if s1 >= max(rows, 1):
+            return SGEMM_OP_T, s1
+    return None
 
 
-def _operand(t, name):
-    """(op, ld) for an operand view: a row-major view is read as stored (SGEMM_OP_N);
-    a transposed view of a row-major matrix (unit row stride) is read in place as a
-    transpose (SGEMM_OP_T), with the stored matrix's row stride as ld."""
-    _check_matrix(t, name)
+def _row_major_c(t):
+    """ldc when C is a row-major view whose rows do not overlap; None otherwise."""
+    form = _stored_form(t)
     rows, cols = t.shape
-    if cols <= 1 or t.stride(1) == 1:
-        return SGEMM_OP_N, _row_major_ld(t, name)
-    if rows <= 1 or t.stride(0) == 1:
-        ld = t.stride(1) if cols > 1 else max(rows, 1)
-        return SGEMM_OP_T, max(ld, rows, 1)
-    raise ValueError(f"{name} needs a unit stride in one dimension (got strides {tuple(t.stride())})")
+    if form is None or (form[0] == SGEMM_OP_T and cols > 1):
+        return None
+    return form[1] if rows > 1 else max(cols, 1)
 
 
 _ACTS = {None: SGEMM_ACT_NONE, "none": SGEMM_ACT_NONE, "gelu_tanh": SGEMM_ACT_GELU_TANH}
@@ -358,18 +373,20 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None, confi
          act=None, workspace="auto"):
     """C <- act(alpha*A@B + beta*C + bias) on GPU float32 tensors.
 
-    A is M x K, B is K x N and C is M x N. A and B may be row-major views or
-    transposed views (``x.t()``) of row-major matrices, read in place. C must be
-    row-major and may have a larger row stride. bias is a length-N float32 GPU
-    vector or None; act is None, "none" or "gelu_tanh". When C is None a new
-    M x N tensor is allocated (then beta must be 0). workspace is "auto" (the cached
-    buffer of ``workspace_for()`` for this device and stream), None (no stream-K), or a
-    zero-initialised uint8 GPU tensor of the caller's. Returns C.
+    A is M x K, B is K x N and C is M x N, any strided views (slices, transposes, expanded
+    dimensions for A and B), read and written in place. Row-major views and transposed
+    views of row-major matrices run the stored-matrix kernels (with stream-K where the
+    workspace allows); other layouts run the general-stride entry point, sgemm_strided
+    (then config must be -1). bias is a length-N float32 GPU vector or None; act is
+    None, "none" or "gelu_tanh". When C is None a new M x N tensor is allocated (then
+    beta must be 0). workspace is "auto" (the cached buffer of ``workspace_for()`` for
+    this device and stream), None (no stream-K), or a zero-initialised uint8 GPU tensor
+    of the caller's. Returns C.
     """
     import torch
 
-    opA, lda = _operand(A, "A")
-    opB, ldb = _operand(B, "B")
+    _check_matrix(A, "A")
+    _check_matrix(B, "B")
     M, K = A.shape
     if B.shape[0] != K:
         raise ValueError(f"Size error: A is {tuple(A.shape)} and B is {tuple(B.shape)}; inner sizes differ")
@@ -385,11 +402,19 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, stream=None, confi
         if beta != 0.0:
             raise ValueError("beta != 0 needs an input C")
         C = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    ldc = _row_major_ld(C, "C")
+    _check_matrix(C, "C")
     if tuple(C.shape) != (M, N):
         raise ValueError(f"Size error: C is {tuple(C.shape)}, expected {(M, N)}")
     if stream is None:
         stream = torch.cuda.current_stream(A.device)
+    fa, fb, ldc = _stored_form(A), _stored_form(B), _row_major_c(C)
+    if fa is None or fb is None or ldc is None:
+        if config != -1:
+            raise ValueError("config applies to row-major or transposed views only; this layout runs sgemm_strided")
+        check(sgemm_strided(M, N, K, alpha, A, A.stride(0), A.stride(1), B, B.stride(0), B.stride(1), beta, C,
+                            C.stride(0), C.stride(1), bias, _ACTS[act], stream), "sgemm_strided")
+        return C
+    (opA, lda), (opB, ldb) = fa, fb
     ws = workspace_for(A.device, stream) if isinstance(workspace, str) and workspace == "auto" else workspace
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     check(sgemm_general_ws(config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, _ACTS[act],
@@ -410,13 +435,14 @@ def _batched_operand(t, name, allow_transposed=True):
     bsz, rows, cols = t.shape
     s0, s1, s2 = t.stride()
     sb = s0 if bsz > 1 else 0
-    if cols <= 1 or s2 == 1:
+    if (cols <= 1 or s2 == 1) and (rows <= 1 or s1 >= cols):
         ld = s1 if rows > 1 else max(cols, 1)
         return SGEMM_OP_N, max(ld, cols, 1), sb
-    if allow_transposed and (rows <= 1 or s1 == 1):
+    if allow_transposed and (rows <= 1 or s1 == 1) and (cols <= 1 or s2 >= rows):
         ld = s2 if cols > 1 else max(rows, 1)
         return SGEMM_OP_T, max(ld, rows, 1), sb
-    what = "a unit stride in one of its last two dimensions" if allow_transposed else "unit column stride"
+    what = ("a unit stride in one of its last two dimensions, rows that do not overlap" if allow_transposed
+            else "unit column stride and rows that do not overlap")
     raise ValueError(f"{name} needs {what} (got strides {tuple(t.stride())})")
 
 

@@ -483,6 +483,7 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     p.bias = bias; p.act = act;
     p.lda = lda; p.ldb = ldb; p.ldc = ldc;
     p.strideA = sA; p.strideB = sB; p.strideC = sC;
+    p.incA = p.incB = p.incC = 1;
 
     if (K == 0 || alpha == 0.0f) {
         // C <- act(beta*C + bias); A and B are not read.
@@ -538,6 +539,91 @@ int general(const int *pos, int config, int opA, int opB, int M, int N, int K, f
         return SGEMM_SUCCESS;
     return run(config, opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, bias, act, 1, ws,
                ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// General-stride operands: op(A)(i,k) = A[i*rsA + k*csA], B(k,j) = B[k*rsB + j*csB],
+// C(i,j) = C[i*rsC + j*csC]. Layouts the stored-matrix forms already cover (a unit stride in
+// one dimension, the other at least the extent it spans) run through them with the auto
+// choice; a column-major C without bias runs as the transposed product C^T = B^T A^T; every
+// other layout runs the general-stride tile kernel.
+
+// An operand of `rows` x `cols` with row stride rs and column stride cs as a stored-matrix
+// form: op SGEMM_OP_N with ld = rs, or SGEMM_OP_T with ld = cs. False if neither fits.
+bool as_stored(int rows, int cols, long long rs, long long cs, int &op, int &ld)
+{
+    const long long kMaxLd = 0x7fffffffLL;
+    if (cols <= 1) {                            // one column: element i at i*rs
+        op = SGEMM_OP_N;
+        if (rows <= 1) { ld = 1; return true; }
+        if (rs < 1 || rs > kMaxLd) return false;
+        ld = (int)rs;
+        return true;
+    }
+    if (rows <= 1) {                            // one row: element j at j*cs
+        if (cs == 1) { op = SGEMM_OP_N; ld = cols; return true; }
+        if (cs < 1 || cs > kMaxLd) return false;
+        op = SGEMM_OP_T; ld = (int)cs;         // stored as a cols x 1 column of stride cs
+        return true;
+    }
+    if (cs == 1 && rs >= cols && rs <= kMaxLd) { op = SGEMM_OP_N; ld = (int)rs; return true; }
+    if (rs == 1 && cs >= rows && cs <= kMaxLd) { op = SGEMM_OP_T; ld = (int)cs; return true; }
+    return false;
+}
+
+hipError_t launch_strided(const GemmArgs &p, hipStream_t s)
+{
+    // The register-staged 64 x 64 tile of two wave groups (mfma_64x64x32_w2x2k2's shape).
+    constexpr int BM = 64, BN = 64, BK = 32, WGM = 2, WGN = 2, WGK = 2, MB = 32, GROUP_M = 8;
+    const unsigned tiles = (((unsigned)p.M + BM - 1) / BM) * (((unsigned)p.N + BN - 1) / BN);
+    hipLaunchKernelGGL((sgemm_impl::sgemm_mfma_strided<BM, BN, BK, WGM, WGN, WGK, MB>), dim3(tiles),
+                       dim3(WGM * WGN * WGK * 64), 0, s, p, GROUP_M);
+    return hipGetLastError();
+}
+
+int strided(int M, int N, int K, float alpha, const float *A, long long rsA, long long csA, const float *B,
+            long long rsB, long long csB, float beta, float *C, long long rsC, long long csC, const float *bias,
+            int act, hipStream_t stream)
+{
+    if (M == 0 || N == 0)
+        return SGEMM_SUCCESS;
+    if (K == 0 || alpha == 0.0f || (csC == 1 || N == 1)) {
+        int opA = SGEMM_OP_N, opB = SGEMM_OP_N, lda = 1, ldb = 1, ldc = 1;
+        const bool quick = K == 0 || alpha == 0.0f;
+        const bool c_rows = (csC == 1 || N == 1) && (M == 1 || (rsC >= N && rsC <= 0x7fffffffLL));
+        if (c_rows)
+            ldc = M == 1 ? (N > 1 ? N : 1) : (int)rsC;
+        if (c_rows && (quick || (as_stored(M, K, rsA, csA, opA, lda) && as_stored(K, N, rsB, csB, opB, ldb))))
+            return run(-1, opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, bias, act, 1, nullptr,
+                       0, stream);
+    }
+    if (rsC == 1 && M > 1 && N > 1 && bias == nullptr) {
+        // Column-major C: its transpose is row-major, C^T = B^T A^T (the same sums, so the
+        // same results), with op(A) <- B^T and op(B) <- A^T.
+        int opA, opB, lda, ldb;
+        if (csC <= 0x7fffffffLL && as_stored(N, K, csB, rsB, opA, lda) && as_stored(K, M, csA, rsA, opB, ldb))
+            return run(-1, opA, opB, N, M, K, alpha, B, lda, 0, A, ldb, 0, beta, C, (int)csC, 0, nullptr, act, 1,
+                       nullptr, 0, stream);
+    }
+    GemmArgs p;
+    p.M = M; p.N = N; p.K = K;
+    p.alpha = alpha; p.beta = beta;
+    p.A = A; p.B = B; p.C = C;
+    p.bias = bias; p.act = act;
+    p.lda = rsA; p.ldb = rsB; p.ldc = rsC;
+    p.strideA = p.strideB = p.strideC = 0;
+    p.incA = csA; p.incB = csB; p.incC = csC;
+    hipError_t e;
+    if (K == 0 || alpha == 0.0f) {
+        const int gx = cdiv64(N, 256) < 64 ? (int)cdiv64(N, 256) : 64;
+        const int gy = M < 1024 ? M : 1024;
+        hipLaunchKernelGGL(sgemm_impl::sgemm_scale, dim3(gx, gy, 1), dim3(256, 1), 0, stream, p);
+        e = hipGetLastError();
+    } else {
+        if (cdiv64(M, 64) * cdiv64(N, 64) * 512ull > 0xFFFFFFFFull)
+            return SGEMM_ERROR_TOO_LARGE;
+        e = launch_strided(p, stream);
+    }
+    return e == hipSuccess ? 0 : (int)e;
 }
 
 static_assert(SGEMM_NOALLOC_SCRATCH_BYTES == kSkCounterBytes + 2ull * 256 * 128 * 128 * sizeof(float),
@@ -683,6 +769,39 @@ int sgemm_general_ws(int config, int opA, int opB, int M, int N, int K, float al
         return -16;
     return general(kPosFused, config, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, stream,
                    workspace, workspace_bytes);
+}
+
+int sgemm_strided(int M, int N, int K, float alpha, const float *A, long long rsA, long long csA, const float *B,
+                  long long rsB, long long csB, float beta, float *C, long long rsC, long long csC,
+                  const float *bias, int act, void *stream)
+{
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
+    if (reads_ab && A == nullptr) return -5;
+    if (rsA < 0) return -6;
+    if (csA < 0) return -7;
+    if (reads_ab && B == nullptr) return -8;
+    if (rsB < 0) return -9;
+    if (csB < 0) return -10;
+    if (M > 0 && N > 0 && C == nullptr) return -12;
+    if (rsC < 0) return -13;
+    if (csC < 0) return -14;
+    // Distinct entries of the M x N window at distinct addresses: one stride walks a row
+    // (or column) without reaching the next one. An empty window has no constraint.
+    if (M > 1 && N > 1) {
+        const bool rows = csC >= 1 && rsC >= (long long)(N - 1) * csC + 1;
+        const bool cols = rsC >= 1 && csC >= (long long)(M - 1) * rsC + 1;
+        if (!rows && !cols) return -13;
+    } else if (M > 1 && N == 1 && rsC < 1) {
+        return -13;
+    } else if (N > 1 && M == 1 && csC < 1) {
+        return -14;
+    }
+    if (act != SGEMM_ACT_NONE && act != SGEMM_ACT_GELU_TANH) return -16;
+    return strided(M, N, K, alpha, A, rsA, csA, B, rsB, csB, beta, C, rsC, csC, bias, act,
+                   static_cast<hipStream_t>(stream));
 }
 
 int sgemm_general_noalloc(int config, int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,

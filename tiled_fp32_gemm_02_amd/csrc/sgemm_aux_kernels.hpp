@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(256) sgemm_scale(GemmArgs p)
     // 64-bit indices: the strides would carry a 32-bit index past 2^31 for M or N near it.
     for (int64_t i = blockIdx.y * blockDim.y + threadIdx.y; i < p.M; i += gridDim.y * blockDim.y)
         for (int64_t j = blockIdx.x * blockDim.x + threadIdx.x; j < p.N; j += gridDim.x * blockDim.x) {
-            float *c = C + i * p.ldc + j;
+            float *c = C + i * p.ldc + j * p.incC;
             *c = finish(0.f, 0.f, p.beta, c, p.bias, (int)j, p.act);
         }
 }

@@ -63,6 +63,9 @@ struct GemmArgs {
     int act;                    // Act
     int64_t lda, ldb, ldc;
     int64_t strideA, strideB, strideC;  // per blockIdx.z (batched form); 0 otherwise
+    // Column strides of general-stride operands (sgemm_mfma_strided: A(i,k) = A[i*lda + k*incA],
+    // B(k,j) = B[k*ldb + j*incB], C(i,j) = C[i*ldc + j*incC]); 1 for every other kernel.
+    int64_t incA, incB, incC;
 };
 
 // ceil(a / b) for a >= 0, b >= 1, in unsigned arithmetic so that a near 2^31 does not overflow.
@@ -168,10 +171,11 @@ struct TileIO {
     // src points at the tile origin; rows/cols are how many rows and columns from the
     // origin lie inside the matrix. VEC: 128-bit loads (row starts 16-byte aligned and
     // the column extent a multiple of 4, so a chunk is wholly in or out); otherwise every
-    // float is checked. EDGE = false promises the whole tile is inside.
-    template <bool VEC, bool EDGE>
+    // float is checked. EDGE = false promises the whole tile is inside. STRIDED: the
+    // columns lie `inc` floats apart (a general-stride operand), read float by float.
+    template <bool VEC, bool EDGE, bool STRIDED = false>
     __device__ __forceinline__ static void load(floatx4 (&r)[CH], const float *__restrict__ src, int64_t ld,
-                                                int rows, int cols, int tid)
+                                                int rows, int cols, int tid, int64_t inc = 1)
     {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
@@ -179,8 +183,14 @@ struct TileIO {
             if (IDLE && idx >= CHUNKS)
                 break;
             const int rr = idx / CPR, cc = (idx % CPR) * 4;
-            const float *p = src + (int64_t)rr * ld + cc;
-            if (VEC) {
+            const float *p = src + (int64_t)rr * ld + (STRIDED ? (int64_t)cc * inc : (int64_t)cc);
+            if constexpr (STRIDED) {
+                const bool rok = rr < rows;
+                r[c].x = (!EDGE || (rok && cc + 0 < cols)) ? p[0] : 0.f;
+                r[c].y = (!EDGE || (rok && cc + 1 < cols)) ? p[inc] : 0.f;
+                r[c].z = (!EDGE || (rok && cc + 2 < cols)) ? p[2 * inc] : 0.f;
+                r[c].w = (!EDGE || (rok && cc + 3 < cols)) ? p[3 * inc] : 0.f;
+            } else if (VEC) {
                 if (!EDGE || (rr < rows && cc < cols))
                     r[c] = *reinterpret_cast<const floatx4 *>(p);
                 else
@@ -469,9 +479,12 @@ struct MfmaBlock<16> {
 // whole-tile kernel below runs product over all of K; the stream-K kernel runs it over
 // the K-tile ranges its workgroup owns.
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
-          bool EDGE, int MB = 32>
+          bool EDGE, int MB = 32, bool GS = false>
 struct MfmaTile {
     static_assert(PF == 1 || PF == 2, "K-tiles in flight ahead of the one being multiplied");
+    // GS: general-stride operands (column strides incA, incB, incC), loaded float by float
+    // through registers; A and B are then read as stored, whatever their strides.
+    static_assert(!GS || (!DMA && !TA && !TB && !VEC && EDGE), "general strides: staged, checked loads");
     static_assert(MB == 32 || MB == 16, "32x32 or 16x16 matrix blocks");
     using BLK = MfmaBlock<MB>;
     using acc_t = typename BLK::acc_t;
@@ -543,7 +556,13 @@ struct MfmaTile {
         // Global -> registers set `slot` for the K-tile starting kr after the range's first k
         // (zero outside the matrix).
         auto load_tile = [&](int kr, int slot) __attribute__((always_inline)) {
-            if constexpr (!USE_DMA) {
+            if constexpr (GS) {
+                const int k0 = kbase + kr;
+                AIO::template load<false, true, true>(ra[slot], A + (int64_t)m0 * lda + (int64_t)k0 * p.incA, lda,
+                                                      M - m0, K - k0, tid, p.incA);
+                BIO::template load<false, true, true>(rb[slot], B + (int64_t)k0 * ldb + (int64_t)n0 * p.incB, ldb,
+                                                      K - k0, N - n0, tid, p.incB);
+            } else if constexpr (!USE_DMA) {
                 const int k0 = kbase + kr;
                 if constexpr (TA)
                     AIO::template load<VEC, EDGE>(ra[slot], A + (int64_t)k0 * lda + m0, lda, K - k0, M - m0, tid);
@@ -889,6 +908,7 @@ struct MfmaTile {
         const float alpha = p.alpha, beta = p.beta;
         const float *bias = p.bias;
         const int act = p.act;
+        const int64_t incc = GS ? p.incC : 1;               // column stride of C
         const bool read_c = beta != 0.f, has_bias = bias != nullptr;
         const bool full = !EDGE || (m0 + BM <= M && n0 + BN <= N);   // whole tile inside C
         // 128- or 64-bit accesses of a lane's TN consecutive columns: aligned, and (N % 4 == 0,
@@ -930,7 +950,7 @@ struct MfmaTile {
                     } else {
     #pragma unroll
                         for (int b = 0; b < TN; ++b)
-                            cv[e][b] = (full || (gr < M && gc[b] < N)) ? crow[gc[b]] : 0.f;
+                            cv[e][b] = (full || (gr < M && gc[b] < N)) ? crow[gc[b] * incc] : 0.f;
                     }
                 }
             }
@@ -954,7 +974,7 @@ struct MfmaTile {
     #pragma unroll
                     for (int b = 0; b < TN; ++b)
                         if (full || (gr < M && gc[b] < N))
-                            crow[gc[b]] = out[b];
+                            crow[gc[b] * incc] = out[b];
                 }
             }
         }
@@ -968,6 +988,23 @@ __attribute__((amdgpu_waves_per_eu(MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, 
 sgemm_mfma(GemmArgs p, int group_m)
 {
     using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE, MB>;
+    __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
+    int tm, tn;
+    tile_coords(blockIdx.x, ceil_div(p.M, BM), ceil_div(p.N, BN), group_m, tm, tn);
+    typename T::acc_t acc[T::TM][T::TN];
+    if (T::product(p, smem, tm * BM, tn * BN, 0, ceil_div(p.K, BK), acc, threadIdx.x))
+        T::epilogue(p, tm * BM, tn * BN, acc, threadIdx.x);
+}
+
+// The same tile kernel on general-stride operands (any row and column strides of A, B
+// and C, zero included for A and B): register-staged, element-wise, checked loads.
+template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int MB>
+__global__ void __launch_bounds__(WGM * WGN * WGK * 64)
+__attribute__((amdgpu_waves_per_eu(MfmaTile<BM, BN, BK, WGM, WGN, WGK, 1, false, false, false, false, true, MB,
+                                            true>::WPE)))
+sgemm_mfma_strided(GemmArgs p, int group_m)
+{
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, 1, false, false, false, false, true, MB, true>;
     __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
     int tm, tn;
     tile_coords(blockIdx.x, ceil_div(p.M, BM), ceil_div(p.N, BN), group_m, tm, tn);
