@@ -259,10 +259,11 @@ struct Candidate {
 // batched ones at half weight (attention's 12-head products 1024 x 1024 x 64 and
 // 1024 x 64 x 1024, the first with K from 16 to 256, and 48 or 3 heads of other sizes),
 // whose short K loops set the per-round costs. With the candidates below the model picks,
-// on average, a configuration within 1.1% of the fastest of all those swept, and the
+// on average, a configuration within 1.4% of the fastest of all those swept, and the
 // fastest on 256^3, 1024^3, 1536^3, 4096^3, the three GPT-2 layers and the attention
-// scores (the attention values product 3.6% off); the worst misses are skinny products:
-// 16384 x 16 x 16384 (19%), 16 x 16384 x 16384 (8%) and 8192 x 128 x 8192 (6%). Candidates were chosen by dropping, one at a time, those
+// scores; the worst misses are 16384 x 16 x 16384 (19%), 768^3 (13%) and the attention
+// values product (10%), both fastest on mfma16_16x64x64_w1x1k4d, which the fit mispredicts
+// on small products and so is left out, and 16 x 16384 x 16384 (8%). Candidates were chosen by dropping, one at a time, those
 // whose removal improved the picks. Unaligned (rows only 4-byte aligned): 24 odd-sized shapes
 // (255^3 ... 6143^3, 2999^3, 511 x 4095 x 4095, 1000 x 1537 x 777, the GPT-2 layers one
 // short in each dimension, long-K and skinny ones); picks average within 0.4% of the
@@ -291,6 +292,7 @@ const Candidate kCandidates[] = {
     {"mfma16_32x96x32_w2x2k1d", 1.70, 0.36, 3.8224, 2.3231}, // GPT-2 QKV, 1536^3
     {"mfma16_32x96x64_w2x2k2d", 2.09, 1.14, 2.8095, 2.2418},
     {"mfma16_64x96x64_w4x2k1d", 2.02, 1.26, 2.4321, 2.1043},
+    {"mfma16_64x64x128_w4x1k4d", 0.00, 4.26, 1.9058, 1.7591}, // long K (1024 x 1024 x 8192, 1000 x 1000 x 4000)
 };
 const Candidate kUnalignedCandidates[] = {
     {"mfma_256x256x32_w2x4d", 5.94, 0.00, 2.0225, 2.0671},
@@ -320,6 +322,7 @@ const Candidate kUnalignedCandidates[] = {
     {"mfma16_32x96x64_w2x2k2d", 1.90, 1.94, 3.1783, 2.5940},
     {"mfma16_64x96x64_w4x2k1d", 0.00, 1.21, 3.5439, 2.5614},
     {"mfma16_32x96x128_w2x2k4d", 0.41, 4.50, 2.6868, 2.6500}, // GPT-2 MLP-down one short
+    {"mfma16_64x64x128_w4x1k4d", 0.20, 5.19, 2.3575, 2.3093}, // long K (999 x 999 x 3999)
 };
 const Candidate kSkCandidates[] = {
     {"sk_128x128x32_w2x2k2p2", 19.09, 0.00, 1.8743, 1.8743},
@@ -483,13 +486,15 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     p.bias = bias; p.act = act;
     p.lda = lda; p.ldb = ldb; p.ldc = ldc;
     p.strideA = sA; p.strideB = sB; p.strideC = sC;
-    p.incA = p.incB = p.incC = 1;
 
     if (K == 0 || alpha == 0.0f) {
         // C <- act(beta*C + bias); A and B are not read.
+        sgemm_impl::StridedArgs q;
+        static_cast<GemmArgs &>(q) = p;
+        q.incA = q.incB = q.incC = 1;
         const int gx = cdiv64(N, 256) < 64 ? (int)cdiv64(N, 256) : 64;
         const int gy = M < 1024 ? M : 1024;
-        hipLaunchKernelGGL(sgemm_impl::sgemm_scale, dim3(gx, gy, batch), dim3(256, 1), 0, stream, p);
+        hipLaunchKernelGGL(sgemm_impl::sgemm_scale, dim3(gx, gy, batch), dim3(256, 1), 0, stream, q);
         const hipError_t e = hipGetLastError();
         return e == hipSuccess ? 0 : (int)e;
     }
@@ -570,7 +575,7 @@ bool as_stored(int rows, int cols, long long rs, long long cs, int &op, int &ld)
     return false;
 }
 
-hipError_t launch_strided(const GemmArgs &p, hipStream_t s)
+hipError_t launch_strided(const sgemm_impl::StridedArgs &p, hipStream_t s)
 {
     // The register-staged 64 x 64 tile of two wave groups (mfma_64x64x32_w2x2k2's shape).
     constexpr int BM = 64, BN = 64, BK = 32, WGM = 2, WGN = 2, WGK = 2, MB = 32, GROUP_M = 8;
@@ -604,7 +609,7 @@ int strided(int M, int N, int K, float alpha, const float *A, long long rsA, lon
             return run(-1, opA, opB, N, M, K, alpha, B, lda, 0, A, ldb, 0, beta, C, (int)csC, 0, nullptr, act, 1,
                        nullptr, 0, stream);
     }
-    GemmArgs p;
+    sgemm_impl::StridedArgs p;
     p.M = M; p.N = N; p.K = K;
     p.alpha = alpha; p.beta = beta;
     p.A = A; p.B = B; p.C = C;

@@ -215,7 +215,7 @@ sgemm_valu(GemmArgs p, int group_m)
 
 // C = act(beta*C + bias) over the M x N window (C not read when beta == 0).
 // Grid-stride in both dimensions; blockIdx.z selects the batch.
-__global__ void __launch_bounds__(256) sgemm_scale(GemmArgs p)
+__global__ void __launch_bounds__(256) sgemm_scale(StridedArgs p)
 {
     float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
     // 64-bit indices: the strides would carry a 32-bit index past 2^31 for M or N near it.

@@ -63,8 +63,12 @@ struct GemmArgs {
     int act;                    // Act
     int64_t lda, ldb, ldc;
     int64_t strideA, strideB, strideC;  // per blockIdx.z (batched form); 0 otherwise
-    // Column strides of general-stride operands (sgemm_mfma_strided: A(i,k) = A[i*lda + k*incA],
-    // B(k,j) = B[k*ldb + j*incB], C(i,j) = C[i*ldc + j*incC]); 1 for every other kernel.
+};
+
+// Arguments of the general-stride kernels (and of the C-scaling kernel, which serves both
+// forms): the column strides as well (A(i,k) = A[i*lda + k*incA], B(k,j) = B[k*ldb + j*incB],
+// C(i,j) = C[i*ldc + j*incC]). The tile kernels keep the smaller GemmArgs.
+struct StridedArgs : GemmArgs {
     int64_t incA, incB, incC;
 };
 
@@ -533,7 +537,8 @@ struct MfmaTile {
     // Multiply K-tiles [kt0, kt1) of the tile at (m0, n0) into acc, which starts at zero;
     // tid_in is the thread's index in the workgroup. With WGK > 1 the groups' sums end up
     // in the waves of group 0; the other waves return false and hold nothing.
-    __device__ __forceinline__ static bool product(const GemmArgs &p, float *smem, int m0, int n0, int kt0,
+    template <class Args>
+    __device__ __forceinline__ static bool product(const Args &p, float *smem, int m0, int n0, int kt0,
                                                    int kt1, acc_t (&acc)[TM][TN], int tid_in)
     {
         const int M = p.M, N = p.N, K = p.K;
@@ -730,29 +735,7 @@ struct MfmaTile {
             // Inside a step, group g+1's fragments are read while group g is multiplied; the
             // last group is multiplied after the barrier, while group 0 of the next stage
             // is read (past the last step that read is of a stage nobody uses; harmless).
-            // The two fragment buffers alternate group by group across the steps: a step whose
-            // group 0 sits in buffer P leaves the next step's group 0 in buffer (NG + P) % 2, so
-            // with an odd number of groups per stage the steps alternate P = 0, 1 (the loop is
-            // unrolled by two to keep the buffer indices compile-time constants).
             constexpr int COPIES = AIO::CH + BIO::CH;       // copy instructions per thread per tile
-            auto step = [&](int t, auto parity) __attribute__((always_inline)) {
-                constexpr int P = decltype(parity)::value;
-                const int ahead = t + PF < nk ? t + PF : nk - 1;
-                copy_tile(ahead * BK, (t + PF) % NSTAGE);
-                const int st = t % NSTAGE;
-    #pragma unroll
-                for (int g = 0; g + 1 < NG; ++g) {
-                    read_frag(st, g + 1, (g + 1 + P) & 1);
-                    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-                    mma_frag((g + P) & 1);
-                }
-                copy_barrier<(PF - 1) * COPIES>();
-                read_frag((t + 1) % NSTAGE, 0, (NG + P) & 1);
-                __builtin_amdgcn_sched_barrier(0);
-                mma_frag((NG - 1 + P) & 1);
-            };
-            using even = std::integral_constant<int, 0>;
-            using odd = std::integral_constant<int, 1>;
     #pragma unroll
             for (int q = 0; q < PF; ++q)
                 copy_tile((q < nk ? q : nk - 1) * BK, q);
@@ -760,16 +743,53 @@ struct MfmaTile {
             __syncthreads();
             read_frag(0, 0, 0);
             if constexpr (NG % 2 == 0) {
-                for (int t = 0; t < nk; ++t)
-                    step(t, even{});
+                // Every stage starts with its group 0 in buffer 0.
+                for (int t = 0; t < nk; ++t) {
+                    const int ahead = t + PF < nk ? t + PF : nk - 1;
+                    copy_tile(ahead * BK, (t + PF) % NSTAGE);
+                    const int st = t % NSTAGE;
+    #pragma unroll
+                    for (int g = 0; g + 1 < NG; ++g) {
+                        read_frag(st, g + 1, (g + 1) & 1);
+                        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+                        mma_frag(g & 1);
+                    }
+                    copy_barrier<(PF - 1) * COPIES>();
+                    read_frag((t + 1) % NSTAGE, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma_frag(1);
+                }
             } else {
+                // An odd number of groups per stage: a step whose group 0 sits in buffer P
+                // leaves the next step's group 0 in buffer 1 - P, so the steps alternate P = 0, 1
+                // (unrolled by two to keep the buffer indices compile-time constants). The loop
+                // for even counts stays a form of its own: with both folded into this one, the
+                // 64 x 64 x 64 four-wave-row kernel ran 30% slower on 1536 x 2048 x 2048 (97 to
+                // 126 us) with fewer workgroups resident, though its machine code differed in
+                // a handful of scalar instructions only; the cause was not found.
+                auto step = [&](int t, auto parity) __attribute__((always_inline)) {
+                    constexpr int P = decltype(parity)::value;
+                    const int ahead = t + PF < nk ? t + PF : nk - 1;
+                    copy_tile(ahead * BK, (t + PF) % NSTAGE);
+                    const int st = t % NSTAGE;
+    #pragma unroll
+                    for (int g = 0; g + 1 < NG; ++g) {
+                        read_frag(st, g + 1, (g + 1 + P) & 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mma_frag((g + P) & 1);
+                    }
+                    copy_barrier<(PF - 1) * COPIES>();
+                    read_frag((t + 1) % NSTAGE, 0, 1 - P);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma_frag((NG - 1 + P) & 1);
+                };
                 int t = 0;
                 for (; t + 1 < nk; t += 2) {
-                    step(t, even{});
-                    step(t + 1, odd{});
+                    step(t, std::integral_constant<int, 0>{});
+                    step(t + 1, std::integral_constant<int, 1>{});
                 }
                 if (t < nk)
-                    step(t, even{});
+                    step(t, std::integral_constant<int, 0>{});
             }
             wait_vmcnt<0>();    // no copy may still write LDS once it is reused or released
         } else if constexpr (PF == 1) {
@@ -889,7 +909,8 @@ struct MfmaTile {
         return true;
     }
 
-    __device__ __forceinline__ static void epilogue(const GemmArgs &p, int m0, int n0,
+    template <class Args>
+    __device__ __forceinline__ static void epilogue(const Args &p, int m0, int n0,
                                                     const acc_t (&acc)[TM][TN], int tid_in)
     {
         const int M = p.M, N = p.N;
@@ -908,7 +929,9 @@ struct MfmaTile {
         const float alpha = p.alpha, beta = p.beta;
         const float *bias = p.bias;
         const int act = p.act;
-        const int64_t incc = GS ? p.incC : 1;               // column stride of C
+        int64_t incc = 1;                                   // column stride of C
+        if constexpr (GS)
+            incc = p.incC;
         const bool read_c = beta != 0.f, has_bias = bias != nullptr;
         const bool full = !EDGE || (m0 + BM <= M && n0 + BN <= N);   // whole tile inside C
         // 128- or 64-bit accesses of a lane's TN consecutive columns: aligned, and (N % 4 == 0,
@@ -1002,7 +1025,7 @@ template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int MB>
 __global__ void __launch_bounds__(WGM * WGN * WGK * 64)
 __attribute__((amdgpu_waves_per_eu(MfmaTile<BM, BN, BK, WGM, WGN, WGK, 1, false, false, false, false, true, MB,
                                             true>::WPE)))
-sgemm_mfma_strided(GemmArgs p, int group_m)
+sgemm_mfma_strided(StridedArgs p, int group_m)
 {
     using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, 1, false, false, false, false, true, MB, true>;
     __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
