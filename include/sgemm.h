@@ -161,6 +161,8 @@ int sgemm_general(int config, int opA, int opB, int M, int N, int K, float alpha
  * section "Tiled matrix multiplication"); this is that form. Strides of A and B may be any
  * value >= 0 (0 repeats a row or column); C's must give distinct entries distinct
  * addresses (csC >= 1 and rsC >= (N-1)*csC + 1, or rsC >= 1 and csC >= (M-1)*rsC + 1).
+ * Each operand's largest offset, (rows-1)*rs + (cols-1)*cs, must be below 2^60 floats
+ * (else the row stride's position is returned).
  * Layouts with a unit stride in one dimension (the other at least the extent it spans)
  * run the stored-matrix kernels with the automatic choice, as sgemm_bias_act would; a
  * column-major C with no bias runs as the transposed product; every other layout runs a

@@ -509,6 +509,8 @@ _STRIDED_OK = (4, 5, 3, 1.0, BAD, 7, 2, BAD, 11, 3, 0.5, BAD, 20, 2, None, 0, No
     (11, None, -12), (12, -1, -13), (13, -1, -14), (15, 2, -16),
     # C windows whose entries would share addresses: rows 2 floats apart with 5 columns 2 apart
     (12, 8, -13),
+    # offsets past 2^60 floats, reported at the operand's row stride
+    (5, 1 << 62, -6), (9, 1 << 61, -9), (12, 1 << 60, -13),
     # a column stride of 0 for C with N > 1
     (13, 0, -13),
 ])

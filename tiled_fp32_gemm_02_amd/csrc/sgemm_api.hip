@@ -805,6 +805,16 @@ int sgemm_strided(int M, int N, int K, float alpha, const float *A, long long rs
         return -14;
     }
     if (act != SGEMM_ACT_NONE && act != SGEMM_ACT_GELU_TANH) return -16;
+    // Every element offset (i*rs + j*cs over the window) must fit the kernels' 64-bit
+    // arithmetic with room to spare: at most 2^60 floats for each operand.
+    auto extent_ok = [](int rows, int cols, long long rs, long long cs) {
+        const unsigned __int128 e = (unsigned __int128)(rows > 0 ? rows - 1 : 0) * (unsigned long long)rs +
+                                    (unsigned __int128)(cols > 0 ? cols - 1 : 0) * (unsigned long long)cs;
+        return e < ((unsigned __int128)1 << 60);
+    };
+    if (reads_ab && !extent_ok(M, K, rsA, csA)) return -6;
+    if (reads_ab && !extent_ok(K, N, rsB, csB)) return -9;
+    if (M > 0 && N > 0 && !extent_ok(M, N, rsC, csC)) return -13;
     return strided(M, N, K, alpha, A, rsA, csA, B, rsB, csB, beta, C, rsC, csC, bias, act,
                    static_cast<hipStream_t>(stream));
 }
