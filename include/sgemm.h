@@ -193,7 +193,8 @@ int sgemm_strided(int M, int N, int K, float alpha,
  * Arguments by position: 1 M, 2 N, 3 K, 4 alpha, 5 A, 6 lda, 7 strideA, 8 B, 9 ldb,
  * 10 strideB, 11 beta, 12 C, 13 ldc, 14 strideC, 15 batch, 16 stream.
  * batch >= 0 and at most 65535; batch == 0 returns 0. strideA, strideB >= 0 (0 reuses
- * one matrix for all batches). The C windows must not overlap, unless batch == 1:
+ * one matrix for all batches), and (batch-1) times each stride at most 2^60 floats. The C
+ * windows must not overlap, unless batch == 1:
  * strideC >= (M-1)*ldc + N (stacked), or N <= strideC and (batch-1)*strideC + N <= ldc
  * (side by side within each row). Other rules as for sgemm.
  */

@@ -137,6 +137,16 @@ def test_batched_op_invalid_arguments(args, code):
     assert sg.sgemm_status_string(code) == f"invalid argument {-code}"
 
 
+def test_batched_strides_bounded():
+    """(batch - 1) * stride past 2^60 floats is rejected at that stride's position."""
+    big = (1 << 60) // 2 + 1
+    assert sg.sgemm_strided_batched(4, 4, 4, 1.0, BAD, 4, big, BAD, 4, 16, 0.0, BAD, 4, 16, 3, None) == -7
+    assert sg.sgemm_strided_batched(4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, big, 0.0, BAD, 4, 16, 3, None) == -10
+    assert sg.sgemm_strided_batched(4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, big, 3, None) == -14
+    # one batch: the stride is never applied
+    assert sg.sgemm_strided_batched(0, 4, 4, 1.0, BAD, 4, 1 << 62, BAD, 4, 16, 0.0, BAD, 4, 16, 1, None) == 0
+
+
 def test_batched_general_checks():
     ok = (0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16)
     assert sg.sgemm_strided_batched_general(-1, *ok, None, 2, 2) == -18          # act

@@ -467,6 +467,13 @@ int check_batch(int M, int N, int ldc, long long sA, long long sB, long long sC,
     if (sB < 0) return pB;
     if (sC < 0) return pC;
     if (batch < 0 || batch > 65535) return pBatch;
+    // The last batch's offset (batch - 1) * stride stays far inside 64-bit arithmetic.
+    const long long kMaxOffset = 1LL << 60;
+    if (batch > 1) {
+        if (sA > kMaxOffset / (batch - 1)) return pA;
+        if (sB > kMaxOffset / (batch - 1)) return pB;
+        if (sC > kMaxOffset / (batch - 1)) return pC;
+    }
     if (batch > 1 && M > 0 && N > 0) {
         const bool stacked = sC >= (long long)(M - 1) * ldc + N;
         const bool side_by_side = sC >= N && (long long)(batch - 1) * sC + N <= ldc;
