@@ -377,8 +377,12 @@ const char *sgemm_config_name(int config);
  *                 element-wise forms of tile16 and valu
  *   lds_bytes     static LDS per workgroup
  *   band          tile rows per band of the workgroup order
- *   unaligned     the form run when rows are only 4-byte aligned: direct-4B, staged-4B,
- *                 or for streamk the data-parallel kernel of its tile, register-staged
+ *   unaligned     the form run when rows are only 4-byte aligned: direct-16B-unaligned
+ *                 (the same 16-byte direct copies from 4-byte aligned addresses, with the
+ *                 K-tile that holds the end of K copied in 4-byte words), staged-4B
+ *                 (16-byte loads through registers, the chunk that crosses a row's end
+ *                 read float by float), or for a register-staged streamk configuration
+ *                 data-parallel-staged-4B (the data-parallel kernel of its tile)
  *   unaligned_bk  the K-tile of that form
  *   compute       the instruction that does the multiply-adds
  * The string is owned by the library and valid for the life of the process.

@@ -301,12 +301,12 @@ def test_config_describe_every_id():
             assert d["compute"] == ("v_mfma_f32_16x16x4_f32" if m.group(1) == "mfma16" else "v_mfma_f32_32x32x2_f32")
             # the stages hold A and B tiles: at least BK * (BM + BN) floats per stage
             assert lds >= 4 * bk * (bm + bn)
-        if d["kind"] == "streamk":
-            assert d["unaligned"] == "data-parallel-staged-4B"
-        elif d["kind"] == "mfma":
-            assert d["unaligned"] in ("direct-4B", "staged-4B")
-            if d["unaligned"] == "direct-4B":
-                assert d["loader"] == "direct-16B" and (bm * bk + bk * bn) // threads <= 16
+        if d["kind"] in ("mfma", "streamk"):
+            # direct-copy configurations keep their copies and K-tile on 4-byte aligned rows
+            direct = d["loader"] == "direct-16B"
+            assert d["unaligned"] == ("direct-16B-unaligned" if direct else
+                                      "data-parallel-staged-4B" if d["kind"] == "streamk" else "staged-4B")
+            assert int(d["unaligned_bk"]) == bk
         if d["kind"] != "streamk":
             st, grid, block = sg.sgemm_launch_shape(cid, 1000, 1537, 777)
             assert st == 0 and block[0] * block[1] * block[2] == threads
@@ -316,7 +316,7 @@ def test_config_describe_every_id():
             sg.describe(bad)
     # the direct-copy large tile: 2 stages of (256 + 256) x 32 floats
     d = sg.describe(names.index("mfma_256x256x32_w2x4d"))
-    assert d["lds_bytes"] == str(2 * 32 * 512 * 4) and d["unaligned"] == "staged-4B"
+    assert d["lds_bytes"] == str(2 * 32 * 512 * 4) and d["unaligned"] == "direct-16B-unaligned"
 
 
 def test_select_config_general_agrees_with_the_plain_query():

@@ -53,8 +53,9 @@ def expected_mfma_kernels(config_names):
     whole-tile and edge variants as configured; for register-staged configurations
     (stream-K ones included) the unaligned variant with their own K-tile and loads in
     flight; for direct-copy ones the register-staged unaligned variant with one K-tile in
-    flight and K-tiles of 16 * WGK, and, with at most 16 copies per thread and K-tile, the
-    unaligned variant with 4-byte direct copies and the configured K-tiles in flight."""
+    flight and K-tiles of 16 * WGK (row strides the direct copies cannot take), and the
+    unaligned variant of the direct copies (16-byte copies from 4-byte aligned rows, the
+    K-tile holding the end of K in 4-byte words) with the configured K-tiles in flight."""
     out = set()
     for name in config_names:
         bm, bn, bk, wm, wn, wk, pf, dma, mb = parse_config(name)
@@ -64,7 +65,7 @@ def expected_mfma_kernels(config_names):
                 if name.startswith("mfma"):
                     for edge in (0, 1):
                         out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge, mb))
-                    if dma and (bm * bk + bk * bn) // nt <= 16:
+                    if dma:
                         out.add((bm, bn, bk, wm, wn, wk, pf, 1, ta, tb, 0, 1, mb))
                     if dma:     # two k groups per wave group: 16 k (32x32 blocks) or 32 k (16x16 blocks)
                         out.add((bm, bn, (512 // mb) * wk, wm, wn, wk, 1, 0, ta, tb, 0, 1, mb))
@@ -72,16 +73,16 @@ def expected_mfma_kernels(config_names):
                         out.add((bm, bn, bk, wm, wn, wk, pf, 0, ta, tb, 0, 1, mb))
                 else:
                     # stream-K: the register-staged tile kernel for operands it cannot take (unaligned
-                    # without a 4-byte-copy form, or rows too long for direct copies)
+                    # ones of a register-staged configuration, or row strides direct copies cannot take)
                     out.add((bm, bn, bk, wm, wn, wk, pf, 0, ta, tb, 0, 1, mb))
     return out
 
 
 def expected_sk_kernels(config_names):
     """Stream-K kernels: the aligned whole-tile and edge variants of each stream-K
-    configuration, and for direct-copy ones with at most 16 copies per thread and K-tile
-    the unaligned variant with 4-byte copies (other configurations run the data-parallel
-    kernel of the tile on unaligned operands)."""
+    configuration, and for direct-copy ones the unaligned variant of the direct copies
+    (register-staged configurations run the data-parallel kernel of the tile on unaligned
+    operands)."""
     out = set()
     for name in config_names:
         bm, bn, bk, wm, wn, wk, pf, dma, mb = parse_config(name)
@@ -90,7 +91,7 @@ def expected_sk_kernels(config_names):
             for tb in (0, 1):
                 for edge in (0, 1):
                     out.add((bm, bn, bk, wm, wn, wk, pf, int(dma), ta, tb, 1, edge, mb))
-                if dma and (bm * bk + bk * bn) // nt <= 16:
+                if dma:
                     out.add((bm, bn, bk, wm, wn, wk, pf, 1, ta, tb, 0, 1, mb))
     return out
 

@@ -11,10 +11,15 @@
 //    B's blocks sit side by side) meet no LDS bank conflict in a
 //    model of the 64-bank LDS that serves 64 dwords per pass (64 lanes of a 4-byte read,
 //    32 of an 8-byte one, 16 of a 16-byte one). The hardware counters are the final
-//    word on conflicts; this catches a layout that cannot be conflict-free.
+//    word on conflicts; this catches a layout that cannot be conflict-free;
+//  - on rows only 4-byte aligned (TileDMA's U form), with the kernels' own copy plans
+//    over every tile and K-tile of a set of odd-sized operands: each 16-byte copy of a
+//    K-tile that does not hold the end of K reads inside the operand, and the 4-byte
+//    copies of the K-tile that does read only elements of the matrix.
 // Prints one line per failure and exits non-zero if any check fails.
 #include <cstdio>
 #include <cstring>
+#include <type_traits>
 #include <vector>
 
 #include "sgemm_configs.inc"
@@ -91,17 +96,82 @@ static void check_read(const char *what, const int *addr, int width)
     }
 }
 
+// The U form's reads for one operand stored as `rows` x `cols` floats with row stride ld,
+// cut into tiles of TR x TC as the kernels cut it (KC: rows run along m or n and columns
+// along k, else rows along k). Every tile and K-tile is walked with the kernel's own copy
+// plan (T::plan, and the 4-byte layout T::Words in the K-tile holding the end of K).
+template <class T, int TR, int TC, int NT, bool KC>
+static void check_u_reads(const char *what, int rows, int cols, int64_t ld)
+{
+    const int mdim = KC ? rows : cols, K = KC ? cols : rows;
+    const int tmn = KC ? TR : TC, kext = KC ? TC : TR;
+    const int64_t extent = (int64_t)(rows - 1) * ld + cols;     // floats of the operand
+    for (int t = 0; t * tmn < mdim; ++t)
+        for (int kt = 0; kt * kext < K; ++kt) {
+            const int mn = mdim - t * tmn, k = K - kt * kext;
+            const int64_t origin = KC ? (int64_t)t * TR * ld + (int64_t)kt * TC : (int64_t)kt * TR * ld + (int64_t)t * TC;
+            for (int tid = 0; tid < NT; ++tid) {
+                if (k > kext) {
+                    const typename T::Lane L = T::template plan<true>(ld, mn, tid);
+                    for (int c = 0; c < T::CH; ++c) {
+                        if (L.off[c] == 0x80000000u)
+                            continue;
+                        const int64_t f = origin + L.off[c] / 4;
+                        CHECK(f >= 0 && f + 4 <= extent, "%s: %dx%d ld %lld tile %d K-tile %d thread %d copy %d reads "
+                              "floats %lld..%lld of %lld", what, rows, cols, (long long)ld, t, kt, tid, c,
+                              (long long)f, (long long)f + 3, (long long)extent);
+                    }
+                } else {
+                    using W = typename T::Words;
+                    for (int c = 0; c < W::CH; ++c) {
+                        int r, col;
+                        W::where(c, tid, r, col);
+                        if (!((KC ? r : col) < mn && (KC ? col : r) < k))
+                            continue;               // not copied: reads as zero
+                        const int64_t sr = (KC ? (int64_t)t * TR : (int64_t)kt * TR) + r;
+                        const int64_t sc = (KC ? (int64_t)kt * TC : (int64_t)t * TC) + col;
+                        CHECK(sr < rows && sc < cols, "%s: %dx%d ld %lld tile %d last K-tile thread %d word %d reads "
+                              "(%lld, %lld)", what, rows, cols, (long long)ld, t, tid, c, (long long)sr, (long long)sc);
+                    }
+                }
+            }
+        }
+}
+
+// Odd-sized operands for check_u_reads: extents around one and two tiles along each
+// dimension, packed and padded row strides, and the shortest strides the host allows.
+template <class T, int TR, int TC, int NT, bool KC>
+static void check_u_operand(const char *what)
+{
+    const int dims[][2] = {{2 * TR + 3, 2 * TC + 1}, {TR - 1, TC + 5}, {1, 4 * TC + 3}, {3, 5}, {TR + 1, 1}};
+    for (const auto &d : dims)
+        for (int pad : {0, 3}) {
+            const int64_t ld = d[1] + pad < 4 ? 4 : d[1] + pad;
+            check_u_reads<T, TR, TC, NT, KC>(what, d[0], d[1], ld);
+        }
+}
+
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int MB, bool TA, bool TB, int VW>
 static void check_config(const char *name)
 {
-    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, 1, true, TA, TB, VW == 4, false, MB>;
-    using A = typename T::AIO;
-    using B = typename T::BIO;
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, 1, true, TA, TB, true, false, MB>;
+    using TU = MfmaTile<BM, BN, BK, WGM, WGN, WGK, 1, true, TA, TB, false, true, MB>;
+    // VW = 4: the 16-byte copies; VW = 1: the 4-byte layout of the same tiles
+    using A = typename std::conditional<VW == 4, typename T::AIO, typename T::AIO::Words>::type;
+    using B = typename std::conditional<VW == 4, typename T::BIO, typename T::BIO::Words>::type;
+    static_assert(std::is_same<typename TU::AIO::Words, typename T::AIO::Words>::value &&
+                  std::is_same<typename TU::BIO::Words, typename T::BIO::Words>::value, "one 4-byte layout");
     char what[160];
     std::snprintf(what, sizeof what, "%s %s%s VW=%d A", name, TA ? "t" : "n", TB ? "t" : "n", VW);
     check_copies<A, TA ? BK : BM, TA ? BM : BK, T::NT, !TA, VW>(what);
     std::snprintf(what, sizeof what, "%s %s%s VW=%d B", name, TA ? "t" : "n", TB ? "t" : "n", VW);
     check_copies<B, TB ? BN : BK, TB ? BK : BN, T::NT, TB, VW>(what);
+    if constexpr (VW == 4) {
+        std::snprintf(what, sizeof what, "%s %s%s unaligned A", name, TA ? "t" : "n", TB ? "t" : "n");
+        check_u_operand<typename TU::AIO, TA ? BK : BM, TA ? BM : BK, T::NT, !TA>(what);
+        std::snprintf(what, sizeof what, "%s %s%s unaligned B", name, TA ? "t" : "n", TB ? "t" : "n");
+        check_u_operand<typename TU::BIO, TB ? BN : BK, TB ? BK : BN, T::NT, TB>(what);
+    }
 
     // The loop's fragment reads, per wave and group of KGRP k (as in MfmaTile::read_frag):
     // lane l is row/column l % MB of its block and supplies k = 4 * (l / MB) + step.

@@ -53,7 +53,7 @@ struct Config {
     int pf;              // K-tiles whose loads run ahead of the one being multiplied
     int lds_bytes;       // static LDS per workgroup (aligned form)
     int unaligned_bk;    // K-tile of the form run for 4-byte aligned rows
-    bool unaligned_dma;  // that form copies 4-byte words HBM -> LDS directly (else register-staged)
+    bool unaligned_dma;  // that form copies HBM -> LDS directly (else register-staged)
     int mb;              // block of the matrix instruction (32 or 16; 0 for the non-matrix kinds)
 };
 
@@ -64,8 +64,10 @@ struct MfmaFacts {
     static constexpr int NT = WGM * WGN * WGK * 64;
     static constexpr int LDS =
         4 * sgemm_impl::MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, false, false, true, false, MB>::SMEM;
-    static constexpr bool DMA4 = DMA && (BM * BK + BK * BN) / NT <= 16;
-    static constexpr int UBK = DMA4 ? BK : (DMA ? 8 * (64 / MB) * WGK : BK);
+    // Rows only 4-byte aligned: direct-copy configurations keep their tile and copies (the
+    // K-tile holding the end of K in 4-byte words), register-staged ones their tile.
+    static constexpr bool UDMA = DMA;
+    static constexpr int UBK = BK;
 };
 
 // Stream-K workspace: per-tile counters at a fixed offset (so a call with more tiles
@@ -179,12 +181,12 @@ hipError_t launch_tile16(const GemmArgs &p, int batch, bool ta, bool tb, bool, b
     {name, KIND_MFMA, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, GROUP_M,                                   \
      launch_mfma<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB>, nullptr, WGM, WGN, WGK, PF,                \
      MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::LDS,                                                   \
-     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::UBK, MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::DMA4, \
+     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::UBK, MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::UDMA, \
      MB},
 #define SGEMM_SK_TABLE_ROW(name, BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB)                        \
     {name, KIND_SK, BM, BN, BK, WGM * WGN * WGK * 64, DMA != 0, GROUP_M, nullptr,                            \
      launch_sk<BM, BN, BK, WGM, WGN, WGK, PF, DMA, GROUP_M, MB>, WGM, WGN, WGK, PF,                          \
-     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::LDS, BK, false, MB},
+     MfmaFacts<BM, BN, BK, WGM, WGN, WGK, PF, DMA, MB>::LDS, BK, DMA != 0, MB},
 // LDS of the two kernels outside the MFMA template: tile16 stages two 16 x 17 tiles; the
 // vector-ALU kernel two k-major 8 x 132 tiles per stage, two stages.
 const Config kConfigs[] = {
@@ -514,8 +516,10 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     if ((c.kind == KIND_MFMA || c.kind == KIND_VALU) && tiles * (uint64_t)c.threads > 0xFFFFFFFFull)
         return SGEMM_ERROR_TOO_LARGE;
     const bool edge = (M % c.bm) != 0 || (N % c.bn) != 0 || (K % c.bk) != 0;
-    // Direct copies address a tile with 32-bit offsets, so long rows take the register-staged kernels.
-    const bool dma_ok = lda < kDmaMaxLd && ldb < kDmaMaxLd;
+    // Direct copies address a tile with 32-bit offsets, so long rows take the register-staged
+    // kernels; so do row strides under 4 floats, where a 16-byte copy of a row's last chunk
+    // could pass more than the next row.
+    const bool dma_ok = lda < kDmaMaxLd && ldb < kDmaMaxLd && lda >= 4 && ldb >= 4;
     if (c.kind == KIND_SK) {
         if (batch != 1 || cus <= 0 || ws_bytes < sk_workspace_bytes(c, cus))
             return SGEMM_ERROR_WORKSPACE;
@@ -905,10 +909,10 @@ const char *sgemm_config_describe(int config)
                                      : c.kind == KIND_VALU ? "staged-k-major"
                                      : c.dma               ? "direct-16B"
                                                            : "staged-16B";
-                const char *unaligned = c.kind == KIND_SK  ? "data-parallel-staged-4B"
-                                        : !mfma            ? loader
-                                        : c.unaligned_dma  ? "direct-4B"
-                                                           : "staged-4B";
+                const char *unaligned = !mfma                             ? loader
+                                        : c.unaligned_dma                   ? "direct-16B-unaligned"
+                                        : c.kind == KIND_SK                 ? "data-parallel-staged-4B"
+                                                                            : "staged-4B";
                 snprintf(text[i], sizeof(text[i]),
                          "name=%s kind=%s tile=%dx%dx%d waves=%dx%d kgroups=%d threads=%d ahead=%d loader=%s "
                          "lds_bytes=%d band=%d unaligned=%s unaligned_bk=%d compute=%s",

@@ -11,7 +11,8 @@
 //    matrix instruction (32x32 outputs, 2 k-steps per issue), or of 16x16 blocks (4
 //    k-steps per issue) for small, skinny and ragged products. A and B tiles reach a
 //    ring of LDS stages with one barrier per K-tile: copied from HBM straight into LDS
-//    (TileDMA; 16-byte copies for 16-byte aligned rows, 4-byte copies otherwise), or
+//    (TileDMA; 16-byte copies, with 4-byte ones in the K-tile holding the end of K
+//    when rows are only 4-byte aligned), or
 //    staged through registers (TileIO). The next K-tile's loads (two with register
 //    staging and PF = 2) are in flight while the current one is multiplied.
 //
@@ -267,7 +268,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 // such swizzle, so the tile is kept as TC / PW panels of TR rows x PW columns, one after
 // the other, each laid out as a TR x PW tile of its own. A read of 16 or 32 consecutive
 // columns that stays inside one panel then meets the banks exactly as in a PW-wide tile.
-template <int TR, int TC, int NT, bool KCONTIG, int VW, bool Q16 = false, int PW = TC>
+//
+// U (VW = 4, rows only 4-byte aligned): 16-byte copies from 4-byte aligned addresses
+// (global memory takes dword-aligned vector accesses, as the register-staged loads also
+// rely on). A chunk then always holds the 4 floats it names, but a chunk that crosses the
+// end of a row brings floats of the next row along. That is harmless along m or n (they
+// land in tile columns or rows past the matrix edge, whose outputs are never written),
+// but not along k, and the last row's crossing chunk would read past the operand. So the
+// K-tile that holds the end of K is copied in 4-byte words (the VW = 1 layout, `Words`)
+// with every float checked, and every other K-tile ends at least one row before the
+// operand's last row, whose row stride (at least 4 floats, checked by the host) keeps a
+// crossing chunk inside the operand.
+template <int TR, int TC, int NT, bool KCONTIG, int VW, bool Q16 = false, int PW = TC, bool U = false>
 struct TileDMA {
     static constexpr int NP = TC / PW;                  // panels
     static constexpr int CPR = PW / 4;                  // chunks per row of a panel
@@ -276,6 +288,8 @@ struct TileDMA {
     static constexpr int CH = SLOTS / NT;               // copy instructions per thread
     static constexpr int SIZE = TR * TC;
     static_assert(VW == 4 || VW == 1, "16- or 4-byte copies");
+    static_assert(!U || VW == 4, "16-byte copies on 4-byte aligned rows");
+    static constexpr int KEXT = KCONTIG ? TC : TR;      // the tile's extent along k
     static_assert(NT % 64 == 0 && SLOTS % NT == 0, "whole copy instructions per wave");
     static_assert(TC % PW == 0 && (NP == 1 || !KCONTIG), "whole panels, along m or n only");
     static_assert(CPR == 4 || CPR == 8 || CPR % 16 == 0, "slot swizzle needs these row lengths");
@@ -330,7 +344,7 @@ struct TileDMA {
         unsigned off[CH];
     };
     template <bool EDGE>
-    __device__ __forceinline__ static Lane plan(int64_t ld, int mn, int tid)
+    __host__ __device__ __forceinline__ static Lane plan(int64_t ld, int mn, int tid)
     {
         Lane L;
 #pragma unroll
@@ -347,14 +361,23 @@ struct TileDMA {
     // Queue this thread's copies of the tile whose origin is src into lds; `k` is how many
     // of the tile's k indices lie inside the matrix (EDGE only; only a K-tile that ends
     // past K needs the per-lane check). The buffer resource (one per tile, wave-uniform)
-    // and the LDS destinations are the only per-step address work.
+    // and the LDS destinations are the only per-step address work. With U, ld (row
+    // stride) and mn (rows or columns inside the matrix along m or n) serve the 4-byte
+    // copies of the K-tile that holds the end of K.
     template <bool EDGE>
-    __device__ __forceinline__ static void load(const Lane &L, const float *src, int k, float *lds, int tid)
+    __device__ __forceinline__ static void load(const Lane &L, const float *src, int k, float *lds, int tid,
+                                                int64_t ld = 0, int mn = 0)
     {
+        if constexpr (U) {
+            if (k <= KEXT) {
+                words(src, ld, mn, k, lds, tid);
+                return;
+            }
+        }
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS base in M0
         const __amdgpu_buffer_rsrc_t rsrc =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), 0, 0x7fffffff, 0x00020000);
-        const bool partial = EDGE && k < (KCONTIG ? TC : TR);
+        const bool partial = EDGE && k < KEXT;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             unsigned off = L.off[c];
@@ -369,6 +392,29 @@ struct TileDMA {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off, 0, 0, 0);
             else
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, off, 0, 0, 0);
+        }
+    }
+
+    // The same tile in the layout of 4-byte copies (the same LDS positions, copied a float
+    // per lane).
+    using Words = TileDMA<TR, TC, NT, KCONTIG, 1, Q16, PW>;
+
+    // The whole tile in 4-byte copies, every float checked against mn (m or n) and k; the
+    // offsets are computed copy by copy in a loop unrolled only by four, so this once-per-tile
+    // path holds few registers (fully unrolled, the 256 x 256 tile spilled).
+    __device__ __forceinline__ static void words(const float *src, int64_t ld, int mn, int k, float *lds, int tid)
+    {
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), 0, 0x7fffffff, 0x00020000);
+#pragma unroll 4
+        for (int c = 0; c < Words::CH; ++c) {
+            int r, col;
+            Words::where(c, tid, r, col);
+            const bool in = (KCONTIG ? r : col) < mn && (KCONTIG ? col : r) < k;
+            const unsigned off = in ? static_cast<unsigned>(((int64_t)r * ld + col) * 4) : 0x80000000u;
+            lds_void *dst = (lds_void *)(lds + wave * 64 + c * NT);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, off, 0, 0, 0);
         }
     }
 };
@@ -496,7 +542,9 @@ struct MfmaTile {
     static constexpr int LG = BLK::LG;                      // lane groups, one k each per issue
     static constexpr int KGRP = 4 * LG;                     // k per group of 4 matrix steps
     static constexpr bool USE_DMA = DMA;                    // direct HBM -> LDS copies
-    static constexpr int VW = VEC ? 4 : 1;                  // floats per lane and copy
+    // Direct copies are 16 bytes wide; on rows only 4-byte aligned (!VEC) the K-tile that
+    // holds the end of K is copied in 4-byte words (TileDMA's U form).
+    static constexpr bool UCOPY = DMA && !VEC;
     static constexpr int NT = WGM * WGN * WGK * 64;
     static constexpr int KSLICE = BK / WGK;                    // k per stage handled by one wave group
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;       // wave tile
@@ -509,10 +557,12 @@ struct MfmaTile {
     // 16-wide panels (TileDMA), which the side-by-side blocks read one panel at a time.
     static constexpr int BPW = (TB || BN % 64 == 0 || BN == 16 || BN == 32) ? (TB ? BK : BN) : (BN % 32 == 0 ? 32 : 16);
     using AIO = typename std::conditional<USE_DMA,
-                                          TileDMA<TA ? BK : BM, TA ? BM : BK, NT, !TA, VW, MB == 16 && TM == 1>,
+                                          TileDMA<TA ? BK : BM, TA ? BM : BK, NT, !TA, 4, MB == 16 && TM == 1,
+                                                  TA ? BM : BK, UCOPY>,
                                           TileIO<TA ? BK : BM, TA ? BM : BK, NT>>::type;
     using BIO = typename std::conditional<USE_DMA,
-                                          TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB, VW, MB == 16 && (TN == 1 || BSIDE), BPW>,
+                                          TileDMA<TB ? BN : BK, TB ? BK : BN, NT, TB, 4, MB == 16 && (TN == 1 || BSIDE),
+                                                  BPW, UCOPY>,
                                           TileIO<TB ? BN : BK, TB ? BK : BN, NT>>::type;
     static constexpr int STAGE = AIO::SIZE + BIO::SIZE;
     static constexpr int NSTAGE = USE_DMA ? PF + 1 : 2;     // LDS stages in the ring
@@ -598,13 +648,15 @@ struct MfmaTile {
                 const int k0 = kbase + kr;
                 float *As = smem + st * STAGE;
                 if constexpr (TA)
-                    AIO::template load<EDGE>(a_lane, A + (int64_t)k0 * lda + m0, K - k0, As, tid);
+                    AIO::template load<EDGE>(a_lane, A + (int64_t)k0 * lda + m0, K - k0, As, tid, lda, M - m0);
                 else
-                    AIO::template load<EDGE>(a_lane, A + (int64_t)m0 * lda + k0, K - k0, As, tid);
+                    AIO::template load<EDGE>(a_lane, A + (int64_t)m0 * lda + k0, K - k0, As, tid, lda, M - m0);
                 if constexpr (TB)
-                    BIO::template load<EDGE>(b_lane, B + (int64_t)n0 * ldb + k0, K - k0, As + AIO::SIZE, tid);
+                    BIO::template load<EDGE>(b_lane, B + (int64_t)n0 * ldb + k0, K - k0, As + AIO::SIZE, tid, ldb,
+                                             N - n0);
                 else
-                    BIO::template load<EDGE>(b_lane, B + (int64_t)k0 * ldb + n0, K - k0, As + AIO::SIZE, tid);
+                    BIO::template load<EDGE>(b_lane, B + (int64_t)k0 * ldb + n0, K - k0, As + AIO::SIZE, tid, ldb,
+                                             N - n0);
             }
         };
 
@@ -731,7 +783,9 @@ struct MfmaTile {
             // multiplies stage t % NSTAGE, waits until its own copies of tile t+1 have landed
             // (the PF-1 newer tiles may stay in flight) and meets the others at the barrier.
             // Past the end the last tile is copied again, so the count of copies in flight
-            // is the same on every step.
+            // is the same on every step. (In the U form the K-tile holding the end of K takes
+            // four times the copies; it is the last tile, or a repeat of it, so the waits
+            // below, counted for 16-byte tiles, then only wait for more than they need.)
             // Inside a step, group g+1's fragments are read while group g is multiplied; the
             // last group is multiplied after the barrier, while group 0 of the next stage
             // is read (past the last step that read is of a stage nobody uses; harmless).

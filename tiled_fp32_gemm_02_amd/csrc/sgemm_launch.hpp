@@ -14,8 +14,9 @@ template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, i
 hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, bool dma_ok, hipStream_t s);
 
 // Stream-K launch of the same tile kernel: `grid` workgroups share the work described
-// by sk (batch 1). Operands that the kernel cannot take (unaligned without a 4-byte-copy
-// form, or rows too long for direct copies) run the data-parallel kernel of the tile.
+// by sk (batch 1). Operands that the kernel cannot take (unaligned ones of a
+// register-staged configuration, or row strides the direct copies cannot take) run the
+// data-parallel kernel of the tile.
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, int GROUP_M, int MB, bool TA,
           bool TB>
 hipError_t launch_mfma_sk_op(const GemmArgs &p, const StreamK &sk, int grid, bool vec, bool edge, bool dma_ok,
