@@ -44,7 +44,7 @@ def test_version_and_configs():
     assert names[0] == "tile16"
     # matrix-core configurations first, then the stream-K ones, then the vector-ALU micro-tile
     kinds = [n.split("_")[0] for n in names[1:]]
-    assert set(kinds) == {"mfma", "mfma16", "sk", "valu"} and kinds == sorted(kinds)
+    assert set(kinds) == {"mfma", "mfma16", "sk", "sk16", "valu"} and kinds == sorted(kinds)
     assert sg.sgemm_config_name(-1) is None and sg.sgemm_config_name(len(names)) is None
 
 
@@ -151,7 +151,7 @@ def test_batched_general_checks():
     ok = (0, 0, 4, 4, 4, 1.0, BAD, 4, 16, BAD, 4, 16, 0.0, BAD, 4, 16)
     assert sg.sgemm_strided_batched_general(-1, *ok, None, 2, 2) == -18          # act
     assert sg.sgemm_strided_batched_general(-2, *ok, None, 0, 2) == sg.SGEMM_ERROR_BAD_CONFIG
-    sk = [i for i, n in enumerate(sg.configs()) if n.startswith("sk_")]
+    sk = [i for i, n in enumerate(sg.configs()) if n.startswith(("sk_", "sk16_"))]
     assert sg.sgemm_strided_batched_general(sk[0], *ok, None, 0, 2) == sg.SGEMM_ERROR_WORKSPACE
     # quick returns: nothing launched, unread pointers may be anything
     assert sg.sgemm_strided_batched_general(-1, *ok, None, 0, 0) == 0
@@ -233,7 +233,7 @@ def test_launch_shape_near_int_max():
             assert st == (0 if fits else sg.SGEMM_ERROR_TOO_LARGE), (name, st)
             if st == 0:
                 assert grid == (-(-big // bm), 1, 1)
-        elif name.startswith("sk_"):
+        elif name.startswith(("sk_", "sk16_")):
             # K-tile steps x (compute units + 1) pass 2^31
             assert sg.sgemm_launch_shape(cid, 64, 64, big)[0] == sg.SGEMM_ERROR_TOO_LARGE, name
 
@@ -261,27 +261,27 @@ def test_select_config():
         bm, bn, _ = (int(x) for x in name.split("_")[1].split("x"))
         tiles = -(-M // bm) * -(-N // bn)
         assert tiles >= 256 or bm <= 64, (M, N, name, tiles)
-    # the measured winners of the benchmark shapes: 16x16-block tiles for the GPT-2 QKV layer
-    # (32 x 96: 768 tiles, three per CU) and MLP-up layer, 1024^3, 1536^3, 256^3 (whole K in
-    # one 256-deep K-tile) and the 32-wide and 32-row products; the 32x32-block tile for MLP-down
-    assert names[sel(1024, 2304, 768)] == "mfma16_32x96x32_w2x2k1d"
-    assert names[sel(1536, 1536, 1536)] == "mfma16_32x96x32_w2x2k1d"
+    # the modelled winners without a workspace: 16x16-block tiles for the GPT-2 QKV layer and
+    # 1536^3 (32 x 96: three tiles per CU), the MLP-up layer, 1024^3, 256^3 (whole K in one
+    # 256-deep K-tile) and the 32-wide and 32-row products; the 32x32-block tile for MLP-down
+    assert names[sel(1024, 2304, 768)] == "mfma16_32x96x64_w2x2k2d"
+    assert names[sel(1536, 1536, 1536)] == "mfma16_32x96x64_w2x2k2d"
     assert names[sel(1024, 3072, 768)] == "mfma16_64x64x32_w4x1k1d"
     assert names[sel(1024, 768, 3072)] == "mfma_32x32x64_w1x1k4d"
     assert names[sel(1024, 1024, 1024)] == "mfma16_64x64x64_w4x1k2d"
     assert names[sel(256, 256, 256)] == "mfma16_16x16x256_w1x1k4d"
     assert names[sel(8192, 32, 8192)] == "mfma16_32x32x128_w2x2k2d"
     assert names[sel(32, 8192, 8192)] == "mfma16_32x32x128_w2x2k2d"
-    # unaligned: the ragged product keeps the 64 x 128 tile with 4-byte copies
+    # unaligned: the ragged product on the 64 x 64 16x16-block tile
     assert names[sg.sgemm_select_config(1000, 1537, 777, 1.0, BAD, 777, BAD, 1537, BAD, 1537)] == \
-        "mfma_64x128x32_w2x2k2d"
+        "mfma16_64x64x32_w4x1k1d"
 
 
 def test_config_describe_every_id():
     """Every configuration has one description line whose fields agree with its name,
     its launch shape and the limits of the hardware; ids out of range give NULL."""
     names = sg.configs()
-    kinds = {"tile16": "tile16", "mfma": "mfma", "mfma16": "mfma", "sk": "streamk", "valu": "valu"}
+    kinds = {"tile16": "tile16", "mfma": "mfma", "mfma16": "mfma", "sk": "streamk", "sk16": "streamk", "valu": "valu"}
     for cid, name in enumerate(names):
         d = sg.describe(cid)
         assert set(d) == {"name", "kind", "tile", "waves", "kgroups", "threads", "ahead", "loader", "lds_bytes",
@@ -292,13 +292,13 @@ def test_config_describe_every_id():
         wk, threads, lds = int(d["kgroups"]), int(d["threads"]), int(d["lds_bytes"])
         assert 0 < lds <= 160 * 1024 and int(d["band"]) >= 1 and int(d["unaligned_bk"]) >= 1
         if d["kind"] in ("mfma", "streamk"):
-            m = re.fullmatch(r"(mfma|mfma16|sk)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
+            m = re.fullmatch(r"(mfma|mfma16|sk|sk16)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
             assert m, name
             assert (bm, bn, bk, wm, wn) == tuple(int(x) for x in m.groups()[1:6])
             assert wk == int(m.group(7) or 1) and int(d["ahead"]) == int(m.group(8) or 1)
             assert threads == wm * wn * wk * 64
             assert d["loader"] == ("direct-16B" if m.group(9) else "staged-16B")
-            assert d["compute"] == ("v_mfma_f32_16x16x4_f32" if m.group(1) == "mfma16" else "v_mfma_f32_32x32x2_f32")
+            assert d["compute"] == ("v_mfma_f32_16x16x4_f32" if m.group(1) in ("mfma16", "sk16") else "v_mfma_f32_32x32x2_f32")
             # the stages hold A and B tiles: at least BK * (BM + BN) floats per stage
             assert lds >= 4 * bk * (bm + bn)
         if d["kind"] in ("mfma", "streamk"):
@@ -412,7 +412,7 @@ WS_ARGS = (0, 0, 4, 4, 4, 1.0, BAD, 4, BAD, 4, 0.0, BAD, 4, None, 0)   # opA .. 
 
 
 def sk_ids():
-    return [i for i, n in enumerate(sg.configs()) if n.startswith("sk_")]
+    return [i for i, n in enumerate(sg.configs()) if n.startswith(("sk_", "sk16_"))]
 
 
 def test_workspace_argument_checks():
@@ -462,20 +462,26 @@ def test_workspace_size_without_a_device_is_zero():
 
 
 def test_launch_shape_stream_k():
+    """Whole rounds of 256 tiles but the last run one tile per workgroup; the last round's
+    tiles x K-tiles are shared by 256 workgroups, or one per K-tile step when fewer."""
     for cid in sk_ids():
-        st, grid, block = sg.sgemm_launch_shape(cid, 1024, 2304, 768)
-        assert st == 0 and grid == (256, 1, 1) and block[0] in (256, 512, 1024)
-        # fewer K-tile steps than compute units: one workgroup per step
-        st, grid, _ = sg.sgemm_launch_shape(cid, 100, 130, 64)
         bm, bn, bk = (int(x) for x in sg.sgemm_config_name(cid).split("_")[1].split("x"))
-        assert st == 0 and grid[0] == -(-100 // bm) * -(-130 // bn) * -(-64 // bk)
+        for M, N, K in [(1024, 2304, 768), (100, 130, 64), (1000, 1537, 777), (4096, 4096, 256), (64, 64, 4096)]:
+            tiles, iters = -(-M // bm) * -(-N // bn), -(-K // bk)
+            whole = 256 * ((tiles - 1) // 256)
+            st, grid, block = sg.sgemm_launch_shape(cid, M, N, K)
+            assert st == 0 and grid == (whole + min(256, (tiles - whole) * iters), 1, 1), (M, N, K, grid)
+            assert block[0] in (256, 512, 1024)
+        # a 64 x 128 tile's QKV layer: 288 tiles, so 256 whole and 32 shared by 256 workgroups
+        if (bm, bn) == (64, 128):
+            assert sg.sgemm_launch_shape(cid, 1024, 2304, 768)[1] == (512, 1, 1)
 
 
 def test_select_without_workspace_never_picks_stream_k():
     names = sg.configs()
     for M, N, K in [(1024, 2304, 768), (1024, 768, 3072), (1025, 1025, 1025), (4096, 4096, 4096)]:
-        assert not names[sg.sgemm_select_config(M, N, K, 1.0, BAD, K, BAD, N, BAD, N)].startswith("sk_")
-        assert not names[sg.sgemm_select_config_ws(M, N, K, 1.0, BAD, K, BAD, N, BAD, N, 0)].startswith("sk_")
+        assert not names[sg.sgemm_select_config(M, N, K, 1.0, BAD, K, BAD, N, BAD, N)].startswith(("sk_", "sk16_"))
+        assert not names[sg.sgemm_select_config_ws(M, N, K, 1.0, BAD, K, BAD, N, BAD, N, 0)].startswith(("sk_", "sk16_"))
 
 
 def test_workspace_cache_does_not_deadlock(monkeypatch):

@@ -40,10 +40,10 @@ def kernels(tmp_path_factory):
 
 
 def parse_config(name):
-    m = re.fullmatch(r"(mfma|mfma16|sk)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
+    m = re.fullmatch(r"(mfma|mfma16|sk|sk16)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)(?:k(\d+))?(?:p(\d+))?(d)?", name)
     assert m, name
     bm, bn, bk, wm, wn = (int(x) for x in m.groups()[1:6])
-    mb = 16 if m.group(1) == "mfma16" else 32
+    mb = 16 if m.group(1) in ("mfma16", "sk16") else 32
     return bm, bn, bk, wm, wn, int(m.group(7) or 1), int(m.group(8) or 1), m.group(9) is not None, mb
 
 
@@ -100,9 +100,9 @@ def test_all_kernels_present(kernels):
     names = " ".join(kernels)
     assert "sgemm_tile16" in names and "sgemm_scale" in names and "sgemm_valu" in names
     import tiled_fp32_gemm_02_amd as sg
-    names = [n for n in sg.configs() if n.startswith(("mfma_", "mfma16_", "sk_"))]
+    names = [n for n in sg.configs() if n.startswith(("mfma_", "mfma16_", "sk_", "sk16_"))]
     for kind, expected in (("sgemm_mfma", expected_mfma_kernels(names)),
-                           ("sgemm_mfma_sk", expected_sk_kernels([c for c in names if c.startswith("sk_")]))):
+                           ("sgemm_mfma_sk", expected_sk_kernels([c for c in names if c.startswith(("sk_", "sk16_"))]))):
         found = set()
         for n in kernels:
             m = re.search(kind + r"<([^>]*)>", n)

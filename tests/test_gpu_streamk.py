@@ -3,8 +3,10 @@
 Every stream-K configuration runs every operand form on shapes that cover the ways
 the work can split: fewer K-tile steps than compute units, tiles shared
 by two or several workgroups, ranges that hold whole tiles between partial ones, edge
-tiles in M, N and K, bias + GELU, and unaligned operands (which run the data-parallel
-kernel of the tile). Results are checked against the oracle's bound, must be bitwise
+tiles in M, N and K, bias + GELU, more tiles than compute units (whole tiles first, the
+last round's tiles shared), and unaligned operands (the direct-copy configurations' own
+kernel, register-staged ones the data-parallel kernel of the tile). Results are checked
+against the oracle's bound, must be bitwise
 identical from run to run, and the workspace's tile counters must be zero again after
 every call.
 """
@@ -41,7 +43,7 @@ def ws():
 
 def sk_ids():
     import tiled_fp32_gemm_02_amd as sg
-    return [i for i, n in enumerate(sg.configs()) if n.startswith("sk_")]
+    return [i for i, n in enumerate(sg.configs()) if n.startswith(("sk_", "sk16_"))]
 
 
 def stored(op, x):
@@ -70,11 +72,13 @@ def counters_clear(ws):
 
 SHAPES = [
     (100, 132, 64),          # fewer K-tile steps than compute units: one workgroup per step
-    (100, 130, 70),          # unaligned: the data-parallel kernel of the tile
+    (100, 130, 70),          # unaligned: direct-copy configurations keep their kernel
     (256, 512, 256),         # each tile shared by several workgroups
     (1024, 768, 1024),       # GPT-2 MLP-down-like: 48..96 tiles, K long
     (1028, 772, 516),        # aligned, with M, N and K edges
     (2048, 1024, 128),       # more tiles than workgroups: whole tiles between partial ones
+    (1028, 1540, 516),       # more tiles than compute units: whole tiles, then the last round shared
+    (1000, 1537, 777),       # the same, unaligned (4-byte aligned rows), edges in M, N and K
 ]
 
 
@@ -157,9 +161,10 @@ def test_auto_choice_with_workspace(ws):
                                         ws.numel())
         picks[(M, N, K)] = names[cid]
     assert picks[(4096, 4096, 4096)] == "mfma_256x256x32_w2x4d"       # one whole tile per CU already
-    assert picks[(2560, 2560, 2560)].startswith("sk_")               # 400 tiles of 128^2, K long
-    # 768 tiles of 32 x 96, three per CU: balanced without stream-K (66 against 71 us measured)
-    assert picks[(1536, 1536, 1536)] == "mfma16_32x96x32_w2x2k1d"
+    assert picks[(2560, 2560, 2560)].startswith(("sk_", "sk16_"))   # long K, a sparse last round of tiles
+    # 576 tiles of 64 x 64: two whole rounds, the last 64 tiles shared by all CUs (60 us measured,
+    # against 66 for 768 tiles of 32 x 96 without stream-K)
+    assert picks[(1536, 1536, 1536)] == "sk16_64x64x32_w4x1k1d"
 
 
 def test_tensor_form_uses_the_workspace():
@@ -173,7 +178,7 @@ def test_tensor_form_uses_the_workspace():
     a, b = draw(rng, (M, K), "normal"), draw(rng, (K, N), "normal002")
     A, B = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
     ws = sg.workspace_for(A.device)
-    assert sg.sgemm_config_name(sg.sgemm_select_config_ws(M, N, K, 1.0, A, K, B, N, A, N, ws.numel())).startswith("sk_")
+    assert sg.sgemm_config_name(sg.sgemm_select_config_ws(M, N, K, 1.0, A, K, B, N, A, N, ws.numel())).startswith(("sk_", "sk16_"))
     say("stream-K through the tensor form")
     C = sg.gemm(A, B)
     C2 = sg.gemm(A, B, workspace=None)
@@ -198,7 +203,7 @@ def test_tensor_form_on_a_side_stream_with_a_fresh_workspace(monkeypatch):
     A, B = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
     torch.cuda.synchronize()
     ws_bytes = sg.sgemm_workspace_size(-1)
-    assert sg.sgemm_config_name(sg.sgemm_select_config_ws(M, N, K, 1.0, A, K, B, N, A, N, ws_bytes)).startswith("sk_")
+    assert sg.sgemm_config_name(sg.sgemm_select_config_ws(M, N, K, 1.0, A, K, B, N, A, N, ws_bytes)).startswith(("sk_", "sk16_"))
     side = torch.cuda.Stream()
     # reuse of a freed allocation: leave nonzero bytes where the workspace may land
     junk = torch.full((sg.sgemm_workspace_size(-1) // 4 + 16,), -1, dtype=torch.int32, device="cuda")

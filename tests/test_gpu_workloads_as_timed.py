@@ -81,10 +81,10 @@ def test_workload_as_timed(name, ws):
 
 def test_timed_configurations(ws):
     """What the cost model picks for the timed launches, with a workspace: the measured
-    winners of the sweep. 16x16-block tiles for GPT-2 QKV (32 x 96, wave tiles of 16 x 48: 768
-    tiles, three per CU), MLP-up (64 x 64, wave tiles of 16 x 64), 1024^3 (64 x 64 x 64) and 256^3
-    (16 x 16, all of K in one K-tile); the 32 x 32 tile of 32x32 blocks for MLP-down; the 256 x 256
-    tile at 4096^3 (no stream-K: each of these beats it)."""
+    winners of the sweep. 16x16-block tiles for GPT-2 QKV (64 x 64 with stream-K: two whole
+    rounds of 256 tiles, the last 64 tiles shared by every CU), MLP-up (64 x 64, wave tiles of
+    16 x 64), 1024^3 (64 x 64 x 64) and 256^3 (16 x 16, all of K in one K-tile); the 32 x 32
+    tile of 32x32 blocks for MLP-down; the 256 x 256 tile at 4096^3 (one tile per CU)."""
     import tiled_fp32_gemm_02_amd as sg
     picks = {}
     for name in ["gpt2_qkv", "gpt2_mlp_up", "gpt2_mlp_down", "sq256", "sq1024", "sq4096"]:
@@ -93,7 +93,7 @@ def test_timed_configurations(ws):
             w.M, w.N, w.K, w.alpha, ws.data_ptr(), w.lda_, ws.data_ptr(), w.ldb_, ws.data_ptr(), w.ldc_,
             ws.numel()))
     say(f"timed configurations: {picks}")
-    assert picks["gpt2_qkv"] == "mfma16_32x96x32_w2x2k1d"
+    assert picks["gpt2_qkv"] == "sk16_64x64x32_w4x1k1d"
     assert picks["gpt2_mlp_up"] == "mfma16_64x64x32_w4x1k1d"
     assert picks["gpt2_mlp_down"] == "mfma_32x32x64_w1x1k4d" and picks["sq256"] == "mfma16_16x16x256_w1x1k4d"
     assert picks["sq1024"] == "mfma16_64x64x64_w4x1k2d"

@@ -78,7 +78,7 @@ def test_noalloc_matches_the_workspace_entry_point():
         outs, ref, bound, pick = _pair(-1, M, N, K, seed, ws)
         _check(outs, ref, bound)
         picks.append(pick)
-    assert all(p.startswith("sk_") for p in picks), picks
+    assert all(p.startswith(("sk_", "sk16_")) for p in picks), picks
 
 
 def test_noalloc_forced_configurations():
@@ -88,7 +88,7 @@ def test_noalloc_forced_configurations():
     import tiled_fp32_gemm_02_amd as sg
     ws = torch.zeros(sg.sgemm_workspace_size(-1), dtype=torch.uint8, device="cuda")
     names = sg.configs()
-    ids = [i for i, n in enumerate(names) if n.startswith("sk_")] + [names.index("mfma_64x64x32_w2x2k2d")]
+    ids = [i for i, n in enumerate(names) if n.startswith(("sk_", "sk16_"))] + [names.index("mfma_64x64x32_w2x2k2d")]
     for cid in ids:
         for (M, N, K), seed, offset in (((1100, 1300, 1028), 3, 0), ((300, 260, 132), 4, 0),
                                         ((257, 255, 131), 5, 1)):

@@ -220,6 +220,19 @@ uint64_t tile_count(const Config &c, int M, int N)
 }
 
 // The stream-K kernel splits work with 32-bit arithmetic: (CUs + 1) * work < 2^31.
+// Stream-K split of `tiles` tiles of `iters` K-tiles over `cus` CUs: whole rounds of tiles,
+// one per CU each, except the last round, run as plain tiles (the first dp tiles); the last
+// round's tiles are shared by one workgroup per CU, or one per K-tile step when there are
+// fewer, so every range is non-empty. dp is a whole number of XCD rounds (8), as the
+// kernel's workgroup order needs. Returns the grid.
+int sk_split(int tiles, int iters, int cus, int &dp)
+{
+    dp = tiles > cus ? (tiles - 1) / cus * cus : 0;
+    dp -= dp % 8;
+    const int shared = (tiles - dp) * iters;
+    return dp + (shared < cus ? shared : cus);
+}
+
 bool sk_work_fits(const Config &c, int M, int N, int K, int cus)
 {
     const uint64_t tiles = tile_count(c, M, N);
@@ -236,8 +249,9 @@ bool sk_work_fits(const Config &c, int M, int N, int K, int cus)
 //    tiles of work (one unit is a 64 x 64 tile, 2 * 64 * 64 * K flop) at the CU's measured
 //    speed, given as microseconds per MFLOP with one workgroup resident (L = 1) or
 //    several (L >= 2). Stream-K candidates (only with a large enough workspace) give
-//    every CU the same share, tiles * units / CUs, plus a fixed cost for the partial
-//    tiles.
+//    every CU the same share, tiles * units / CUs, at the one- or several-workgroup speed
+//    (several when whole-tile rounds run beside the shared one), plus a fixed cost and a
+//    cost per round.
 //  - HBM: each operand's compulsory bytes (A and B read, C written) at a bandwidth that
 //    depends on the contiguous bytes per row a tile reads (BK floats of A, BN of B and C):
 //    5.7 TB/s for 512-byte rows, falling as (bytes / 512)^0.19 for shorter ones (measured
@@ -260,83 +274,98 @@ struct Candidate {
 // GPT-2-small linear layers, long-K and skinny products down to 16 rows or columns) and 10
 // batched ones at half weight (attention's 12-head products 1024 x 1024 x 64 and
 // 1024 x 64 x 1024, the first with K from 16 to 256, and 48 or 3 heads of other sizes),
-// whose short K loops set the per-round costs. With the candidates below the model picks,
-// on average, a configuration within 1.4% of the fastest of all those swept, and the
-// fastest on 256^3, 1024^3, 1536^3, 4096^3, the three GPT-2 layers and the attention
-// scores; the worst misses are 16384 x 16 x 16384 (19%), 768^3 (13%) and the attention
-// values product (10%), both fastest on mfma16_16x64x64_w1x1k4d, which the fit mispredicts
-// on small products and so is left out, and 16 x 16384 x 16384 (8%). Candidates were chosen by dropping, one at a time, those
-// whose removal improved the picks. Unaligned (rows only 4-byte aligned): 24 odd-sized shapes
-// (255^3 ... 6143^3, 2999^3, 511 x 4095 x 4095, 1000 x 1537 x 777, the GPT-2 layers one
-// short in each dimension, long-K and skinny ones); picks average within 0.4% of the
-// fastest, the worst 3.3% (2559^3), and the ragged 1000 x 1537 x 777 and the three GPT-2
-// layers get the fastest.
+// whose short K loops set the per-round costs. Unaligned (rows only 4-byte aligned): 24
+// odd-sized shapes (255^3 ... 6143^3, 2999^3, 511 x 4095 x 4095, 1000 x 1537 x 777, the
+// GPT-2 layers one short in each dimension, long-K and skinny ones). Candidates were chosen
+// by dropping, one at a time, those whose removal improved the picks, scored both for
+// callers with a stream-K workspace and without one. Aligned, the picks average within
+// 1.4% of the fastest of all those swept; the benchmark shapes get the fastest (the GPT-2
+// QKV layer and 1536^3 on the 16x16-block stream-K tile when a workspace is passed) except
+// the attention values product (7%); the worst misses are 16384 x 16 x 16384 (19%), 768^3
+// (13%) and 16 x 16384 x 16384 (8%). Unaligned, within 0.6% on average and 5.7% at worst,
+// the ragged 1000 x 1537 x 777 at 2.4% (33.5 against 32.7 us for the 64 x 128 tile).
 const Candidate kCandidates[] = {
-    {"mfma_256x256x32_w2x4d", 0.00, 10.68, 1.7024, 1.7316}, // one workgroup per CU (4096^3)
     {"mfma_128x128x32_w2x2k2d", 0.00, 5.53, 1.8246, 1.7719},
-    {"mfma16_64x128x32_w4x2k1d", 0.56, 1.63, 1.9927, 1.7666},
-    {"mfma16_64x64x64_w4x1k2d", 1.28, 1.32, 2.0562, 1.8045}, // 1024^3, 3072^3
-    {"mfma16_64x64x32_w4x1k1d", 0.08, 0.86, 2.7331, 1.8368}, // GPT-2 MLP-up
+    {"mfma_256x128x32_w4x2d", 0.00, 0.00, 1.9088, 3.3975},
+    {"mfma_256x256x32_w2x4d", 0.00, 10.68, 1.7024, 1.7316}, // one workgroup per CU (4096^3)
+    {"mfma_32x128x64_w1x4k2d", 2.09, 1.92, 2.2306, 1.9510},
     {"mfma_32x32x64_w1x1k4d", 2.02, 0.84, 4.6692, 2.1984}, // GPT-2 MLP-down
-    {"mfma16_16x16x128_w1x1k4d", 2.15, 0.50, 16.3796, 2.7659},
-    {"mfma16_16x64x128_w1x1k4d", 2.34, 0.70, 3.5422, 2.4972}, // 16- and 32-row products
-    {"mfma16_32x64x128_w2x1k4d", 0.99, 2.40, 2.0417, 2.0110},
-    {"mfma16_64x64x64_w2x2k2d", 1.26, 1.35, 2.0657, 1.8103},
+    {"mfma_32x64x64_w1x2k2d", 2.66, 1.11, 2.5009, 2.0088},
+    {"mfma_32x96x64_w1x1k4d", 3.32, 2.26, 2.5438, 2.1241},
     {"mfma_64x128x32_w2x2k2d", 0.70, 2.33, 2.0154, 1.7883},
+    {"mfma_64x64x32_w2x2k2d", 0.00, 2.00, 2.7466, 1.9709},
     {"mfma_64x64x64_w2x2k4d", 0.20, 4.07, 2.1338, 1.9515},
     {"mfma16_128x64x32_w8x1k1d", 0.45, 1.61, 2.0761, 1.8242},
-    {"mfma_64x64x32_w2x2k2d", 0.00, 2.00, 2.7466, 1.9709},
-    {"mfma16_64x16x64_w4x1k1d", 2.09, 0.27, 4.5657, 2.7117},
-    {"mfma16_16x16x256_w1x1k4d", 1.99, 0.87, 10.9830, 3.5898}, // 256^3, 16-wide products
+    {"mfma16_16x16x128_w1x1k4d", 2.15, 0.50, 16.3796, 2.7659},
     {"mfma16_16x16x128_w1x1k4p2d", 2.66, 0.49, 9.5499, 3.4119},
-    {"mfma16_32x32x128_w2x2k2d", 1.99, 0.99, 2.8169, 2.2152}, // 512^3, 32- and 64-wide products
-    {"mfma_32x96x64_w1x1k4d", 3.32, 2.26, 2.5438, 2.1241},
-    {"mfma16_32x96x32_w2x2k1d", 1.70, 0.36, 3.8224, 2.3231}, // GPT-2 QKV, 1536^3
-    {"mfma16_32x96x64_w2x2k2d", 2.09, 1.14, 2.8095, 2.2418},
+    {"mfma16_16x16x256_w1x1k4d", 1.99, 0.87, 10.9830, 3.5898}, // 256^3
+    {"mfma16_16x64x128_w1x1k4d", 2.34, 0.70, 3.5422, 2.4972},
+    {"mfma16_32x128x64_w2x2k2d", 1.57, 1.35, 2.2657, 1.9571},
+    {"mfma16_32x32x128_w2x2k2d", 1.99, 0.99, 2.8169, 2.2152},
+    {"mfma16_32x32x64_w2x2k1d", 2.11, 0.40, 4.1882, 2.3430}, // attention values
+    {"mfma16_32x64x128_w2x1k4d", 0.99, 2.40, 2.0417, 2.0110},
+    {"mfma16_32x96x128_w2x2k4d", 0.91, 3.37, 2.3607, 2.2939},
+    {"mfma16_32x96x64_w2x2k2d", 2.09, 1.14, 2.8095, 2.2418}, // GPT-2 QKV without a workspace
+    {"mfma16_64x128x32_w4x2k1d", 0.56, 1.63, 1.9927, 1.7666}, // attention scores
+    {"mfma16_64x16x64_w4x1k1d", 2.09, 0.27, 4.5657, 2.7117},
+    {"mfma16_64x64x128_w4x1k4d", 0.00, 4.26, 1.9058, 1.7591},
+    {"mfma16_64x64x32_w4x1k1d", 0.08, 0.86, 2.7331, 1.8368}, // GPT-2 MLP-up
+    {"mfma16_64x64x64_w2x2k2d", 1.26, 1.35, 2.0657, 1.8103},
+    {"mfma16_64x64x64_w4x1k2d", 1.28, 1.32, 2.0562, 1.8045}, // 1024^3
     {"mfma16_64x96x64_w4x2k1d", 2.02, 1.26, 2.4321, 2.1043},
-    {"mfma16_64x64x128_w4x1k4d", 0.00, 4.26, 1.9058, 1.7591}, // long K (1024 x 1024 x 8192, 1000 x 1000 x 4000)
 };
 const Candidate kUnalignedCandidates[] = {
-    {"mfma_256x256x32_w2x4d", 5.94, 0.00, 2.0225, 2.0671},
-    {"mfma_256x256x16_w2x4p2d", 7.88, 0.00, 1.9201, 2.0263},
-    {"mfma_128x128x32_w2x2k2d", 6.57, 0.00, 2.1279, 2.1380},
-    {"mfma_64x128x32_w2x2k2d", 2.32, 2.86, 2.2324, 2.0580}, // 1000 x 1537 x 777
-    {"mfma_64x64x32_w2x2k2d", 2.75, 2.73, 2.9376, 2.1774},
-    {"mfma_32x128x64_w1x4k2d", 3.65, 2.15, 3.4416, 2.5125},
-    {"mfma_32x64x64_w1x2k2d", 5.65, 0.00, 5.7274, 2.7701},
-    {"mfma16_128x64x32_w8x1k1d", 1.26, 3.67, 2.3279, 2.0705},
-    {"mfma16_64x128x32_w4x2k1d", 1.32, 3.72, 2.3340, 2.0783},
-    {"mfma16_64x64x64_w4x1k2d", 1.73, 2.72, 2.4920, 2.1934},
-    {"mfma16_64x64x64_w2x2k2d", 1.86, 2.40, 2.4844, 2.1924},
-    {"mfma16_64x64x32_w4x1k1d", 0.83, 2.57, 3.2597, 2.2475},
-    {"mfma16_64x16x64_w4x1k1d", 0.07, 0.00, 11.1018, 4.1094},
-    {"mfma16_32x128x64_w2x2k2d", 0.00, 3.39, 3.2870, 3.1858},
-    {"mfma16_32x64x128_w2x1k4d", 0.59, 2.83, 3.5119, 3.4162},
-    {"mfma16_32x64x64_w2x1k2d", 3.10, 0.36, 4.5025, 2.8383},
-    {"mfma16_32x32x128_w2x2k2d", 2.49, 1.29, 4.4149, 3.0238},
-    {"mfma16_32x32x64_w2x2k1d", 3.13, 0.38, 5.9164, 3.1477},
-    {"mfma16_16x64x128_w1x1k4d", 1.16, 2.59, 6.2842, 5.7675},
-    {"mfma16_16x16x256_w1x1k4d", 2.06, 0.19, 17.2871, 5.6646},
-    {"mfma16_16x16x128_w1x1k4p2d", 3.91, 0.51, 4.4454, 5.5433},
-    {"mfma16_16x16x128_w1x1k4d", 2.77, 0.21, 14.6886, 5.5336},
-    {"mfma_32x96x64_w1x1k4d", 2.30, 4.28, 4.0505, 2.8843},
-    {"mfma16_32x96x32_w2x2k1d", 2.87, 0.49, 4.2756, 2.6846}, // GPT-2 QKV one short, 1535^3
-    {"mfma16_32x96x64_w2x2k2d", 1.90, 1.94, 3.1783, 2.5940},
-    {"mfma16_64x96x64_w4x2k1d", 0.00, 1.21, 3.5439, 2.5614},
-    {"mfma16_32x96x128_w2x2k4d", 0.41, 4.50, 2.6868, 2.6500}, // GPT-2 MLP-down one short
-    {"mfma16_64x64x128_w4x1k4d", 0.20, 5.19, 2.3575, 2.3093}, // long K (999 x 999 x 3999)
+    {"mfma_256x256x32_w2x4d", 11.60, 0.00, 1.7854, 1.8544},
+    {"mfma_256x256x16_w2x4p2d", 12.78, 0.00, 1.7545, 1.7966},
+    {"mfma_128x128x32_w2x2k2d", 8.72, 0.00, 1.8399, 1.8067},
+    {"mfma_64x128x32_w2x2k2d", 3.07, 2.89, 2.0071, 1.7607},
+    {"mfma_64x64x32_w2x2k2d", 2.25, 3.59, 2.7145, 1.8655},
+    {"mfma_32x128x64_w1x4k2d", 4.22, 4.33, 2.1928, 1.9099},
+    {"mfma_32x64x64_w1x2k2d", 5.59, 2.40, 2.7398, 1.9596},
+    {"mfma16_128x64x32_w8x1k1d", 0.00, 5.51, 2.1567, 1.7931},
+    {"mfma16_64x128x32_w4x2k1d", 0.00, 5.52, 2.1800, 1.7990},
+    {"mfma16_64x64x64_w4x1k2d", 1.73, 3.99, 2.1388, 1.8218},
+    {"mfma16_64x64x64_w2x2k2d", 1.29, 3.99, 2.2337, 1.8231},
+    {"mfma16_64x64x32_w4x1k1d", 1.74, 2.41, 2.7993, 1.8952}, // 1000 x 1537 x 777
+    {"mfma16_64x16x64_w4x1k1d", 3.81, 0.02, 5.8753, 3.2649},
+    {"mfma16_32x128x64_w2x2k2d", 1.03, 4.68, 2.2379, 1.8437},
+    {"mfma16_32x64x128_w2x1k4d", 0.83, 5.10, 2.4195, 2.3993},
+    {"mfma16_32x64x64_w2x1k2d", 4.05, 1.35, 3.1301, 2.0748},
+    {"mfma16_32x32x128_w2x2k2d", 2.54, 2.22, 3.6887, 2.3801},
+    {"mfma16_32x32x64_w2x2k1d", 3.61, 0.84, 4.9674, 2.4750},
+    {"mfma16_16x64x128_w1x1k4d", 4.16, 3.15, 4.0959, 2.5782},
+    {"mfma16_16x16x256_w1x1k4d", 2.21, 2.43, 15.8183, 3.9950},
+    {"mfma16_16x16x128_w1x1k4p2d", 5.17, 1.15, 0.6230, 4.2812},
+    {"mfma16_16x16x128_w1x1k4d", 2.42, 0.87, 17.6683, 3.9763},
+    {"mfma_32x96x64_w1x1k4d", 3.10, 5.69, 2.5896, 1.9926},
+    {"mfma16_32x96x32_w2x2k1d", 3.34, 1.01, 3.7496, 2.2723}, // GPT-2 QKV one short
+    {"mfma16_32x96x64_w2x2k2d", 2.00, 3.40, 2.6920, 2.1282},
+    {"mfma16_64x96x64_w4x2k1d", 0.70, 5.13, 2.3708, 2.0133},
+    {"mfma16_32x96x128_w2x2k4d", 0.47, 7.06, 2.2167, 2.1710}, // GPT-2 MLP-down one short
+    {"mfma16_64x64x128_w4x1k4d", 0.38, 7.11, 1.9224, 1.8894}, // long K (999 x 999 x 3999)
 };
 const Candidate kSkCandidates[] = {
-    {"sk_128x128x32_w2x2k2p2", 19.09, 0.00, 1.8743, 1.8743},
-    {"sk_64x128x32_w2x2k2p2", 12.20, 0.00, 2.0418, 2.0418},
+    {"sk16_32x64x64_w2x1k2d", 6.30, 0.00, 3.7689, 2.3631},
+    {"sk16_64x64x32_w4x1k1d", 7.50, 0.00, 3.4726, 1.9353}, // GPT-2 QKV, 1536^3
+    {"sk_128x128x32_w2x2k2p2", 19.84, 0.00, 1.8525, 1.9200},
+    {"sk_64x128x32_w2x2k2p2", 12.55, 0.00, 2.0030, 1.9223}, // long K, few tiles
+};
+const Candidate kSkUnalignedCandidates[] = {
+    {"sk_64x128x32_w2x2k2d", 14.31, 0.21, 1.9721, 1.7961}, // 1535^3, 2999^3
+    {"sk16_64x64x32_w4x1k1d", 9.10, 0.94, 2.7304, 1.8988},
+    {"sk16_32x64x64_w2x1k2d", 7.62, 1.43, 3.0561, 2.0590},
 };
 constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
 constexpr int kNumUnalignedCandidates = sizeof(kUnalignedCandidates) / sizeof(kUnalignedCandidates[0]);
 constexpr int kNumSkCandidates = sizeof(kSkCandidates) / sizeof(kSkCandidates[0]);
+constexpr int kNumSkUnalignedCandidates = sizeof(kSkUnalignedCandidates) / sizeof(kSkUnalignedCandidates[0]);
+// A stream-K candidate is taken only when its modelled time, 3% longer, still beats the
+// data-parallel one: its shared tiles are the part of the model with the widest spread.
+constexpr double kSkMargin = 1.03;
 constexpr double kHbmBytesPerUs = 5.7e6;          // 5.7 TB/s for rows of 512 contiguous bytes
 constexpr double kHbmRowExponent = 0.19;
 constexpr double kL2BytesPerUs = 20.0e6;          // tile-fill bytes, 16-byte aligned rows
-constexpr double kL2BytesPerUsUnaligned = 14.75e6; // and 4-byte aligned rows
+constexpr double kL2BytesPerUsUnaligned = 16.8e6;  // and 4-byte aligned rows
 
 int find_config(const char *name)
 {
@@ -351,12 +380,13 @@ int find_config(const char *name)
 
 // Table ids of the candidates, looked up once.
 struct CandidateIds {
-    int id[kNumCandidates], un[kNumUnalignedCandidates], sk[kNumSkCandidates];
+    int id[kNumCandidates], un[kNumUnalignedCandidates], sk[kNumSkCandidates], sku[kNumSkUnalignedCandidates];
     CandidateIds()
     {
         for (int i = 0; i < kNumCandidates; ++i) id[i] = find_config(kCandidates[i].name);
         for (int i = 0; i < kNumUnalignedCandidates; ++i) un[i] = find_config(kUnalignedCandidates[i].name);
         for (int i = 0; i < kNumSkCandidates; ++i) sk[i] = find_config(kSkCandidates[i].name);
+        for (int i = 0; i < kNumSkUnalignedCandidates; ++i) sku[i] = find_config(kSkUnalignedCandidates[i].name);
     }
 };
 
@@ -374,8 +404,8 @@ double memory_us(const Config &c, int M, int N, int K, int batch, bool vec)
 }
 
 // The configuration with the least modelled time. Stream-K candidates are considered
-// only for one product (batch 1) with aligned operands, when `ws_bytes` holds their
-// workspace for `cus` compute units (cus > 0).
+// only for one product (batch 1), when `ws_bytes` holds their workspace for `cus` compute
+// units (cus > 0); for operands only 4-byte aligned, only direct-copy ones.
 int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0, int batch = 1)
 {
     static const CandidateIds ids;
@@ -403,21 +433,29 @@ int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0, int 
             best_us = us;
         }
     }
-    for (int i = 0; vec && cus > 0 && batch == 1 && i < kNumSkCandidates; ++i) {
-        const Candidate &cand = kSkCandidates[i];
-        if (ids.sk[i] < 0)
+    const Candidate *sk_table = vec ? kSkCandidates : kSkUnalignedCandidates;
+    const int *sk_ids = vec ? ids.sk : ids.sku;
+    const int sk_len = vec ? kNumSkCandidates : kNumSkUnalignedCandidates;
+    for (int i = 0; cus > 0 && batch == 1 && i < sk_len; ++i) {
+        const Candidate &cand = sk_table[i];
+        if (sk_ids[i] < 0)
             continue;
-        const Config &c = kConfigs[ids.sk[i]];
+        const Config &c = kConfigs[sk_ids[i]];
         const uint64_t tiles = tile_count(c, M, N);
         if (!sk_work_fits(c, M, N, K, cus) || ws_bytes < sk_workspace_bytes(c, cus))
             continue;
+        // whole-tile rounds (dp / CUs of them) and the shared last round, with the CU's
+        // work spread evenly; one workgroup per CU when every tile is shared (dp = 0)
+        int dp = 0;
+        sk_split((int)tiles, (int)cdiv64(K, c.bk), cus, dp);
         const double units = (double)c.bm * c.bn / 4096.0;
-        double us = cand.fixed_us + (double)tiles * units / (double)kCUs * unit_mflop * cand.us_one;
+        double us = cand.fixed_us + ((double)dp / (double)kCUs + 1.0) * cand.round_us +
+                    (double)tiles * units / (double)kCUs * unit_mflop * (dp == 0 ? cand.us_one : cand.us_many);
         const double mem = memory_us(c, M, N, K, 1, vec);
         us = us > mem ? us : mem;
-        if (us < best_us) {
-            best = ids.sk[i];
-            best_us = us;
+        if (us * kSkMargin < best_us) {
+            best = sk_ids[i];
+            best_us = us * kSkMargin;
         }
     }
     return best;
@@ -533,8 +571,7 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
         sk.iters = (int)cdiv64(K, c.bk);
         sk.group_m = c.group_m;
         sk.work = (int)tiles * sk.iters;
-        // At most one workgroup per K-tile step, so every workgroup's range is non-empty.
-        const int grid = sk.work < cus ? sk.work : cus;
+        const int grid = sk_split((int)tiles, sk.iters, cus, sk.dp);
         const hipError_t e = c.launch_sk(p, sk, grid, opA != 0, opB != 0, vec, edge, dma_ok, stream);
         return e == hipSuccess ? 0 : (int)e;
     }
@@ -948,10 +985,11 @@ int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3
     }
     const uint64_t tiles = tile_count(c, M, N);
     if (c.kind == KIND_SK) {
-        // One workgroup per compute unit (MI355X has 256), at most one per K-tile step.
+        // The split of a 256-CU device (MI355X): whole-tile rounds, then one workgroup per
+        // CU (at most one per K-tile step) for the last round's tiles.
         if (!sk_work_fits(c, M, N, K, 256)) return SGEMM_ERROR_TOO_LARGE;
-        const uint64_t work = tiles * cdiv64(K, c.bk);
-        grid[0] = work < 256 ? (int)work : 256; grid[1] = 1; grid[2] = 1;
+        int dp = 0;
+        grid[0] = sk_split((int)tiles, (int)cdiv64(K, c.bk), 256, dp); grid[1] = 1; grid[2] = 1;
         block[0] = c.threads; block[1] = 1; block[2] = 1;
         return 0;
     }

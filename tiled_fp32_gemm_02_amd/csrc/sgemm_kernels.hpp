@@ -1092,24 +1092,31 @@ sgemm_mfma_strided(StridedArgs p, int group_m)
 
 // Work split of a stream-K launch (computed on the host).
 struct StreamK {
-    float *partials;        // 2 slots of BM*BN floats per workgroup: its first and its last tile
+    float *partials;        // 2 slots of BM*BN floats per sharing workgroup: its first and last tile
     unsigned *counters;     // one per tile; zero before the launch, left zero after it
     int tiles_m, tiles_n;
     int iters;              // K-tiles per output tile, I
     int group_m;
     int work;               // tiles * I, the K-tile steps of the whole product; (grid+1)*work < 2^31
+    int dp;                 // leading tiles taken whole, one per workgroup (a multiple of 8); the
+                            // other workgroups share the remaining steps
 };
 
 // Stream-K: the tiles * I K-tile steps of the product, taken in tile order, are split
-// into gridDim.x equal contiguous ranges, one per workgroup, so every CU does the same
-// amount of work whatever the tile count. The grid is at most the number of steps, so
-// no range is empty and the workgroups whose ranges meet a tile are exactly those
-// between the owners of its first and last step. A workgroup walks its range tile by tile. A
-// tile wholly inside the range gets the ordinary epilogue. A tile the range covers only
-// in part leaves its partial sum in the workgroup's slot and takes a ticket from the
-// tile's counter; the contributor that draws the last ticket adds the partial sums in
-// contributor order (the same order whoever comes last, so results do not depend on
-// timing) and writes C. No workgroup ever waits for another.
+// into contiguous ranges, one per workgroup, so every CU does the same amount of work
+// whatever the tile count. The first sk.dp workgroups take one whole tile each (the
+// first sk.dp tiles, as the data-parallel kernel would); the other G - dp workgroups
+// split the remaining steps into equal ranges. Their count is at most the number of those
+// steps, so no range is empty and the workgroups whose ranges meet a tile are exactly
+// those between the owners of its first and last step. A workgroup walks its range tile
+// by tile. A tile wholly inside the range gets the ordinary epilogue. A tile the range
+// covers only in part leaves its partial sum in the workgroup's slot and takes a ticket
+// from the tile's counter; the contributor that draws the last ticket adds the partial
+// sums in contributor order (the same order whoever comes last, so results do not depend
+// on timing) and writes C. No workgroup ever waits for another.
+// Each part is spread over the XCDs on its own (dp is a multiple of their count, so a
+// workgroup keeps its XCD), so the whole tiles and the shared ranges each land evenly on
+// every XCD, and neighbouring ranges share an XCD's L2.
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
           bool EDGE, int MB>
 __global__ void __launch_bounds__(WGM * WGN * WGK * 64)
@@ -1123,11 +1130,16 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
     __shared__ unsigned ticket;
 
     const int G = gridDim.x;
-    const int g = xcd_contiguous(blockIdx.x, G);         // neighbouring ranges share an XCD's L2
     const int W = sk.work;
     const int I = sk.iters;
-    auto range_start = [&](int wg) { return wg * W / G; };
-    auto owner = [&](int w) { return ((w + 1) * G - 1) / W; };   // workgroup whose range holds w
+    const int D = sk.dp;
+    const int WS = W - D * I, GS = G - D;               // the shared steps and their workgroups
+    const int b = blockIdx.x;
+    const int g = b < D ? xcd_contiguous(b, D) : D + xcd_contiguous(b - D, GS);
+    auto range_start = [&](int wg) { return wg <= D ? wg * I : D * I + (wg - D) * WS / GS; };
+    auto owner = [&](int w) {                            // workgroup whose range holds step w
+        return w < D * I ? w / I : D + ((w - D * I + 1) * GS - 1) / WS;
+    };
     auto slot_of = [&](int wg, int t) { return t == range_start(wg) / I ? 0 : 1; };
 
     const int w_end = range_start(g + 1);
@@ -1172,7 +1184,7 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
             // to buffer_wbl2 / buffer_inv of the whole XCD L2; with it the GPT-2 QKV layer
             // took 143 us instead of 41 us, so the per-access form is kept.
             if (holds) {
-                float *dst = sk.partials + ((int64_t)g * 2 + slot_of(g, t)) * TILE + wslot * PER_WAVE;
+                float *dst = sk.partials + ((int64_t)(g - D) * 2 + slot_of(g, t)) * TILE + wslot * PER_WAVE;
 #pragma unroll
                 for (int a = 0; a < T::TM; ++a)
 #pragma unroll
@@ -1194,7 +1206,7 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
                 // Every contributor's partial, this workgroup's included, is in its slot: sum
                 // them in contributor order straight into acc.
                 for (int c = first; holds && c <= last; ++c) {
-                    const float *src = sk.partials + ((int64_t)c * 2 + slot_of(c, t)) * TILE + wslot * PER_WAVE;
+                    const float *src = sk.partials + ((int64_t)(c - D) * 2 + slot_of(c, t)) * TILE + wslot * PER_WAVE;
 #pragma unroll
                     for (int a = 0; a < T::TM; ++a)
 #pragma unroll
