@@ -462,19 +462,22 @@ def test_workspace_size_without_a_device_is_zero():
 
 
 def test_launch_shape_stream_k():
-    """Whole rounds of 256 tiles but the last run one tile per workgroup; the last round's
-    tiles x K-tiles are shared by 256 workgroups, or one per K-tile step when fewer."""
+    """Direct-copy configurations run whole rounds of 256 tiles but the last one tile per
+    workgroup; the remaining tiles x K-tiles (all of them for register-staged
+    configurations) are shared by 256 workgroups, or one per K-tile step when fewer."""
     for cid in sk_ids():
-        bm, bn, bk = (int(x) for x in sg.sgemm_config_name(cid).split("_")[1].split("x"))
+        name = sg.sgemm_config_name(cid)
+        bm, bn, bk = (int(x) for x in name.split("_")[1].split("x"))
         for M, N, K in [(1024, 2304, 768), (100, 130, 64), (1000, 1537, 777), (4096, 4096, 256), (64, 64, 4096)]:
             tiles, iters = -(-M // bm) * -(-N // bn), -(-K // bk)
-            whole = 256 * ((tiles - 1) // 256)
+            whole = 256 * ((tiles - 1) // 256) if name.endswith("d") else 0
             st, grid, block = sg.sgemm_launch_shape(cid, M, N, K)
             assert st == 0 and grid == (whole + min(256, (tiles - whole) * iters), 1, 1), (M, N, K, grid)
             assert block[0] in (256, 512, 1024)
-        # a 64 x 128 tile's QKV layer: 288 tiles, so 256 whole and 32 shared by 256 workgroups
+        # a 64 x 128 direct-copy tile's QKV layer: 288 tiles, so 256 whole and 32 shared by 256
+        # workgroups; the register-staged one shares all 288 among 256
         if (bm, bn) == (64, 128):
-            assert sg.sgemm_launch_shape(cid, 1024, 2304, 768)[1] == (512, 1, 1)
+            assert sg.sgemm_launch_shape(cid, 1024, 2304, 768)[1] == ((512 if name.endswith("d") else 256), 1, 1)
 
 
 def test_select_without_workspace_never_picks_stream_k():

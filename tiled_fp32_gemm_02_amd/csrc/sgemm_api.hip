@@ -220,14 +220,17 @@ uint64_t tile_count(const Config &c, int M, int N)
 }
 
 // The stream-K kernel splits work with 32-bit arithmetic: (CUs + 1) * work < 2^31.
-// Stream-K split of `tiles` tiles of `iters` K-tiles over `cus` CUs: whole rounds of tiles,
-// one per CU each, except the last round, run as plain tiles (the first dp tiles); the last
-// round's tiles are shared by one workgroup per CU, or one per K-tile step when there are
+// Stream-K split of `tiles` tiles of `iters` K-tiles over `cus` CUs. Direct-copy
+// configurations (`whole` true) run whole rounds of tiles, one per CU each, except the last
+// round, as plain tiles (the first dp tiles), and share the last round's tiles; register-
+// staged ones share every tile (dp = 0): their stream-K kernels hold more than 128 registers,
+// so only one workgroup fits a CU and whole-tile rounds beside the shared one would not
+// overlap. The shared steps go to one workgroup per CU, or one per step when there are
 // fewer, so every range is non-empty. dp is a whole number of XCD rounds (8), as the
 // kernel's workgroup order needs. Returns the grid.
-int sk_split(int tiles, int iters, int cus, int &dp)
+int sk_split(int tiles, int iters, int cus, bool whole, int &dp)
 {
-    dp = tiles > cus ? (tiles - 1) / cus * cus : 0;
+    dp = whole && tiles > cus ? (tiles - 1) / cus * cus : 0;
     dp -= dp % 8;
     const int shared = (tiles - dp) * iters;
     return dp + (shared < cus ? shared : cus);
@@ -345,15 +348,15 @@ const Candidate kUnalignedCandidates[] = {
     {"mfma16_64x64x128_w4x1k4d", 0.38, 7.11, 1.9224, 1.8894}, // long K (999 x 999 x 3999)
 };
 const Candidate kSkCandidates[] = {
-    {"sk16_32x64x64_w2x1k2d", 6.30, 0.00, 3.7689, 2.3631},
-    {"sk16_64x64x32_w4x1k1d", 7.50, 0.00, 3.4726, 1.9353}, // GPT-2 QKV, 1536^3
-    {"sk_128x128x32_w2x2k2p2", 19.84, 0.00, 1.8525, 1.9200},
-    {"sk_64x128x32_w2x2k2p2", 12.55, 0.00, 2.0030, 1.9223}, // long K, few tiles
+    {"sk16_32x64x64_w2x1k2d", 6.48, 0.00, 3.8051, 2.2519},
+    {"sk16_64x64x32_w4x1k1d", 7.97, 0.00, 3.4711, 1.9340}, // GPT-2 QKV, 1536^3, 2560^3
+    {"sk_128x128x32_w2x2k2p2", 0.00, 20.97, 1.8670, 0.0000},
+    {"sk_64x128x32_w2x2k2p2", 0.00, 12.80, 2.0335, 0.0000}, // long K, few tiles
 };
 const Candidate kSkUnalignedCandidates[] = {
-    {"sk_64x128x32_w2x2k2d", 14.31, 0.21, 1.9721, 1.7961}, // 1535^3, 2999^3
-    {"sk16_64x64x32_w4x1k1d", 9.10, 0.94, 2.7304, 1.8988},
-    {"sk16_32x64x64_w2x1k2d", 7.62, 1.43, 3.0561, 2.0590},
+    {"sk_64x128x32_w2x2k2d", 15.09, 0.00, 1.9619, 1.7960}, // 1535^3, 2999^3
+    {"sk16_64x64x32_w4x1k1d", 9.95, 0.63, 2.7560, 1.9178},
+    {"sk16_32x64x64_w2x1k2d", 8.06, 1.40, 3.0379, 2.0663},
 };
 constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
 constexpr int kNumUnalignedCandidates = sizeof(kUnalignedCandidates) / sizeof(kUnalignedCandidates[0]);
@@ -447,7 +450,7 @@ int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0, int 
         // whole-tile rounds (dp / CUs of them) and the shared last round, with the CU's
         // work spread evenly; one workgroup per CU when every tile is shared (dp = 0)
         int dp = 0;
-        sk_split((int)tiles, (int)cdiv64(K, c.bk), cus, dp);
+        sk_split((int)tiles, (int)cdiv64(K, c.bk), cus, c.dma, dp);
         const double units = (double)c.bm * c.bn / 4096.0;
         double us = cand.fixed_us + ((double)dp / (double)kCUs + 1.0) * cand.round_us +
                     (double)tiles * units / (double)kCUs * unit_mflop * (dp == 0 ? cand.us_one : cand.us_many);
@@ -571,7 +574,7 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
         sk.iters = (int)cdiv64(K, c.bk);
         sk.group_m = c.group_m;
         sk.work = (int)tiles * sk.iters;
-        const int grid = sk_split((int)tiles, sk.iters, cus, sk.dp);
+        const int grid = sk_split((int)tiles, sk.iters, cus, c.dma, sk.dp);
         const hipError_t e = c.launch_sk(p, sk, grid, opA != 0, opB != 0, vec, edge, dma_ok, stream);
         return e == hipSuccess ? 0 : (int)e;
     }
@@ -985,11 +988,12 @@ int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3
     }
     const uint64_t tiles = tile_count(c, M, N);
     if (c.kind == KIND_SK) {
-        // The split of a 256-CU device (MI355X): whole-tile rounds, then one workgroup per
-        // CU (at most one per K-tile step) for the last round's tiles.
+        // The split of a 256-CU device (MI355X): whole-tile rounds (direct-copy
+        // configurations), then one workgroup per CU (at most one per K-tile step) for the
+        // shared tiles.
         if (!sk_work_fits(c, M, N, K, 256)) return SGEMM_ERROR_TOO_LARGE;
         int dp = 0;
-        grid[0] = sk_split((int)tiles, (int)cdiv64(K, c.bk), 256, dp); grid[1] = 1; grid[2] = 1;
+        grid[0] = sk_split((int)tiles, (int)cdiv64(K, c.bk), 256, c.dma, dp); grid[1] = 1; grid[2] = 1;
         block[0] = c.threads; block[1] = 1; block[2] = 1;
         return 0;
     }

@@ -1130,23 +1130,29 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
     __shared__ unsigned ticket;
 
     const int G = gridDim.x;
-    const int W = sk.work;
-    const int I = sk.iters;
-    const int D = sk.dp;
-    const int WS = W - D * I, GS = G - D;               // the shared steps and their workgroups
+    int I = sk.iters;
     const int b = blockIdx.x;
+    int D = sk.dp;
+    int WS = sk.work - D * I, GS = G - D;               // the shared steps and their workgroups
     const int g = b < D ? xcd_contiguous(b, D) : D + xcd_contiguous(b - D, GS);
-    auto range_start = [&](int wg) { return wg <= D ? wg * I : D * I + (wg - D) * WS / GS; };
+    // The split's constants are kept in vector registers: they serve a few computations per
+    // tile, and held as scalars across the K loop they pushed its scalar registers into spills
+    // (re-reading them from the kernel's arguments instead made the loop 20% slower). Results
+    // that steer control flow are made uniform again with readfirstlane.
+    asm volatile("" : "+v"(D), "+v"(WS), "+v"(GS), "+v"(I));
+    auto range_start = [&](int wg) {
+        return __builtin_amdgcn_readfirstlane(wg <= D ? wg * I : D * I + (wg - D) * WS / GS);
+    };
     auto owner = [&](int w) {                            // workgroup whose range holds step w
-        return w < D * I ? w / I : D + ((w - D * I + 1) * GS - 1) / WS;
+        return __builtin_amdgcn_readfirstlane(w < D * I ? w / I : D + ((w - D * I + 1) * GS - 1) / WS);
     };
     auto slot_of = [&](int wg, int t) { return t == range_start(wg) / I ? 0 : 1; };
 
     const int w_end = range_start(g + 1);
     for (int w = range_start(g); w < w_end;) {
-        const int t = w / I;
-        const int kt0 = w - t * I;
-        const int kt1 = (w_end - t * I) < I ? (w_end - t * I) : I;
+        const int t = __builtin_amdgcn_readfirstlane(w / I);
+        const int kt0 = __builtin_amdgcn_readfirstlane(w - t * I);
+        const int kt1 = __builtin_amdgcn_readfirstlane((w_end - t * I) < I ? (w_end - t * I) : I);
         int tm, tn;
         band_coords(t, sk.tiles_m, sk.tiles_n, sk.group_m, tm, tn);
         typename T::acc_t acc[T::TM][T::TN];
@@ -1157,7 +1163,7 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
         asm volatile("" : "+v"(tid_l));
         const int lane = tid_l & 63, wslot = (tid_l >> 6) % (WGM * WGN);
         const bool holds = T::product(p, smem, tm * BM, tn * BN, kt0, kt1, acc, tid_l);
-        bool finish = kt0 == 0 && kt1 == I;              // the whole tile is this workgroup's
+        bool finish = kt0 == 0 && kt1 == __builtin_amdgcn_readfirstlane(I);   // the whole tile is this workgroup's
         if (!finish) {
             const int first = owner(t * I), last = owner(t * I + I - 1);
             // Ordering of the hand-off. The accesses are relaxed, so the C++/HIP memory
@@ -1184,7 +1190,7 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
             // to buffer_wbl2 / buffer_inv of the whole XCD L2; with it the GPT-2 QKV layer
             // took 143 us instead of 41 us, so the per-access form is kept.
             if (holds) {
-                float *dst = sk.partials + ((int64_t)(g - D) * 2 + slot_of(g, t)) * TILE + wslot * PER_WAVE;
+                float *dst = sk.partials + ((int64_t)(g - sk.dp) * 2 + slot_of(g, t)) * TILE + wslot * PER_WAVE;
 #pragma unroll
                 for (int a = 0; a < T::TM; ++a)
 #pragma unroll
@@ -1206,7 +1212,7 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
                 // Every contributor's partial, this workgroup's included, is in its slot: sum
                 // them in contributor order straight into acc.
                 for (int c = first; holds && c <= last; ++c) {
-                    const float *src = sk.partials + ((int64_t)(c - D) * 2 + slot_of(c, t)) * TILE + wslot * PER_WAVE;
+                    const float *src = sk.partials + ((int64_t)(c - sk.dp) * 2 + slot_of(c, t)) * TILE + wslot * PER_WAVE;
 #pragma unroll
                     for (int a = 0; a < T::TM; ++a)
 #pragma unroll
@@ -1224,7 +1230,7 @@ sgemm_mfma_sk(GemmArgs p, StreamK sk)
         }
         if (finish && holds)
             T::epilogue(p, tm * BM, tn * BN, acc, tid_l);
-        w = (t + 1) * I;
+        w = __builtin_amdgcn_readfirstlane((t + 1) * I);
         __syncthreads();                                 // the LDS ring is reused by the next tile
     }
 }
