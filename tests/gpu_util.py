@@ -21,15 +21,15 @@ class DevMatrix:
     """A rows x ld float32 matrix inside a flat device buffer with guard bands.
 
     `offset` shifts the start by that many floats (0..3) to test unaligned bases.
-    Columns >= `cols` (the ld gap) and the guard bands hold CANARY.
+    Columns >= `cols` (the ld gap) and the guard bands hold `gap` (CANARY by default).
     """
 
     def __init__(self, host: np.ndarray | None, rows: int, cols: int, ld: int, offset: int = 0,
-                 fill=None):
+                 fill=None, gap=CANARY):
         import torch
         self.rows, self.cols, self.ld, self.offset = rows, cols, ld, offset
         n = rows * ld
-        self.flat = np.full(GUARD + offset + n + GUARD, CANARY, dtype=np.float32)
+        self.flat = np.full(GUARD + offset + n + GUARD, gap, dtype=np.float32)
         win = self.flat[GUARD + offset: GUARD + offset + n].reshape(rows, ld) if n else None
         if n:
             if host is not None:
