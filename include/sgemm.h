@@ -256,15 +256,18 @@ int sgemm_strided_batched_general(int config, int opA, int opB, int M, int N, in
 
 /*
  * sgemm_general with a workspace, which lets the library use stream-K configurations
- * (names starting "sk_"). Those split the product's tiles x K-tiles work into one equal
- * contiguous share per compute unit, so the chip stays full when the tile count does
- * not divide evenly over the compute units and K is long enough to pay for the fixup
- * (for example 1536^3, 2560^3 and 3072^3).
+ * (names starting "sk_" or "sk16_"). Those split the product's tiles x K-tiles work into
+ * one equal contiguous share per compute unit, so the chip stays full when the tile count
+ * does not divide evenly over the compute units (for example the GPT-2 QKV layer, 1536^3
+ * and 2560^3). The direct-copy ones (names ending "d") first run every whole round of
+ * tiles but the last one tile per workgroup and split only the last round's tiles; the
+ * register-staged ones split all of them.
  * A tile shared by several workgroups is finished by the one that arrives last, which
  * adds the partial sums in a fixed order: results stay bitwise reproducible from run
- * to run, and within the same error bound as every other configuration. Stream-K runs
- * on 16-byte aligned operands (as defined for sgemm); with unaligned ones a stream-K
- * configuration runs the data-parallel kernel of its tile instead.
+ * to run, and within the same error bound as every other configuration. On operands only
+ * 4-byte aligned, a direct-copy stream-K configuration runs with the unaligned copy form
+ * (sgemm_config_describe) and a register-staged one runs the data-parallel kernel of its
+ * tile instead.
  *
  *  workspace        device memory of workspace_bytes, 16-byte aligned, owned by the
  *                   caller. Zero-fill it once before its first use: its first 64 KiB
@@ -322,7 +325,8 @@ int sgemm_general_noalloc(int config, int opA, int opB, int M, int N, int K, flo
 
 /*
  * Workspace bytes that stream-K configuration `config` needs on the current device
- * (64 KiB of counters plus two partial tiles per compute unit), or with config == -1
+ * (64 KiB of counters plus two partial tiles per compute unit: one sharing workgroup per
+ * compute unit at most), or with config == -1
  * the most any of them needs. 0 for other configurations, or when the device cannot be
  * queried.
  */
@@ -366,7 +370,8 @@ const char *sgemm_config_name(int config);
  * "Tile parameters"), as this library sizes them:
  *   name          as sgemm_config_name
  *   kind          tile16 (one output per thread), mfma (one workgroup per tile),
- *                 streamk (equal shares of tiles x K-tiles per compute unit), valu
+ *                 streamk (whole-tile rounds, then equal shares of the remaining tiles x
+ *                 K-tiles per compute unit), valu
  *                 (register micro-tile on vector FMAs)
  *   tile          BMxBNxBK: the workgroup's output tile and the k depth of one LDS stage
  *   waves         WGMxWGN: waves over the tile (1x1 for the non-matrix kinds)
@@ -403,8 +408,10 @@ int sgemm_select_config(int M, int N, int K, float alpha,
 /*
  * Launch shape of configuration `config` for an M x N x K product (host logic only).
  * Writes grid[3] and block[3] (dim3 order x, y, z). Stream-K configurations launch one
- * workgroup per compute unit, and at most one per K-tile step (tiles x ceil(K / BK));
- * the shape reported for them assumes MI355X's 256 compute units. Returns 0, SGEMM_ERROR_BAD_CONFIG,
+ * workgroup per tile of the whole rounds they run unsplit (direct-copy ones: 256 x
+ * floor((tiles - 1) / 256)), then one per compute unit for the shared tiles, and at most
+ * one per K-tile step of those; the shape reported for them assumes MI355X's 256 compute
+ * units. Returns 0, SGEMM_ERROR_BAD_CONFIG,
  * SGEMM_ERROR_TOO_LARGE, or -1/-2/-3 for a negative M/N/K.
  */
 int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3]);
