@@ -319,6 +319,25 @@ def test_config_describe_every_id():
     assert d["lds_bytes"] == str(2 * 32 * 512 * 4) and d["unaligned"] == "direct-16B-unaligned"
 
 
+def test_select_config_repeats_and_interleaves():
+    """The host keeps a small memo of recent choices per thread: the pick for a shape is the
+    same however queries for other shapes (more than the memo holds) and alignments are
+    interleaved with it."""
+    names = sg.configs()
+    shapes = [(256, 256, 256), (1024, 2304, 768), (4096, 4096, 4096), (1000, 1537, 777), (1024, 768, 3072),
+              (8192, 32, 8192), (32, 8192, 8192), (1536, 1536, 1536), (3000, 3000, 3000), (16, 16384, 16384),
+              (1024, 1024, 64), (512, 512, 8192)]
+    def pick(M, N, K, lda, ws):
+        return sg.sgemm_select_config_ws(M, N, K, 1.0, BAD, lda, BAD, N, BAD, N, ws)
+    first = {(s, a, w): pick(*s, s[2] + a, w) for s in shapes for a in (0, 1) for w in (0, 1 << 26)}
+    rng = __import__("random").Random(3)
+    keys = list(first) * 3
+    rng.shuffle(keys)
+    for (s, a, w) in keys:
+        assert pick(*s, s[2] + a, w) == first[(s, a, w)], (s, a, w)
+    assert names[first[((4096, 4096, 4096), 0, 0)]] == "mfma_256x256x32_w2x4d"
+
+
 def test_select_config_general_agrees_with_the_plain_query():
     """batch == 1 with plain operands: the same pick as sgemm_select_config; the batch
     multiplies the tile count the cost model spreads over the compute units."""

@@ -409,7 +409,7 @@ double memory_us(const Config &c, int M, int N, int K, int batch, bool vec)
 // The configuration with the least modelled time. Stream-K candidates are considered
 // only for one product (batch 1), when `ws_bytes` holds their workspace for `cus` compute
 // units (cus > 0); for operands only 4-byte aligned, only direct-copy ones.
-int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0, int batch = 1)
+int choose_model(int M, int N, int K, bool vec, size_t ws_bytes, int cus, int batch)
 {
     static const CandidateIds ids;
     const Candidate *table = vec ? kCandidates : kUnalignedCandidates;
@@ -462,6 +462,33 @@ int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0, int 
         }
     }
     return best;
+}
+
+// The same choice with a small per-thread memo of recent queries: the pick depends only on
+// these arguments, and the model costs about 2 us of host time per call, as much as a small
+// product's kernel. Calls that repeat a shape, as training and serving loops do, skip it.
+int choose(int M, int N, int K, bool vec, size_t ws_bytes = 0, int cus = 0, int batch = 1)
+{
+    struct Query {
+        int M, N, K, cus, batch;
+        size_t ws_bytes;
+        bool vec;
+        int id;
+    };
+    constexpr int kMemo = 8;
+    thread_local Query memo[kMemo];
+    thread_local int used = 0, next = 0;
+    for (int i = 0; i < used; ++i) {
+        const Query &q = memo[i];
+        if (q.M == M && q.N == N && q.K == K && q.cus == cus && q.batch == batch && q.ws_bytes == ws_bytes &&
+            q.vec == vec)
+            return q.id;
+    }
+    const int id = choose_model(M, N, K, vec, ws_bytes, cus, batch);
+    memo[next] = Query{M, N, K, cus, batch, ws_bytes, vec, id};
+    next = (next + 1) % kMemo;
+    used = used < kMemo ? used + 1 : kMemo;
+    return id;
 }
 
 // Arguments that can be invalid, independent of any entry point's numbering.
