@@ -338,6 +338,22 @@ def test_select_config_repeats_and_interleaves():
     assert names[first[((4096, 4096, 4096), 0, 0)]] == "mfma_256x256x32_w2x4d"
 
 
+def test_batched_products_take_the_batched_list():
+    """Strided-batched products choose among the tiles fitted on batched shapes: the 64 x 128
+    16x16-block tile for attention's scores (12 x 1024^2 x 64, K transposed) and the short-K
+    forms, the 16 x 64 one for its values (12 x 1024 x 64 x 1024); never the 256-wide tiles,
+    which a 12 x 1024^2 x 16 product once took from the single-product list."""
+    names = sg.configs()
+    def sel(b, M, N, K, opB):
+        return names[sg.sgemm_select_config_general(0, opB, M, N, K, 1.0, BAD, K, M * K, BAD, K if opB else N, K * N,
+                                                    BAD, N, M * N, b)]
+    assert sel(12, 1024, 1024, 64, 1) == "mfma16_64x128x32_w4x2k1d"
+    assert sel(12, 1024, 64, 1024, 0) == "mfma16_16x64x64_w1x1k4d"
+    for K in (16, 32, 128, 256):
+        assert sel(12, 1024, 1024, K, 1) == "mfma16_64x128x32_w4x2k1d"
+    assert sel(1, 1024, 1024, 1024, 0) == "mfma16_64x64x64_w4x1k2d"     # one product: the single list
+
+
 def test_select_config_general_agrees_with_the_plain_query():
     """batch == 1 with plain operands: the same pick as sgemm_select_config; the batch
     multiplies the tile count the cost model spreads over the compute units."""
