@@ -342,7 +342,9 @@ def test_batched_products_take_the_batched_list():
     """Strided-batched products choose among the tiles fitted on batched shapes: the 64 x 128
     16x16-block tile for attention's scores (12 x 1024^2 x 64, K transposed) and the short-K
     forms, the 16 x 64 one for its values (12 x 1024 x 64 x 1024); never the 256-wide tiles,
-    which a 12 x 1024^2 x 16 product once took from the single-product list."""
+    which a 12 x 1024^2 x 16 product once took from the single-product list. Unaligned
+    operands (odd row lengths) use the same list, not the unaligned single-product one, whose
+    128 x 128 tile ran 5-47% behind these on attention-like shapes."""
     names = sg.configs()
     def sel(b, M, N, K, opB):
         return names[sg.sgemm_select_config_general(0, opB, M, N, K, 1.0, BAD, K, M * K, BAD, K if opB else N, K * N,
@@ -352,6 +354,11 @@ def test_batched_products_take_the_batched_list():
     for K in (16, 32, 128, 256):
         assert sel(12, 1024, 1024, K, 1) == "mfma16_64x128x32_w4x2k1d"
     assert sel(1, 1024, 1024, 1024, 0) == "mfma16_64x64x64_w4x1k2d"     # one product: the single list
+    # rows only 4-byte aligned (odd K or N) take the same list, run with unaligned direct copies
+    assert sel(12, 1024, 1024, 63, 1) == "mfma16_64x128x32_w4x2k1d"
+    assert sel(12, 1023, 1023, 127, 1) == "mfma16_64x128x32_w4x2k1d"
+    assert sel(12, 1023, 63, 1023, 0) == "mfma16_16x64x64_w1x1k4d"
+    assert sel(12, 1024, 65, 2047, 0) == "mfma16_32x32x64_w2x2k1d"
 
 
 def test_select_config_general_agrees_with_the_plain_query():
@@ -371,14 +378,17 @@ def test_select_config_general_agrees_with_the_plain_query():
                                                   1024, 1 << 20, 12, 0)]
     area = lambda n: int(n.split("_")[1].split("x")[0]) * int(n.split("_")[1].split("x")[1])
     assert area(twelve) >= area(one), (one, twelve)
-    # odd strides take the unaligned table, as a misaligned pointer does
-    odd = sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD, 768, 3, BAD, 2304, 0, BAD, 2304,
-                                         1 << 22, 2, 0)
-    misaligned = sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD + 4, 768, 4, BAD, 2304, 0, BAD,
-                                                2304, 1 << 22, 2, 0)
-    aligned = sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD, 768, 4, BAD, 2304, 0, BAD, 2304,
+    # one product: a misaligned pointer takes the unaligned table
+    misaligned = sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD + 4, 768, 0, BAD, 2304, 0, BAD,
+                                                2304, 0, 1, 0)
+    aligned = sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD, 768, 0, BAD, 2304, 0, BAD, 2304,
+                                             0, 1, 0)
+    assert misaligned != aligned, (names[misaligned], names[aligned])
+    # two products, aligned or with odd strides: the batched list's tile for a few large products
+    for sA in (3, 4):
+        two = sg.sgemm_select_config_general(0, 0, 1024, 2304, 768, 1.0, BAD, 768, sA, BAD, 2304, 0, BAD, 2304,
                                              1 << 22, 2, 0)
-    assert odd == misaligned != aligned, (names[odd], names[misaligned], names[aligned])
+        assert names[two] == "mfma16_64x96x64_w4x2k1d", (sA, names[two])
 
 
 def test_status_strings():

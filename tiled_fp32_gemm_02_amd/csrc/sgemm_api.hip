@@ -347,16 +347,24 @@ const Candidate kUnalignedCandidates[] = {
     {"mfma16_32x96x128_w2x2k4d", 0.47, 7.06, 2.2167, 2.1710}, // GPT-2 MLP-down one short
     {"mfma16_64x64x128_w4x1k4d", 0.38, 7.11, 1.9224, 1.8894}, // long K (999 x 999 x 3999)
 };
-// Strided-batched products (batch > 1, 16-byte aligned operands) take their own short list,
+// Strided-batched products (batch > 1, aligned or not) take their own short list,
 // fitted on batched shapes only (attention-like products: 12 to 48 heads of 1024 x 1024 x 16..256
 // and of 1024 x 64 x 1024..4096, 3 x 2048^2 x 64 and 4096^2 x 64, 16 x 256^3 and 16 x 128^2 x 64,
 // and the shapes with a 64-wide output): the single-product list, whose larger tiles were never
 // swept on batched shapes, sent 12 x 1024^2 x 16 and x 32 to the 256 x 128 tile (30-36% behind).
-// With this list the picks average within 2.2% of the fastest measured, 13% at worst.
+// With this list the picks average within 2.1% of the fastest measured on 34 batched shapes.
+// Batches of a few large products (2 x 1024 x 2304 x 768) took the 32 x 32 tile, 15-24%
+// behind the 64 x 96 one; that tile, fitted alone with the other three unchanged, joined last.
+// Operands only 4-byte aligned run the same tiles with their unaligned direct copies: on
+// 12-head attention shapes with K or N of 63, 65, 127 or 17 and on 16 x 255^3 these tiles
+// ran 5-47% ahead of the 128 x 128 tile the unaligned single-product list picked there; the
+// picks came within 6% of the fastest measured but for 16 x 255^3 (the 16 x 64 tile, 12.6 us
+// against 10.6 us for the 64 x 64 tile of the single-product list).
 const Candidate kBatchedCandidates[] = {
     {"mfma16_64x128x32_w4x2k1d", 1.61, 1.51, 2.0773, 1.7591}, // attention scores
     {"mfma16_16x64x64_w1x1k4d", 3.07, 0.63, 8.4280, 2.1437},  // attention values
     {"mfma16_32x32x64_w2x2k1d", 4.45, 0.48, 0.0000, 2.0692},
+    {"mfma16_64x96x64_w4x2k1d", 7.13, 0.67, 2.1684, 2.0067},  // a few large products (2 x QKV)
 };
 const Candidate kSkCandidates[] = {
     {"sk16_32x64x64_w2x1k2d", 6.48, 0.00, 3.8051, 2.2519},
@@ -426,7 +434,7 @@ double memory_us(const Config &c, int M, int N, int K, int batch, bool vec)
 int choose_model(int M, int N, int K, bool vec, size_t ws_bytes, int cus, int batch)
 {
     static const CandidateIds ids;
-    const bool batched = vec && batch > 1;
+    const bool batched = batch > 1;
     const Candidate *table = batched ? kBatchedCandidates : vec ? kCandidates : kUnalignedCandidates;
     const int *table_ids = batched ? ids.bt : vec ? ids.id : ids.un;
     const int table_len = batched ? kNumBatchedCandidates : vec ? kNumCandidates : kNumUnalignedCandidates;
