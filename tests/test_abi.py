@@ -205,7 +205,11 @@ def test_launch_shape_mfma():
         for M, N in [(4096, 4096), (1000, 1537), (1, 1), (bm + 1, bn - 1)]:
             st, grid, block = sg.sgemm_launch_shape(cid, M, N, 64)
             assert st == 0
-            assert grid == (-(-M // bm) * -(-N // bn), 1, 1)
+            tiles = -(-M // bm) * -(-N // bn)
+            whole = -(-M // bm) * (N // bn)
+            if 1 <= N % bn <= 8 and whole >= 256:       # fringe columns: whole tiles + two rows each
+                tiles = whole + -(-M // 2)
+            assert grid == (tiles, 1, 1)
             assert block == (wm * wn * wk * 64, 1, 1)
         assert sg.sgemm_launch_shape(cid, -1, 4, 4)[0] == -1
     st, _, _ = sg.sgemm_launch_shape(1, 2**31 - 1, 2**31 - 1, 1)
@@ -272,9 +276,10 @@ def test_select_config():
     assert names[sel(256, 256, 256)] == "mfma16_16x16x256_w1x1k4d"
     assert names[sel(8192, 32, 8192)] == "mfma16_32x32x128_w2x2k2d"
     assert names[sel(32, 8192, 8192)] == "mfma16_32x32x128_w2x2k2d"
-    # unaligned: the ragged product on the 64 x 64 16x16-block tile
+    # unaligned: the ragged product on the 32 x 64 16x16-block tile, 32 x 24 whole tiles (three
+    # per CU) and one fringe column
     assert names[sg.sgemm_select_config(1000, 1537, 777, 1.0, BAD, 777, BAD, 1537, BAD, 1537)] == \
-        "mfma16_64x64x32_w4x1k1d"
+        "mfma16_32x64x64_w2x1k2d"
 
 
 def test_config_describe_every_id():
@@ -598,3 +603,25 @@ def test_strided_checks_and_quick_returns():
     # M == 1 or N == 1: only the stride that walks the window must be positive
     assert sg.sgemm_strided(1, 5, 3, 1.0, BAD, 0, 0, BAD, 0, 0, 0.0, BAD, 0, 0, None, 0, None) == -14
     assert sg.sgemm_strided(4, 1, 3, 1.0, BAD, 0, 0, BAD, 0, 0, 0.0, BAD, 0, 7, None, 0, None) == -13
+
+
+def test_launch_shape_fringe_columns():
+    """Data-parallel matrix configurations hand the last N mod BN columns (1..8 of them) to
+    workgroups of their own, two rows each, once the whole tiles number 256 or more: the
+    1000 x 1537 x 777 product on 64 x 64 tiles runs 16 x 24 tiles and 500 fringe workgroups.
+    Nine columns over, too few whole tiles, stream-K and the vector-ALU kernel keep the plain
+    grid."""
+    names = sg.configs()
+    c64 = names.index("mfma16_64x64x32_w4x1k1d")
+    assert sg.sgemm_launch_shape(c64, 1000, 1537, 777) == (0, (16 * 24 + 500, 1, 1), (256, 1, 1))
+    assert sg.sgemm_launch_shape(c64, 1000, 1544, 777)[1][0] == 16 * 24 + 500
+    assert sg.sgemm_launch_shape(c64, 1000, 1545, 777)[1][0] == 16 * 25          # 9 columns over
+    assert sg.sgemm_launch_shape(c64, 1000, 1536, 777)[1][0] == 16 * 24          # none over
+    assert sg.sgemm_launch_shape(c64, 1000, 961, 777)[1][0] == 16 * 16           # 240 whole tiles: too few
+    assert sg.sgemm_launch_shape(c64, 1023, 1025, 777)[1][0] == 16 * 16 + 512
+    c32 = names.index("mfma16_32x64x64_w2x1k2d")
+    assert sg.sgemm_launch_shape(c32, 1000, 1537, 777)[1][0] == 32 * 24 + 500
+    sk = names.index("sk16_64x64x32_w4x1k1d")
+    assert sg.sgemm_launch_shape(sk, 1000, 1537, 777)[1][0] == 256 + 256    # 400 tiles: 256 whole, 144 shared
+    valu = names.index("valu_128x128x8_t8x8")
+    assert sg.sgemm_launch_shape(valu, 1000, 1537, 777)[1][0] == 8 * 13

@@ -219,6 +219,34 @@ uint64_t tile_count(const Config &c, int M, int N)
     return cdiv64(M, c.bm) * cdiv64(N, c.bn);
 }
 
+// Fringe columns of a data-parallel MFMA launch: when N mod BN = r is 1..kFringeCols, the
+// whole tiles stop at column N - r and workgroups of their own, kFringeRows rows each, compute
+// the last r columns (sgemm_mfma). Taken when the whole tiles still number at least
+// kFringeMinTiles over the batch: a column of edge tiles then adds a round of tiles on
+// some CUs, while in a smaller grid it runs beside the others. The fringe kernel indexes
+// rows with 32-bit offsets, so it takes row strides under kDmaMaxLd only (ld_ok). Returns r,
+// or 0 for none.
+constexpr uint64_t kFringeMinTiles = 256;
+int fringe_cols(const Config &c, int M, int N, int batch, bool ld_ok = true)
+{
+    if (c.kind != KIND_MFMA || N < c.bn || !ld_ok)
+        return 0;
+    const int r = N % c.bn;
+    if (r == 0 || r > sgemm_impl::kFringeCols)
+        return 0;
+    return cdiv64(M, c.bm) * (uint64_t)(N / c.bn) * (uint64_t)batch >= kFringeMinTiles ? r : 0;
+}
+
+// Whole tiles of a launch with `fringe` fringe columns, and all its workgroups (per batch entry).
+uint64_t main_tiles(const Config &c, int M, int N, int fringe)
+{
+    return fringe > 0 ? cdiv64(M, c.bm) * (uint64_t)((N - fringe) / c.bn) : tile_count(c, M, N);
+}
+uint64_t grid_count(const Config &c, int M, int N, int fringe)
+{
+    return main_tiles(c, M, N, fringe) + (fringe > 0 ? cdiv64(M, sgemm_impl::kFringeRows) : 0);
+}
+
 // The stream-K kernel splits work with 32-bit arithmetic: (CUs + 1) * work < 2^31.
 // Stream-K split of `tiles` tiles of `iters` K-tiles over `cus` CUs. Direct-copy
 // configurations (`whole` true) run whole rounds of tiles, one per CU each, except the last
@@ -318,34 +346,34 @@ const Candidate kCandidates[] = {
     {"mfma16_64x96x64_w4x2k1d", 2.02, 1.26, 2.4321, 2.1043},
 };
 const Candidate kUnalignedCandidates[] = {
-    {"mfma_256x256x32_w2x4d", 11.60, 0.00, 1.7854, 1.8544},
-    {"mfma_256x256x16_w2x4p2d", 12.78, 0.00, 1.7545, 1.7966},
-    {"mfma_128x128x32_w2x2k2d", 8.72, 0.00, 1.8399, 1.8067},
-    {"mfma_64x128x32_w2x2k2d", 3.07, 2.89, 2.0071, 1.7607},
-    {"mfma_64x64x32_w2x2k2d", 2.25, 3.59, 2.7145, 1.8655},
-    {"mfma_32x128x64_w1x4k2d", 4.22, 4.33, 2.1928, 1.9099},
-    {"mfma_32x64x64_w1x2k2d", 5.59, 2.40, 2.7398, 1.9596},
-    {"mfma16_128x64x32_w8x1k1d", 0.00, 5.51, 2.1567, 1.7931},
-    {"mfma16_64x128x32_w4x2k1d", 0.00, 5.52, 2.1800, 1.7990},
-    {"mfma16_64x64x64_w4x1k2d", 1.73, 3.99, 2.1388, 1.8218},
-    {"mfma16_64x64x64_w2x2k2d", 1.29, 3.99, 2.2337, 1.8231},
-    {"mfma16_64x64x32_w4x1k1d", 1.74, 2.41, 2.7993, 1.8952}, // 1000 x 1537 x 777
-    {"mfma16_64x16x64_w4x1k1d", 3.81, 0.02, 5.8753, 3.2649},
-    {"mfma16_32x128x64_w2x2k2d", 1.03, 4.68, 2.2379, 1.8437},
-    {"mfma16_32x64x128_w2x1k4d", 0.83, 5.10, 2.4195, 2.3993},
-    {"mfma16_32x64x64_w2x1k2d", 4.05, 1.35, 3.1301, 2.0748},
-    {"mfma16_32x32x128_w2x2k2d", 2.54, 2.22, 3.6887, 2.3801},
-    {"mfma16_32x32x64_w2x2k1d", 3.61, 0.84, 4.9674, 2.4750},
-    {"mfma16_16x64x128_w1x1k4d", 4.16, 3.15, 4.0959, 2.5782},
-    {"mfma16_16x16x256_w1x1k4d", 2.21, 2.43, 15.8183, 3.9950},
-    {"mfma16_16x16x128_w1x1k4p2d", 5.17, 1.15, 0.6230, 4.2812},
-    {"mfma16_16x16x128_w1x1k4d", 2.42, 0.87, 17.6683, 3.9763},
-    {"mfma_32x96x64_w1x1k4d", 3.10, 5.69, 2.5896, 1.9926},
-    {"mfma16_32x96x32_w2x2k1d", 3.34, 1.01, 3.7496, 2.2723}, // GPT-2 QKV one short
-    {"mfma16_32x96x64_w2x2k2d", 2.00, 3.40, 2.6920, 2.1282},
-    {"mfma16_64x96x64_w4x2k1d", 0.70, 5.13, 2.3708, 2.0133},
-    {"mfma16_32x96x128_w2x2k4d", 0.47, 7.06, 2.2167, 2.1710}, // GPT-2 MLP-down one short
-    {"mfma16_64x64x128_w4x1k4d", 0.38, 7.11, 1.9224, 1.8894}, // long K (999 x 999 x 3999)
+    {"mfma_256x256x32_w2x4d", 14.78, 0.00, 1.7817, 1.8531},
+    {"mfma_256x256x16_w2x4p2d", 14.54, 0.00, 1.7496, 1.7959},
+    {"mfma_128x128x32_w2x2k2d", 0.00, 9.77, 1.8349, 1.7573},
+    {"mfma_64x128x32_w2x2k2d", 4.33, 2.24, 1.9886, 1.7675},
+    {"mfma_64x64x32_w2x2k2d", 1.92, 3.51, 2.6994, 1.8526},
+    {"mfma_32x128x64_w1x4k2d", 2.73, 4.95, 2.2349, 1.8643},
+    {"mfma_32x64x64_w1x2k2d", 5.17, 2.48, 2.7642, 1.9188},
+    {"mfma16_128x64x32_w8x1k1d", 3.03, 3.60, 2.1501, 1.8255},
+    {"mfma16_64x128x32_w4x2k1d", 1.42, 4.83, 2.1884, 1.8116},
+    {"mfma16_64x64x64_w4x1k2d", 1.26, 4.12, 2.1441, 1.8023},
+    {"mfma16_64x64x64_w2x2k2d", 1.09, 3.93, 2.2359, 1.8118},
+    {"mfma16_64x64x32_w4x1k1d", 2.58, 2.02, 2.7551, 1.9236},
+    {"mfma16_64x16x64_w4x1k1d", 3.95, 0.02, 5.8074, 3.2313},
+    {"mfma16_32x128x64_w2x2k2d", 0.21, 4.99, 2.2664, 1.8117},
+    {"mfma16_32x64x128_w2x1k4d", 0.89, 5.62, 2.3737, 2.3601},
+    {"mfma16_32x64x64_w2x1k2d", 4.02, 1.08, 3.1609, 2.1112}, // 1000 x 1537 x 777 (a fringe column)
+    {"mfma16_32x32x128_w2x2k2d", 3.11, 1.98, 3.5664, 2.4989},
+    {"mfma16_32x32x64_w2x2k1d", 3.62, 0.90, 4.9465, 2.4911},
+    {"mfma16_16x64x128_w1x1k4d", 5.14, 2.17, 4.0984, 3.0357},
+    {"mfma16_16x16x256_w1x1k4d", 2.71, 2.31, 12.8703, 4.1376},
+    {"mfma16_16x16x128_w1x1k4p2d", 4.83, 1.18, 3.0110, 4.2615},
+    {"mfma16_16x16x128_w1x1k4d", 3.08, 0.59, 14.8043, 4.4668},
+    {"mfma_32x96x64_w1x1k4d", 3.09, 5.34, 2.6664, 2.0092},
+    {"mfma16_32x96x32_w2x2k1d", 4.77, 0.57, 3.7008, 2.3108}, // GPT-2 QKV one short
+    {"mfma16_32x96x64_w2x2k2d", 1.92, 3.26, 2.7099, 2.1238},
+    {"mfma16_64x96x64_w4x2k1d", 2.13, 4.04, 2.3752, 2.0313},
+    {"mfma16_32x96x128_w2x2k4d", 2.11, 6.38, 2.1529, 2.2173}, // GPT-2 MLP-down one short
+    {"mfma16_64x64x128_w4x1k4d", 1.61, 6.29, 1.9046, 1.9373}, // long K (999 x 999 x 3999)
 };
 // Strided-batched products (batch > 1, aligned or not) take their own short list,
 // fitted on batched shapes only (attention-like products: 12 to 48 heads of 1024 x 1024 x 16..256
@@ -373,9 +401,9 @@ const Candidate kSkCandidates[] = {
     {"sk_64x128x32_w2x2k2p2", 0.00, 12.80, 2.0335, 0.0000}, // long K, few tiles
 };
 const Candidate kSkUnalignedCandidates[] = {
-    {"sk_64x128x32_w2x2k2d", 15.09, 0.00, 1.9619, 1.7960}, // 1535^3, 2999^3
-    {"sk16_64x64x32_w4x1k1d", 9.95, 0.63, 2.7560, 1.9178},
-    {"sk16_32x64x64_w2x1k2d", 8.06, 1.40, 3.0379, 2.0663},
+    {"sk_64x128x32_w2x2k2d", 15.24, 0.00, 2.0504, 1.7412}, // 1535^3, 2999^3
+    {"sk16_64x64x32_w4x1k1d", 11.80, 0.00, 2.7647, 1.9379},
+    {"sk16_32x64x64_w2x1k2d", 9.13, 1.23, 2.9775, 2.1131},
 };
 constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
 constexpr int kNumUnalignedCandidates = sizeof(kUnalignedCandidates) / sizeof(kUnalignedCandidates[0]);
@@ -385,6 +413,8 @@ constexpr int kNumSkUnalignedCandidates = sizeof(kSkUnalignedCandidates) / sizeo
 // A stream-K candidate is taken only when its modelled time, 3% longer, still beats the
 // data-parallel one: its shared tiles are the part of the model with the widest spread.
 constexpr double kSkMargin = 1.03;
+// Modelled time of a launch's fringe workgroups beyond its tiles (us).
+constexpr double kFringeUs = 2.0;
 constexpr double kHbmBytesPerUs = 5.7e6;          // 5.7 TB/s for rows of 512 contiguous bytes
 constexpr double kHbmRowExponent = 0.19;
 constexpr double kL2BytesPerUs = 20.0e6;          // tile-fill bytes, 16-byte aligned rows
@@ -447,11 +477,13 @@ int choose_model(int M, int N, int K, bool vec, size_t ws_bytes, int cus, int ba
         if (table_ids[i] < 0)
             continue;
         const Config &c = kConfigs[table_ids[i]];
-        const uint64_t tiles = tile_count(c, M, N) * (uint64_t)batch;
+        const int fringe = fringe_cols(c, M, N, batch);
+        const uint64_t tiles = main_tiles(c, M, N, fringe) * (uint64_t)batch;
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
         const double units = (double)c.bm * c.bn / 4096.0;
         double us = cand.fixed_us + (double)rounds * cand.round_us +
-                    (double)rounds * units * unit_mflop * (rounds >= 2 ? cand.us_many : cand.us_one);
+                    (double)rounds * units * unit_mflop * (rounds >= 2 ? cand.us_many : cand.us_one) +
+                    (fringe > 0 ? kFringeUs : 0.0);
         const double mem = memory_us(c, M, N, K, batch, vec);
         us = us > mem ? us : mem;
         if (best < 0 || us < best_us) {
@@ -583,7 +615,7 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     p.M = M; p.N = N; p.K = K;
     p.alpha = alpha; p.beta = beta;
     p.A = A; p.B = B; p.C = C;
-    p.bias = bias; p.act = act;
+    p.bias = bias; p.act = act; p.fringe = 0;
     p.lda = lda; p.ldb = ldb; p.ldc = ldc;
     p.strideA = sA; p.strideB = sB; p.strideC = sC;
 
@@ -603,10 +635,12 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     const int cus = (ws != nullptr && batch == 1) ? device_cus() : 0;
     const int id = config >= 0 ? config : choose(M, N, K, vec, ws_bytes, cus, batch);
     const Config &c = kConfigs[id];
+    const int fringe = fringe_cols(c, M, N, batch, lda < kDmaMaxLd && ldb < kDmaMaxLd);
     const uint64_t tiles = tile_count(c, M, N);
-    if ((c.kind == KIND_MFMA || c.kind == KIND_VALU) && tiles * (uint64_t)c.threads > 0xFFFFFFFFull)
+    if ((c.kind == KIND_MFMA || c.kind == KIND_VALU) && grid_count(c, M, N, fringe) * (uint64_t)c.threads > 0xFFFFFFFFull)
         return SGEMM_ERROR_TOO_LARGE;
-    const bool edge = (M % c.bm) != 0 || (N % c.bn) != 0 || (K % c.bk) != 0;
+    p.fringe = fringe;
+    const bool edge = (M % c.bm) != 0 || ((N - fringe) % c.bn) != 0 || (K % c.bk) != 0;
     // Direct copies address a tile with 32-bit offsets, so long rows take the register-staged
     // kernels; so do row strides under 4 floats, where a 16-byte copy of a row's last chunk
     // could pass more than the next row.
@@ -714,7 +748,7 @@ int strided(int M, int N, int K, float alpha, const float *A, long long rsA, lon
     p.M = M; p.N = N; p.K = K;
     p.alpha = alpha; p.beta = beta;
     p.A = A; p.B = B; p.C = C;
-    p.bias = bias; p.act = act;
+    p.bias = bias; p.act = act; p.fringe = 0;
     p.lda = rsA; p.ldb = rsB; p.ldc = rsC;
     p.strideA = p.strideB = p.strideC = 0;
     p.incA = csA; p.incB = csB; p.incC = csC;
@@ -1047,8 +1081,9 @@ int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3
         block[0] = c.threads; block[1] = 1; block[2] = 1;
         return 0;
     }
-    if (tiles * (uint64_t)c.threads > 0xFFFFFFFFull) return SGEMM_ERROR_TOO_LARGE;
-    grid[0] = (int)tiles; grid[1] = 1; grid[2] = 1;
+    const uint64_t wgs = grid_count(c, M, N, fringe_cols(c, M, N, 1));
+    if (wgs * (uint64_t)c.threads > 0xFFFFFFFFull) return SGEMM_ERROR_TOO_LARGE;
+    grid[0] = (int)wgs; grid[1] = 1; grid[2] = 1;
     block[0] = c.threads; block[1] = 1; block[2] = 1;
     return 0;
 }

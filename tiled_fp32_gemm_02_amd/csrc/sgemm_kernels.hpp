@@ -62,6 +62,7 @@ struct GemmArgs {
     float *C;
     const float *bias;          // N entries (one per column) or null
     int act;                    // Act
+    int fringe;                 // last columns of C left to the fringe workgroups (see sgemm_mfma)
     int64_t lda, ldb, ldc;
     int64_t strideA, strideB, strideC;  // per blockIdx.z (batched form); 0 otherwise
 };
@@ -1058,6 +1059,152 @@ struct MfmaTile {
     }
 };
 
+// Fringe columns: the last r = p.fringe columns of C (1 <= r <= kFringeCols), which the
+// tile grid leaves out when it stops at the last whole column of tiles. One workgroup takes
+// kFringeRows rows of C; its waves and lanes split K (thread t of wave w takes k = 64 (w + W u)
+// + lane, u = 0, 1, ...) and each thread sums, for those rows, the products with the last R
+// columns of B, R a compile-time 1, 2, 4 or 8 >= r (N >= R always, since the grid holds a
+// whole column of tiles). The R floats of a row of B come in one or two vector loads that the
+// rows share (and the rows of A in one, when A is transposed), so a step issues a few loads
+// rather than one per entry: one per entry, each lane on its own row of B, runs at the rate
+// the cache takes line requests, not at its bandwidth. Indices past K or M are clamped, so
+// every load is unconditional, and the products of clamped k are dropped. Then a butterfly of
+// lane exchanges adds the G R sums over the wave, halving them at each step (G R - 1 exchanges
+// for G R <= 16 sums rather than 6 G R), and the waves' totals meet in LDS.
+constexpr int kFringeCols = 8;
+constexpr int kFringeRows = 2;
+
+typedef float floatx2u __attribute__((ext_vector_type(2), aligned(4)));
+
+template <int NT, bool TA, bool TB, int R>
+__device__ __forceinline__ void fringe_columns(const GemmArgs &p, int f, float *red, int tid)
+{
+    constexpr int G = kFringeRows, W = NT / 64, NV = G * R;
+    constexpr int LOGN = NV == 2 ? 1 : NV == 4 ? 2 : NV == 8 ? 3 : NV == 16 ? 4 : 5;
+    static_assert(NV == (1 << LOGN), "G R must be a power of two up to 32");
+    // Steps of 64 W k whose loads are in flight together: U (G + R) loaded floats, their
+    // addresses and the G R sums stay under what the tile kernels hold, so the branch does
+    // not lower the tiles' occupancy.
+    constexpr int U = R <= 2 ? 4 : R == 4 ? 2 : 1;
+    const int lane = tid & 63, w = tid >> 6;
+    const int M = p.M, K = p.K, r = p.fringe, c0 = p.N - R;
+    const int m0 = f * G;
+    const bool full = m0 + G <= M;
+    const float *__restrict__ A = p.A + (int64_t)blockIdx.z * p.strideA;
+    const float *__restrict__ B = p.B + (int64_t)blockIdx.z * p.strideB;
+    float *__restrict__ C = p.C + (int64_t)blockIdx.z * p.strideC;
+    const int64_t lda = p.lda, ldb = p.ldb;
+    // Rows of A (plain) and columns of B (transposed) are read from one base each with
+    // 32-bit offsets (the host takes fringes only for row strides under 2^20 floats).
+    const float *__restrict__ Am = A + (int64_t)m0 * lda;
+    const float *__restrict__ Bn = B + (int64_t)c0 * ldb;
+    int arow[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        arow[g] = (m0 + g < M ? g : M - 1 - m0) * (int)lda;
+    float v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        v[i] = 0.f;
+    for (int kb = 64 * w + lane; kb < K; kb += 64 * W * U) {
+        float a[U][G], b[U][R];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = kb + 64 * W * u;
+            const int kc = k < K ? k : K - 1;
+            if constexpr (TA) {
+                const float *ak = A + (int64_t)kc * lda;
+                if (full) {
+                    const floatx4u x = *reinterpret_cast<const floatx4u *>(ak + m0);
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        a[u][g] = x[g];
+                } else {
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        a[u][g] = ak[m0 + g < M ? m0 + g : M - 1];
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    a[u][g] = Am[arow[g] + kc];
+            }
+            if constexpr (TB) {
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+                    b[u][j] = Bn[j * (int)ldb + kc];
+            } else {
+                const float *bk = B + (int64_t)kc * ldb + c0;
+                if constexpr (R == 1) {
+                    b[u][0] = bk[0];
+                } else if constexpr (R == 2) {
+                    const floatx2u x = *reinterpret_cast<const floatx2u *>(bk);
+                    b[u][0] = x[0];
+                    b[u][1] = x[1];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < R / 4; ++q) {
+                        const floatx4u x = *reinterpret_cast<const floatx4u *>(bk + 4 * q);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            b[u][4 * q + e] = x[e];
+                    }
+                }
+            }
+            if (k >= K) {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    a[u][g] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+                    v[g * R + j] = fmaf(a[u][g], b[u][j], v[g * R + j]);
+    }
+    // Halving steps (offsets 32, 16, ...): the lane keeps the half of its sums picked by its
+    // bit at that offset and adds its partner's copy of that half. After LOGN steps lane l
+    // holds one sum, index l >> (6 - LOGN), over the 2^LOGN lanes that differ from l only in
+    // the top LOGN bits; plain exchanges over the remaining offsets complete it over the wave.
+#pragma unroll
+    for (int st = 0; st < LOGN; ++st) {
+        const int o = 32 >> st;
+        const int half = NV >> (st + 1);
+        const bool hi = (lane & o) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float send = hi ? v[i] : v[i + half];
+            const float keep = hi ? v[i + half] : v[i];
+            v[i] = keep + __shfl_xor(send, o);
+        }
+    }
+#pragma unroll
+    for (int o = 32 >> LOGN; o > 0; o >>= 1)
+        v[0] += __shfl_xor(v[0], o);
+    if ((lane & ((64 >> LOGN) - 1)) == 0)
+        red[w * NV + (lane >> (6 - LOGN))] = v[0];
+    __syncthreads();
+    if (tid < NV) {
+        float t = 0.f;
+#pragma unroll
+        for (int q = 0; q < W; ++q)
+            t += red[q * NV + tid];
+        const int g = tid / R, j = tid % R;
+        if (j >= R - r && m0 + g < M) {
+            const int col = c0 + j;
+            float *cptr = C + (int64_t)(m0 + g) * p.ldc + col;
+            *cptr = finish(t, p.alpha, p.beta, cptr, p.bias, col, p.act);
+        }
+    }
+}
+
+// One workgroup per output tile. With p.fringe = r > 0 the tiles cover the first N - r
+// columns (a whole number of tiles) and the workgroups after them compute the last r
+// columns, kFringeRows rows each (fringe_columns): a thin strip of columns then costs a
+// short pass rather than a column of nearly empty tiles.
 template <int BM, int BN, int BK, int WGM, int WGN, int WGK, int PF, bool DMA, bool TA, bool TB, bool VEC,
           bool EDGE, int MB>
 __global__ void __launch_bounds__(WGM * WGN * WGK * 64)
@@ -1065,9 +1212,24 @@ __attribute__((amdgpu_waves_per_eu(MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, 
 sgemm_mfma(GemmArgs p, int group_m)
 {
     using T = MfmaTile<BM, BN, BK, WGM, WGN, WGK, PF, DMA, TA, TB, VEC, EDGE, MB>;
+    constexpr int NT = WGM * WGN * WGK * 64;
     __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
+    const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N - p.fringe, BN);
+    static_assert(T::SMEM >= NT / 64 * kFringeRows * kFringeCols, "LDS too small for the fringe sums");
+    if (p.fringe > 0 && (int)blockIdx.x >= tiles_m * tiles_n) {
+        const int f = blockIdx.x - tiles_m * tiles_n;
+        if (p.fringe <= 1)
+            fringe_columns<NT, TA, TB, 1>(p, f, smem, threadIdx.x);
+        else if (p.fringe <= 2)
+            fringe_columns<NT, TA, TB, 2>(p, f, smem, threadIdx.x);
+        else if (p.fringe <= 4)
+            fringe_columns<NT, TA, TB, 4>(p, f, smem, threadIdx.x);
+        else
+            fringe_columns<NT, TA, TB, 8>(p, f, smem, threadIdx.x);
+        return;
+    }
     int tm, tn;
-    tile_coords(blockIdx.x, ceil_div(p.M, BM), ceil_div(p.N, BN), group_m, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     typename T::acc_t acc[T::TM][T::TN];
     if (T::product(p, smem, tm * BM, tn * BN, 0, ceil_div(p.K, BK), acc, threadIdx.x))
         T::epilogue(p, tm * BM, tn * BN, acc, threadIdx.x);

@@ -28,7 +28,10 @@ hipError_t launch_mfma_op(const GemmArgs &p, int batch, bool vec, bool edge, boo
     constexpr int BKU = DMA ? 8 * (64 / MB) * WGK : BK;  // K-tile of the register-staged unaligned variant
     // The caller has checked that tiles x NT fits one launch; the sums are unsigned so that
     // M or N near 2^31 does not overflow.
-    const unsigned tiles = (((unsigned)p.M + BM - 1) / BM) * (((unsigned)p.N + BN - 1) / BN);
+    // With p.fringe > 0 the tiles stop at column N - fringe and kFringeRows rows of the last
+    // columns go to each workgroup after them.
+    const unsigned tiles = (((unsigned)p.M + BM - 1) / BM) * (((unsigned)(p.N - p.fringe) + BN - 1) / BN) +
+                           (p.fringe > 0 ? ((unsigned)p.M + kFringeRows - 1) / kFringeRows : 0u);
     const dim3 grid(tiles, 1, batch), block(NT);
     if (DMA && !dma_ok)
         vec = false;                                    // only the register-staged variant takes long rows
