@@ -33,7 +33,8 @@ def kernels(tmp_path_factory):
         meta = yaml.safe_load(block.replace("\t", "  "))
         for k in meta["amdhsa.kernels"]:
             name = k[".name"]
-            body = re.search(r"^" + re.escape(name) + r":[^\n]*\n(.*?)s_endpgm", text, re.S | re.M).group(1)
+            # the whole function, up to its end label (a kernel can end in several places)
+            body = re.search(r"^" + re.escape(name) + r":[^\n]*\n(.*?)^\.Lfunc_end\d+:", text, re.S | re.M).group(1)
             demangled = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip()
             out[demangled] = (k, body)
     return out
