@@ -621,6 +621,10 @@ def test_launch_shape_fringe_columns():
     assert sg.sgemm_launch_shape(c64, 1023, 1025, 777)[1][0] == 16 * 16 + 512
     c32 = names.index("mfma16_32x64x64_w2x1k2d")
     assert sg.sgemm_launch_shape(c32, 1000, 1537, 777)[1][0] == 32 * 24 + 500
+    # a grid that its fringe workgroups would take past 2^32 threads keeps the plain tiles
+    tall = 1 << 25
+    assert sg.sgemm_launch_shape(c64, tall, 65, 64) == (0, ((tall // 64) * 2, 1, 1), (256, 1, 1))
+    assert sg.sgemm_launch_shape(c64, 1 << 21, 65, 64)[1][0] == (1 << 15) + (1 << 20)
     sk = names.index("sk16_64x64x32_w4x1k1d")
     assert sg.sgemm_launch_shape(sk, 1000, 1537, 777)[1][0] == 256 + 256    # 400 tiles: 256 whole, 144 shared
     valu = names.index("valu_128x128x8_t8x8")

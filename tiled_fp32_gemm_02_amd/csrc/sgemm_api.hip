@@ -224,8 +224,9 @@ uint64_t tile_count(const Config &c, int M, int N)
 // the last r columns (sgemm_mfma). Taken when the whole tiles still number at least
 // kFringeMinTiles over the batch: a column of edge tiles then adds a round of tiles on
 // some CUs, while in a smaller grid it runs beside the others. The fringe kernel indexes
-// rows with 32-bit offsets, so it takes row strides under kDmaMaxLd only (ld_ok). Returns r,
-// or 0 for none.
+// rows with 32-bit offsets, so it takes row strides under kDmaMaxLd only (ld_ok), and a
+// grid too large for one launch with its fringe workgroups keeps the plain tiles. Returns
+// r, or 0 for none.
 constexpr uint64_t kFringeMinTiles = 256;
 int fringe_cols(const Config &c, int M, int N, int batch, bool ld_ok = true)
 {
@@ -234,7 +235,13 @@ int fringe_cols(const Config &c, int M, int N, int batch, bool ld_ok = true)
     const int r = N % c.bn;
     if (r == 0 || r > sgemm_impl::kFringeCols)
         return 0;
-    return cdiv64(M, c.bm) * (uint64_t)(N / c.bn) * (uint64_t)batch >= kFringeMinTiles ? r : 0;
+    const uint64_t whole = cdiv64(M, c.bm) * (uint64_t)(N / c.bn);
+    if (whole * (uint64_t)batch < kFringeMinTiles)
+        return 0;
+    // ceil(M / kFringeRows) more workgroups: a grid that would then pass one launch's
+    // 2^32 threads keeps its plain column of edge tiles instead
+    const uint64_t wgs = whole + cdiv64(M, sgemm_impl::kFringeRows);
+    return wgs * (uint64_t)c.threads <= 0xFFFFFFFFull ? r : 0;
 }
 
 // Whole tiles of a launch with `fringe` fringe columns, and all its workgroups (per batch entry).
