@@ -408,9 +408,10 @@ int sgemm_select_config(int M, int N, int K, float alpha,
 /*
  * Launch shape of configuration `config` for an M x N x K product (host logic only).
  * Writes grid[3] and block[3] (dim3 order x, y, z). Data-parallel matrix configurations
- * launch one workgroup per BM x BN tile; when N mod BN = r is 1..8 and the whole tiles
+ * launch one workgroup per BM x BN tile; when N mod BN = r is 1..8, the whole tiles
  * number at least 256 (over the batch, in a batched call; the shape reported here is for
- * one product), the tiles stop at column N - r and ceil(M / 2) more workgroups follow them,
+ * one product) and K is at most 3 x 64 x (threads / 64) x U (U = 4 for r <= 2, 2 for r <= 4,
+ * 1 for r <= 8), the tiles stop at column N - r and ceil(M / 2) more workgroups follow them,
  * each computing two rows of the last r columns (fringe columns; they also require row
  * strides under 2^20 floats, which this query, having no strides, assumes). Stream-K
  * configurations launch one

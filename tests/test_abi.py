@@ -607,14 +607,19 @@ def test_strided_checks_and_quick_returns():
 
 def test_launch_shape_fringe_columns():
     """Data-parallel matrix configurations hand the last N mod BN columns (1..8 of them) to
-    workgroups of their own, two rows each, once the whole tiles number 256 or more: the
-    1000 x 1537 x 777 product on 64 x 64 tiles runs 16 x 24 tiles and 500 fringe workgroups.
-    Nine columns over, too few whole tiles, stream-K and the vector-ALU kernel keep the plain
-    grid."""
+    workgroups of their own, two rows each, once the whole tiles number 256 or more and a
+    fringe workgroup needs at most three memory round trips (its threads take 64 (NT / 64) U k
+    per trip, U = 4, 2 or 1 for up to 2, 4 or 8 columns): the 1000 x 1537 x 777 product on
+    64 x 64 tiles runs 16 x 24 tiles and 500 fringe workgroups. Nine columns over, too long a
+    K, too few whole tiles, stream-K and the vector-ALU kernel keep the plain grid."""
     names = sg.configs()
     c64 = names.index("mfma16_64x64x32_w4x1k1d")
     assert sg.sgemm_launch_shape(c64, 1000, 1537, 777) == (0, (16 * 24 + 500, 1, 1), (256, 1, 1))
-    assert sg.sgemm_launch_shape(c64, 1000, 1544, 777)[1][0] == 16 * 24 + 500
+    # eight columns: one k step of 256 per round trip, so K up to 768 (three trips)
+    assert sg.sgemm_launch_shape(c64, 1000, 1544, 768)[1][0] == 16 * 24 + 500
+    assert sg.sgemm_launch_shape(c64, 1000, 1544, 777)[1][0] == 16 * 25       # four trips: plain tiles
+    assert sg.sgemm_launch_shape(c64, 1000, 1537, 3072)[1][0] == 16 * 24 + 500
+    assert sg.sgemm_launch_shape(c64, 1000, 1537, 3073)[1][0] == 16 * 25
     assert sg.sgemm_launch_shape(c64, 1000, 1545, 777)[1][0] == 16 * 25          # 9 columns over
     assert sg.sgemm_launch_shape(c64, 1000, 1536, 777)[1][0] == 16 * 24          # none over
     assert sg.sgemm_launch_shape(c64, 1000, 961, 777)[1][0] == 16 * 16           # 240 whole tiles: too few

@@ -228,12 +228,24 @@ uint64_t tile_count(const Config &c, int M, int N)
 // grid too large for one launch with its fringe workgroups keeps the plain tiles. Returns
 // r, or 0 for none.
 constexpr uint64_t kFringeMinTiles = 256;
-int fringe_cols(const Config &c, int M, int N, int batch, bool ld_ok = true)
+// Memory round trips of one fringe workgroup: its NT threads take 64 (NT / 64) U k per trip,
+// U the k steps in flight per thread in fringe_columns (4 for up to 2 columns, 2 for 3-4, 1
+// for 5-8; the kernel sets them to keep its registers low). Long K with many columns costs
+// many trips: 999 x 999 x 3999 with 7 columns ran 13-36% slower on 16- and 32-wide tiles
+// with the fringe (16 trips) than without, while one column at K = 777 (one trip) saved up to
+// 39%. So the fringe is taken for at most kFringeMaxTrips.
+constexpr int kFringeMaxTrips = 3;
+int fringe_trips(const Config &c, int K, int r)
+{
+    const int steps = r <= 2 ? 4 : r <= 4 ? 2 : 1;
+    return (int)cdiv64(K, 64 * (c.threads / 64) * steps);
+}
+int fringe_cols(const Config &c, int M, int N, int K, int batch, bool ld_ok = true)
 {
     if (c.kind != KIND_MFMA || N < c.bn || !ld_ok)
         return 0;
     const int r = N % c.bn;
-    if (r == 0 || r > sgemm_impl::kFringeCols)
+    if (r == 0 || r > sgemm_impl::kFringeCols || fringe_trips(c, K, r) > kFringeMaxTrips)
         return 0;
     const uint64_t whole = cdiv64(M, c.bm) * (uint64_t)(N / c.bn);
     if (whole * (uint64_t)batch < kFringeMinTiles)
@@ -353,34 +365,34 @@ const Candidate kCandidates[] = {
     {"mfma16_64x96x64_w4x2k1d", 2.02, 1.26, 2.4321, 2.1043},
 };
 const Candidate kUnalignedCandidates[] = {
-    {"mfma_256x256x32_w2x4d", 14.78, 0.00, 1.7817, 1.8531},
-    {"mfma_256x256x16_w2x4p2d", 14.54, 0.00, 1.7496, 1.7959},
-    {"mfma_128x128x32_w2x2k2d", 0.00, 9.77, 1.8349, 1.7573},
-    {"mfma_64x128x32_w2x2k2d", 4.33, 2.24, 1.9886, 1.7675},
-    {"mfma_64x64x32_w2x2k2d", 1.92, 3.51, 2.6994, 1.8526},
-    {"mfma_32x128x64_w1x4k2d", 2.73, 4.95, 2.2349, 1.8643},
-    {"mfma_32x64x64_w1x2k2d", 5.17, 2.48, 2.7642, 1.9188},
-    {"mfma16_128x64x32_w8x1k1d", 3.03, 3.60, 2.1501, 1.8255},
-    {"mfma16_64x128x32_w4x2k1d", 1.42, 4.83, 2.1884, 1.8116},
-    {"mfma16_64x64x64_w4x1k2d", 1.26, 4.12, 2.1441, 1.8023},
-    {"mfma16_64x64x64_w2x2k2d", 1.09, 3.93, 2.2359, 1.8118},
-    {"mfma16_64x64x32_w4x1k1d", 2.58, 2.02, 2.7551, 1.9236},
-    {"mfma16_64x16x64_w4x1k1d", 3.95, 0.02, 5.8074, 3.2313},
-    {"mfma16_32x128x64_w2x2k2d", 0.21, 4.99, 2.2664, 1.8117},
-    {"mfma16_32x64x128_w2x1k4d", 0.89, 5.62, 2.3737, 2.3601},
-    {"mfma16_32x64x64_w2x1k2d", 4.02, 1.08, 3.1609, 2.1112}, // 1000 x 1537 x 777 (a fringe column)
-    {"mfma16_32x32x128_w2x2k2d", 3.11, 1.98, 3.5664, 2.4989},
-    {"mfma16_32x32x64_w2x2k1d", 3.62, 0.90, 4.9465, 2.4911},
+    {"mfma_256x256x32_w2x4d", 14.80, 0.00, 1.7815, 1.8531},
+    {"mfma_256x256x16_w2x4p2d", 14.57, 0.00, 1.7493, 1.7959},
+    {"mfma_128x128x32_w2x2k2d", 9.76, 0.00, 1.8352, 1.8036},
+    {"mfma_64x128x32_w2x2k2d", 4.27, 2.30, 1.9893, 1.7655},
+    {"mfma_64x64x32_w2x2k2d", 1.90, 3.53, 2.7001, 1.8506},
+    {"mfma_32x128x64_w1x4k2d", 2.71, 4.98, 2.2361, 1.8618},
+    {"mfma_32x64x64_w1x2k2d", 5.17, 2.49, 2.7631, 1.9155},
+    {"mfma16_128x64x32_w8x1k1d", 2.61, 4.06, 2.1476, 1.8057},
+    {"mfma16_64x128x32_w4x2k1d", 0.92, 5.31, 2.1907, 1.7932},
+    {"mfma16_64x64x64_w4x1k2d", 1.24, 4.14, 2.1442, 1.8001},
+    {"mfma16_64x64x64_w2x2k2d", 1.05, 3.96, 2.2426, 1.8103},
+    {"mfma16_64x64x32_w4x1k1d", 2.57, 2.03, 2.7560, 1.9233},
+    {"mfma16_64x16x64_w4x1k1d", 3.94, 0.00, 5.8194, 3.2452},
+    {"mfma16_32x128x64_w2x2k2d", 0.20, 4.99, 2.2661, 1.8105},
+    {"mfma16_32x64x128_w2x1k4d", 0.88, 5.66, 2.3716, 2.3479},
+    {"mfma16_32x64x64_w2x1k2d", 4.03, 1.07, 3.1605, 2.1120}, // 1000 x 1537 x 777 (a fringe column)
+    {"mfma16_32x32x128_w2x2k2d", 3.09, 2.02, 3.5613, 2.4795},
+    {"mfma16_32x32x64_w2x2k1d", 3.62, 0.93, 4.9384, 2.4736},
     {"mfma16_16x64x128_w1x1k4d", 5.14, 2.17, 4.0984, 3.0357},
-    {"mfma16_16x16x256_w1x1k4d", 2.71, 2.31, 12.8703, 4.1376},
-    {"mfma16_16x16x128_w1x1k4p2d", 4.83, 1.18, 3.0110, 4.2615},
-    {"mfma16_16x16x128_w1x1k4d", 3.08, 0.59, 14.8043, 4.4668},
-    {"mfma_32x96x64_w1x1k4d", 3.09, 5.34, 2.6664, 2.0092},
-    {"mfma16_32x96x32_w2x2k1d", 4.77, 0.57, 3.7008, 2.3108}, // GPT-2 QKV one short
-    {"mfma16_32x96x64_w2x2k2d", 1.92, 3.26, 2.7099, 2.1238},
-    {"mfma16_64x96x64_w4x2k1d", 2.13, 4.04, 2.3752, 2.0313},
-    {"mfma16_32x96x128_w2x2k4d", 2.11, 6.38, 2.1529, 2.2173}, // GPT-2 MLP-down one short
-    {"mfma16_64x64x128_w4x1k4d", 1.61, 6.29, 1.9046, 1.9373}, // long K (999 x 999 x 3999)
+    {"mfma16_16x16x256_w1x1k4d", 2.71, 2.32, 12.8062, 4.1227},
+    {"mfma16_16x16x128_w1x1k4p2d", 4.83, 1.18, 3.0145, 4.2636},
+    {"mfma16_16x16x128_w1x1k4d", 2.96, 0.69, 14.9652, 4.2246},
+    {"mfma_32x96x64_w1x1k4d", 3.03, 5.42, 2.6653, 1.9967},
+    {"mfma16_32x96x32_w2x2k1d", 4.79, 0.55, 3.7010, 2.3138}, // GPT-2 QKV one short
+    {"mfma16_32x96x64_w2x2k2d", 1.94, 3.24, 2.7101, 2.1268},
+    {"mfma16_64x96x64_w4x2k1d", 2.12, 4.06, 2.3739, 2.0297},
+    {"mfma16_32x96x128_w2x2k4d", 2.14, 6.34, 2.1533, 2.2237}, // GPT-2 MLP-down one short
+    {"mfma16_64x64x128_w4x1k4d", 1.60, 6.32, 1.9030, 1.9336}, // long K (999 x 999 x 3999)
 };
 // Strided-batched products (batch > 1, aligned or not) take their own short list,
 // fitted on batched shapes only (attention-like products: 12 to 48 heads of 1024 x 1024 x 16..256
@@ -408,9 +420,9 @@ const Candidate kSkCandidates[] = {
     {"sk_64x128x32_w2x2k2p2", 0.00, 12.80, 2.0335, 0.0000}, // long K, few tiles
 };
 const Candidate kSkUnalignedCandidates[] = {
-    {"sk_64x128x32_w2x2k2d", 15.24, 0.00, 2.0504, 1.7412}, // 1535^3, 2999^3
-    {"sk16_64x64x32_w4x1k1d", 11.80, 0.00, 2.7647, 1.9379},
-    {"sk16_32x64x64_w2x1k2d", 9.13, 1.23, 2.9775, 2.1131},
+    {"sk_64x128x32_w2x2k2d", 15.23, 0.00, 2.0518, 1.7418}, // 1535^3, 2999^3
+    {"sk16_64x64x32_w4x1k1d", 11.80, 0.00, 2.7649, 1.9380},
+    {"sk16_32x64x64_w2x1k2d", 9.13, 1.23, 2.9773, 2.1127},
 };
 constexpr int kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
 constexpr int kNumUnalignedCandidates = sizeof(kUnalignedCandidates) / sizeof(kUnalignedCandidates[0]);
@@ -420,8 +432,9 @@ constexpr int kNumSkUnalignedCandidates = sizeof(kSkUnalignedCandidates) / sizeo
 // A stream-K candidate is taken only when its modelled time, 3% longer, still beats the
 // data-parallel one: its shared tiles are the part of the model with the widest spread.
 constexpr double kSkMargin = 1.03;
-// Modelled time of a launch's fringe workgroups beyond its tiles (us).
-constexpr double kFringeUs = 2.0;
+// Modelled time of a launch's fringe workgroups beyond its tiles (us), per memory round
+// trip of one fringe workgroup and fixed.
+constexpr double kFringeTripUs = 1.0, kFringeFixedUs = 1.0;
 constexpr double kHbmBytesPerUs = 5.7e6;          // 5.7 TB/s for rows of 512 contiguous bytes
 constexpr double kHbmRowExponent = 0.19;
 constexpr double kL2BytesPerUs = 20.0e6;          // tile-fill bytes, 16-byte aligned rows
@@ -484,13 +497,13 @@ int choose_model(int M, int N, int K, bool vec, size_t ws_bytes, int cus, int ba
         if (table_ids[i] < 0)
             continue;
         const Config &c = kConfigs[table_ids[i]];
-        const int fringe = fringe_cols(c, M, N, batch);
+        const int fringe = fringe_cols(c, M, N, K, batch);
         const uint64_t tiles = main_tiles(c, M, N, fringe) * (uint64_t)batch;
         const uint64_t rounds = (tiles + kCUs - 1) / kCUs;
         const double units = (double)c.bm * c.bn / 4096.0;
         double us = cand.fixed_us + (double)rounds * cand.round_us +
                     (double)rounds * units * unit_mflop * (rounds >= 2 ? cand.us_many : cand.us_one) +
-                    (fringe > 0 ? kFringeUs : 0.0);
+                    (fringe > 0 ? kFringeFixedUs + kFringeTripUs * fringe_trips(c, K, fringe) : 0.0);
         const double mem = memory_us(c, M, N, K, batch, vec);
         us = us > mem ? us : mem;
         if (best < 0 || us < best_us) {
@@ -642,7 +655,7 @@ int run(int config, int opA, int opB, int M, int N, int K, float alpha, const fl
     const int cus = (ws != nullptr && batch == 1) ? device_cus() : 0;
     const int id = config >= 0 ? config : choose(M, N, K, vec, ws_bytes, cus, batch);
     const Config &c = kConfigs[id];
-    const int fringe = fringe_cols(c, M, N, batch, lda < kDmaMaxLd && ldb < kDmaMaxLd);
+    const int fringe = fringe_cols(c, M, N, K, batch, lda < kDmaMaxLd && ldb < kDmaMaxLd);
     const uint64_t tiles = tile_count(c, M, N);
     if ((c.kind == KIND_MFMA || c.kind == KIND_VALU) && grid_count(c, M, N, fringe) * (uint64_t)c.threads > 0xFFFFFFFFull)
         return SGEMM_ERROR_TOO_LARGE;
@@ -1088,7 +1101,7 @@ int sgemm_launch_shape(int config, int M, int N, int K, int grid[3], int block[3
         block[0] = c.threads; block[1] = 1; block[2] = 1;
         return 0;
     }
-    const uint64_t wgs = grid_count(c, M, N, fringe_cols(c, M, N, 1));
+    const uint64_t wgs = grid_count(c, M, N, fringe_cols(c, M, N, K, 1));
     if (wgs * (uint64_t)c.threads > 0xFFFFFFFFull) return SGEMM_ERROR_TOO_LARGE;
     grid[0] = (int)wgs; grid[1] = 1; grid[2] = 1;
     block[0] = c.threads; block[1] = 1; block[2] = 1;
