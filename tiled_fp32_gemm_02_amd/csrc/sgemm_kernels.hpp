@@ -1116,11 +1116,11 @@ __device__ __forceinline__ void fringe_columns(const GemmArgs &p, int f, float *
             const int kc = k < K ? k : K - 1;
             if constexpr (TA) {
                 const float *ak = A + (int64_t)kc * lda;
-                if (full) {
-                    const floatx4u x = *reinterpret_cast<const floatx4u *>(ak + m0);
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        a[u][g] = x[g];
+                if (full) {     // the G rows m0.. in one load of exactly G floats
+                    static_assert(G == 2, "one two-float load per k");
+                    const floatx2u x = *reinterpret_cast<const floatx2u *>(ak + m0);
+                    a[u][0] = x[0];
+                    a[u][1] = x[1];
                 } else {
 #pragma unroll
                     for (int g = 0; g < G; ++g)
