@@ -231,7 +231,7 @@ constexpr uint64_t kFringeMinTiles = 256;
 // Memory round trips of one fringe workgroup: its NT threads take 64 (NT / 64) U k per trip,
 // U the k steps in flight per thread in fringe_columns (4 for up to 2 columns, 2 for 3-4, 1
 // for 5-8; the kernel sets them to keep its registers low). Long K with many columns costs
-// many trips: 999 x 999 x 3999 with 7 columns ran 13-36% slower on 16- and 32-wide tiles
+// many trips: 999 x 999 x 3999 with 7 columns ran 7-36% slower on 16- and 32-wide tiles
 // with the fringe (16 trips) than without, while one column at K = 777 (one trip) saved up to
 // 39%. So the fringe is taken for at most kFringeMaxTrips.
 constexpr int kFringeMaxTrips = 3;
