@@ -980,9 +980,11 @@ struct MfmaTile {
         // row at a time: all of the block's reads of C are issued before the first is used,
         // so the block waits out one memory round trip (two with EB = 8) rather than one per
         // entry. C is written with non-temporal stores: this kernel never reads it back, and
-        // streamed out it leaves the L2 to the operand panels other tiles still read (2-4%
-        // faster on the GPT-2 layers and on attention's scores; the same at 4096^3). Lane columns: TN consecutive ones (interleaved blocks), or one per MB-column
-        // block (side by side). Rows: those of accumulator element e, see MfmaBlock.
+        // streamed out it leaves the L2 to the operand panels other tiles still read (back to
+        // back 2-5% faster on the GPT-2 layers and attention's scores, the same at 4096^3, 1%
+        // slower on the ragged 1000 x 1537 x 777). Lane columns: TN consecutive ones
+        // (interleaved blocks), or one per MB-column block (side by side). Rows: those of
+        // accumulator element e, see MfmaBlock.
         const float alpha = p.alpha, beta = p.beta;
         const float *bias = p.bias;
         const int act = p.act;
