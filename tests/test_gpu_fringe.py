@@ -9,6 +9,8 @@ of the fringe columns and of the last whole column before them, and a random sam
 rest. Row-stride gaps and guard bands hold NaN, so a load outside the matrices would show; A
 and B must be untouched, and C outside its window too. The launch shape is checked to be the
 fringe one, so a change of rule cannot silently route these cases around the fringe path.
+Further cases: batched products, long K against the full oracle, and M and K multiples of the
+tile on aligned rows, where the tiles beside the fringe run the kernel without edge tests.
 """
 
 import numpy as np
@@ -157,3 +159,41 @@ def test_fringe_columns_long_k_workload_shape():
         ref, bound = oracle.gemm(0, 0, M, N, K, 1.0, a, K, b, N, 0.0, c, N)
         ok, worst, idx = oracle.within_bound(out, ref, bound)
         assert ok, (name, worst, idx, out[idx], ref[idx])
+
+
+@pytest.mark.parametrize("opA,opB", OPS)
+def test_fringe_columns_beside_whole_tiles(opA, opB):
+    """M and K multiples of the tile and 4 or 8 columns over on 16-byte aligned rows: the tiles
+    run the whole-tile kernel (no edge tests; the grid stops at column N - r, a multiple of BN)
+    and the fringe workgroups the last columns. Every configuration and operand form, checked
+    as above."""
+    import torch
+    import tiled_fp32_gemm_02_amd as sg
+    for n, cid in enumerate(matrix_configs()):
+        bm, bn, threads = tile_of(cid)
+        bk = int(sg.describe(cid)["tile"].split("x")[2])
+        r = (4, 8)[n % 2]
+        steps = 2 if r == 4 else 1
+        K = bk * max(1, min(4, 3 * threads * steps // bk))
+        M, N = 16 * bm, 16 * bn + r
+        st, grid, _ = sg.sgemm_launch_shape(cid, M, N, K)
+        assert st == 0 and grid[0] == 256 + M // 2, (cid, grid)
+        rng = np.random.default_rng(7 * cid + 100 * opA + 1000 * opB)
+        a, b, c = draw(rng, (M, K), "normal"), draw(rng, (K, N), "normal"), draw(rng, (M, N), "uniform")
+        bias = draw(rng, (N,), "normal") if n % 3 == 0 else None
+        As, Bs = stored(opA, a), stored(opB, b)
+        lda, ldb, ldc = As.shape[1] + 4, Bs.shape[1] + 8, N + 4
+        say(f"fringe beside whole tiles: config {cid} op {opA}{opB} {M}x{N}x{K} r {r}")
+        dA = DevMatrix(As, As.shape[0], As.shape[1], lda, 0, gap=np.nan)
+        dB = DevMatrix(Bs, Bs.shape[0], Bs.shape[1], ldb, 0, gap=np.nan)
+        dC = DevMatrix(c, M, N, ldc, 0, gap=np.nan)
+        dbias = torch.from_numpy(bias).cuda() if bias is not None else None
+        st = sg.sgemm_general(cid, opA, opB, M, N, K, 0.5, dA.ptr, lda, dB.ptr, ldb, 1.5, dC.ptr, ldc, dbias, 0,
+                              torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        flat = dC.fetch()
+        assert st == 0, (cid, st)
+        assert dA.unchanged() and dB.unchanged() and dC.outside_unchanged(flat), cid
+        out = dC.window(flat)
+        rows, cols = fringe_samples(rng, M, N, r)
+        check_entries(out, opA, opB, M, N, K, 0.5, As, Bs, 1.5, c, bias, 0, rows, cols, cid)
