@@ -410,8 +410,10 @@ int sgemm_select_config(int M, int N, int K, float alpha,
  * Writes grid[3] and block[3] (dim3 order x, y, z). Data-parallel matrix configurations
  * launch one workgroup per BM x BN tile; when N mod BN = r is 1..8, the whole tiles
  * number at least 256 (over the batch, in a batched call; the shape reported here is for
- * one product) and K is at most 3 x 64 x (threads / 64) x U (U = 4 for r <= 2, 2 for r <= 4,
- * 1 for r <= 8), the tiles stop at column N - r and ceil(M / 2) more workgroups follow them,
+ * one product) and the fringe workgroups' memory round trips, ceil(K / (64 x (threads / 64) x U))
+ * (U = 4 for r <= 2, 2 for r <= 4, 1 for r <= 8), times the rounds they run in (ceil(M / 2) of
+ * them over 256 CUs, as many per CU as the configuration's LDS and 32 waves allow), are at most
+ * 3, the tiles stop at column N - r and ceil(M / 2) more workgroups follow them,
  * each computing two rows of the last r columns (fringe columns; they also require row
  * strides under 2^20 floats, which this query, having no strides, assumes). Stream-K
  * configurations launch one

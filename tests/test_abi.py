@@ -626,10 +626,16 @@ def test_launch_shape_fringe_columns():
     assert sg.sgemm_launch_shape(c64, 1023, 1025, 777)[1][0] == 16 * 16 + 512
     c32 = names.index("mfma16_32x64x64_w2x1k2d")
     assert sg.sgemm_launch_shape(c32, 1000, 1537, 777)[1][0] == 32 * 24 + 500
-    # a grid that its fringe workgroups would take past 2^32 threads keeps the plain tiles
+    # a tall product whose fringe workgroups would run in many rounds (or pass 2^32 threads)
+    # keeps the plain tiles
     tall = 1 << 25
     assert sg.sgemm_launch_shape(c64, tall, 65, 64) == (0, ((tall // 64) * 2, 1, 1), (256, 1, 1))
-    assert sg.sgemm_launch_shape(c64, 1 << 21, 65, 64)[1][0] == (1 << 15) + (1 << 20)
+    assert sg.sgemm_launch_shape(c64, 1 << 21, 65, 64)[1][0] == (1 << 15) * 2
+    # the 256 x 256 tile holds 128 KiB of LDS, one workgroup per CU, fringe ones included: 2048
+    # fringe workgroups would run in eight rounds, 256 of them in one
+    big = names.index("mfma_256x256x32_w2x4d")
+    assert sg.sgemm_launch_shape(big, 4096, 4100, 1024)[1][0] == 16 * 17
+    assert sg.sgemm_launch_shape(big, 512, 128 * 256 + 4, 1024)[1][0] == 256 + 256
     sk = names.index("sk16_64x64x32_w4x1k1d")
     assert sg.sgemm_launch_shape(sk, 1000, 1537, 777)[1][0] == 256 + 256    # 400 tiles: 256 whole, 144 shared
     valu = names.index("valu_128x128x8_t8x8")

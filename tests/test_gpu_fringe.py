@@ -3,7 +3,8 @@
 When N mod BN = r is 1..8 and the whole tiles number at least 256 (over the batch), the tile
 grid stops at column N - r and extra workgroups compute the last r columns, two rows of C
 each, their threads splitting K. These cases run every data-parallel matrix configuration in every
-operand form on a shape of 16 x 16 whole tiles plus r fringe columns, with the full epilogue
+operand form on a shape of 2 x 128 whole tiles plus r fringe columns (fewer than 256 fringe
+workgroups, so one round of them even where one workgroup fills a CU's LDS), with the full epilogue
 (alpha, beta, and on some of them a bias and the GELU), and check against the oracle every row
 of the fringe columns and of the last whole column before them, and a random sample of the
 rest. Row-stride gaps and guard bands hold NaN, so a load outside the matrices would show; A
@@ -74,7 +75,7 @@ def test_fringe_columns_every_configuration(opA, opB):
         r = FRINGES[n % len(FRINGES)]
         # K ragged and within the three memory round trips a fringe workgroup may take
         steps = 4 if r <= 2 else 2 if r <= 4 else 1
-        M, N, K = 16 * bm - 3, 16 * bn + r, min((45, 300, 1100)[n % 3], 3 * threads * steps - 5)
+        M, N, K = 2 * bm - 3, 128 * bn + r, min((45, 300, 1100)[n % 3], 3 * threads * steps - 5)
         st, grid, _ = sg.sgemm_launch_shape(cid, M, N, K)
         assert st == 0 and grid[0] == 256 + -(-M // 2), (cid, grid)
         rng = np.random.default_rng(cid + 100 * opA + 1000 * opB)
@@ -175,7 +176,7 @@ def test_fringe_columns_beside_whole_tiles(opA, opB):
         r = (4, 8)[n % 2]
         steps = 2 if r == 4 else 1
         K = bk * max(1, min(4, 3 * threads * steps // bk))
-        M, N = 16 * bm, 16 * bn + r
+        M, N = 2 * bm, 128 * bn + r
         st, grid, _ = sg.sgemm_launch_shape(cid, M, N, K)
         assert st == 0 and grid[0] == 256 + M // 2, (cid, grid)
         rng = np.random.default_rng(7 * cid + 100 * opA + 1000 * opB)

@@ -234,21 +234,38 @@ constexpr uint64_t kFringeMinTiles = 256;
 // many trips: 999 x 999 x 3999 with 7 columns ran 7-36% slower on 16- and 32-wide tiles
 // with the fringe (16 trips) than without, while one column at K = 777 (one trip) saved up to
 // 39%. So the fringe is taken for at most kFringeMaxTrips.
+// The fringe workgroups hold the kernel's LDS as its tiles do, so a CU runs as many of them
+// at once as of the tiles: with 128 KiB tiles (256 x 256, 64 x 64 x 128) one, and then the
+// ceil(M / 2) fringe workgroups of a tall product run in several rounds after the tiles (3072 x
+// 3080 x 3072 on the 64 x 64 x 128 tile: six rounds, 516 us against 438 for 3072^3). The limit
+// is on trips x rounds.
 constexpr int kFringeMaxTrips = 3;
 int fringe_trips(const Config &c, int K, int r)
 {
     const int steps = r <= 2 ? 4 : r <= 4 ? 2 : 1;
     return (int)cdiv64(K, 64 * (c.threads / 64) * steps);
 }
+uint64_t fringe_rounds(const Config &c, int M, int batch)
+{
+    constexpr int kLdsPerCu = 160 * 1024, kWavesPerCu = 32, kCUs = 256;
+    const int by_lds = c.lds_bytes > 0 ? kLdsPerCu / c.lds_bytes : kWavesPerCu;
+    const int by_waves = kWavesPerCu / (c.threads / 64);
+    int per_cu = by_lds < by_waves ? by_lds : by_waves;
+    per_cu = per_cu > 0 ? per_cu : 1;
+    const uint64_t slots = (uint64_t)kCUs * per_cu;
+    return (cdiv64(M, sgemm_impl::kFringeRows) * (uint64_t)batch + slots - 1) / slots;
+}
 int fringe_cols(const Config &c, int M, int N, int K, int batch, bool ld_ok = true)
 {
     if (c.kind != KIND_MFMA || N < c.bn || !ld_ok)
         return 0;
     const int r = N % c.bn;
-    if (r == 0 || r > sgemm_impl::kFringeCols || fringe_trips(c, K, r) > kFringeMaxTrips)
+    if (r == 0 || r > sgemm_impl::kFringeCols)
         return 0;
     const uint64_t whole = cdiv64(M, c.bm) * (uint64_t)(N / c.bn);
     if (whole * (uint64_t)batch < kFringeMinTiles)
+        return 0;
+    if ((uint64_t)fringe_trips(c, K, r) * fringe_rounds(c, M, batch) > (uint64_t)kFringeMaxTrips)
         return 0;
     // ceil(M / kFringeRows) more workgroups: a grid that would then pass one launch's
     // 2^32 threads keeps its plain column of edge tiles instead
@@ -432,8 +449,8 @@ constexpr int kNumSkUnalignedCandidates = sizeof(kSkUnalignedCandidates) / sizeo
 // A stream-K candidate is taken only when its modelled time, 3% longer, still beats the
 // data-parallel one: its shared tiles are the part of the model with the widest spread.
 constexpr double kSkMargin = 1.03;
-// Modelled time of a launch's fringe workgroups beyond its tiles (us), per memory round
-// trip of one fringe workgroup and fixed.
+// Modelled time of a launch's fringe workgroups beyond its tiles (us): fixed, and per memory
+// round trip of one fringe workgroup and round of fringe workgroups.
 constexpr double kFringeTripUs = 1.0, kFringeFixedUs = 1.0;
 constexpr double kHbmBytesPerUs = 5.7e6;          // 5.7 TB/s for rows of 512 contiguous bytes
 constexpr double kHbmRowExponent = 0.19;
@@ -503,7 +520,8 @@ int choose_model(int M, int N, int K, bool vec, size_t ws_bytes, int cus, int ba
         const double units = (double)c.bm * c.bn / 4096.0;
         double us = cand.fixed_us + (double)rounds * cand.round_us +
                     (double)rounds * units * unit_mflop * (rounds >= 2 ? cand.us_many : cand.us_one) +
-                    (fringe > 0 ? kFringeFixedUs + kFringeTripUs * fringe_trips(c, K, fringe) : 0.0);
+                    (fringe > 0 ? kFringeFixedUs + kFringeTripUs * fringe_trips(c, K, fringe) *
+                                      (double)fringe_rounds(c, M, batch) : 0.0);
         const double mem = memory_us(c, M, N, K, batch, vec);
         us = us > mem ? us : mem;
         if (best < 0 || us < best_us) {
